@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for the DeMo momentum codec.
+
+This module is shared by the CPU oracle side (tests, cpu baseline) and the
+HIP side (tests, bench, smoke).  It holds no step of the codec itself: only
+the workload descriptions (tensor shapes and hyper-parameters) and the
+seeded random draws that stand in for gradients, initial parameters and the
+Gaussian matrices of the random-projection variant.
+
+Workloads stand in for the pages' OLMo-300M / OLMo-1B training runs on
+Dolma ("DeMo: Decoupled Momentum Optimization", §5 Experimental Analysis,
+Evaluation Methodology): no dataset or trained weight is used; gradients are
+i.i.d. Gaussian draws of the stated spread, every tensor of a set is drawn
+from its own stream.
+
+Seeding: every array comes from PCG64 seeded with
+``SeedSequence([config_id, role, worker, step, tensor])`` where role 0 is a
+gradient, role 1 the initial parameters and role 2 a projection draw.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+ROLE_GRAD = 0
+ROLE_PARAM = 1
+ROLE_BASIS = 2
+
+PHI_SIGN = "sign"
+PHI_IDENTITY = "identity"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One workload: a tensor list plus the codec hyper-parameters."""
+
+    name: str
+    config_id: int
+    shapes: Tuple[Tuple[int, ...], ...]
+    grad_std: float
+    grad_bf16: bool
+    beta: float
+    alpha: float
+    k: int
+    workers: int
+    phi: str
+    eta: float
+    lam: float
+    steps: int
+    param_std: float = 0.02
+    random_basis: bool = False
+
+    @property
+    def n_params(self) -> int:
+        return int(sum(int(np.prod(s)) for s in self.shapes))
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _olmo_block(d: int) -> List[Tuple[int, ...]]:
+    # QKV, attention out, MLP up, MLP down, two norm vectors
+    return [(d, 3 * d), (d, d), (d, 4 * d), (4 * d, d), (d,), (d,)]
+
+
+def _olmo_set(d: int, blocks: int) -> Tuple[Tuple[int, ...], ...]:
+    out: List[Tuple[int, ...]] = []
+    for _ in range(blocks):
+        out.extend(_olmo_block(d))
+    return tuple(out)
+
+
+WORKLOADS = {
+    # one 256x256 fp32 weight, 16 chunks
+    "tiny_256": Workload("tiny_256", 1, ((256, 256),), 1e-3, False,
+                         0.999, 0.2, 8, 2, PHI_SIGN, 1e-3, 0.01, 10),
+    # one 4096x4096 weight, gradients drawn then rounded to bf16
+    "single_4096": Workload("single_4096", 2, ((4096, 4096),), 1e-2, True,
+                            0.999, 0.2, 8, 4, PHI_SIGN, 1e-3, 0.01, 20),
+    # OLMo-300M-shaped set: 24 blocks at d=1024 (302,039,040 parameters)
+    "olmo_300m": Workload("olmo_300m", 3, _olmo_set(1024, 24), 1e-3, False,
+                          0.999, 0.2, 8, 8, PHI_SIGN, 1e-3, 0.01, 3),
+    # OLMo-1B-shaped set: 16 blocks at d=2048 (805,371,904 parameters)
+    "olmo_1b": Workload("olmo_1b", 4, _olmo_set(2048, 16), 1e-3, False,
+                        0.999, 0.5, 32, 16, PHI_IDENTITY, 1e-3, 0.01, 3),
+    # padded chunks, 1-D vectors of awkward lengths, extreme k
+    "edge_mix": Workload("edge_mix", 5, ((1000, 777), (3, 5000), (777,), (1000,), (64,), (1,)),
+                         1e-3, False, 0.999, 0.2, 1, 4, PHI_SIGN, 1e-3, 0.01, 3),
+}
+
+
+def rng(config_id: int, role: int, worker: int, step: int, tensor: int) -> np.random.Generator:
+    ss = np.random.SeedSequence([int(config_id), int(role), int(worker), int(step), int(tensor)])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), returned as float32."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> 16) & 1
+    b = (b + 0x7FFF + lsb) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def gradient(w: Workload, worker: int, step: int, tensor: int) -> np.ndarray:
+    """Worker ``worker``'s gradient of tensor ``tensor`` at ``step`` (float32)."""
+    shape = w.shapes[tensor]
+    g = rng(w.config_id, ROLE_GRAD, worker, step, tensor).standard_normal(shape, dtype=np.float32)
+    g *= np.float32(w.grad_std)
+    if w.grad_bf16:
+        g = round_to_bf16(g)
+    return g
+
+
+def initial_params(w: Workload, tensor: int) -> np.ndarray:
+    shape = w.shapes[tensor]
+    x = rng(w.config_id, ROLE_PARAM, 0, 0, tensor).standard_normal(shape, dtype=np.float32)
+    return x * np.float32(w.param_std)
+
+
+def gaussian_matrix(w: Workload, step: int, which: int, s: int = 64) -> np.ndarray:
+    """Fresh N(0, 1) s x s draw for the random-projection variant (float64).
+
+    The same draw is used by every worker at a step; ``which`` is 0 for the
+    dimension-0 matrix and 1 for the dimension-1 matrix.
+    """
+    return rng(w.config_id, ROLE_BASIS, which, step, 0).standard_normal((s, s))

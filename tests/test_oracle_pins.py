@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a closed form, a library routine
+(SciPy's DCT, NumPy's QR), brute force over every index subset on tiny
+chunks, or a number the pages print (tests/golden/pages_numbers.json).
+They are chosen so that a dropped term, a flipped sign, a wrong index or a
+transposed operand in the oracle fails at least one of them.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.fft
+
+from oracle import demo_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------- P1/P2/P3: the basis
+
+@pytest.mark.parametrize("s", [2, 4, 8, 64, 128])
+def test_dct_basis_is_scipy_orthonormal_dct2(s):
+    P = O.dct_basis(s)
+    assert np.abs(P @ P.T - np.eye(s)).max() < 1e-13
+    assert np.abs(P.T @ P - np.eye(s)).max() < 1e-13
+    ref = scipy.fft.dct(np.eye(s), type=2, norm="ortho", axis=0)
+    assert np.abs(P - ref).max() < 1e-14
+
+
+def test_project_matches_scipy_dctn_and_idctn():
+    rng = _rng(1)
+    P = O.dct_basis(64)
+    B = rng.standard_normal((5, 64, 64))
+    Q = O.project(B, P, P)
+    assert np.abs(Q - scipy.fft.dctn(B, type=2, norm="ortho", axes=(1, 2))).max() < 1e-12
+    assert np.abs(O.unproject(Q, P, P) - scipy.fft.idctn(Q, type=2, norm="ortho", axes=(1, 2))).max() < 1e-12
+    b = rng.standard_normal((7, 64))
+    q = O.project(b, P, P)
+    assert np.abs(q - scipy.fft.dct(b, type=2, norm="ortho", axis=1)).max() < 1e-12
+    assert np.abs(O.unproject(q, P, P) - b).max() < 1e-12
+
+
+def test_round_trip_exact_in_fp64():
+    rng = _rng(2)
+    P = O.dct_basis(64)
+    B = rng.standard_normal((3, 64, 64)) * 1e-3
+    R = O.unproject(O.project(B, P, P), P, P)
+    assert np.abs(R - B).max() <= 1e-13 * np.abs(B).max()
+
+
+def test_parseval_per_chunk_including_padded_chunks():
+    rng = _rng(3)
+    T = rng.standard_normal((1000, 777))
+    P = O.dct_basis(64)
+    C = O.split_chunks(T)
+    Q = O.project(C, P, P)
+    nb = np.sqrt((C ** 2).sum(axis=(1, 2)))
+    nq = np.sqrt((Q ** 2).sum(axis=(1, 2)))
+    assert np.abs(nb - nq).max() <= 1e-12 * nb.max()
+    assert abs(np.sqrt((nq ** 2).sum()) - np.linalg.norm(T)) <= 1e-10 * np.linalg.norm(T)
+
+
+# --------------------------------------------------------------------------- chunking
+
+def test_chunk_layout_row_major_with_zero_padding():
+    T = np.arange(130 * 200, dtype=np.float64).reshape(130, 200)
+    C = O.split_chunks(T)
+    assert C.shape == (3 * 4, 64, 64)
+    # chunk (1, 2) starts at row 64, column 128
+    assert C[1 * 4 + 2, 0, 0] == T[64, 128]
+    assert C[1 * 4 + 2, 5, 7] == T[69, 135]
+    # last chunk (2, 3): rows 128..129, columns 192..199 valid, rest zero
+    last = C[2 * 4 + 3]
+    assert last[1, 7] == T[129, 199]
+    assert np.all(last[2:, :] == 0) and np.all(last[:, 8:] == 0)
+    assert np.array_equal(O.merge_chunks(C, T.shape), T)
+    v = np.arange(130, dtype=np.float64)
+    c1 = O.split_chunks(v)
+    assert c1.shape == (3, 64) and c1[2, 1] == 129 and np.all(c1[2, 2:] == 0)
+    assert np.array_equal(O.merge_chunks(c1, v.shape), v)
+
+
+# --------------------------------------------------------------------------- P4: payload sizes
+
+def test_payload_ratio_matches_printed_per_chunk_compression():
+    gold = json.load(open(GOLDEN))
+    for row in gold["per_chunk_compression"]:
+        s, k = row["s"], row["k"]
+        n = O.payload_entries([(s, s)], k, s)
+        assert n == k
+        assert (s * s) / n == row["ratio"]
+    # sum over chunks of keff, clamped per chunk kind
+    shapes = [(1000, 777), (3, 5000), (777,), (1,)]
+    grids = [16 * 13, 1 * 79, 13, 1]
+    assert O.payload_entries(shapes, 8) == 8 * (grids[0] + grids[1]) + 8 * (grids[2] + grids[3])
+    assert O.payload_entries(shapes, 4096) == 4096 * (grids[0] + grids[1]) + 64 * (grids[2] + grids[3])
+
+
+# --------------------------------------------------------------------------- momentum update
+
+def test_momentum_half_life_printed_on_the_page():
+    gold = json.load(open(GOLDEN))["momentum_half_life"]
+    beta = gold["beta"]
+    G = np.ones((4,))
+    M = O.momentum_update(np.zeros(4), G, beta)          # impulse at step 0
+    M0 = M.copy()
+    for _ in range(gold["steps"]):
+        M = O.momentum_update(M, np.zeros(4), beta)
+    assert M0[0] == pytest.approx(1.0 - beta)
+    assert M[0] / M0[0] == pytest.approx(gold["weight"], rel=2e-3)
+
+
+@pytest.mark.parametrize("plain", [False, True])
+def test_ddp_equivalence_closed_form_lossless_alpha0(plain):
+    """k = numel, alpha = 0: M_t has the EMA's closed form and M* is the workers' mean."""
+    beta, steps, W = 0.9, 5, 3
+    rng = _rng(4)
+    G = rng.standard_normal((64, 128)).astype(np.float32)
+    Ms = [np.zeros_like(G) for _ in range(W)]
+    for _ in range(steps):
+        outs = [O.encode(Ms[w], G, beta=beta, alpha=0.0, k=4096, plain=plain) for w in range(W)]
+        Ms = [o["M"] for o in outs]
+    closed = ((1 - beta ** steps) / (1 - beta) if plain else (1 - beta ** steps)) * G.astype(np.float64)
+    for w in range(W):
+        assert np.abs(Ms[w] - closed).max() <= 1e-6 * np.abs(closed).max()
+    vals = np.stack([o["values"] for o in outs])
+    idx = np.stack([o["idx"] for o in outs])
+    X = np.zeros_like(G)
+    dec = O.decode_apply(X, vals, idx, phi="identity", eta=1.0, lam=0.0)
+    assert np.abs(dec["Mstar"] - closed).max() <= 1e-6 * np.abs(closed).max()
+    assert np.abs(dec["X"] + closed).max() <= 1e-6 * np.abs(closed).max()
+
+
+def test_mean_of_local_momenta_is_momentum_of_mean_gradient():
+    beta, W, steps = 0.99, 4, 6
+    rng = _rng(5)
+    Ms = [np.zeros(50) for _ in range(W)]
+    Mg = np.zeros(50)
+    for _ in range(steps):
+        Gs = [rng.standard_normal(50) for _ in range(W)]
+        Ms = [O.momentum_update(Ms[w], Gs[w], beta) for w in range(W)]
+        Mg = O.momentum_update(Mg, np.mean(Gs, axis=0), beta)
+    assert np.abs(np.mean(Ms, axis=0) - Mg).max() < 1e-14
+
+
+# --------------------------------------------------------------------------- P5: lossless, subtraction
+
+@pytest.mark.parametrize("shape", [(64, 64), (130, 70), (100,), (1, 1)])
+def test_lossless_alpha1_leaves_zero_residual(shape):
+    rng = _rng(6)
+    M = rng.standard_normal(shape).astype(np.float32)
+    G = rng.standard_normal(shape).astype(np.float32)
+    out = O.encode(M, G, beta=0.9, alpha=1.0, k=4096)
+    Mp = O.momentum_update(M, G, 0.9)
+    assert np.abs(out["M"]).max() <= 1e-13 * np.abs(Mp).max()
+    half = O.encode(M, G, beta=0.9, alpha=0.5, k=4096)
+    assert np.abs(half["M"] - 0.5 * Mp).max() <= 1e-6 * np.abs(Mp).max()
+
+
+def test_subtraction_decay_printed_on_the_page():
+    gold = json.load(open(GOLDEN))["subtraction_decay"]
+    rng = _rng(7)
+    M = rng.standard_normal((64, 64)).astype(np.float32)
+    beta = 0.999
+    out = O.encode(M, np.zeros_like(M), beta=beta, alpha=gold["alpha"], k=4096)
+    assert np.abs(out["M"] - gold["kept_fraction"] * beta * M).max() <= 1e-6 * np.abs(M).max()
+
+
+def test_lossless_decode_is_mean_of_worker_momenta():
+    rng = _rng(8)
+    W = 3
+    Mps, vals, idxs = [], [], []
+    for w in range(W):
+        M = rng.standard_normal((70, 64)).astype(np.float32)
+        G = rng.standard_normal((70, 64)).astype(np.float32)
+        o = O.encode(M, G, beta=0.5, alpha=1.0, k=4096)
+        Mps.append(O.momentum_update(M, G, 0.5))
+        vals.append(o["values"])
+        idxs.append(o["idx"])
+    X = rng.standard_normal((70, 64)).astype(np.float32)
+    d = O.decode_apply(X, np.stack(vals), np.stack(idxs), phi="identity", eta=0.1, lam=0.0)
+    mean = np.mean(Mps, axis=0)
+    assert np.abs(d["Mstar"] - mean).max() <= 1e-6 * np.abs(mean).max()
+    assert np.abs(d["X"] - (X - 0.1 * mean)).max() <= 1e-6
+
+
+# --------------------------------------------------------------------------- P7: top-k error bound and optimality
+
+def test_topk_error_bound_and_optimality():
+    rng = _rng(9)
+    P = O.dct_basis(64)
+    B = rng.standard_normal((6, 64, 64))
+    Q = O.project(B, P, P)
+    for k in (1, 8, 32, 500):
+        S = O.select_topk(Q.reshape(6, -1), k)
+        for c in range(6):
+            q = Q[c].ravel()
+            qh = np.zeros_like(q)
+            qh[S[c]] = q[S[c]]
+            err = np.linalg.norm(q - qh)
+            assert err <= np.sqrt(1 - k / 4096) * np.linalg.norm(q) + 1e-12
+            # any other k-subset leaves at least as large a residual
+            for _ in range(20):
+                T = rng.choice(4096, size=k, replace=False)
+                other = np.zeros_like(q)
+                other[T] = q[T]
+                assert np.linalg.norm(q - other) >= err - 1e-12
+
+
+# --------------------------------------------------------------------------- P8: brute force on tiny chunks
+
+def _brute_force_set(B, P, keff):
+    """Lowest-residual keff-subset, lexicographically smallest among (near) equal residuals."""
+    Q = O.project(B[None], P, P)[0]
+    numel = Q.size
+    best, best_sets = None, []
+    for S in itertools.combinations(range(numel), keff):
+        qh = np.zeros(numel)
+        qh[list(S)] = Q.ravel()[list(S)]
+        r = np.linalg.norm(B - O.unproject(qh.reshape(Q.shape)[None], P, P)[0])
+        if best is None or r < best - 1e-12:
+            best, best_sets = r, [S]
+        elif abs(r - best) <= 1e-12:
+            best_sets.append(S)
+    return min(best_sets)
+
+
+@pytest.mark.parametrize("s", [2, 4])
+@pytest.mark.parametrize("ndim", [1, 2])
+def test_topk_equals_brute_force_on_tiny_chunks(s, ndim):
+    rng = _rng(10 + s + ndim)
+    P = O.dct_basis(s)
+    numel = s if ndim == 1 else s * s
+    shape = (s,) if ndim == 1 else (s, s)
+    cases = [rng.standard_normal(shape) for _ in range(4)]
+    # exact ties: a chunk whose coefficients are +-1, +-1, 0.5, ... in a fixed pattern
+    Qd = np.zeros(numel)
+    Qd[::2] = 1.0
+    Qd[1::3] = -1.0
+    cases.append(O.unproject(Qd.reshape(shape)[None], P, P)[0])
+    cases.append(np.zeros(shape))
+    for B in cases:
+        Q = O.project(B[None], P, P).reshape(1, numel)
+        for keff in range(1, numel + 1):
+            if numel == 16 and keff > 6:
+                continue
+            S = O.select_topk(Q, keff)[0]
+            assert tuple(S) == _brute_force_set(B, P, keff)
+
+
+def test_full_encode_at_s4_matches_brute_force_residual():
+    rng = _rng(20)
+    s, k, alpha, beta = 4, 3, 0.3, 0.9
+    P = O.dct_basis(s)
+    M = rng.standard_normal((6, 9)).astype(np.float32)
+    G = rng.standard_normal((6, 9)).astype(np.float32)
+    out = O.encode(M, G, beta=beta, alpha=alpha, k=k, P0=P, P1=P, s=s)
+    Mp = O.split_chunks(beta * M.astype(np.float64) + (1 - beta) * G.astype(np.float64), s)
+    expect = []
+    for c in range(Mp.shape[0]):
+        S = _brute_force_set(Mp[c], P, k)
+        assert tuple(out["idx"][c]) == S
+        Q = O.project(Mp[c][None], P, P)[0].ravel()
+        qh = np.zeros(s * s)
+        qh[list(S)] = Q[list(S)]
+        expect.append(Mp[c] - alpha * O.unproject(qh.reshape(s, s)[None], P, P)[0])
+    ref = O.merge_chunks(np.stack(expect), M.shape, s)
+    assert np.abs(out["M"] - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+# --------------------------------------------------------------------------- P9/P10: closed-form chunks
+
+def test_single_basis_function_chunk():
+    P = O.dct_basis(64)
+    u, v, c = 5, 17, 0.75
+    B = c * np.outer(P[u], P[v])
+    out = O.encode(np.zeros((64, 64), np.float32), B.astype(np.float32), beta=0.0, alpha=1.0, k=1)
+    assert out["idx"][0, 0] == u * 64 + v
+    assert out["values"][0, 0] == pytest.approx(c, rel=1e-6)
+    assert np.abs(out["M"]).max() < 1e-7
+
+
+def test_nonsymmetric_basis_pair_is_not_transposed():
+    """With P0 != P1, B = c * P0[u]^T P1[v] must land at (u, v), not (v, u)."""
+    rng = _rng(21)
+    P0 = O.orthonormal_rows(rng.standard_normal((64, 64)))
+    P1 = O.orthonormal_rows(rng.standard_normal((64, 64)))
+    u, v, c = 3, 40, -2.0
+    B = c * np.outer(P0[u], P1[v])
+    Q = O.project(B[None], P0, P1)[0]
+    expect = np.zeros((64, 64))
+    expect[u, v] = c
+    assert np.abs(Q - expect).max() < 1e-12
+    out = O.encode(np.zeros((64, 64), np.float32), B.astype(np.float32), beta=0.0, alpha=0.5, k=1, P0=P0, P1=P1)
+    assert out["idx"][0, 0] == u * 64 + v
+    assert np.abs(out["M"] - 0.5 * B).max() < 1e-6
+
+
+def test_constant_chunk_dc_coefficient():
+    P = O.dct_basis(64)
+    c = 0.3
+    Q = O.project(np.full((1, 64, 64), c), P, P)[0]
+    assert Q[0, 0] == pytest.approx(64 * c, rel=1e-13)
+    assert np.abs(Q.ravel()[1:]).max() < 1e-13
+    q = O.project(np.full((1, 64), c), P, P)[0]
+    assert q[0] == pytest.approx(8 * c, rel=1e-13)
+
+
+def test_all_zero_chunk_payload_and_decode():
+    Z = np.zeros((64, 128), np.float32)
+    out = O.encode(Z, Z, beta=0.9, alpha=0.2, k=5)
+    assert np.array_equal(out["idx"], np.tile(np.arange(5, dtype=np.uint16), (2, 1)))
+    assert np.all(out["values"] == 0)
+    X = _rng(22).standard_normal((64, 128)).astype(np.float32)
+    d = O.decode_apply(X, out["values"][None], out["idx"][None], phi="sign", eta=1e-3, lam=0.01)
+    assert np.all(d["Mstar"] == 0)
+    assert np.array_equal(d["X"], (X.astype(np.float64) * (1 - 1e-3 * 0.01)).astype(np.float32))
+
+
+# --------------------------------------------------------------------------- P11: aggregation modes
+
+def test_aggregation_modes():
+    v = np.array([[[1.0, 2.0, 3.0]]], np.float32)
+    i = np.array([[[0, 5, 9]]], np.uint16)
+    same_v, same_i = np.repeat(v, 3, axis=0), np.repeat(i, 3, axis=0)
+    for mode in ("count", "workers"):
+        Qb = O.aggregate(same_v, same_i, 16, mode)
+        assert Qb[0, 0] == 1.0 and Qb[0, 5] == 2.0 and Qb[0, 9] == 3.0
+    dv = np.array([[[1.0, 2.0]], [[4.0, 8.0]]], np.float32)
+    di = np.array([[[0, 1]], [[2, 3]]], np.uint16)
+    Qc = O.aggregate(dv, di, 4, "count")
+    Qw = O.aggregate(dv, di, 4, "workers")
+    assert list(Qc[0]) == [1.0, 2.0, 4.0, 8.0]
+    assert list(Qw[0]) == [0.5, 1.0, 2.0, 4.0]
+    # index 1 held by two of three workers, one of them with a 0.0 value (still a contributor)
+    pv = np.array([[[6.0]], [[0.0]], [[9.0]]], np.float32)
+    pi = np.array([[[1]], [[1]], [[2]]], np.uint16)
+    Qc = O.aggregate(pv, pi, 4, "count")
+    Qw = O.aggregate(pv, pi, 4, "workers")
+    assert Qc[0, 1] == 3.0 and Qc[0, 2] == 9.0 and Qc[0, 0] == 0.0
+    assert Qw[0, 1] == 2.0 and Qw[0, 2] == 3.0
+
+
+# --------------------------------------------------------------------------- P12: random orthonormal basis
+
+def test_random_basis_is_gram_schmidt_of_the_draw():
+    g = _rng(23).standard_normal((64, 64))
+    P = O.orthonormal_rows(g)
+    assert np.abs(P @ P.T - np.eye(64)).max() < 1e-12
+    q, r = np.linalg.qr(g.T)
+    ref = (q * np.sign(np.diag(r))).T
+    assert np.abs(P - ref).max() < 1e-10
+    P32 = P.astype(np.float32)
+    assert np.abs(P32.astype(np.float64) @ P32.T.astype(np.float64) - np.eye(64)).max() < 1e-6
+    B = _rng(24).standard_normal((2, 64, 64))
+    rt = O.unproject(O.project(B, P32, P32), P32, P32)
+    assert np.abs(rt - B).max() < 1e-5
+
+
+# --------------------------------------------------------------------------- update rule compositions
+
+def test_signum_update_on_lossless_single_worker():
+    rng = _rng(25)
+    M = rng.standard_normal((64, 64)).astype(np.float32)
+    G = rng.standard_normal((64, 64)).astype(np.float32)
+    o = O.encode(M, G, beta=0.9, alpha=0.2, k=4096)
+    X = rng.standard_normal((64, 64)).astype(np.float32)
+    d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="sign", eta=0.01, lam=0.1)
+    Mp = 0.9 * M.astype(np.float64) + 0.1 * G.astype(np.float64)
+    ref = X.astype(np.float64) * (1 - 0.01 * 0.1) - 0.01 * np.sign(Mp)
+    # one float32 rounding of the stored result
+    assert np.all(np.abs(d["X"] - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 64), (64, 1), (2, 3), (65, 65), (3, 5000), (777,), (1,)])
+def test_tiny_and_ragged_shapes_run_and_keep_payload_sorted(shape):
+    rng = _rng(26)
+    M = rng.standard_normal(shape).astype(np.float32)
+    G = rng.standard_normal(shape).astype(np.float32)
+    for k in (1, 4, 64, 4096):
+        o = O.encode(M, G, beta=0.9, alpha=0.2, k=k)
+        numel = 64 if len(shape) == 1 else 4096
+        assert o["idx"].shape == (int(np.prod(O.chunk_grid(shape))), min(k, numel))
+        assert np.all(np.diff(o["idx"].astype(np.int64), axis=1) > 0)
+        assert o["M"].shape == shape and o["M"].dtype == np.float32
