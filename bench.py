@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Throughput of the DeMo momentum codec on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload olmo_1b]
+
+One step is the whole per-step hot path for one worker: encode (momentum
+update, 64x64 chunking, DCT, per-chunk top-k, payload, momentum subtraction)
+of every tensor, then decode/apply of all W workers' payloads (sparse
+average, inverse DCT, phi, weight-decayed update) of every tensor.  The
+tensor list is passed as two calls per half, matrices and vectors, so HIP
+events on the launch stream time each kernel separately.
+
+Inputs are synthetic and resident in HBM before timing: gradients drawn once
+with a seeded device generator, momentum starting at zero, parameters
+N(0, 0.02^2); the W-1 other workers' payloads are encoded once, untimed,
+from their own seeded gradients.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import demo_inputs as DI  # noqa: E402
+
+METRIC = "params/s for encode+decode/apply per step; achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "communication_compressed_optimizer_demo_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmo_1b", choices=sorted(DI.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+
+def _foreign_payload(args):
+    name, worker, tensor = args
+    from threadpoolctl import threadpool_limits
+    from oracle import demo_oracle as O
+    w = DI.WORKLOADS[name]
+    with threadpool_limits(1):
+        g = DI.gradient(w, worker, 0, tensor)
+        import numpy as np
+        out = O.encode(np.zeros_like(g), g, beta=w.beta, alpha=w.alpha, k=w.k)
+    return out["values"], out["idx"]
+
+
+def cpu_baseline(w: DI.Workload):
+    """The oracle, as it stands, on one tensor of the workload (its first, largest-kind matrix)."""
+    import concurrent.futures
+    import multiprocessing as mp
+
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import demo_oracle as O
+    t_idx = 0
+    shape = w.shapes[t_idx]
+    ctx = mp.get_context("fork")
+    nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ProcessPoolExecutor(nproc, mp_context=ctx) as ex:
+        foreign = list(ex.map(_foreign_payload, [(w.name, wk, t_idx) for wk in range(1, w.workers)]))
+    g0 = DI.gradient(w, 0, 0, t_idx)
+    m0 = np.zeros_like(g0)
+    x0 = DI.initial_params(w, t_idx)
+    t0 = time.perf_counter()
+    out = O.encode(m0, g0, beta=w.beta, alpha=w.alpha, k=w.k)
+    vals = np.stack([out["values"]] + [f[0] for f in foreign])
+    idx = np.stack([out["idx"]] + [f[1] for f in foreign])
+    O.decode_apply(x0, vals, idx, phi=w.phi, eta=w.eta, lam=w.lam)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    n = int(np.prod(shape))
+    return {
+        "value": n / dt,
+        "unit": "params/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"one {shape[0]}x{shape[1]} tensor of the workload ({n} params): worker-0 encode + "
+                   f"decode/apply over W={w.workers} payloads (W-1 foreign payloads precomputed, untimed); "
+                   f"{dt:.2f} s"),
+    }
+
+
+# ----------------------------------------------------------------------------- GPU leg
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernels_hip_sha256") != src:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def gpu_bench(w: DI.Workload, steps: int, warmup: int):
+    import torch
+
+    from communication_compressed_optimizer_demo_amd import binding as B
+    if not os.path.exists(B.LIB_PATH):
+        from communication_compressed_optimizer_demo_amd import build
+        build.build()
+    B.load_library()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    W = w.workers
+    groups = []
+    for want in (2, 1):
+        idx = [i for i, s in enumerate(w.shapes) if len(s) == want]
+        if not idx:
+            continue
+        shapes = [w.shapes[i] for i in idx]
+        codec = B.Codec(shapes, w.k, w.beta, w.alpha)
+        groups.append({"ndim": want, "idx": idx, "shapes": shapes, "codec": codec})
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + w.config_id)
+    gdt = torch.bfloat16 if w.grad_bf16 else torch.float32
+
+    def draw(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std)
+
+    for gr in groups:
+        gr["G"] = [draw(s, w.grad_std).to(gdt) for s in gr["shapes"]]
+        gr["M"] = [torch.zeros(s, device=dev) for s in gr["shapes"]]
+        gr["X"] = [draw(s, w.param_std) for s in gr["shapes"]]
+        gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
+        ne = gr["codec"].n_entries
+        gr["ne"] = ne
+        # other workers' payloads, untimed
+        scratch_m = [torch.zeros(s, device=dev) for s in gr["shapes"]]
+        for wk in range(1, W):
+            for t in scratch_m:
+                t.zero_()
+            gf = [draw(s, w.grad_std).to(gdt) for s in gr["shapes"]]
+            gr["codec"].encode(gf, scratch_m, gr["vals"][wk * ne:(wk + 1) * ne], gr["pidx"][wk * ne:(wk + 1) * ne])
+            del gf
+        del scratch_m
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    phi = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev):
+        # ev: list of 2 * len(groups) + 1 events, or None
+        j = 0
+        if ev:
+            ev[j].record(stream)
+        for gr in groups:
+            ne = gr["ne"]
+            gr["codec"].encode(gr["G"], gr["M"], gr["vals"][:ne], gr["pidx"][:ne], stream=stream)
+            if ev:
+                j += 1
+                ev[j].record(stream)
+        for gr in groups:
+            gr["codec"].decode_apply(gr["X"], W, gr["vals"], gr["pidx"], phi, w.eta, w.lam, stream=stream)
+            if ev:
+                j += 1
+                ev[j].record(stream)
+
+    for _ in range(warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(groups) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        one_step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = [f"encode{g['ndim']}d" for g in groups] + [f"decode{g['ndim']}d" for g in groups]
+    per = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: v / steps for n, v in per.items()}
+
+    gbytes = 2 if w.grad_bf16 else 4
+    kern = {}
+    for gr in groups:
+        numel = sum(int(torch.tensor(s).prod()) for s in gr["shapes"])
+        ne = gr["ne"]
+        enc = numel * (gbytes + 8) + ne * 6
+        dec = numel * 8 + W * ne * 6
+        for name, b in ((f"encode{gr['ndim']}d", enc), (f"decode{gr['ndim']}d", dec)):
+            ms = per[name]
+            kern[name] = {"ms": round(ms, 4), "algorithmic_bytes": int(b), "GBps": round(b / ms / 1e6, 1),
+                          "params": numel}
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+    dk = kern[dom]
+    achieved = dk["algorithmic_bytes"] / dk["ms"] / 1e6
+    total_bytes = sum(k["algorithmic_bytes"] for k in kern.values())
+    ms_per_step = elapsed / steps * 1e3
+    return {
+        "ms_per_step": ms_per_step,
+        "value": w.n_params / (ms_per_step / 1e3),
+        "step_GBps": total_bytes / (ms_per_step / 1e3) / 1e9,
+        "kernels": kern,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic(f"{dom}_kernel", w.name),
+        },
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures the "
+              "codec on one GPU's share; collectives across GPUs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+    w = DI.WORKLOADS[args.workload]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    g = gpu_bench(w, args.steps, args.warmup)
+    line = {
+        "metric": METRIC,
+        "value": g["value"],
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": g["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": ("synthetic: gradients N(0, {:g}) drawn once on the device (seeded), M0 = 0, X0 ~ N(0, {:g}^2), "
+                 "W-1 foreign payloads encoded untimed from their own seeded gradients").format(w.grad_std,
+                                                                                                w.param_std),
+        "config": {
+            "workload": w.name,
+            "tensors": len(w.shapes),
+            "params": w.n_params,
+            "chunk": 64,
+            "k": w.k,
+            "workers": w.workers,
+            "alpha": w.alpha,
+            "beta": w.beta,
+            "phi": w.phi,
+            "grad_dtype": "bf16" if w.grad_bf16 else "fp32",
+        },
+        "step_GBps": round(g["step_GBps"], 1),
+        "kernels": g["kernels"],
+        "roofline": g["roofline"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""ctypes binding of libdemo_codec.so, one Python function per C entry point.
+
+Argument marshalling only: tensors are passed as device pointers and every
+step of the codec runs in the library's HIP kernels.  There is no fallback:
+if the library is missing, or no gfx950 device is present, the calls raise.
+PyTorch tensors are accepted as buffers (it supplies device memory and
+streams); torch is imported lazily so the library can be inspected without it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdemo_codec.so")
+
+DEMO_CHUNK = 64
+DEMO_MAX_WORKERS = 255
+
+# demo_status
+DEMO_OK = 0
+STATUS_NAMES = {0: "DEMO_OK", 1: "DEMO_ERR_INVALID", 2: "DEMO_ERR_SHAPE", 3: "DEMO_ERR_RANGE",
+                4: "DEMO_ERR_PAYLOAD", 5: "DEMO_ERR_DEVICE", 6: "DEMO_ERR_HIP", 7: "DEMO_ERR_ALIGN"}
+# enums
+DEMO_F32, DEMO_BF16 = 0, 1
+DEMO_MOMENTUM_DAMPED, DEMO_MOMENTUM_PLAIN = 0, 1
+DEMO_BASIS_DCT, DEMO_BASIS_USER = 0, 1
+DEMO_PHI_SIGN, DEMO_PHI_IDENTITY = 0, 1
+DEMO_AVG_CONTRIBUTORS, DEMO_AVG_WORKERS = 0, 1
+
+
+class DemoError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class demo_shape(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("dims", ctypes.c_int64 * 2)]
+
+
+class demo_codec_cfg(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("k", ctypes.c_int32), ("beta", ctypes.c_float),
+                ("alpha", ctypes.c_float), ("momentum_form", ctypes.c_int32), ("basis", ctypes.c_int32),
+                ("P0", ctypes.c_void_p), ("P1", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m communication_compressed_optimizer_demo_amd.build`")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    P = ctypes.POINTER
+    lib.demo_last_error.restype = ctypes.c_char_p
+    lib.demo_last_error.argtypes = []
+    lib.demo_ctx_create.restype = i32
+    lib.demo_ctx_create.argtypes = [i32, P(vp)]
+    lib.demo_ctx_destroy.restype = None
+    lib.demo_ctx_destroy.argtypes = [vp]
+    lib.demo_plan.restype = i32
+    lib.demo_plan.argtypes = [P(demo_shape), i32, i32, i32, P(i64), P(i64), P(i64)]
+    lib.demo_encode.restype = i32
+    lib.demo_encode.argtypes = [vp, i32, P(demo_shape), P(vp), i32, P(vp), P(demo_codec_cfg),
+                                vp, vp, i64, vp]
+    lib.demo_decode_apply.restype = i32
+    lib.demo_decode_apply.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32,
+                                      vp, vp, i64, i32, f32, f32, i32, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != DEMO_OK:
+        raise DemoError(status, load_library().demo_last_error().decode())
+
+
+def _shapes(shapes: Sequence[Sequence[int]]):
+    arr = (demo_shape * max(1, len(shapes)))()
+    for i, s in enumerate(shapes):
+        arr[i].ndim = len(s)
+        arr[i].dims[0] = int(s[0]) if len(s) > 0 else 0
+        arr[i].dims[1] = int(s[1]) if len(s) > 1 else 0
+    return arr
+
+
+def _ptrs(values: Sequence[int]):
+    arr = (ctypes.c_void_p * max(1, len(values)))()
+    for i, v in enumerate(values):
+        arr[i] = v
+    return arr
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_cfg(k: int, beta: float = 0.999, alpha: float = 0.2, plain: bool = False,
+             P0=None, P1=None, chunk: int = DEMO_CHUNK) -> demo_codec_cfg:
+    """Codec configuration; P0/P1 (device float32 64x64 tensors) select the user basis."""
+    cfg = demo_codec_cfg()
+    cfg.chunk = chunk
+    cfg.k = int(k)
+    cfg.beta = float(beta)
+    cfg.alpha = float(alpha)
+    cfg.momentum_form = DEMO_MOMENTUM_PLAIN if plain else DEMO_MOMENTUM_DAMPED
+    if P0 is None:
+        cfg.basis = DEMO_BASIS_DCT
+        cfg.P0 = cfg.P1 = None
+    else:
+        cfg.basis = DEMO_BASIS_USER
+        cfg.P0 = _device_ptr(P0, 4)
+        cfg.P1 = _device_ptr(P1 if P1 is not None else P0, 4)
+    return cfg
+
+
+def _device_ptr(t, elem_size: int) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensor must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if t.element_size() != elem_size:
+        raise ValueError(f"tensor element size {t.element_size()} != {elem_size}")
+    return t.data_ptr()
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def demo_plan(shapes: Sequence[Sequence[int]], k: int, chunk: int = DEMO_CHUNK) -> Tuple[int, int, List[int]]:
+    """(n_chunks, n_entries, entry_begin[n+1]) of a tensor list; host-only."""
+    lib = load_library()
+    n = len(shapes)
+    sh = _shapes(shapes)
+    nc, ne = ctypes.c_int64(), ctypes.c_int64()
+    eb = (ctypes.c_int64 * (n + 1))()
+    _check(lib.demo_plan(sh, n, chunk, int(k), ctypes.byref(nc), ctypes.byref(ne), eb))
+    return nc.value, ne.value, list(eb)
+
+
+def demo_ctx_create(device: int = 0) -> int:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.demo_ctx_create(int(device), ctypes.byref(h)))
+    return h.value
+
+
+def demo_ctx_destroy(ctx: int) -> None:
+    load_library().demo_ctx_destroy(ctx)
+
+
+def demo_encode(ctx: int, grads, moms, cfg: demo_codec_cfg, pay_values, pay_idx, stream=None) -> None:
+    """Encode one worker's tensors: moms updated in place, payload written."""
+    lib = load_library()
+    import torch
+    n = len(grads)
+    if len(moms) != n:
+        raise ValueError("grads and moms differ in length")
+    shapes = []
+    for g, m in zip(grads, moms):
+        if tuple(g.shape) != tuple(m.shape):
+            raise ValueError("gradient and momentum shapes differ")
+        if m.dtype != torch.float32:
+            raise ValueError("momentum must be float32")
+        shapes.append(tuple(m.shape))
+    gdt = grads[0].dtype if n else torch.float32
+    if any(g.dtype != gdt for g in grads):
+        raise ValueError("all gradients must share one dtype")
+    if gdt == torch.float32:
+        code, gsz = DEMO_F32, 4
+    elif gdt == torch.bfloat16:
+        code, gsz = DEMO_BF16, 2
+    else:
+        raise ValueError("gradients must be float32 or bfloat16")
+    _check(lib.demo_encode(ctx, n, _shapes(shapes), _ptrs([_device_ptr(g, gsz) for g in grads]), code,
+                           _ptrs([_device_ptr(m, 4) for m in moms]), ctypes.byref(cfg),
+                           _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), pay_values.numel(),
+                           _stream_handle(stream)))
+
+
+def demo_decode_apply(ctx: int, params, cfg: demo_codec_cfg, workers: int, pay_values, pay_idx,
+                      phi: int = DEMO_PHI_SIGN, eta: float = 1e-3, lam: float = 0.0,
+                      avg: int = DEMO_AVG_CONTRIBUTORS, stream=None) -> None:
+    """Average ``workers`` payloads (worker-major rows) and update params in place."""
+    lib = load_library()
+    import torch
+    n = len(params)
+    for x in params:
+        if x.dtype != torch.float32:
+            raise ValueError("parameters must be float32")
+    if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
+        raise ValueError("payload arrays must hold workers x entries elements")
+    per = pay_values.numel() // workers
+    _check(lib.demo_decode_apply(ctx, n, _shapes([tuple(x.shape) for x in params]),
+                                 _ptrs([_device_ptr(x, 4) for x in params]), ctypes.byref(cfg), int(workers),
+                                 _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per, int(phi),
+                                 float(eta), float(lam), int(avg), _stream_handle(stream)))
+
+
+class Codec:
+    """A context bound to one device plus the codec configuration of a tensor list."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], k: int, beta: float = 0.999, alpha: float = 0.2,
+                 plain: bool = False, device: int = 0):
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.k = int(k)
+        self.beta = float(beta)
+        self.alpha = float(alpha)
+        self.plain = bool(plain)
+        self.n_chunks, self.n_entries, self.entry_begin = demo_plan(self.shapes, self.k)
+        self.ctx = demo_ctx_create(device)
+
+    def close(self) -> None:
+        if self.ctx:
+            demo_ctx_destroy(self.ctx)
+            self.ctx = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def cfg(self, P0=None, P1=None) -> demo_codec_cfg:
+        return make_cfg(self.k, self.beta, self.alpha, self.plain, P0, P1)
+
+    def alloc_payload(self, workers: int = 1, device="cuda"):
+        """Empty payload buffers: float32 values and 16-bit indices (int16 storage of uint16)."""
+        import torch
+        v = torch.empty(workers * self.n_entries, dtype=torch.float32, device=device)
+        i = torch.empty(workers * self.n_entries, dtype=torch.int16, device=device)
+        return v, i
+
+    def encode(self, grads, moms, pay_values, pay_idx, P0=None, P1=None, stream=None) -> None:
+        demo_encode(self.ctx, grads, moms, self.cfg(P0, P1), pay_values, pay_idx, stream)
+
+    def decode_apply(self, params, workers, pay_values, pay_idx, phi=DEMO_PHI_SIGN, eta=1e-3, lam=0.0,
+                     avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
+        demo_decode_apply(self.ctx, params, self.cfg(P0, P1), workers, pay_values, pay_idx, phi, eta, lam,
+                          avg, stream)

@@ -1,0 +1,285 @@
+// C ABI of the DeMo momentum codec: argument validation, chunk planning and
+// launch batching.  Every check runs on the host before anything is enqueued;
+// the kernels themselves live in kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "demo_codec.h"
+#include "launch.h"
+
+struct demo_ctx {
+  int device;
+};
+
+namespace {
+
+using demo::kChunk;
+using demo::kMaxTensorsPerLaunch;
+using demo::LaunchTable;
+
+thread_local std::string g_last_error;
+
+demo_status fail(demo_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+struct TensorPlan {
+  int ndim;
+  int64_t rows, cols;   // 1-D: rows = length, cols = 1
+  int64_t chunks;       // chunks of the tensor
+  int32_t keff;         // entries per chunk
+  int64_t entry_begin;  // payload offset of the first chunk
+  int64_t items;        // work items: chunks (2-D) or 64-chunk slabs (1-D)
+  int32_t grid1;        // 2-D: chunks along dim 1; 1-D: chunk count
+};
+
+demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_t k, std::vector<TensorPlan>* out,
+                      int64_t* entries, int64_t* chunks) {
+  if (n < 0) return fail(DEMO_ERR_RANGE, "tensor count is negative");
+  if (n > 0 && shapes == nullptr) return fail(DEMO_ERR_INVALID, "shapes is NULL");
+  if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "chunk size must be 64");
+  if (k < 1) return fail(DEMO_ERR_RANGE, "k must be >= 1");
+  int64_t e = 0, c = 0;
+  if (out) out->clear();
+  for (int32_t i = 0; i < n; ++i) {
+    const demo_shape& s = shapes[i];
+    TensorPlan t{};
+    t.ndim = s.ndim;
+    if (s.ndim != 1 && s.ndim != 2)
+      return fail(DEMO_ERR_SHAPE, "tensor " + std::to_string(i) + ": ndim must be 1 or 2");
+    for (int d = 0; d < s.ndim; ++d) {
+      if (s.dims[d] < 1 || s.dims[d] > INT32_MAX)
+        return fail(DEMO_ERR_SHAPE, "tensor " + std::to_string(i) + ": dimension out of 1..2^31-1");
+    }
+    if (s.ndim == 2) {
+      t.rows = s.dims[0];
+      t.cols = s.dims[1];
+      const int64_t g0 = (t.rows + kChunk - 1) / kChunk, g1 = (t.cols + kChunk - 1) / kChunk;
+      t.chunks = g0 * g1;
+      t.keff = k < kChunk * kChunk ? k : kChunk * kChunk;
+      t.items = t.chunks;
+      t.grid1 = int32_t(g1);
+    } else {
+      t.rows = s.dims[0];
+      t.cols = 1;
+      t.chunks = (t.rows + kChunk - 1) / kChunk;
+      t.keff = k < kChunk ? k : kChunk;
+      t.items = (t.chunks + kChunk - 1) / kChunk;
+      t.grid1 = int32_t(t.chunks);
+    }
+    if (t.items > INT32_MAX) return fail(DEMO_ERR_SHAPE, "tensor " + std::to_string(i) + ": too many chunks");
+    t.entry_begin = e;
+    e += t.chunks * t.keff;
+    c += t.chunks;
+    if (out) out->push_back(t);
+  }
+  if (entries) *entries = e;
+  if (chunks) *chunks = c;
+  return DEMO_OK;
+}
+
+demo_status check_device(const demo_ctx* ctx) {
+  if (ctx == nullptr) return fail(DEMO_ERR_INVALID, "context is NULL");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(DEMO_ERR_HIP, "hipGetDevice failed");
+  if (cur != ctx->device)
+    return fail(DEMO_ERR_DEVICE, "current device " + std::to_string(cur) + " is not the context's device " +
+                                     std::to_string(ctx->device));
+  return DEMO_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+demo_status check_basis(const demo_codec_cfg* cfg, const std::vector<TensorPlan>& plan, const float** p0,
+                        const float** p1) {
+  *p0 = nullptr;
+  *p1 = nullptr;
+  if (cfg->basis == DEMO_BASIS_DCT) return DEMO_OK;
+  if (cfg->basis != DEMO_BASIS_USER) return fail(DEMO_ERR_INVALID, "unknown basis");
+  bool any2d = false;
+  for (const auto& t : plan) any2d = any2d || t.ndim == 2;
+  if (cfg->P0 == nullptr) return fail(DEMO_ERR_INVALID, "user basis without P0");
+  if (any2d && cfg->P1 == nullptr) return fail(DEMO_ERR_INVALID, "user basis without P1 for a matrix");
+  if (!aligned(cfg->P0, 4) || (cfg->P1 && !aligned(cfg->P1, 4))) return fail(DEMO_ERR_ALIGN, "basis misaligned");
+  *p0 = cfg->P0;
+  *p1 = cfg->P1 ? cfg->P1 : cfg->P0;
+  return DEMO_OK;
+}
+
+// Fills launch tables of one kind (ndim) and calls `launch` for each batch.
+template <class Fill, class Launch>
+demo_status for_each_batch(const std::vector<TensorPlan>& plan, int ndim, Fill&& fill, Launch&& launch) {
+  LaunchTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  auto flush = [&]() -> demo_status {
+    if (tab.n == 0) return DEMO_OK;
+    const hipError_t err = launch(tab);
+    if (err != hipSuccess) return fail(DEMO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
+    std::memset(&tab, 0, sizeof(tab));
+    return DEMO_OK;
+  };
+  for (size_t i = 0; i < plan.size(); ++i) {
+    const TensorPlan& t = plan[i];
+    if (t.ndim != ndim) continue;
+    if (tab.n == kMaxTensorsPerLaunch || int64_t(tab.items) + t.items > INT32_MAX) {
+      const demo_status s = flush();
+      if (s != DEMO_OK) return s;
+    }
+    demo::TensorSlot& slot = tab.t[tab.n++];
+    slot.entry_begin = t.entry_begin;
+    slot.rows = int32_t(t.rows);
+    slot.cols = int32_t(t.cols);
+    slot.item_begin = tab.items;
+    slot.grid1 = t.grid1;
+    fill(slot, i);
+    tab.items += int32_t(t.items);
+  }
+  return flush();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* demo_last_error(void) { return g_last_error.c_str(); }
+
+demo_status demo_ctx_create(int32_t device, demo_ctx** out) {
+  if (out == nullptr) return fail(DEMO_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return fail(DEMO_ERR_DEVICE, "no HIP device");
+  if (device < 0 || device >= count) return fail(DEMO_ERR_DEVICE, "device ordinal out of range");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return fail(DEMO_ERR_HIP, "hipGetDeviceProperties failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(DEMO_ERR_DEVICE, std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
+  demo_ctx* c = new (std::nothrow) demo_ctx;
+  if (c == nullptr) return fail(DEMO_ERR_INVALID, "out of host memory");
+  c->device = device;
+  *out = c;
+  return DEMO_OK;
+}
+
+void demo_ctx_destroy(demo_ctx* ctx) { delete ctx; }
+
+demo_status demo_plan(const demo_shape* shapes, int32_t n, int32_t chunk, int32_t k, int64_t* n_chunks,
+                      int64_t* n_entries, int64_t* entry_begin) {
+  std::vector<TensorPlan> plan;
+  int64_t e = 0, c = 0;
+  const demo_status s = plan_list(shapes, n, chunk, k, &plan, &e, &c);
+  if (s != DEMO_OK) return s;
+  if (n_chunks) *n_chunks = c;
+  if (n_entries) *n_entries = e;
+  if (entry_begin) {
+    for (int32_t i = 0; i < n; ++i) entry_begin[i] = plan[i].entry_begin;
+    entry_begin[n] = e;
+  }
+  return DEMO_OK;
+}
+
+demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, const void* const* grads,
+                        demo_dtype grad_dtype, float* const* moms, const demo_codec_cfg* cfg, float* pay_values,
+                        uint16_t* pay_idx, int64_t n_entries, hipStream_t stream) {
+  if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
+  std::vector<TensorPlan> plan;
+  int64_t entries = 0;
+  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr);
+  if (s != DEMO_OK) return s;
+  if (grad_dtype != DEMO_F32 && grad_dtype != DEMO_BF16) return fail(DEMO_ERR_INVALID, "unknown gradient dtype");
+  if (cfg->momentum_form != DEMO_MOMENTUM_DAMPED && cfg->momentum_form != DEMO_MOMENTUM_PLAIN)
+    return fail(DEMO_ERR_INVALID, "unknown momentum form");
+  if (!std::isfinite(cfg->beta) || !std::isfinite(cfg->alpha)) return fail(DEMO_ERR_INVALID, "beta/alpha not finite");
+  if (n_entries != entries)
+    return fail(DEMO_ERR_PAYLOAD, "payload holds " + std::to_string(n_entries) + " entries, plan needs " +
+                                      std::to_string(entries));
+  if (n > 0 && (grads == nullptr || moms == nullptr)) return fail(DEMO_ERR_INVALID, "tensor pointer list is NULL");
+  const size_t gsz = grad_dtype == DEMO_BF16 ? 2 : 4;
+  for (int32_t i = 0; i < n; ++i) {
+    if (grads[i] == nullptr || moms[i] == nullptr)
+      return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
+    if (!aligned(grads[i], gsz) || !aligned(moms[i], 4))
+      return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
+  }
+  if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr)) return fail(DEMO_ERR_INVALID, "payload is NULL");
+  if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
+  const float *p0, *p1;
+  if ((s = check_basis(cfg, plan, &p0, &p1)) != DEMO_OK) return s;
+  if ((s = check_device(ctx)) != DEMO_OK) return s;
+
+  demo::EncodeParams p{};
+  p.pay_val = pay_values;
+  p.pay_idx = pay_idx;
+  p.beta = cfg->beta;
+  p.gcoef = cfg->momentum_form == DEMO_MOMENTUM_PLAIN ? 1.0f : float(1.0 - double(cfg->beta));
+  p.alpha = cfg->alpha;
+  const bool bf16 = grad_dtype == DEMO_BF16;
+  auto fill = [&](demo::TensorSlot& slot, size_t i) {
+    slot.src = grads[i];
+    slot.dst = moms[i];
+  };
+  p.keff = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
+  s = for_each_batch(plan, 2, fill,
+                     [&](const LaunchTable& t) { return demo::launch_encode2d(t, p, bf16, p0, p1, stream); });
+  if (s != DEMO_OK) return s;
+  p.keff = cfg->k < kChunk ? cfg->k : kChunk;
+  return for_each_batch(plan, 1, fill,
+                        [&](const LaunchTable& t) { return demo::launch_encode1d(t, p, bf16, p0, stream); });
+}
+
+demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                              const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                              const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
+                              demo_average avg, hipStream_t stream) {
+  if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
+  std::vector<TensorPlan> plan;
+  int64_t entries = 0;
+  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr);
+  if (s != DEMO_OK) return s;
+  if (workers < 1 || workers > demo::kMaxWorkers) return fail(DEMO_ERR_RANGE, "workers must be in 1..255");
+  if (phi != DEMO_PHI_SIGN && phi != DEMO_PHI_IDENTITY) return fail(DEMO_ERR_INVALID, "unknown phi");
+  if (avg != DEMO_AVG_CONTRIBUTORS && avg != DEMO_AVG_WORKERS) return fail(DEMO_ERR_INVALID, "unknown average");
+  if (!std::isfinite(eta) || !std::isfinite(lambda)) return fail(DEMO_ERR_INVALID, "eta/lambda not finite");
+  if (n_entries != entries)
+    return fail(DEMO_ERR_PAYLOAD, "payload holds " + std::to_string(n_entries) + " entries per worker, plan needs " +
+                                      std::to_string(entries));
+  if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    if (params[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
+    if (!aligned(params[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
+  }
+  if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr)) return fail(DEMO_ERR_INVALID, "payload is NULL");
+  if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
+  const float *p0, *p1;
+  if ((s = check_basis(cfg, plan, &p0, &p1)) != DEMO_OK) return s;
+  if ((s = check_device(ctx)) != DEMO_OK) return s;
+
+  demo::DecodeParams p{};
+  p.pay_val = pay_values;
+  p.pay_idx = pay_idx;
+  p.entries = entries;
+  p.workers = workers;
+  p.eta = eta;
+  p.lam = lambda;
+  p.inv_workers = float(1.0 / double(workers));
+  p.phi_sign = phi == DEMO_PHI_SIGN ? 1 : 0;
+  p.avg_workers = avg == DEMO_AVG_WORKERS ? 1 : 0;
+  auto fill = [&](demo::TensorSlot& slot, size_t i) {
+    slot.src = nullptr;
+    slot.dst = params[i];
+  };
+  p.keff = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
+  s = for_each_batch(plan, 2, fill,
+                     [&](const LaunchTable& t) { return demo::launch_decode2d(t, p, p0, p1, stream); });
+  if (s != DEMO_OK) return s;
+  p.keff = cfg->k < kChunk ? cfg->k : kChunk;
+  return for_each_batch(plan, 1, fill, [&](const LaunchTable& t) { return demo::launch_decode1d(t, p, p0, stream); });
+}
+
+}  // extern "C"

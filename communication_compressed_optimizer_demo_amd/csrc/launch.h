@@ -1,0 +1,70 @@
+// Kernel-argument layout shared by the host side (codec.cpp) and the kernels.
+//
+// A launch covers up to kMaxTensorsPerLaunch tensors of one kind (2-D
+// matrices, or 1-D vectors).  The tensor table travels by value in the kernel
+// arguments, so no device-side table is allocated or copied.  A work item is
+// one 64x64 chunk (2-D) or one slab of up to 64 consecutive 64-element chunks
+// of a vector (1-D); items are numbered consecutively over the launch's
+// tensors in list order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace demo {
+
+constexpr int kChunk = 64;
+constexpr int kMaxTensorsPerLaunch = 64;
+constexpr int kMaxWorkers = 255;  // counts are kept in 8 bits
+
+struct TensorSlot {
+  const void* src;      // encode: gradient (fp32 or bf16); unused by decode
+  float* dst;           // encode: momentum (in/out); decode: parameters (in/out)
+  int64_t entry_begin;  // payload entry of the tensor's first chunk
+  int32_t rows;         // 2-D: dim 0; 1-D: length
+  int32_t cols;         // 2-D: dim 1; 1-D: 1
+  int32_t item_begin;   // first work item of this tensor within the launch
+  int32_t grid1;        // 2-D: chunks along dim 1; 1-D: number of 64-element chunks
+};
+
+struct LaunchTable {
+  int32_t n;
+  int32_t items;
+  TensorSlot t[kMaxTensorsPerLaunch];
+};
+
+struct EncodeParams {
+  float* pay_val;
+  uint16_t* pay_idx;
+  float beta;
+  float gcoef;  // (1 - beta) or 1
+  float alpha;
+  int32_t keff;
+};
+
+struct DecodeParams {
+  const float* pay_val;
+  const uint16_t* pay_idx;
+  int64_t entries;  // entries per worker payload
+  int32_t workers;
+  int32_t keff;
+  float eta;
+  float lam;
+  float inv_workers;
+  int32_t phi_sign;     // 1: sign, 0: identity
+  int32_t avg_workers;  // 1: divide by W, 0: by contributor count
+};
+
+// Host entry points into the kernels (kernels.hip).  basis_p0/p1 are null for
+// the DCT basis.  Return the hipError_t of the launch.
+hipError_t launch_encode2d(const LaunchTable& tab, const EncodeParams& p, bool g_bf16,
+                           const float* basis_p0, const float* basis_p1, hipStream_t stream);
+hipError_t launch_encode1d(const LaunchTable& tab, const EncodeParams& p, bool g_bf16,
+                           const float* basis_p0, hipStream_t stream);
+hipError_t launch_decode2d(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0,
+                           const float* basis_p1, hipStream_t stream);
+hipError_t launch_decode1d(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0,
+                           hipStream_t stream);
+
+}  // namespace demo

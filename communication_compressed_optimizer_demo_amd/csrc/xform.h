@@ -1,0 +1,304 @@
+// In-register transforms of one 64-element vector per lane.
+//
+// The orthonormal DCT-II basis of the DeMo codec ("DeMo: Decoupled Momentum
+// Optimization", §3.4 Blockwise Linear Projection (DCT)) is applied with a
+// fast factorisation instead of a 64x64 matrix product:
+//   * DCT-II of length N splits into a DCT-II of length N/2 on the sums
+//     x[n] + x[N-1-n] (even outputs) and a DCT-IV of length N/2 on the
+//     differences x[n] - x[N-1-n] (odd outputs);
+//   * a DCT-IV of length M is a complex DFT of length M/2 between a pre- and
+//     a post-rotation (pairs x[2n] + i x[M-1-2n]);
+//   * the DFT is radix-2 decimation in time.
+// DCT-III (the transpose, used for the inverse) runs the same graph backwards.
+// The orthonormal scale factors are folded into the rotation constants.
+// Every twiddle is a compile-time constant computed in double precision and
+// rounded once to float; all loops are unrolled at compile time so the
+// arrays live in VGPRs.
+//
+// A caller-supplied basis (random orthonormal projection, same section) has
+// no fast form; DenseBasis applies it as a plain matrix-vector product whose
+// rows are read through uniform (scalar) loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+namespace demo {
+namespace xf {
+
+// ---------------------------------------------------------------- compile-time trig
+
+constexpr double kPi = 3.14159265358979323846264338327950288;
+
+constexpr double taylor_sin(double x) {  // |x| <= pi/4
+  double x2 = x * x, term = x, sum = x;
+  for (int n = 1; n < 14; ++n) {
+    term *= -x2 / double((2 * n) * (2 * n + 1));
+    sum += term;
+  }
+  return sum;
+}
+
+constexpr double taylor_cos(double x) {  // |x| <= pi/4
+  double x2 = x * x, term = 1.0, sum = 1.0;
+  for (int n = 1; n < 14; ++n) {
+    term *= -x2 / double((2 * n - 1) * (2 * n));
+    sum += term;
+  }
+  return sum;
+}
+
+// cos(pi * p / q), q > 0, by reduction to [0, pi/4]
+constexpr double cospi(long p, long q) {
+  long t = p % (2 * q);
+  if (t < 0) t += 2 * q;
+  if (t > q) t = 2 * q - t;  // angle in [0, pi]
+  double sign = 1.0;
+  if (2 * t > q) {  // angle in (pi/2, pi]
+    t = q - t;
+    sign = -1.0;
+  }
+  if (4 * t > q) return sign * taylor_sin(kPi * double(q - 2 * t) / double(2 * q));
+  return sign * taylor_cos(kPi * double(t) / double(q));
+}
+
+// sin(pi p / q) = cos(pi (2p - q) / (2q))
+constexpr double sinpi(long p, long q) { return cospi(2 * p - q, 2 * q); }
+
+constexpr double csqrt(double v) {
+  double r = v > 1.0 ? v : 1.0;
+  for (int i = 0; i < 64; ++i) r = 0.5 * (r + v / r);
+  return r;
+}
+
+// Scale tags (C++17 has no floating-point template parameters).
+struct Unit {
+  static constexpr double v = 1.0;
+};
+template <int N>
+struct Ortho {  // sqrt(2 / N): the non-DC row scale of the orthonormal DCT-II of length N
+  static constexpr double v = csqrt(2.0 / double(N));
+};
+
+// ---------------------------------------------------------------- compile-time loop
+
+template <int B, int E, class F>
+__host__ __device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    sfor<B + 1, E>(f);
+  }
+}
+
+// ---------------------------------------------------------------- complex DFT, radix 2
+
+// Z[k] = sum_n z[n] exp(-2 pi i n k / L), natural order in and out.
+template <int L>
+__host__ __device__ __forceinline__ void fft(float (&re)[L], float (&im)[L]) {
+  if constexpr (L == 1) {
+    return;
+  } else if constexpr (L == 2) {
+    const float r0 = re[0], i0 = im[0];
+    re[0] = r0 + re[1];
+    im[0] = i0 + im[1];
+    re[1] = r0 - re[1];
+    im[1] = i0 - im[1];
+  } else {
+    constexpr int H = L / 2;
+    float er[H], ei[H], orr[H], oi[H];
+    sfor<0, H>([&](auto I) {
+      constexpr int n = decltype(I)::value;
+      er[n] = re[2 * n];
+      ei[n] = im[2 * n];
+      orr[n] = re[2 * n + 1];
+      oi[n] = im[2 * n + 1];
+    });
+    fft<H>(er, ei);
+    fft<H>(orr, oi);
+    sfor<0, H>([&](auto I) {
+      constexpr int k = decltype(I)::value;
+      float tr, ti;
+      if constexpr (k == 0) {
+        tr = orr[k];
+        ti = oi[k];
+      } else if constexpr (4 * k == L) {  // times -i
+        tr = oi[k];
+        ti = -orr[k];
+      } else {
+        constexpr float c = float(cospi(2 * k, L));
+        constexpr float s = float(sinpi(2 * k, L));
+        tr = fmaf(orr[k], c, oi[k] * s);
+        ti = fmaf(oi[k], c, -(orr[k] * s));
+      }
+      re[k] = er[k] + tr;
+      im[k] = ei[k] + ti;
+      re[k + H] = er[k] - tr;
+      im[k + H] = ei[k] - ti;
+    });
+  }
+}
+
+// ---------------------------------------------------------------- DCT-IV
+
+// y[m] = Pre*Post * sum_n x[n] cos(pi (2n+1)(2m+1) / (4M)).
+// Pre and Post are scale tags; only their product matters mathematically,
+// they say on which side of the graph the factor is folded in.
+template <int M, class Pre, class Post>
+__host__ __device__ __forceinline__ void dct4(float (&x)[M]) {
+  constexpr double g = Pre::v * Post::v;
+  if constexpr (M == 1) {
+    x[0] *= float(g * cospi(1, 4));
+  } else if constexpr (M == 2) {
+    constexpr float c1 = float(g * cospi(1, 8));
+    constexpr float c3 = float(g * cospi(3, 8));
+    const float a = x[0], b = x[1];
+    x[0] = fmaf(a, c1, b * c3);
+    x[1] = fmaf(a, c3, -(b * c1));
+  } else {
+    constexpr int L = M / 2;
+    float re[L], im[L];
+    sfor<0, L>([&](auto I) {
+      constexpr int n = decltype(I)::value;
+      constexpr float c = float(Pre::v * cospi(4 * n + 1, 4 * M));
+      constexpr float s = float(Pre::v * sinpi(4 * n + 1, 4 * M));
+      const float a = x[2 * n], b = x[M - 1 - 2 * n];
+      re[n] = fmaf(a, c, b * s);
+      im[n] = fmaf(b, c, -(a * s));
+    });
+    fft<L>(re, im);
+    sfor<0, L>([&](auto I) {
+      constexpr int k = decltype(I)::value;
+      constexpr float c = float(Post::v * cospi(k, M));
+      constexpr float s = float(Post::v * sinpi(k, M));
+      float ur, ui;
+      if constexpr (k == 0) {
+        if constexpr (Post::v == 1.0) {
+          ur = re[0];
+          ui = im[0];
+        } else {
+          ur = re[0] * c;
+          ui = im[0] * c;
+        }
+      } else {
+        ur = fmaf(re[k], c, im[k] * s);
+        ui = fmaf(im[k], c, -(re[k] * s));
+      }
+      x[2 * k] = ur;
+      x[M - 1 - 2 * k] = -ui;
+    });
+  }
+}
+
+// ---------------------------------------------------------------- DCT-II / DCT-III
+
+// Forward: X[k] = S_k * sum_n x[n] cos(pi (2n+1) k / (2N)), with S_k = Sig::v
+// for k > 0 and Sig::v / sqrt(2) for k = 0.  Sig = Ortho<N> gives the
+// orthonormal DCT-II.
+template <int N, class Sig>
+__host__ __device__ __forceinline__ void dct2(float (&x)[N]) {
+  constexpr double r2 = 0.70710678118654752440084436210484904;
+  if constexpr (N == 1) {
+    x[0] *= float(Sig::v * r2);
+  } else if constexpr (N == 2) {
+    constexpr float h = float(Sig::v * r2);
+    const float a = x[0], b = x[1];
+    x[0] = (a + b) * h;
+    x[1] = (a - b) * h;
+  } else {
+    constexpr int H = N / 2;
+    float a[H], b[H];
+    sfor<0, H>([&](auto I) {
+      constexpr int n = decltype(I)::value;
+      a[n] = x[n] + x[N - 1 - n];
+      b[n] = x[n] - x[N - 1 - n];
+    });
+    dct2<H, Sig>(a);
+    dct4<H, Unit, Sig>(b);
+    sfor<0, H>([&](auto I) {
+      constexpr int m = decltype(I)::value;
+      x[2 * m] = a[m];
+      x[2 * m + 1] = b[m];
+    });
+  }
+}
+
+// Inverse (transpose of dct2 with the same scaling): x[n] = sum_k S_k X[k] cos(pi (2n+1) k / (2N)).
+template <int N, class Sig>
+__host__ __device__ __forceinline__ void dct3(float (&x)[N]) {
+  constexpr double r2 = 0.70710678118654752440084436210484904;
+  if constexpr (N == 1) {
+    x[0] *= float(Sig::v * r2);
+  } else if constexpr (N == 2) {
+    constexpr float h = float(Sig::v * r2);
+    const float a = x[0], b = x[1];
+    x[0] = (a + b) * h;
+    x[1] = (a - b) * h;
+  } else {
+    constexpr int H = N / 2;
+    float a[H], b[H];
+    sfor<0, H>([&](auto I) {
+      constexpr int m = decltype(I)::value;
+      a[m] = x[2 * m];
+      b[m] = x[2 * m + 1];
+    });
+    dct3<H, Sig>(a);
+    dct4<H, Sig, Unit>(b);
+    sfor<0, H>([&](auto I) {
+      constexpr int n = decltype(I)::value;
+      x[n] = a[n] + b[n];
+      x[N - 1 - n] = a[n] - b[n];
+    });
+  }
+}
+
+// ---------------------------------------------------------------- bases as kernel policies
+
+// Orthonormal DCT-II on both dimensions (P0 = P1 = P).
+struct DctBasis {
+  // y = P x
+  __host__ __device__ __forceinline__ void fwd0(float (&x)[64]) const { dct2<64, Ortho<64>>(x); }
+  __host__ __device__ __forceinline__ void fwd1(float (&x)[64]) const { dct2<64, Ortho<64>>(x); }
+  // y = P^T x
+  __host__ __device__ __forceinline__ void inv0(float (&x)[64]) const { dct3<64, Ortho<64>>(x); }
+  __host__ __device__ __forceinline__ void inv1(float (&x)[64]) const { dct3<64, Ortho<64>>(x); }
+};
+
+// Caller-supplied orthonormal P0 / P1 (64 x 64, row-major, rows are basis vectors).
+struct DenseBasis {
+  const float* __restrict__ p0;
+  const float* __restrict__ p1;
+
+  static __device__ __forceinline__ void apply(const float* __restrict__ P, float (&x)[64]) {
+    float y[64];
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int n = 0; n < 64; ++n) acc = fmaf(P[u * 64 + n], x[n], acc);
+      y[u] = acc;
+    }
+#pragma unroll
+    for (int u = 0; u < 64; ++u) x[u] = y[u];
+  }
+  static __device__ __forceinline__ void apply_t(const float* __restrict__ P, float (&x)[64]) {
+    float y[64];
+#pragma unroll
+    for (int n = 0; n < 64; ++n) y[n] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+#pragma unroll
+      for (int n = 0; n < 64; ++n) y[n] = fmaf(P[u * 64 + n], x[u], y[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < 64; ++n) x[n] = y[n];
+  }
+  __device__ __forceinline__ void fwd0(float (&x)[64]) const { apply(p0, x); }
+  __device__ __forceinline__ void fwd1(float (&x)[64]) const { apply(p1, x); }
+  __device__ __forceinline__ void inv0(float (&x)[64]) const { apply_t(p0, x); }
+  __device__ __forceinline__ void inv1(float (&x)[64]) const { apply_t(p1, x); }
+};
+
+}  // namespace xf
+}  // namespace demo

@@ -1,0 +1,152 @@
+/*
+ * demo_codec.h -- C ABI of the MI355X (gfx950) DeMo per-step momentum codec.
+ *
+ * The codec is the data-parallel hot path of DeMo ("DeMo: Decoupled Momentum
+ * Optimization", paper-graph-ui summary of arXiv 2411.19870, §3.4 Detailed,
+ * sentence-based technical breakdown).  It is split where the pages place the
+ * all-gather between workers (§3.4 Top-k Sparsification, last paragraph):
+ *
+ *   demo_encode        one worker, before communication: momentum update,
+ *                      chunking, DCT, per-chunk top-k, payload, momentum
+ *                      subtraction.
+ *   demo_decode_apply  after communication: sparse averaging of W payloads,
+ *                      inverse DCT, phi, parameter update.
+ *
+ * Conventions for every call:
+ *   - Tensors are dense, row-major, contiguous device buffers.  Matrices
+ *     (ndim 2) are cut into 64x64 chunks, vectors (ndim 1) into 64-element
+ *     chunks; trailing chunks are zero-padded for the transform and cropped
+ *     on store.  Chunks are numbered tensor by tensor in list order,
+ *     row-major inside a matrix.
+ *   - A payload holds, for every chunk in that order, keff = min(k, chunk
+ *     element count) entries: a float32 value array and a uint16 index array
+ *     (index = u*64 + v inside a 64x64 chunk, u the dimension-0 frequency;
+ *     the frequency itself for a vector chunk), entries of a chunk in
+ *     ascending index order.  demo_plan gives the entry count and offsets.
+ *   - The caller owns every buffer.  Device pointers must be device memory of
+ *     the context's device; host arrays (shape lists, pointer lists, the
+ *     config) are read during the call only.
+ *   - Calls enqueue kernels on `stream` and return without synchronising.
+ *     They allocate no device memory and touch none before validation has
+ *     passed: a non-DEMO_OK status means nothing was enqueued, except
+ *     DEMO_ERR_HIP from a failed launch (earlier launches of the same call
+ *     may then have been enqueued).
+ *   - Inputs must be finite; NaN or Inf give unspecified (but memory-safe)
+ *     results.  Payload indices outside a chunk are masked into it.
+ *   - Calls are thread-safe; concurrent calls that write the same buffers race.
+ *   - demo_last_error() returns a thread-local message for the last failure.
+ */
+#ifndef DEMO_CODEC_H
+#define DEMO_CODEC_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DEMO_CHUNK 64        /* the only chunk size built (pages' default s = 64) */
+#define DEMO_MAX_WORKERS 255 /* decode keeps per-coefficient contributor counts in 8 bits */
+
+typedef enum demo_status {
+  DEMO_OK = 0,
+  DEMO_ERR_INVALID = 1, /* null pointer, unknown enum value, non-finite scalar */
+  DEMO_ERR_SHAPE = 2,   /* ndim not 1 or 2, a zero or too large dimension */
+  DEMO_ERR_RANGE = 3,   /* k < 1, chunk != 64, workers outside 1..255, n < 0 */
+  DEMO_ERR_PAYLOAD = 4, /* payload entry count differs from the plan */
+  DEMO_ERR_DEVICE = 5,  /* no gfx950 device, or the current device is not the context's */
+  DEMO_ERR_HIP = 6,     /* a HIP runtime call or launch failed */
+  DEMO_ERR_ALIGN = 7    /* a device pointer is not aligned to its element size */
+} demo_status;
+
+/* Element type of the gradients (momentum, parameters and payload values are float32). */
+typedef enum demo_dtype { DEMO_F32 = 0, DEMO_BF16 = 1 } demo_dtype;
+
+/* Local momentum update, DeMo summary §3.4 Decoupled Local Momentum Updates:
+ * DAMPED  M <- beta M + (1 - beta) G   (that section's equation)
+ * PLAIN   M <- beta M + G              (the papernotes.org note's flowchart) */
+typedef enum demo_momentum_form { DEMO_MOMENTUM_DAMPED = 0, DEMO_MOMENTUM_PLAIN = 1 } demo_momentum_form;
+
+/* Projection, DeMo summary §3.4 Blockwise Linear Projection (DCT):
+ * DCT   orthonormal DCT-II on both chunk dimensions (P0 = P1 = P, P^T = P^-1)
+ * USER  caller-supplied orthonormal P0, P1 (e.g. the random orthonormal
+ *       projection re-drawn every step, identical on all workers) */
+typedef enum demo_basis { DEMO_BASIS_DCT = 0, DEMO_BASIS_USER = 1 } demo_basis;
+
+/* phi of DeMo summary §3.4 Base Optimizer Update: sign (Signum) or identity (SGD). */
+typedef enum demo_phi { DEMO_PHI_SIGN = 0, DEMO_PHI_IDENTITY = 1 } demo_phi;
+
+/* Denominator of the sparse average, DeMo summary §3.4 Server-Side Aggregation:
+ * CONTRIBUTORS  number of workers whose payload holds the index (default)
+ * WORKERS       W (a worker without the index contributes a zero) */
+typedef enum demo_average { DEMO_AVG_CONTRIBUTORS = 0, DEMO_AVG_WORKERS = 1 } demo_average;
+
+typedef struct demo_shape {
+  int32_t ndim;    /* 1 or 2 */
+  int64_t dims[2]; /* dims[1] ignored for ndim 1; each in 1 .. 2^31-1 */
+} demo_shape;
+
+typedef struct demo_codec_cfg {
+  int32_t chunk;         /* chunk edge s; must be DEMO_CHUNK */
+  int32_t k;             /* coefficients kept per chunk, >= 1; clamped to the chunk's element count */
+  float beta;            /* momentum decay (DeMo summary §3.4 Decoupled Local Momentum Updates) */
+  float alpha;           /* momentum-subtraction coefficient (§3.4 Momentum Subtraction) */
+  int32_t momentum_form; /* demo_momentum_form */
+  int32_t basis;         /* demo_basis */
+  const float* P0;       /* DEMO_BASIS_USER: device 64x64 fp32 row-major, rows are the basis
+                            vectors; acts on dimension 0 and on vectors */
+  const float* P1;       /* DEMO_BASIS_USER with any matrix: device 64x64, acts on dimension 1 */
+} demo_codec_cfg;
+
+typedef struct demo_ctx demo_ctx;
+
+/* Bind a context to HIP device `device`; fails with DEMO_ERR_DEVICE unless it is gfx950.
+ * Every later call must run with that device current. */
+demo_status demo_ctx_create(int32_t device, demo_ctx** out);
+void demo_ctx_destroy(demo_ctx* ctx);
+
+/* Thread-local description of the last non-DEMO_OK status of this thread ("" if none). */
+const char* demo_last_error(void);
+
+/* Host-only planning (no device work, no context needed).
+ * n_chunks:    total chunks of the list (may be NULL)
+ * n_entries:   payload entries per worker, sum over chunks of keff (may be NULL)
+ * entry_begin: if not NULL, n+1 entries: payload offset of every tensor's first
+ *              chunk, and the total at [n]. */
+demo_status demo_plan(const demo_shape* shapes, int32_t n, int32_t chunk, int32_t k, int64_t* n_chunks,
+                      int64_t* n_entries, int64_t* entry_begin);
+
+/* One worker's encode of a tensor list (DeMo summary §3.4: Decoupled Local
+ * Momentum Updates, Tensor Chunking, Blockwise Linear Projection, Top-k
+ * Sparsification, Momentum Subtraction as Implicit Error Feedback).
+ *   grads[i]:  device, shapes[i], element type grad_dtype; read only
+ *   moms[i]:   device float32, shapes[i]; read and overwritten with
+ *              M' - alpha * unchunk(P0^T Q_hat P1), where M' is the updated
+ *              momentum and Q_hat this worker's own selected coefficients
+ *   pay_values / pay_idx: device arrays of n_entries entries, written
+ * Top-k ranks float32 magnitudes; equal magnitudes go to the lower index. */
+demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, const void* const* grads,
+                        demo_dtype grad_dtype, float* const* moms, const demo_codec_cfg* cfg, float* pay_values,
+                        uint16_t* pay_idx, int64_t n_entries, hipStream_t stream);
+
+/* Decode W payloads and apply the update to a tensor list (DeMo summary §3.4:
+ * Server-Side Aggregation and Momentum Reconstruction, Inverse DCT and
+ * Unchunking, Base Optimizer Update).
+ *   params[i]:  device float32, shapes[i]; read and overwritten with
+ *               X - eta * (phi(M*) + lambda * X), X the pre-update value
+ *   pay_values / pay_idx: device, workers x n_entries entries (worker-major, as
+ *               an all-gather lays them out); read only
+ * cfg supplies chunk, k and the basis; its beta, alpha and momentum_form are unused.
+ * Coefficients are summed in worker order 0..W-1; the result is deterministic. */
+demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                              const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                              const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
+                              demo_average avg, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DEMO_CODEC_H */

@@ -1,0 +1,189 @@
+"""Comparison rules between the HIP path and the CPU oracle.
+
+Tolerance (floating point), elementwise:
+    |gpu - ref| <= atol + RTOL * |ref|,  atol = max(ATOL, NOISE * ||chunk||_F)
+RTOL = 1e-5 and ATOL = 1e-7 are the stated float32 tolerances; at the
+workloads' data scales (momenta of 1e-6..1e-5) ATOL is the binding term.
+NOISE * ||chunk||_F only matters for unit-scale stress inputs: a float32
+orthonormal transform's rounding error scales with the chunk's norm, not
+with the element, so near-zero elements of a large chunk get an absolute
+floor of 2^-20 of the chunk norm (about 16 float32 ulps of it).
+
+Top-k indices must equal the oracle's exactly, except at near ties: with K
+the oracle's keff-th largest magnitude, coefficients with |Q| > K + tol are
+forced, those within tol of K form the tie window, tol = RTOL * K +
+NOISE * ||Q||_F.  A GPU set that holds every forced index and fills the
+rest from the window is valid; its residual is then compared with the
+oracle's residual for that same set, taken from the oracle-side list of all
+valid sets.  The chunk is marked diverged and left out of later steps
+(its state legitimately differs from then on).
+
+Signum: elements with |M*_ref| <= RTOL * max|M*_ref| over their chunk may
+flip sign (a rounding artefact); there X may differ by up to 2 eta, and the
+element is marked diverged.
+"""
+from __future__ import annotations
+
+import itertools
+from math import comb
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from oracle import demo_oracle as O
+
+RTOL = 1e-5
+ATOL = 1e-7
+NOISE = 2.0 ** -20
+MAX_ALTERNATIVES = 256
+
+
+def layout(shapes: Sequence[Sequence[int]], k: int, s: int = 64) -> List[Tuple[int, int, int]]:
+    """(n_chunks, keff, entry_begin) per tensor, counted by the oracle's rules."""
+    out, e = [], 0
+    for shp in shapes:
+        n = int(np.prod(O.chunk_grid(shp, s)))
+        keff = O.k_effective(k, s if len(shp) == 1 else s * s)
+        out.append((n, keff, e))
+        e += n * keff
+    return out
+
+
+def chunk_mask_to_elements(mask: np.ndarray, shape, s: int = 64) -> np.ndarray:
+    """Expand a per-chunk boolean mask to the tensor's elements."""
+    n = mask.shape[0]
+    block = (n, s) if len(shape) == 1 else (n, s, s)
+    full = np.broadcast_to(mask.reshape((n,) + (1,) * (len(block) - 1)), block)
+    return O.merge_chunks(full, shape, s).astype(bool)
+
+
+def _tol(ref: np.ndarray, atol) -> np.ndarray:
+    return atol + RTOL * np.abs(ref)
+
+
+def topk_window(q: np.ndarray, keff: int):
+    """(forced, window, quota) of one chunk's valid top-k sets (oracle values, float64)."""
+    mags = np.abs(q)
+    numel = mags.size
+    if keff >= numel:
+        return np.arange(numel), np.array([], dtype=np.int64), 0
+    key = mags.astype(np.float32)
+    order = np.argsort(-key, kind="stable")
+    kth = mags[order[keff - 1]]
+    tol = RTOL * kth + NOISE * np.linalg.norm(q)
+    forced = np.nonzero(mags > kth + tol)[0]
+    window = np.nonzero(np.abs(mags - kth) <= tol)[0]
+    return forced, window, keff - forced.size
+
+
+class EncodeReport:
+    def __init__(self):
+        self.chunks = 0
+        self.exact = 0
+        self.ties = 0
+        self.skipped = 0
+
+
+def compare_encode(out: dict, shape, keff: int, alpha: float, P0, P1, gpu_M: np.ndarray,
+                   gpu_vals: np.ndarray, gpu_idx: np.ndarray, diverged: np.ndarray,
+                   report: EncodeReport, where: str = "") -> np.ndarray:
+    """Check one tensor's encode; returns the updated diverged-chunk mask.
+
+    out: oracle.encode(...) result (float64 Mp_chunks and Q included).
+    gpu_vals / gpu_idx: [n_chunks, keff] payload of the tensor.
+    """
+    n = out["Q"].shape[0]
+    Qf = out["Q"].reshape(n, -1)
+    norms = np.linalg.norm(Qf, axis=1)
+    oidx = out["idx"].astype(np.int64)
+    gidx = gpu_idx.astype(np.int64)
+    assert gidx.shape == oidx.shape, where
+    # payload indices are ascending inside each chunk
+    if keff > 1:
+        assert np.all(np.diff(gidx, axis=1) > 0), f"{where}: payload indices not ascending"
+    same = np.all(gidx == oidx, axis=1)
+    new_div = diverged.copy()
+    expect_chunks = None
+    extra_atol = np.zeros(n)
+    for c in np.nonzero(~same & ~diverged)[0]:
+        forced, window, quota = topk_window(Qf[c], keff)
+        g = set(gidx[c].tolist())
+        ok = set(forced.tolist()) <= g and g <= set(forced.tolist()) | set(window.tolist())
+        assert ok, (f"{where}: chunk {c} GPU top-k set is not a valid top-{keff}: "
+                    f"differs from oracle at {sorted(g ^ set(oidx[c].tolist()))[:8]}")
+        report.ties += 1
+        new_div[c] = True
+        if expect_chunks is None:
+            expect_chunks = O.split_chunks(out["M"].astype(np.float64))
+        if comb(window.size, quota) <= MAX_ALTERNATIVES:
+            alts = [np.sort(np.concatenate([forced, np.array(sub, dtype=np.int64)]))
+                    for sub in itertools.combinations(window.tolist(), quota)]
+            match = [a for a in alts if np.array_equal(a, gidx[c])]
+            assert match, f"{where}: chunk {c} set not among the oracle's valid sets"
+            S = match[0][None, :]
+            expect_chunks[c] = O.subtract_selected(out["Mp_chunks"][c:c + 1], out["Q"][c:c + 1], S, alpha,
+                                                   P0, P1)[0]
+        else:
+            # huge window: coefficients in it are near the noise floor; bound the residual difference
+            kth = np.abs(Qf[c][oidx[c]]).min()
+            tol = RTOL * kth + NOISE * norms[c]
+            extra_atol[c] = 2.0 * quota * (kth + tol) * abs(alpha) * (2.0 / 64.0) * 1.01
+    report.chunks += n
+    report.exact += int(np.sum(same & ~diverged))
+    report.skipped += int(np.sum(diverged))
+
+    # payload values at the GPU's indices, against the oracle's Q there
+    live = ~diverged
+    qg = np.take_along_axis(Qf, gidx, axis=1)
+    atol_c = np.maximum(ATOL, NOISE * norms)[:, None]
+    bad = np.abs(gpu_vals - qg) > _tol(qg, atol_c)
+    bad &= live[:, None]
+    assert not bad.any(), f"{where}: payload values differ (chunk {np.nonzero(bad.any(axis=1))[0][:5]})"
+
+    # new momentum, per element, chunks not diverged before this step
+    ref_M = out["M"].astype(np.float64) if expect_chunks is None else O.merge_chunks(expect_chunks, shape)
+    mp_norm = np.linalg.norm(out["Mp_chunks"].reshape(n, -1), axis=1)
+    atol_e = chunk_values_to_elements(np.maximum(ATOL, NOISE * mp_norm) + extra_atol, shape)
+    emask = chunk_mask_to_elements(live, shape)
+    diff = np.abs(gpu_M.astype(np.float64) - ref_M)
+    bad = (diff > _tol(ref_M, atol_e)) & emask
+    if bad.any():
+        i = np.argmax(np.where(bad, diff, 0))
+        raise AssertionError(f"{where}: momentum differs at flat {i}: gpu {gpu_M.ravel()[i]!r} "
+                             f"ref {ref_M.ravel()[i]!r} ({int(bad.sum())} elements)")
+    return new_div
+
+
+def chunk_values_to_elements(vals: np.ndarray, shape, s: int = 64) -> np.ndarray:
+    n = vals.shape[0]
+    block = (n, s) if len(shape) == 1 else (n, s, s)
+    full = np.broadcast_to(vals.reshape((n,) + (1,) * (len(block) - 1)), block)
+    return O.merge_chunks(full, shape, s)
+
+
+def compare_decode(dec: dict, shape, phi: str, eta: float, gpu_X: np.ndarray, chunk_diverged: np.ndarray,
+                   elem_diverged: Optional[np.ndarray], where: str = "") -> np.ndarray:
+    """Check one tensor's decode/apply; returns the updated diverged-element mask."""
+    ref = dec["X"].astype(np.float64)
+    Mstar = dec["Mstar"]
+    emask = ~chunk_mask_to_elements(chunk_diverged, shape)
+    if elem_diverged is not None:
+        emask &= ~elem_diverged
+    new_elem = np.zeros(shape, dtype=bool) if elem_diverged is None else elem_diverged.copy()
+    diff = np.abs(gpu_X.astype(np.float64) - ref)
+    tol = _tol(ref, ATOL)
+    if phi == "sign":
+        ch = O.split_chunks(np.abs(Mstar))
+        cmax = ch.reshape(ch.shape[0], -1).max(axis=1)
+        thresh = chunk_values_to_elements(RTOL * cmax, shape)
+        near0 = np.abs(Mstar) <= thresh
+        flip = near0 & (diff > tol)
+        assert not np.any(flip & emask & (diff > 2 * eta + tol)), f"{where}: near-zero sign element off by > 2 eta"
+        new_elem |= flip
+        emask &= ~flip
+    bad = (diff > tol) & emask
+    if bad.any():
+        i = np.argmax(np.where(bad, diff, 0))
+        raise AssertionError(f"{where}: parameters differ at flat {i}: gpu {gpu_X.ravel()[i]!r} "
+                             f"ref {ref.ravel()[i]!r} M* {Mstar.ravel()[i]!r} ({int(bad.sum())} elements)")
+    return new_elem

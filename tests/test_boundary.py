@@ -1,0 +1,171 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load on a machine without a GPU, export every function the
+public header declares, plan payloads exactly as the oracle counts them, and
+reject every malformed argument before touching a device (a NULL context is
+only reported once all other arguments passed).
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import demo_inputs as DI
+from communication_compressed_optimizer_demo_amd import binding as B
+from oracle import demo_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from communication_compressed_optimizer_demo_amd import build
+        build.build()
+    return B.load_library()
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w \*]*?\b(demo_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("demo_encode", "demo_decode_apply", "demo_plan", "demo_ctx_create", "demo_ctx_destroy",
+                     "demo_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("name", sorted(DI.WORKLOADS))
+def test_plan_matches_oracle_payload_count(lib, name):
+    w = DI.WORKLOADS[name]
+    for k in (1, w.k, 64, 4096, 5000):
+        n_chunks, n_entries, begin = B.demo_plan(w.shapes, k)
+        assert n_entries == O.payload_entries(w.shapes, k)
+        assert n_chunks == sum(int(__import__("numpy").prod(O.chunk_grid(s))) for s in w.shapes)
+        acc = 0
+        for i, s in enumerate(w.shapes):
+            assert begin[i] == acc
+            numel = 64 if len(s) == 1 else 4096
+            acc += int(__import__("numpy").prod(O.chunk_grid(s))) * O.k_effective(k, numel)
+        assert begin[len(w.shapes)] == acc == n_entries
+
+
+def test_plan_olmo_sizes(lib):
+    # payload sizes the survey tabulates for the OLMo-shaped sets
+    assert B.demo_plan(DI.WORKLOADS["olmo_1b"].shapes, 32)[:2] == (197632, 6324224)
+    assert B.demo_plan(DI.WORKLOADS["olmo_300m"].shapes, 8)[:2] == (74496, 595968)
+    assert DI.WORKLOADS["olmo_1b"].n_params == 805371904
+    assert DI.WORKLOADS["olmo_300m"].n_params == 302039040
+
+
+def _call_encode(lib, shapes, k=8, chunk=64, grad_dtype=0, beta=0.9, alpha=0.2, form=0, basis=0,
+                 P0=None, P1=None, entries=None, grads=0x1000, moms=0x2000, vals=0x3000, idx=0x4000):
+    cfg = B.demo_codec_cfg(chunk, k, beta, alpha, form, basis, P0, P1)
+    n = len(shapes)
+    sh = B._shapes(shapes)
+    if entries is None:
+        entries = O.payload_entries(shapes, max(k, 1)) if k >= 1 and chunk == 64 else 0
+    gp = B._ptrs([grads] * n)
+    mp = B._ptrs([moms] * n)
+    return lib.demo_encode(None, n, sh, gp, grad_dtype, mp, ctypes.byref(cfg), vals, idx, entries, None)
+
+
+def _call_decode(lib, shapes, k=8, workers=2, phi=0, avg=0, eta=1e-3, lam=0.0, entries=None, params=0x1000,
+                 vals=0x3000, idx=0x4000, basis=0, P0=None, P1=None):
+    cfg = B.demo_codec_cfg(64, k, 0.9, 0.2, 0, basis, P0, P1)
+    n = len(shapes)
+    if entries is None:
+        entries = O.payload_entries(shapes, k)
+    return lib.demo_decode_apply(None, n, B._shapes(shapes), B._ptrs([params] * n), ctypes.byref(cfg), workers,
+                                 vals, idx, entries, phi, eta, lam, avg, None)
+
+
+def _msg(lib):
+    return lib.demo_last_error().decode()
+
+
+def test_valid_arguments_reach_the_context_check(lib):
+    assert _call_encode(lib, [(128, 64), (100,)]) == 1 and "context" in _msg(lib)
+    assert _call_decode(lib, [(128, 64), (100,)]) == 1 and "context" in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shapes=[(0, 5)]), 2),
+    (dict(shapes=[(5, 0)]), 2),
+    (dict(shapes=[(3, 4, 5)]), 2),
+    (dict(shapes=[(2 ** 31, 4)]), 2),
+    (dict(k=0), 3),
+    (dict(k=-3), 3),
+    (dict(chunk=128), 3),
+    (dict(grad_dtype=7), 1),
+    (dict(form=2), 1),
+    (dict(beta=float("nan")), 1),
+    (dict(alpha=float("inf")), 1),
+    (dict(entries=5), 4),
+    (dict(grads=0), 1),
+    (dict(moms=0), 1),
+    (dict(vals=0), 1),
+    (dict(grads=0x1002), 7),
+    (dict(grads=0x1002, grad_dtype=1), 1 + 0 * 7),  # bf16 needs 2-byte alignment only: reaches ctx check
+    (dict(moms=0x2001), 7),
+    (dict(vals=0x3002), 7),
+    (dict(idx=0x4001), 7),
+    (dict(basis=5), 1),
+    (dict(basis=1), 1),
+    (dict(basis=1, P0=0x5000), 1),
+    (dict(basis=1, P0=0x5002, P1=0x6000), 7),
+])
+def test_encode_rejects_bad_arguments(lib, kw, status):
+    shapes = kw.pop("shapes", [(128, 64), (100,)])
+    assert _call_encode(lib, shapes, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(workers=0), 3),
+    (dict(workers=256), 3),
+    (dict(phi=2), 1),
+    (dict(avg=2), 1),
+    (dict(eta=float("nan")), 1),
+    (dict(lam=float("inf")), 1),
+    (dict(entries=1), 4),
+    (dict(params=0), 1),
+    (dict(params=0x1001), 7),
+    (dict(vals=0), 1),
+    (dict(idx=0x4001), 7),
+    (dict(k=0), 3),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert _call_decode(lib, [(128, 64), (100,)], **kw) == status
+
+
+def test_vectors_only_user_basis_needs_no_p1(lib):
+    # 1-D tensors use P0 only: valid arguments reach the context check
+    assert _call_encode(lib, [(100,)], basis=1, P0=0x5000) == 1 and "context" in _msg(lib)
+
+
+def test_empty_tensor_list_is_valid(lib):
+    assert _call_encode(lib, [], entries=0) == 1 and "context" in _msg(lib)
+    nc, ne, begin = B.demo_plan([], 8)
+    assert (nc, ne, begin) == (0, 0, [0])
+
+
+def test_ctx_create_without_gpu_fails_cleanly(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(B.DemoError):
+        B.demo_ctx_create(0)

@@ -1,0 +1,204 @@
+"""Parity of the HIP codec with the CPU oracle, through the C ABI.
+
+Every case runs W simulated workers: each worker encodes its own seeded
+gradients on the GPU and in the oracle, both free-running from the same
+initial state; then all W payloads are decoded and applied on the GPU and
+in the oracle.  Comparison rules (tolerances, near-tie and sign exemptions)
+are in parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import demo_inputs as DI
+import parity as PR
+from communication_compressed_optimizer_demo_amd import binding as B
+from oracle import demo_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+    return torch.device("cuda:0")
+
+
+class Sim:
+    """W workers of one workload, GPU next to the oracle."""
+
+    def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None):
+        self.w = w
+        self.plain = plain
+        self.avg = avg
+        self.inputs = inputs  # optional callable (worker, step, tensor) -> float32 gradient
+        self.shapes = [tuple(s) for s in w.shapes]
+        self.codec = B.Codec(self.shapes, w.k, w.beta, w.alpha, plain)
+        self.lay = PR.layout(self.shapes, w.k)
+        nc, ne, eb = B.demo_plan(self.shapes, w.k)
+        assert ne == sum(n * k for n, k, _ in self.lay)
+        assert eb[:-1] == [e for _, _, e in self.lay]
+        W = w.workers
+        self.M_gpu = [[torch.zeros(s, dtype=torch.float32, device="cuda") for s in self.shapes] for _ in range(W)]
+        self.M_or = [[np.zeros(s, dtype=np.float32) for s in self.shapes] for _ in range(W)]
+        X0 = [DI.initial_params(w, i) for i in range(len(self.shapes))]
+        self.X_gpu = [torch.from_numpy(x.copy()).cuda() for x in X0]
+        self.X_or = [x.copy() for x in X0]
+        self.vals, self.idx = self.codec.alloc_payload(W)
+        self.cdiv = [[np.zeros(n, dtype=bool) for n, _, _ in self.lay] for _ in range(W)]
+        self.ediv = [None for _ in self.shapes]
+        self.report = PR.EncodeReport()
+
+    def grad(self, worker, step, i):
+        if self.inputs is not None:
+            return self.inputs(worker, step, i)
+        return DI.gradient(self.w, worker, step, i)
+
+    def basis(self, step):
+        if not self.w.random_basis:
+            return None, None, None, None
+        P0 = O.orthonormal_rows(DI.gaussian_matrix(self.w, step, 0)).astype(np.float32)
+        P1 = O.orthonormal_rows(DI.gaussian_matrix(self.w, step, 1)).astype(np.float32)
+        return P0, P1, torch.from_numpy(P0).cuda(), torch.from_numpy(P1).cuda()
+
+    def step(self, t):
+        w = self.w
+        W = w.workers
+        P0, P1, P0d, P1d = self.basis(t)
+        ne = self.codec.n_entries
+        phi_c = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
+        avg_c = B.DEMO_AVG_CONTRIBUTORS if self.avg == "count" else B.DEMO_AVG_WORKERS
+        or_vals = [[None] * W for _ in self.shapes]
+        or_idx = [[None] * W for _ in self.shapes]
+        for wk in range(W):
+            G = [self.grad(wk, t, i) for i in range(len(self.shapes))]
+            gd = [torch.from_numpy(g).cuda() for g in G]
+            if w.grad_bf16:
+                gd = [g.to(torch.bfloat16) for g in gd]
+            say(f"  [{w.name}] step {t} worker {wk}: GPU encode")
+            self.codec.encode(gd, self.M_gpu[wk], self.vals[wk * ne:(wk + 1) * ne],
+                              self.idx[wk * ne:(wk + 1) * ne], P0d, P1d)
+            torch.cuda.synchronize()
+            gv = self.vals[wk * ne:(wk + 1) * ne].cpu().numpy()
+            gi = self.idx[wk * ne:(wk + 1) * ne].cpu().numpy().view(np.uint16)
+            for i, shp in enumerate(self.shapes):
+                n, keff, e0 = self.lay[i]
+                out = O.encode(self.M_or[wk][i], G[i], beta=w.beta, alpha=w.alpha, k=w.k, plain=self.plain,
+                               P0=P0, P1=P1)
+                gM = self.M_gpu[wk][i].cpu().numpy()
+                self.cdiv[wk][i] = PR.compare_encode(
+                    out, shp, keff, w.alpha, O.dct_basis() if P0 is None else P0,
+                    O.dct_basis() if P1 is None else P1, gM, gv[e0:e0 + n * keff].reshape(n, keff),
+                    gi[e0:e0 + n * keff].reshape(n, keff), self.cdiv[wk][i], self.report,
+                    where=f"{w.name} step {t} worker {wk} tensor {i} {shp}")
+                self.M_or[wk][i] = out["M"]
+                or_vals[i][wk] = out["values"]
+                or_idx[i][wk] = out["idx"]
+        say(f"  [{w.name}] step {t}: GPU decode/apply over {W} payloads")
+        self.codec.decode_apply(self.X_gpu, W, self.vals, self.idx, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
+        torch.cuda.synchronize()
+        for i, shp in enumerate(self.shapes):
+            dec = O.decode_apply(self.X_or[i], np.stack(or_vals[i]), np.stack(or_idx[i]), phi=w.phi, eta=w.eta,
+                                 lam=w.lam, mode=self.avg, P0=P0, P1=P1)
+            cd = np.zeros_like(self.cdiv[0][i])
+            for wk in range(W):
+                cd |= self.cdiv[wk][i]
+            self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
+                                             where=f"{w.name} step {t} tensor {i} {shp}")
+            self.X_or[i] = dec["X"]
+
+    def run(self, steps):
+        for t in range(steps):
+            self.step(t)
+        r = self.report
+        say(f"  [{self.w.name}] chunks checked {r.chunks}: exact {r.exact}, near-tie {r.ties}, skipped {r.skipped}")
+        assert r.ties + r.skipped <= max(2, 0.02 * r.chunks), "too many near-tie divergences"
+        return r
+
+
+def test_single_chunk_one_worker(dev):
+    w = DI.WORKLOADS["tiny_256"].replace(shapes=((64, 64),), workers=1, steps=2)
+    Sim(w).run(2)
+
+
+def test_tiny_256_ten_steps(dev):
+    w = DI.WORKLOADS["tiny_256"]
+    Sim(w).run(w.steps)
+
+
+@pytest.mark.parametrize("k,alpha,rand", [(1, 0.2, False), (4096, 1.0, False), (4096, 0.2, False),
+                                           (4, 0.2, True), (4096, 1.0, True), (37, 0.5, False)])
+def test_edge_mix(dev, k, alpha, rand):
+    w = DI.WORKLOADS["edge_mix"].replace(k=k, alpha=alpha, random_basis=rand)
+    Sim(w).run(w.steps)
+
+
+def test_single_4096_bf16_gradients(dev):
+    w = DI.WORKLOADS["single_4096"]
+    Sim(w).run(2)
+
+
+@pytest.mark.parametrize("k", [1, 8, 64, 4096])
+def test_tiny_and_ragged_shapes(dev, k):
+    w = DI.WORKLOADS["tiny_256"].replace(
+        name=f"ragged_k{k}", shapes=((1, 1), (1, 64), (64, 1), (2, 3), (65, 65), (1,), (63,), (65,), (130,)),
+        k=k, workers=2)
+    Sim(w).run(2)
+
+
+@pytest.mark.parametrize("plain,avg,phi", [(True, "count", "sign"), (False, "workers", "sign"),
+                                           (False, "count", "identity"), (True, "workers", "identity")])
+def test_momentum_form_average_and_phi(dev, plain, avg, phi):
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"modes_{plain}_{avg}_{phi}", shapes=((256, 192), (300,)),
+                                         phi=phi, workers=3)
+    Sim(w, plain=plain, avg=avg).run(3)
+
+
+def test_unit_scale_inputs(dev):
+    """Unit-scale momenta exercise the relative tolerance, not the 1e-7 floor."""
+    w = DI.WORKLOADS["tiny_256"].replace(name="unit_scale", shapes=((192, 320), (129,)), grad_std=1.0,
+                                         param_std=1.0, beta=0.9, k=16, workers=3, eta=0.01)
+    Sim(w, plain=True).run(3)
+
+
+def test_degenerate_chunks(dev):
+    """All-zero, constant and single-basis-function gradients (exact ties in the top-k)."""
+    P = O.dct_basis()
+    w = DI.WORKLOADS["tiny_256"].replace(name="degenerate", shapes=((64, 64), (64, 128), (64, 64), (200,)),
+                                         k=8, workers=2)
+
+    def inputs(worker, step, i):
+        if i == 0:
+            return np.zeros((64, 64), np.float32)
+        if i == 1:
+            return np.full((64, 128), 1e-3 * (worker + 1), np.float32)
+        if i == 2:
+            return (1e-3 * np.outer(P[3], P[7])).astype(np.float32)
+        return np.full((200,), -2e-3, np.float32)
+
+    Sim(w, inputs=inputs).run(2)
+
+
+def test_deterministic_repeat(dev):
+    w = DI.WORKLOADS["tiny_256"].replace(name="repeat", shapes=((256, 256), (100,)), workers=3)
+    results = []
+    for _ in range(2):
+        codec = B.Codec(w.shapes, w.k, w.beta, w.alpha)
+        M = [[torch.zeros(s, device="cuda") for s in w.shapes] for _ in range(3)]
+        X = [torch.from_numpy(DI.initial_params(w, i)).cuda() for i in range(2)]
+        v, ix = codec.alloc_payload(3)
+        ne = codec.n_entries
+        for t in range(3):
+            for wk in range(3):
+                g = [torch.from_numpy(DI.gradient(w, wk, t, i)).cuda() for i in range(2)]
+                codec.encode(g, M[wk], v[wk * ne:(wk + 1) * ne], ix[wk * ne:(wk + 1) * ne])
+            codec.decode_apply(X, 3, v, ix, B.DEMO_PHI_SIGN, w.eta, w.lam)
+        torch.cuda.synchronize()
+        results.append([t.cpu().numpy() for t in [v, ix] + X + M[0] + M[1] + M[2]])
+    for a, b in zip(*results):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
