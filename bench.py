@@ -35,6 +35,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "communication_compressed_optimizer_demo_amd", "csrc", "kernels.hip")
 
 
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,8 +76,10 @@ def cpu_baseline(w: DI.Workload):
     shape = w.shapes[t_idx]
     ctx = mp.get_context("fork")
     nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+    log(f"cpu baseline: {w.workers - 1} foreign payloads of a {shape} tensor on {nproc} processes")
     with concurrent.futures.ProcessPoolExecutor(nproc, mp_context=ctx) as ex:
         foreign = list(ex.map(_foreign_payload, [(w.name, wk, t_idx) for wk in range(1, w.workers)]))
+    log("cpu baseline: timing the oracle")
     g0 = DI.gradient(w, 0, 0, t_idx)
     m0 = np.zeros_like(g0)
     x0 = DI.initial_params(w, t_idx)
@@ -83,6 +89,7 @@ def cpu_baseline(w: DI.Workload):
     idx = np.stack([out["idx"]] + [f[1] for f in foreign])
     O.decode_apply(x0, vals, idx, phi=w.phi, eta=w.eta, lam=w.lam)
     dt = time.perf_counter() - t0
+    log(f"cpu baseline: {dt:.2f} s")
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     n = int(np.prod(shape))
     return {
@@ -144,6 +151,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int):
         gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
         ne = gr["codec"].n_entries
         gr["ne"] = ne
+        log(f"{len(gr['shapes'])} tensors of ndim {gr['ndim']}: encoding {W - 1} foreign payloads")
         # other workers' payloads, untimed
         scratch_m = [torch.zeros(s, device=dev) for s in gr["shapes"]]
         for wk in range(1, W):
@@ -176,9 +184,11 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int):
                 j += 1
                 ev[j].record(stream)
 
+    log(f"warmup {warmup} steps")
     for _ in range(warmup):
         one_step(None)
     torch.cuda.synchronize()
+    log(f"timing {steps} steps")
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(groups) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -112,12 +112,12 @@ class Sim:
                                              where=f"{w.name} step {t} tensor {i} {shp}")
             self.X_or[i] = dec["X"]
 
-    def run(self, steps):
+    def run(self, steps, max_tie_fraction=0.02):
         for t in range(steps):
             self.step(t)
         r = self.report
         say(f"  [{self.w.name}] chunks checked {r.chunks}: exact {r.exact}, near-tie {r.ties}, skipped {r.skipped}")
-        assert r.ties + r.skipped <= max(2, 0.02 * r.chunks), "too many near-tie divergences"
+        assert r.ties + r.skipped <= max(2, max_tie_fraction * r.chunks), "too many near-tie divergences"
         return r
 
 
@@ -181,7 +181,9 @@ def test_degenerate_chunks(dev):
             return (1e-3 * np.outer(P[3], P[7])).astype(np.float32)
         return np.full((200,), -2e-3, np.float32)
 
-    Sim(w, inputs=inputs).run(2)
+    # constant and single-frequency chunks tie exactly at zero: every such chunk may take the window path
+    r = Sim(w, inputs=inputs).run(2, max_tie_fraction=1.0)
+    assert r.exact >= 4
 
 
 def test_deterministic_repeat(dev):
