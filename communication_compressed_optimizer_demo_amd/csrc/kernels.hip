@@ -4,7 +4,7 @@
 // 64-element chunks (1-D).  Data move between two register layouts:
 //   column layout: lane j holds column j, x[i] = element (i, j);
 //   row layout:    lane u holds row u,    x[v] = element (u, v).
-// A coalesced global access of one row per instruction (64 lanes x 4 bytes)
+// A coalesced global access of one 256-byte row segment per instruction
 // fills the column layout directly; a 64x65-float LDS tile (row stride 65:
 // row and column accesses are both bank-conflict free) converts between the
 // two.  Each 64-point transform runs inside one lane's registers.
@@ -14,15 +14,19 @@
 // Subtraction):
 //   load G, M -> M' = beta M + c G (registers, column layout)
 //   Q = P0 M' P1^T  (column pass, LDS transpose, row pass)
-//   exact top-k of |Q| over the chunk, lower index wins ties
-//   payload (value, index) in index order
-//   R = P0^T Q_hat P1 (row pass, LDS transpose, column pass); M = M' - alpha R
+//   exact top-k of |Q| over the chunk, lower index wins ties; payload
+//   (value, index) in index order
+//   M = P0^T (Q - alpha Q_hat) P1 (row pass, LDS transpose, column pass),
+//   which equals M' - alpha P0^T Q_hat P1 because P0, P1 are orthonormal
 // decode/apply (§3.4 Server-Side Aggregation, Inverse DCT and Unchunking,
 // Base Optimizer Update):
-//   scatter-add W payloads into an LDS accumulator with 8-bit counts, in
-//   worker order 0..W-1 (indices are distinct within one payload, so no
-//   atomics); average; M* = P0^T Q_bar P1; X = X - eta (phi(M*) + lambda X).
+//   scatter-add W payloads into an LDS accumulator with 8-bit contributor
+//   counts, one LDS atomic instruction per worker in worker order 0..W-1
+//   (indices are distinct within one payload, so the lanes of one
+//   instruction never collide and the sum order is fixed); average;
+//   M* = P0^T Q_bar P1; X = X - eta (phi(M*) + lambda X).
 #include "launch.h"
+#include "topk.h"
 #include "xform.h"
 
 namespace demo {
@@ -31,31 +35,11 @@ namespace {
 using xf::DctBasis;
 using xf::DenseBasis;
 
-constexpr int kLd = 65;  // LDS tile row stride in floats
+constexpr int kLd = 65;     // LDS tile row stride in floats
+constexpr int kCntLd = 17;  // count rows: 16 words of 8-bit counts + 1 pad word
+constexpr int kWorkerBatch = 16;
 
-// ---------------------------------------------------------------- wave helpers
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
-  int s = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(s, o);
-    if (lane >= o) s += t;
-  }
-  return s - v;
-}
+// ---------------------------------------------------------------- helpers
 
 __device__ __forceinline__ int find_tensor(const LaunchTable& tab, int item) {
   int lo = 0, hi = tab.n - 1;
@@ -101,146 +85,50 @@ __device__ __forceinline__ void row_to_col(float* tile, float (&x)[64], int lane
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- top-k of one 64x64 chunk
+struct ChunkPos {
+  int local;     // chunk ordinal within its tensor
+  int vr, vc;    // valid rows / columns of the chunk
+  int64_t base;  // element offset of the chunk's (0, 0)
+  bool full;
+};
 
-// Row layout in q (lane u holds Q[u][0..63]).  Keeps the keff largest |Q|
-// (ties: lower index u*64+v first), writes them in index order to outv/outi
-// and zeroes every other entry of q (q becomes Q_hat).
-//
-// Exact selection: K, the keff-th largest magnitude, is built bit by bit
-// from the top (a candidate T is kept when at least keff magnitudes are
-// >= T).  Then every |Q| > K is taken, and of the |Q| == K the first
-// keff - #(|Q| > K) in index order.
-__device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, float* __restrict__ outv,
-                                           uint16_t* __restrict__ outi) {
-  if (keff >= 4096) {
-#pragma unroll
-    for (int v = 0; v < 64; ++v) {
-      outv[lane * 64 + v] = q[v];
-      outi[lane * 64 + v] = static_cast<uint16_t>(lane * 64 + v);
-    }
-    return;
-  }
-  float lmax = 0.f;
-#pragma unroll
-  for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(q[v]));
-  const uint32_t hi = __float_as_uint(wave_max(lmax));
-  uint32_t T = 0;
-  for (int b = 30; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    if (cand > hi) continue;
-    const float cf = __uint_as_float(cand);
-    int c = 0;
-#pragma unroll
-    for (int v = 0; v < 64; ++v) c += fabsf(q[v]) >= cf ? 1 : 0;
-    if (wave_sum(c) >= keff) T = cand;
-  }
-  const float K = __uint_as_float(T);
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int v = 0; v < 64; ++v) {
-    const float a = fabsf(q[v]);
-    gt += a > K ? 1 : 0;
-    eq += a == K ? 1 : 0;
-  }
-  const int quota = keff - wave_sum(gt);
-  const int eq_before = wave_excl_scan(eq, lane);
-  const int take_eq = min(max(quota - eq_before, 0), eq);
-  int off = wave_excl_scan(gt + take_eq, lane);
-  int eqr = eq_before;
-#pragma unroll
-  for (int v = 0; v < 64; ++v) {
-    const float a = fabsf(q[v]);
-    const bool is_eq = a == K;
-    const bool keep = a > K || (is_eq && eqr < quota);
-    eqr += is_eq ? 1 : 0;
-    if (keep) {
-      outv[off] = q[v];
-      outi[off] = static_cast<uint16_t>(lane * 64 + v);
-      ++off;
-    } else {
-      q[v] = 0.f;
-    }
-  }
-}
-
-// Per-lane top-k of one 64-element chunk held in q (1-D chunks, lane = chunk).
-__device__ __forceinline__ void topk_lane(float (&q)[64], int keff, bool write, float* __restrict__ outv,
-                                          uint16_t* __restrict__ outi) {
-  if (keff >= 64) {
-    if (write) {
-#pragma unroll
-      for (int v = 0; v < 64; ++v) {
-        outv[v] = q[v];
-        outi[v] = static_cast<uint16_t>(v);
-      }
-    }
-    return;
-  }
-  float lmax = 0.f;
-#pragma unroll
-  for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(q[v]));
-  const uint32_t hi = __float_as_uint(lmax);
-  uint32_t T = 0;
-  for (int b = 30; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    const float cf = __uint_as_float(cand);
-    int c = 0;
-#pragma unroll
-    for (int v = 0; v < 64; ++v) c += fabsf(q[v]) >= cf ? 1 : 0;
-    if (cand <= hi && c >= keff) T = cand;
-  }
-  const float K = __uint_as_float(T);
-  int gt = 0;
-#pragma unroll
-  for (int v = 0; v < 64; ++v) gt += fabsf(q[v]) > K ? 1 : 0;
-  const int quota = keff - gt;
-  int eqr = 0, off = 0;
-#pragma unroll
-  for (int v = 0; v < 64; ++v) {
-    const float a = fabsf(q[v]);
-    const bool is_eq = a == K;
-    const bool keep = a > K || (is_eq && eqr < quota);
-    eqr += is_eq ? 1 : 0;
-    if (keep) {
-      if (write) {
-        outv[off] = q[v];
-        outi[off] = static_cast<uint16_t>(v);
-      }
-      ++off;
-    } else {
-      q[v] = 0.f;
-    }
-  }
+__device__ __forceinline__ ChunkPos chunk_pos(const TensorSlot& ts, int item) {
+  ChunkPos c;
+  c.local = item - ts.item_begin;
+  const int cr = c.local / ts.grid1;
+  const int cc = c.local - cr * ts.grid1;
+  c.vr = min(64, ts.rows - cr * 64);
+  c.vc = min(64, ts.cols - cc * 64);
+  c.base = int64_t(cr) * 64 * ts.cols + int64_t(cc) * 64;
+  c.full = (c.vr == 64) && (c.vc == 64);
+  return c;
 }
 
 // ---------------------------------------------------------------- encode, 2-D chunks
 
 template <bool kFull, bool kBf16>
-__device__ __forceinline__ void load_momentum(float (&mp)[64], const TensorSlot& ts, int64_t base, int vr,
-                                              int vc, int lane, float beta, float gcoef) {
+__device__ __forceinline__ void load_momentum(float (&q)[64], const TensorSlot& ts, const ChunkPos& c, int lane,
+                                              float beta, float gcoef) {
   const int64_t ld = ts.cols;
-  const float* __restrict__ m = ts.dst;
+  const float* __restrict__ m = ts.dst + c.base;
+  const char* __restrict__ g = static_cast<const char*>(ts.src) + c.base * (kBf16 ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    float g = 0.f, mv = 0.f;
-    if (kFull || (lane < vc && i < vr)) {
-      const int64_t off = base + i * ld + lane;
-      g = load_src<kBf16>(ts.src, off);
-      mv = m[off];
+    float gv = 0.f, mv = 0.f;
+    if (kFull || (lane < c.vc && i < c.vr)) {
+      gv = load_src<kBf16>(g, i * ld + lane);
+      mv = m[i * ld + lane];
     }
-    mp[i] = fmaf(beta, mv, gcoef * g);
+    q[i] = fmaf(beta, mv, gcoef * gv);
   }
 }
 
 template <bool kFull>
-__device__ __forceinline__ void store_residual(const float (&mp)[64], const float (&r)[64], const TensorSlot& ts,
-                                               int64_t base, int vr, int vc, int lane, float alpha) {
-  const int64_t ld = ts.cols;
-  float* __restrict__ m = ts.dst;
+__device__ __forceinline__ void store_rows(const float (&q)[64], float* __restrict__ dst, int64_t ld,
+                                           const ChunkPos& c, int lane) {
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    if (kFull || (lane < vc && i < vr)) m[base + i * ld + lane] = fmaf(-alpha, r[i], mp[i]);
+    if (kFull || (lane < c.vc && i < c.vr)) dst[i * ld + lane] = q[i];
   }
 }
 
@@ -248,40 +136,31 @@ template <class Basis, bool kBf16>
 __global__ __launch_bounds__(64) void encode2d_kernel(LaunchTable tab, EncodeParams p, Basis basis) {
   __shared__ float tile[64 * kLd];
   const int lane = threadIdx.x;
-  const int item = blockIdx.x;
-  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
-  const int local = item - ts.item_begin;
-  const int cr = local / ts.grid1;
-  const int cc = local - cr * ts.grid1;
-  const int vr = min(64, ts.rows - cr * 64);
-  const int vc = min(64, ts.cols - cc * 64);
-  const int64_t base = int64_t(cr) * 64 * ts.cols + int64_t(cc) * 64;
-  const bool full = (vr == 64) && (vc == 64);
-
-  float mp[64];
-  if (full)
-    load_momentum<true, kBf16>(mp, ts, base, vr, vc, lane, p.beta, p.gcoef);
-  else
-    load_momentum<false, kBf16>(mp, ts, base, vr, vc, lane, p.beta, p.gcoef);
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const ChunkPos c = chunk_pos(ts, blockIdx.x);
 
   float q[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) q[i] = mp[i];
+  if (c.full)
+    load_momentum<true, kBf16>(q, ts, c, lane, p.beta, p.gcoef);
+  else
+    load_momentum<false, kBf16>(q, ts, c, lane, p.beta, p.gcoef);
+
   basis.fwd0(q);
   col_to_row(tile, q, lane);
   basis.fwd1(q);
 
-  const int64_t e0 = ts.entry_begin + int64_t(local) * p.keff;
-  topk_chunk(q, p.keff, lane, p.pay_val + e0, p.pay_idx + e0);
+  const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff;
+  tk::topk_chunk(q, p.keff, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
+  __syncthreads();
 
   basis.inv1(q);
   row_to_col(tile, q, lane);
   basis.inv0(q);
 
-  if (full)
-    store_residual<true>(mp, q, ts, base, vr, vc, lane, p.alpha);
+  if (c.full)
+    store_rows<true>(q, ts.dst + c.base, ts.cols, c, lane);
   else
-    store_residual<false>(mp, q, ts, base, vr, vc, lane, p.alpha);
+    store_rows<false>(q, ts.dst + c.base, ts.cols, c, lane);
 }
 
 // ---------------------------------------------------------------- encode, 1-D chunks
@@ -298,9 +177,9 @@ __global__ __launch_bounds__(64) void encode1d_kernel(LaunchTable tab, EncodePar
   const int slab = item - ts.item_begin;
   const int64_t first = int64_t(slab) * 64 * 64;  // element offset of the slab
   const int64_t len = ts.rows;
-  const float* __restrict__ m = ts.dst;
+  float* __restrict__ m = ts.dst;
 
-  float mp[64];
+  float q[64];
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
     const int64_t off = first + int64_t(c) * 64 + lane;
@@ -309,104 +188,134 @@ __global__ __launch_bounds__(64) void encode1d_kernel(LaunchTable tab, EncodePar
       g = load_src<kBf16>(ts.src, off);
       mv = m[off];
     }
-    mp[c] = fmaf(p.beta, mv, p.gcoef * g);
+    q[c] = fmaf(p.beta, mv, p.gcoef * g);
   }
-  float q[64];
-#pragma unroll
-  for (int c = 0; c < 64; ++c) q[c] = mp[c];
   col_to_row(tile, q, lane);
   basis.fwd0(q);
 
   const int chunk = slab * 64 + lane;  // this lane's chunk within the tensor
   const bool live = chunk < ts.grid1;
   const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff;
-  topk_lane(q, p.keff, live, p.pay_val + e0, p.pay_idx + e0);
+  tk::topk_lane(q, p.keff, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
 
   basis.inv0(q);
   row_to_col(tile, q, lane);
-  float* __restrict__ mo = ts.dst;
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
     const int64_t off = first + int64_t(c) * 64 + lane;
-    if (off < len) mo[off] = fmaf(-p.alpha, q[c], mp[c]);
+    if (off < len) m[off] = q[c];
   }
 }
 
 // ---------------------------------------------------------------- decode / apply
-
-__device__ __forceinline__ float average(float s, int c, const DecodeParams& p) {
-  if (p.avg_workers) return s * p.inv_workers;
-  return c ? s * __builtin_amdgcn_rcpf(float(c)) : 0.f;
-}
 
 __device__ __forceinline__ float update(float x, float m, const DecodeParams& p) {
   const float ph = p.phi_sign ? sign_of(m) : m;
   return fmaf(-p.eta, fmaf(p.lam, x, ph), x);
 }
 
-template <class Basis>
-__global__ __launch_bounds__(64) void decode2d_kernel(LaunchTable tab, DecodeParams p, Basis basis) {
-  __shared__ float acc[64 * kLd];
-  __shared__ uint32_t cntw[1024];
-  uint8_t* cnt = reinterpret_cast<uint8_t*>(cntw);
-  const int lane = threadIdx.x;
-  const int item = blockIdx.x;
-  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
-  const int local = item - ts.item_begin;
-  const int cr = local / ts.grid1;
-  const int cc = local - cr * ts.grid1;
-  const int vr = min(64, ts.rows - cr * 64);
-  const int vc = min(64, ts.cols - cc * 64);
-  const int64_t base = int64_t(cr) * 64 * ts.cols + int64_t(cc) * 64;
-
+// Zero the accumulator tile and the count rows.
+__device__ __forceinline__ void clear_acc(float* acc, uint32_t* cntw, int lane) {
   for (int i = lane; i < 64 * kLd; i += 64) acc[i] = 0.f;
-  for (int i = lane; i < 1024; i += 64) cntw[i] = 0u;
-  __syncthreads();
+  for (int i = lane; i < 64 * kCntLd; i += 64) cntw[i] = 0u;
+}
 
-  const int64_t e0 = ts.entry_begin + int64_t(local) * p.keff;
-  for (int w = 0; w < p.workers; ++w) {
-    const float* __restrict__ pv = p.pay_val + w * p.entries + e0;
-    const uint16_t* __restrict__ pi = p.pay_idx + w * p.entries + e0;
-    for (int e = lane; e < p.keff; e += 64) {
-      const int id = pi[e] & 4095;
-      acc[(id >> 6) * kLd + (id & 63)] += pv[e];
-      cnt[id] += 1;
+// Scatter-add the W payload segments of one 64x64 chunk (entries e0 ..
+// e0 + keff of every worker).  One LDS atomic instruction per (worker, entry
+// block); within it the indices are distinct, so no lanes collide and every
+// coefficient receives its terms in worker order.
+__device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0,
+                                              int lane) {
+  for (int eb = 0; eb < p.keff; eb += 64) {
+    const int e = eb + lane;
+    const bool on = e < p.keff;
+    for (int w0 = 0; w0 < p.workers; w0 += kWorkerBatch) {
+      float val[kWorkerBatch];
+      uint32_t ix[kWorkerBatch];
+#pragma unroll
+      for (int j = 0; j < kWorkerBatch; ++j) {
+        const int64_t off = int64_t(w0 + j) * p.entries + e0 + e;
+        const bool ok = on && (w0 + j) < p.workers;
+        val[j] = ok ? p.pay_val[off] : 0.f;
+        ix[j] = ok ? p.pay_idx[off] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kWorkerBatch; ++j) {
+        if (on && (w0 + j) < p.workers) {
+          const uint32_t id = ix[j] & 4095u;
+          const uint32_t u = id >> 6, v = id & 63u;
+          atomicAdd(&acc[u * kLd + v], val[j]);
+          atomicAdd(&cntw[u * kCntLd + (v >> 2)], 1u << ((v & 3u) * 8u));
+        }
+      }
     }
-    __syncthreads();
   }
+}
 
-  float q[64];
+// Row u of the average into q (row layout).
+__device__ __forceinline__ void average_row(float (&q)[64], const float* acc, const uint32_t* cntw,
+                                            const DecodeParams& p, int lane) {
+  if (p.avg_workers) {
 #pragma unroll
-  for (int v = 0; v < 64; ++v) q[v] = average(acc[lane * kLd + v], cnt[lane * 64 + v], p);
-  __syncthreads();
-  basis.inv1(q);
-  row_to_col(acc, q, lane);
-  basis.inv0(q);
-
-  float* __restrict__ x = ts.dst;
-  const int64_t ld = ts.cols;
-  if (vr == 64 && vc == 64) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const int64_t off = base + i * ld + lane;
-      x[off] = update(x[off], q[i], p);
-    }
+    for (int v = 0; v < 64; ++v) q[v] = acc[lane * kLd + v] * p.inv_workers;
   } else {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if (lane < vc && i < vr) {
-        const int64_t off = base + i * ld + lane;
-        x[off] = update(x[off], q[i], p);
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t w = cntw[lane * kCntLd + j];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float n = float((w >> (8 * b)) & 255u);
+        // n == 0 means no worker sent the coefficient; its sum is 0 as well
+        q[4 * j + b] = acc[lane * kLd + 4 * j + b] * __builtin_amdgcn_rcpf(fmaxf(n, 1.f));
       }
     }
   }
 }
 
 template <class Basis>
+__global__ __launch_bounds__(64) void decode2d_kernel(LaunchTable tab, DecodeParams p, Basis basis) {
+  __shared__ float acc[64 * kLd];
+  __shared__ uint32_t cntw[64 * kCntLd];
+  const int lane = threadIdx.x;
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const ChunkPos c = chunk_pos(ts, blockIdx.x);
+
+  clear_acc(acc, cntw, lane);
+  __syncthreads();
+  scatter_chunk(acc, cntw, p, ts.entry_begin + int64_t(c.local) * p.keff, lane);
+  __syncthreads();
+
+  // parameters are fetched now; they land while the average and the inverse transform run
+  const int64_t ld = ts.cols;
+  float* __restrict__ xp = ts.dst + c.base;
+  float x[64];
+  if (c.full) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = xp[i * ld + lane];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = (lane < c.vc && i < c.vr) ? xp[i * ld + lane] : 0.f;
+  }
+
+  float q[64];
+  average_row(q, acc, cntw, p, lane);
+  __syncthreads();
+  basis.inv1(q);
+  row_to_col(acc, q, lane);
+  basis.inv0(q);
+
+#pragma unroll
+  for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
+  if (c.full)
+    store_rows<true>(x, xp, ld, c, lane);
+  else
+    store_rows<false>(x, xp, ld, c, lane);
+}
+
+template <class Basis>
 __global__ __launch_bounds__(64) void decode1d_kernel(LaunchTable tab, DecodeParams p, Basis basis) {
   __shared__ float acc[64 * kLd];
-  __shared__ uint32_t cntw[1024];
-  uint8_t* cnt = reinterpret_cast<uint8_t*>(cntw);
+  __shared__ uint32_t cntw[64 * kCntLd];
   const int lane = threadIdx.x;
   const int item = blockIdx.x;
   const TensorSlot& ts = tab.t[find_tensor(tab, item)];
@@ -414,10 +323,8 @@ __global__ __launch_bounds__(64) void decode1d_kernel(LaunchTable tab, DecodePar
   const int64_t first = int64_t(slab) * 64 * 64;
   const int64_t len = ts.rows;
 
-  for (int i = lane; i < 64 * kLd; i += 64) acc[i] = 0.f;
-  for (int i = lane; i < 1024; i += 64) cntw[i] = 0u;
+  clear_acc(acc, cntw, lane);
   __syncthreads();
-
   // lane c gathers the payload entries of its own chunk into LDS row c
   const int chunk = slab * 64 + lane;
   if (chunk < ts.grid1) {
@@ -426,16 +333,15 @@ __global__ __launch_bounds__(64) void decode1d_kernel(LaunchTable tab, DecodePar
       const float* __restrict__ pv = p.pay_val + w * p.entries + e0;
       const uint16_t* __restrict__ pi = p.pay_idx + w * p.entries + e0;
       for (int e = 0; e < p.keff; ++e) {
-        const int id = pi[e] & 63;
+        const uint32_t id = pi[e] & 63u;
         acc[lane * kLd + id] += pv[e];
-        cnt[lane * 64 + id] += 1;
+        cntw[lane * kCntLd + (id >> 2)] += 1u << ((id & 3u) * 8u);
       }
     }
   }
   __syncthreads();
   float q[64];
-#pragma unroll
-  for (int v = 0; v < 64; ++v) q[v] = average(acc[lane * kLd + v], cnt[lane * 64 + v], p);
+  average_row(q, acc, cntw, p, lane);
   __syncthreads();
   basis.inv0(q);
   row_to_col(acc, q, lane);
