@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,7 +33,8 @@ import demo_inputs as DI  # noqa: E402
 METRIC = "params/s for encode+decode/apply per step; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "communication_compressed_optimizer_demo_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "communication_compressed_optimizer_demo_amd", "csrc")
+COPY_PROBE_BYTES = 1 << 30
 
 
 def log(msg: str) -> None:
@@ -46,6 +48,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmo_1b", choices=sorted(DI.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one untimed 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-probe run into profiles/traffic_<kernel>_<workload>.json and exit")
     return ap.parse_args()
 
 
@@ -63,8 +70,11 @@ def _foreign_payload(args):
     return out["values"], out["idx"]
 
 
+CPU_SAMPLE_PARAMS = 100_000_000  # about 10 s of oracle work on a few host cores
+
+
 def cpu_baseline(w: DI.Workload):
-    """The oracle, as it stands, on one tensor of the workload (its first, largest-kind matrix)."""
+    """The oracle, as it stands, on a bounded leading sample of the workload's tensor list."""
     import concurrent.futures
     import multiprocessing as mp
 
@@ -72,38 +82,54 @@ def cpu_baseline(w: DI.Workload):
     from threadpoolctl import threadpool_info
 
     from oracle import demo_oracle as O
-    t_idx = 0
-    shape = w.shapes[t_idx]
+    sample, n = [], 0
+    for i, shp in enumerate(w.shapes):
+        if n >= CPU_SAMPLE_PARAMS:
+            break
+        sample.append(i)
+        n += int(np.prod(shp))
     ctx = mp.get_context("fork")
     nproc = max(1, min(16, len(os.sched_getaffinity(0))))
-    log(f"cpu baseline: {w.workers - 1} foreign payloads of a {shape} tensor on {nproc} processes")
+    log(f"cpu baseline: {w.workers - 1} foreign payloads of {len(sample)} tensors ({n} params) on {nproc} processes")
+    jobs = [(w.name, wk, t) for t in sample for wk in range(1, w.workers)]
     with concurrent.futures.ProcessPoolExecutor(nproc, mp_context=ctx) as ex:
-        foreign = list(ex.map(_foreign_payload, [(w.name, wk, t_idx) for wk in range(1, w.workers)]))
+        res = list(ex.map(_foreign_payload, jobs))
+    foreign = {(t, wk): r for (_, wk, t), r in zip(jobs, res)}
     log("cpu baseline: timing the oracle")
-    g0 = DI.gradient(w, 0, 0, t_idx)
-    m0 = np.zeros_like(g0)
-    x0 = DI.initial_params(w, t_idx)
-    t0 = time.perf_counter()
-    out = O.encode(m0, g0, beta=w.beta, alpha=w.alpha, k=w.k)
-    vals = np.stack([out["values"]] + [f[0] for f in foreign])
-    idx = np.stack([out["idx"]] + [f[1] for f in foreign])
-    O.decode_apply(x0, vals, idx, phi=w.phi, eta=w.eta, lam=w.lam)
-    dt = time.perf_counter() - t0
+    dt = 0.0
+    for t in sample:
+        g0 = DI.gradient(w, 0, 0, t)
+        x0 = DI.initial_params(w, t)
+        t0 = time.perf_counter()
+        out = O.encode(np.zeros_like(g0), g0, beta=w.beta, alpha=w.alpha, k=w.k)
+        vals = np.stack([out["values"]] + [foreign[(t, wk)][0] for wk in range(1, w.workers)])
+        idx = np.stack([out["idx"]] + [foreign[(t, wk)][1] for wk in range(1, w.workers)])
+        O.decode_apply(x0, vals, idx, phi=w.phi, eta=w.eta, lam=w.lam)
+        dt += time.perf_counter() - t0
     log(f"cpu baseline: {dt:.2f} s")
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    n = int(np.prod(shape))
     return {
         "value": n / dt,
         "unit": "params/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"one {shape[0]}x{shape[1]} tensor of the workload ({n} params): worker-0 encode + "
-                   f"decode/apply over W={w.workers} payloads (W-1 foreign payloads precomputed, untimed); "
+        "sample": (f"the first {len(sample)} tensors of the list ({n} params, "
+                   f"{sum(1 for t in sample if len(w.shapes[t]) == 2)} matrices): worker-0 encode + decode/apply "
+                   f"over W={w.workers} payloads, tensor by tensor (W-1 foreign payloads precomputed, untimed); "
                    f"{dt:.2f} s"),
     }
 
 
 # ----------------------------------------------------------------------------- GPU leg
+
+def kernel_source_hash() -> str:
+    """sha256 over every file of the kernel sources (counter figures are void once they change)."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
 
 def _traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this source."""
@@ -111,13 +137,60 @@ def _traffic(kernel: str, workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("kernels_hip_sha256") != src:
+    if rec.get("kernel_sources_sha256") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
 
-def gpu_bench(w: DI.Workload, steps: int, warmup: int):
+def _read_pmc(path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter of a counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def pmc_summary(w: DI.Workload, fetch_csv: str, write_csv: str):
+    """Per-launch HBM traffic of the codec kernels, calibrated on the 1 GiB copy probe."""
+    fetch = _read_pmc(fetch_csv, "FETCH_SIZE")
+    write = _read_pmc(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copy" in k.lower() or "elementwise_kernel" in k]
+
+    def probe(d):
+        # the copy probe is the only dispatch of its kernel that moves ~1 GiB
+        vals = [v for k in copy for v in d.get(k, []) if v * 1024 > 0.5 * COPY_PROBE_BYTES]
+        assert vals, "no 1 GiB copy dispatch found: run bench.py with --copy-probe"
+        return max(vals) * 1024
+    f_cal = probe(fetch) / COPY_PROBE_BYTES
+    w_cal = probe(write) / COPY_PROBE_BYTES
+    src = kernel_source_hash()
+    recs = {}
+    for k in fetch:
+        m = re.search(r"(encode|decode)[12]d_kernel", k)
+        if m is None:
+            continue
+        short = m.group(0)
+        fb = [v * 1024 / f_cal for v in fetch[k]]
+        wb = [v * 1024 / w_cal for v in write.get(k, [])]
+        # the timed launches are the last ones of a kernel (foreign-payload encodes come first)
+        rec = {
+            "kernel": short, "workload": w.name,
+            "fetch_bytes_per_launch": fb[-1], "write_bytes_per_launch": wb[-1] if wb else None,
+            "bytes_per_launch": fb[-1] + (wb[-1] if wb else 0.0),
+            "calibration": {"copy_bytes": COPY_PROBE_BYTES, "fetch_factor": f_cal, "write_factor": w_cal},
+            "dispatches": len(fb), "kernel_sources_sha256": src,
+        }
+        recs[short] = rec
+        with open(os.path.join(PROFILES, f"traffic_{short}_{w.name}.json"), "w") as fo:
+            json.dump(rec, fo, indent=1)
+    return recs
+
+
+def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False):
     import torch
 
     from communication_compressed_optimizer_demo_amd import binding as B
@@ -137,17 +210,10 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int):
         codec = B.Codec(shapes, w.k, w.beta, w.alpha)
         groups.append({"ndim": want, "idx": idx, "shapes": shapes, "codec": codec})
 
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1000 + w.config_id)
-    gdt = torch.bfloat16 if w.grad_bf16 else torch.float32
-
-    def draw(shape, std):
-        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std)
-
     for gr in groups:
-        gr["G"] = [draw(s, w.grad_std).to(gdt) for s in gr["shapes"]]
+        gr["G"] = [DI.device_gradient(w, 0, 0, i, dev) for i in gr["idx"]]
         gr["M"] = [torch.zeros(s, device=dev) for s in gr["shapes"]]
-        gr["X"] = [draw(s, w.param_std) for s in gr["shapes"]]
+        gr["X"] = [DI.device_initial_params(w, i, dev) for i in gr["idx"]]
         gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
         ne = gr["codec"].n_entries
         gr["ne"] = ne
@@ -157,12 +223,21 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int):
         for wk in range(1, W):
             for t in scratch_m:
                 t.zero_()
-            gf = [draw(s, w.grad_std).to(gdt) for s in gr["shapes"]]
+            gf = [DI.device_gradient(w, wk, 0, i, dev) for i in gr["idx"]]
             gr["codec"].encode(gf, scratch_m, gr["vals"][wk * ne:(wk + 1) * ne], gr["pidx"][wk * ne:(wk + 1) * ne])
             del gf
         del scratch_m
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if copy_probe:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        src = torch.ones(COPY_PROBE_BYTES // 4, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+        log(f"copy probe: {COPY_PROBE_BYTES} bytes copied")
 
     phi = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
     stream = torch.cuda.current_stream()
@@ -244,8 +319,12 @@ def main():
               "codec on one GPU's share; collectives across GPUs are not part of it.", file=sys.stderr)
         sys.exit(2)
     w = DI.WORKLOADS[args.workload]
+    if args.pmc_summary:
+        for name, rec in pmc_summary(w, *args.pmc_summary).items():
+            print(json.dumps(rec))
+        return
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
-    g = gpu_bench(w, args.steps, args.warmup)
+    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe)
     line = {
         "metric": METRIC,
         "value": g["value"],

@@ -126,3 +126,38 @@ def gaussian_matrix(w: Workload, step: int, which: int, s: int = 64) -> np.ndarr
     dimension-0 matrix and 1 for the dimension-1 matrix.
     """
     return rng(w.config_id, ROLE_BASIS, which, step, 0).standard_normal((s, s))
+
+
+# ---------------------------------------------------------------------------
+# device-side draws for full-size lists
+# ---------------------------------------------------------------------------
+#
+# Host PCG64 draws of the OLMo-shaped lists (hundreds of millions of values
+# per worker and step) would take minutes, so full-size runs draw on the
+# device with torch's seeded generator instead.  The values are inputs, not
+# codec results: a test copies the chunks it samples back to the host and
+# hands exactly those float32 values to the oracle.
+
+def device_seed(config_id: int, role: int, worker: int, step: int, tensor: int) -> int:
+    """A 63-bit seed for torch's generator, derived from the same key as ``rng``."""
+    ss = np.random.SeedSequence([int(config_id), int(role), int(worker), int(step), int(tensor)])
+    return int(ss.generate_state(2, dtype=np.uint32).view(np.uint64)[0] >> np.uint64(1))
+
+
+def device_normal(shape, std: float, seed: int, device, bf16: bool = False):
+    """float32 (or bf16-rounded, returned as bf16) N(0, std^2) draw on ``device``."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    t = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    t.mul_(float(std))
+    return t.to(torch.bfloat16) if bf16 else t
+
+
+def device_gradient(w: Workload, worker: int, step: int, tensor: int, device):
+    return device_normal(w.shapes[tensor], w.grad_std, device_seed(w.config_id, ROLE_GRAD, worker, step, tensor),
+                         device, w.grad_bf16)
+
+
+def device_initial_params(w: Workload, tensor: int, device):
+    return device_normal(w.shapes[tensor], w.param_std, device_seed(w.config_id, ROLE_PARAM, 0, 0, tensor), device)
