@@ -7,8 +7,8 @@ One step is the whole per-step hot path for one worker: encode (momentum
 update, 64x64 chunking, DCT, per-chunk top-k, payload, momentum subtraction)
 of every tensor, then decode/apply of all W workers' payloads (sparse
 average, inverse DCT, phi, weight-decayed update) of every tensor.  The
-tensor list is passed as two calls per half, matrices and vectors, so HIP
-events on the launch stream time each kernel separately.
+whole tensor list goes into one call per half (one launch each for up to 96
+tensors); HIP events on the launch stream time each half.
 
 Inputs are synthetic and resident in HBM before timing: gradients drawn once
 with a seeded device generator, momentum starting at zero, parameters
@@ -170,7 +170,7 @@ def pmc_summary(w: DI.Workload, fetch_csv: str, write_csv: str):
     src = kernel_source_hash()
     recs = {}
     for k in fetch:
-        m = re.search(r"(encode|decode)[12]d_kernel", k)
+        m = re.search(r"(encode|decode)(_dense)?_kernel", k)
         if m is None:
             continue
         short = m.group(0)
@@ -201,32 +201,24 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     W = w.workers
-    groups = []
-    for want in (2, 1):
-        idx = [i for i, s in enumerate(w.shapes) if len(s) == want]
-        if not idx:
-            continue
-        shapes = [w.shapes[i] for i in idx]
-        codec = B.Codec(shapes, w.k, w.beta, w.alpha)
-        groups.append({"ndim": want, "idx": idx, "shapes": shapes, "codec": codec})
-
-    for gr in groups:
-        gr["G"] = [DI.device_gradient(w, 0, 0, i, dev) for i in gr["idx"]]
-        gr["M"] = [torch.zeros(s, device=dev) for s in gr["shapes"]]
-        gr["X"] = [DI.device_initial_params(w, i, dev) for i in gr["idx"]]
-        gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
-        ne = gr["codec"].n_entries
-        gr["ne"] = ne
-        log(f"{len(gr['shapes'])} tensors of ndim {gr['ndim']}: encoding {W - 1} foreign payloads")
-        # other workers' payloads, untimed
-        scratch_m = [torch.zeros(s, device=dev) for s in gr["shapes"]]
-        for wk in range(1, W):
-            for t in scratch_m:
-                t.zero_()
-            gf = [DI.device_gradient(w, wk, 0, i, dev) for i in gr["idx"]]
-            gr["codec"].encode(gf, scratch_m, gr["vals"][wk * ne:(wk + 1) * ne], gr["pidx"][wk * ne:(wk + 1) * ne])
-            del gf
-        del scratch_m
+    # the whole list in one call per half, as a training step would pass it
+    shapes = [tuple(s) for s in w.shapes]
+    codec = B.Codec(shapes, w.k, w.beta, w.alpha)
+    launches = -(-len(shapes) // B.DEMO_MAX_TENSORS_PER_LAUNCH)
+    G = [DI.device_gradient(w, 0, 0, i, dev) for i in range(len(shapes))]
+    M = [torch.zeros(s, device=dev) for s in shapes]
+    X = [DI.device_initial_params(w, i, dev) for i in range(len(shapes))]
+    vals, pidx = codec.alloc_payload(W)
+    ne = codec.n_entries
+    log(f"{len(shapes)} tensors ({launches} launch(es) per call): encoding {W - 1} foreign payloads")
+    scratch_m = [torch.zeros(s, device=dev) for s in shapes]
+    for wk in range(1, W):  # the other workers' payloads, untimed
+        for t in scratch_m:
+            t.zero_()
+        gf = [DI.device_gradient(w, wk, 0, i, dev) for i in range(len(shapes))]
+        codec.encode(gf, scratch_m, vals[wk * ne:(wk + 1) * ne], pidx[wk * ne:(wk + 1) * ne])
+        del gf
+    del scratch_m
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if copy_probe:
@@ -243,28 +235,21 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
     stream = torch.cuda.current_stream()
 
     def one_step(ev):
-        # ev: list of 2 * len(groups) + 1 events, or None
-        j = 0
         if ev:
-            ev[j].record(stream)
-        for gr in groups:
-            ne = gr["ne"]
-            gr["codec"].encode(gr["G"], gr["M"], gr["vals"][:ne], gr["pidx"][:ne], stream=stream)
-            if ev:
-                j += 1
-                ev[j].record(stream)
-        for gr in groups:
-            gr["codec"].decode_apply(gr["X"], W, gr["vals"], gr["pidx"], phi, w.eta, w.lam, stream=stream)
-            if ev:
-                j += 1
-                ev[j].record(stream)
+            ev[0].record(stream)
+        codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream)
+        if ev:
+            ev[1].record(stream)
+        codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream)
+        if ev:
+            ev[2].record(stream)
 
     log(f"warmup {warmup} steps")
     for _ in range(warmup):
         one_step(None)
     torch.cuda.synchronize()
     log(f"timing {steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(groups) + 1)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
@@ -272,24 +257,15 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    names = [f"encode{g['ndim']}d" for g in groups] + [f"decode{g['ndim']}d" for g in groups]
-    per = {n: 0.0 for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            per[n] += ev[j].elapsed_time(ev[j + 1])
-    per = {n: v / steps for n, v in per.items()}
-
+    per = {"encode": sum(ev[0].elapsed_time(ev[1]) for ev in events) / steps,
+           "decode": sum(ev[1].elapsed_time(ev[2]) for ev in events) / steps}
     gbytes = 2 if w.grad_bf16 else 4
+    numel = w.n_params
     kern = {}
-    for gr in groups:
-        numel = sum(int(torch.tensor(s).prod()) for s in gr["shapes"])
-        ne = gr["ne"]
-        enc = numel * (gbytes + 8) + ne * 6
-        dec = numel * 8 + W * ne * 6
-        for name, b in ((f"encode{gr['ndim']}d", enc), (f"decode{gr['ndim']}d", dec)):
-            ms = per[name]
-            kern[name] = {"ms": round(ms, 4), "algorithmic_bytes": int(b), "GBps": round(b / ms / 1e6, 1),
-                          "params": numel}
+    for name, b in (("encode", numel * (gbytes + 8) + ne * 6), ("decode", numel * 8 + W * ne * 6)):
+        ms = per[name]
+        kern[name] = {"ms": round(ms, 4), "launches": launches, "algorithmic_bytes": int(b),
+                      "GBps": round(b / ms / 1e6, 1), "params": numel}
     dom = max(kern, key=lambda n: kern[n]["ms"])
     dk = kern[dom]
     achieved = dk["algorithmic_bytes"] / dk["ms"] / 1e6
@@ -307,7 +283,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": _traffic(f"{dom}_kernel", w.name),
+            "traffic": _traffic(f"{dom}_kernel", w.name) if launches == 1 else None,
         },
     }
 

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libdemo_codec.so")
 
 DEMO_CHUNK = 64
 DEMO_MAX_WORKERS = 255
+DEMO_MAX_TENSORS_PER_LAUNCH = 96  # one kernel launch per this many tensors of a call
 
 # demo_status
 DEMO_OK = 0

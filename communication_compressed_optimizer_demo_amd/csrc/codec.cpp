@@ -21,6 +21,8 @@ namespace {
 
 using demo::kChunk;
 using demo::kMaxTensorsPerLaunch;
+static_assert(kMaxTensorsPerLaunch == DEMO_MAX_TENSORS_PER_LAUNCH, "header and launch table disagree");
+static_assert(demo::kMaxWorkers == DEMO_MAX_WORKERS, "header and kernels disagree");
 using demo::LaunchTable;
 
 thread_local std::string g_last_error;
@@ -37,7 +39,6 @@ struct TensorPlan {
   int32_t keff;         // entries per chunk
   int64_t entry_begin;  // payload offset of the first chunk
   int64_t items;        // work items: chunks (2-D) or 64-chunk slabs (1-D)
-  int32_t grid1;        // 2-D: chunks along dim 1; 1-D: chunk count
 };
 
 demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_t k, std::vector<TensorPlan>* out,
@@ -65,14 +66,12 @@ demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_
       t.chunks = g0 * g1;
       t.keff = k < kChunk * kChunk ? k : kChunk * kChunk;
       t.items = t.chunks;
-      t.grid1 = int32_t(g1);
     } else {
       t.rows = s.dims[0];
       t.cols = 1;
       t.chunks = (t.rows + kChunk - 1) / kChunk;
       t.keff = k < kChunk ? k : kChunk;
       t.items = (t.chunks + kChunk - 1) / kChunk;
-      t.grid1 = int32_t(t.chunks);
     }
     if (t.items > INT32_MAX) return fail(DEMO_ERR_SHAPE, "tensor " + std::to_string(i) + ": too many chunks");
     t.entry_begin = e;
@@ -113,9 +112,10 @@ demo_status check_basis(const demo_codec_cfg* cfg, const std::vector<TensorPlan>
   return DEMO_OK;
 }
 
-// Fills launch tables of one kind (ndim) and calls `launch` for each batch.
+// Fills launch tables (vectors first, then matrices, each kind in list order)
+// and calls `launch` for each batch of up to kMaxTensorsPerLaunch tensors.
 template <class Fill, class Launch>
-demo_status for_each_batch(const std::vector<TensorPlan>& plan, int ndim, Fill&& fill, Launch&& launch) {
+demo_status for_each_batch(const std::vector<TensorPlan>& plan, Fill&& fill, Launch&& launch) {
   LaunchTable tab;
   std::memset(&tab, 0, sizeof(tab));
   auto flush = [&]() -> demo_status {
@@ -125,21 +125,22 @@ demo_status for_each_batch(const std::vector<TensorPlan>& plan, int ndim, Fill&&
     std::memset(&tab, 0, sizeof(tab));
     return DEMO_OK;
   };
-  for (size_t i = 0; i < plan.size(); ++i) {
-    const TensorPlan& t = plan[i];
-    if (t.ndim != ndim) continue;
-    if (tab.n == kMaxTensorsPerLaunch || int64_t(tab.items) + t.items > INT32_MAX) {
-      const demo_status s = flush();
-      if (s != DEMO_OK) return s;
+  for (int ndim : {1, 2}) {
+    for (size_t i = 0; i < plan.size(); ++i) {
+      const TensorPlan& t = plan[i];
+      if (t.ndim != ndim) continue;
+      if (tab.n == kMaxTensorsPerLaunch || int64_t(tab.items) + t.items > INT32_MAX) {
+        const demo_status s = flush();
+        if (s != DEMO_OK) return s;
+      }
+      demo::TensorSlot& slot = tab.t[tab.n++];
+      slot.entry_begin = t.entry_begin;
+      slot.rows = int32_t(t.rows);
+      slot.cols = t.ndim == 2 ? int32_t(t.cols) : 0;
+      slot.item_begin = tab.items;
+      fill(slot, i);
+      tab.items += int32_t(t.items);
     }
-    demo::TensorSlot& slot = tab.t[tab.n++];
-    slot.entry_begin = t.entry_begin;
-    slot.rows = int32_t(t.rows);
-    slot.cols = int32_t(t.cols);
-    slot.item_begin = tab.items;
-    slot.grid1 = t.grid1;
-    fill(slot, i);
-    tab.items += int32_t(t.items);
   }
   return flush();
 }
@@ -224,13 +225,10 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
     slot.src = grads[i];
     slot.dst = moms[i];
   };
-  p.keff = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
-  s = for_each_batch(plan, 2, fill,
-                     [&](const LaunchTable& t) { return demo::launch_encode2d(t, p, bf16, p0, p1, stream); });
-  if (s != DEMO_OK) return s;
-  p.keff = cfg->k < kChunk ? cfg->k : kChunk;
-  return for_each_batch(plan, 1, fill,
-                        [&](const LaunchTable& t) { return demo::launch_encode1d(t, p, bf16, p0, stream); });
+  p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
+  p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
+  return for_each_batch(plan, fill,
+                        [&](const LaunchTable& t) { return demo::launch_encode(t, p, bf16, p0, p1, stream); });
 }
 
 demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
@@ -274,12 +272,9 @@ demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes
     slot.src = nullptr;
     slot.dst = params[i];
   };
-  p.keff = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
-  s = for_each_batch(plan, 2, fill,
-                     [&](const LaunchTable& t) { return demo::launch_decode2d(t, p, p0, p1, stream); });
-  if (s != DEMO_OK) return s;
-  p.keff = cfg->k < kChunk ? cfg->k : kChunk;
-  return for_each_batch(plan, 1, fill, [&](const LaunchTable& t) { return demo::launch_decode1d(t, p, p0, stream); });
+  p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
+  p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
+  return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_decode(t, p, p0, p1, stream); });
 }
 
 }  // extern "C"

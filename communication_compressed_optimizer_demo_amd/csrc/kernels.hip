@@ -1,13 +1,19 @@
 // HIP kernels of the DeMo per-step momentum codec for CDNA4 (gfx950).
 //
-// One wave64 owns one 64x64 chunk (2-D) or one slab of 64 consecutive
-// 64-element chunks (1-D).  Data move between two register layouts:
+// One launch covers a batch of tensors of both kinds.  A work item is one
+// 64x64 chunk of a matrix, or one slab of up to 64 consecutive 64-element
+// chunks of a vector; the host puts the vector slabs first so their longer,
+// serial lanes start early and finish under the matrix chunks.  One wave64
+// owns one item.
+//
+// Data move between two register layouts:
 //   column layout: lane j holds column j, x[i] = element (i, j);
 //   row layout:    lane u holds row u,    x[v] = element (u, v).
 // A coalesced global access of one 256-byte row segment per instruction
 // fills the column layout directly; a 64x65-float LDS tile (row stride 65:
 // row and column accesses are both bank-conflict free) converts between the
-// two.  Each 64-point transform runs inside one lane's registers.
+// two.  Each 64-point transform runs inside one lane's registers.  G, M and X
+// are streamed once, so their loads and stores carry the non-temporal hint.
 //
 // encode (DeMo summary, §3.4 Decoupled Local Momentum Updates, Tensor
 // Chunking, Blockwise Linear Projection, Top-k Sparsification, Momentum
@@ -53,13 +59,20 @@ __device__ __forceinline__ int find_tensor(const LaunchTable& tab, int item) {
   return lo;
 }
 
+template <class T>
+__device__ __forceinline__ T stream_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+__device__ __forceinline__ void stream_store(float v, float* p) { __builtin_nontemporal_store(v, p); }
+
 template <bool kBf16>
 __device__ __forceinline__ float load_src(const void* p, int64_t off) {
   if constexpr (kBf16) {
-    const uint32_t b = static_cast<const uint16_t*>(p)[off];
+    const uint32_t b = stream_load(static_cast<const uint16_t*>(p) + off);
     return __uint_as_float(b << 16);
   } else {
-    return static_cast<const float*>(p)[off];
+    return stream_load(static_cast<const float*>(p) + off);
   }
 }
 
@@ -95,8 +108,9 @@ struct ChunkPos {
 __device__ __forceinline__ ChunkPos chunk_pos(const TensorSlot& ts, int item) {
   ChunkPos c;
   c.local = item - ts.item_begin;
-  const int cr = c.local / ts.grid1;
-  const int cc = c.local - cr * ts.grid1;
+  const int grid1 = int((uint32_t(ts.cols) + 63u) >> 6);  // chunks along dimension 1
+  const int cr = c.local / grid1;
+  const int cc = c.local - cr * grid1;
   c.vr = min(64, ts.rows - cr * 64);
   c.vc = min(64, ts.cols - cc * 64);
   c.base = int64_t(cr) * 64 * ts.cols + int64_t(cc) * 64;
@@ -104,7 +118,16 @@ __device__ __forceinline__ ChunkPos chunk_pos(const TensorSlot& ts, int item) {
   return c;
 }
 
-// ---------------------------------------------------------------- encode, 2-D chunks
+template <bool kFull>
+__device__ __forceinline__ void store_rows(const float (&q)[64], float* __restrict__ dst, int64_t ld,
+                                           const ChunkPos& c, int lane) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (kFull || (lane < c.vc && i < c.vr)) stream_store(q[i], &dst[i * ld + lane]);
+  }
+}
+
+// ---------------------------------------------------------------- encode, 64x64 chunk
 
 template <bool kFull, bool kBf16>
 __device__ __forceinline__ void load_momentum(float (&q)[64], const TensorSlot& ts, const ChunkPos& c, int lane,
@@ -117,26 +140,16 @@ __device__ __forceinline__ void load_momentum(float (&q)[64], const TensorSlot& 
     float gv = 0.f, mv = 0.f;
     if (kFull || (lane < c.vc && i < c.vr)) {
       gv = load_src<kBf16>(g, i * ld + lane);
-      mv = m[i * ld + lane];
+      mv = stream_load(&m[i * ld + lane]);
     }
     q[i] = fmaf(beta, mv, gcoef * gv);
   }
 }
 
-template <bool kFull>
-__device__ __forceinline__ void store_rows(const float (&q)[64], float* __restrict__ dst, int64_t ld,
-                                           const ChunkPos& c, int lane) {
-#pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    if (kFull || (lane < c.vc && i < c.vr)) dst[i * ld + lane] = q[i];
-  }
-}
-
 template <class Basis, bool kBf16>
-__global__ __launch_bounds__(64) void encode2d_kernel(LaunchTable tab, EncodeParams p, Basis basis) {
-  __shared__ float tile[64 * kLd];
+__device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const EncodeParams& p, const Basis& basis,
+                                              float* tile) {
   const int lane = threadIdx.x;
-  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
   const ChunkPos c = chunk_pos(ts, blockIdx.x);
 
   float q[64];
@@ -149,8 +162,8 @@ __global__ __launch_bounds__(64) void encode2d_kernel(LaunchTable tab, EncodePar
   col_to_row(tile, q, lane);
   basis.fwd1(q);
 
-  const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff;
-  tk::topk_chunk(q, p.keff, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
+  const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
+  tk::topk_chunk(q, p.keff2, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
   __syncthreads();
 
   basis.inv1(q);
@@ -163,48 +176,71 @@ __global__ __launch_bounds__(64) void encode2d_kernel(LaunchTable tab, EncodePar
     store_rows<false>(q, ts.dst + c.base, ts.cols, c, lane);
 }
 
-// ---------------------------------------------------------------- encode, 1-D chunks
+// ---------------------------------------------------------------- encode, vector slab
 
 // Slab view of a vector: V[c][e] = vec[(64 * slab + c) * 64 + e], chunk c of
 // the slab is row c.  Column layout after the load (lane e), row layout
-// (lane c = one chunk) after the transpose.
+// (lane c = one chunk) after the transpose; each lane then transforms and
+// selects its own chunk.
 template <class Basis, bool kBf16>
-__global__ __launch_bounds__(64) void encode1d_kernel(LaunchTable tab, EncodeParams p, Basis basis) {
-  __shared__ float tile[64 * kLd];
+__device__ __forceinline__ void encode_vector(const TensorSlot& ts, const EncodeParams& p, const Basis& basis,
+                                              float* tile) {
   const int lane = threadIdx.x;
-  const int item = blockIdx.x;
-  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
-  const int slab = item - ts.item_begin;
-  const int64_t first = int64_t(slab) * 64 * 64;  // element offset of the slab
-  const int64_t len = ts.rows;
-  float* __restrict__ m = ts.dst;
+  const int slab = blockIdx.x - ts.item_begin;
+  const int64_t first = int64_t(slab) * 64 * 64 + lane;  // this lane's element of the slab's chunk 0
+  const int64_t rem = int64_t(ts.rows) - first;          // elements c * 64 < rem exist
+  float* __restrict__ m = ts.dst + first;
+  const char* __restrict__ g = static_cast<const char*>(ts.src) + first * (kBf16 ? 2 : 4);
 
   float q[64];
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
-    const int64_t off = first + int64_t(c) * 64 + lane;
-    float g = 0.f, mv = 0.f;
-    if (off < len) {
-      g = load_src<kBf16>(ts.src, off);
-      mv = m[off];
+    float gv = 0.f, mv = 0.f;
+    if (c * 64 < rem) {
+      gv = load_src<kBf16>(g, c * 64);
+      mv = stream_load(&m[c * 64]);
     }
-    q[c] = fmaf(p.beta, mv, p.gcoef * g);
+    q[c] = fmaf(p.beta, mv, p.gcoef * gv);
   }
   col_to_row(tile, q, lane);
   basis.fwd0(q);
 
   const int chunk = slab * 64 + lane;  // this lane's chunk within the tensor
-  const bool live = chunk < ts.grid1;
-  const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff;
-  tk::topk_lane(q, p.keff, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
+  const bool live = chunk < int((uint32_t(ts.rows) + 63u) >> 6);
+  const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff1;
+  tk::topk_lane(q, p.keff1, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
 
   basis.inv0(q);
   row_to_col(tile, q, lane);
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
-    const int64_t off = first + int64_t(c) * 64 + lane;
-    if (off < len) m[off] = q[c];
+    if (c * 64 < rem) stream_store(q[c], &m[c * 64]);
   }
+}
+
+template <class Basis, bool kBf16>
+__device__ __forceinline__ void encode_item(const LaunchTable& tab, const EncodeParams& p, const Basis& basis,
+                                            float* tile) {
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  if (ts.cols == 0)
+    encode_vector<Basis, kBf16>(ts, p, basis, tile);
+  else
+    encode_matrix<Basis, kBf16>(ts, p, basis, tile);
+}
+
+// The DCT kernel fits 168 VGPRs, i.e. three waves per SIMD; the dense
+// (caller-basis) kernel needs more and is left to the compiler.
+template <bool kBf16>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void encode_kernel(LaunchTable tab,
+                                                                                             EncodeParams p) {
+  __shared__ float tile[64 * kLd];
+  encode_item<DctBasis, kBf16>(tab, p, DctBasis{}, tile);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(64) void encode_dense_kernel(LaunchTable tab, EncodeParams p, DenseBasis basis) {
+  __shared__ float tile[64 * kLd];
+  encode_item<DenseBasis, kBf16>(tab, p, basis, tile);
 }
 
 // ---------------------------------------------------------------- decode / apply
@@ -220,15 +256,22 @@ __device__ __forceinline__ void clear_acc(float* acc, uint32_t* cntw, int lane) 
   for (int i = lane; i < 64 * kCntLd; i += 64) cntw[i] = 0u;
 }
 
+// Add one payload entry (value v at coefficient (u, col)) to the accumulator.
+__device__ __forceinline__ void accumulate(float* acc, uint32_t* cntw, uint32_t u, uint32_t col, float v) {
+  atomicAdd(&acc[u * kLd + col], v);
+  atomicAdd(&cntw[u * kCntLd + (col >> 2)], 1u << ((col & 3u) * 8u));
+}
+
 // Scatter-add the W payload segments of one 64x64 chunk (entries e0 ..
 // e0 + keff of every worker).  One LDS atomic instruction per (worker, entry
 // block); within it the indices are distinct, so no lanes collide and every
 // coefficient receives its terms in worker order.
 __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0,
                                               int lane) {
-  for (int eb = 0; eb < p.keff; eb += 64) {
+  const int keff = p.keff2;
+  for (int eb = 0; eb < keff; eb += 64) {
     const int e = eb + lane;
-    const bool on = e < p.keff;
+    const bool on = e < keff;
     for (int w0 = 0; w0 < p.workers; w0 += kWorkerBatch) {
       float val[kWorkerBatch];
       uint32_t ix[kWorkerBatch];
@@ -243,16 +286,44 @@ __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const 
       for (int j = 0; j < kWorkerBatch; ++j) {
         if (on && (w0 + j) < p.workers) {
           const uint32_t id = ix[j] & 4095u;
-          const uint32_t u = id >> 6, v = id & 63u;
-          atomicAdd(&acc[u * kLd + v], val[j]);
-          atomicAdd(&cntw[u * kCntLd + (v >> 2)], 1u << ((v & 3u) * 8u));
+          accumulate(acc, cntw, id >> 6, id & 63u, val[j]);
         }
       }
     }
   }
 }
 
-// Row u of the average into q (row layout).
+// Scatter-add the W payload segments of the nc <= 64 vector chunks of a slab
+// (entries e0 .. e0 + nc * keff of every worker, chunk r of the slab into
+// accumulator row r).  Entry f of a segment belongs to chunk f / keff; one
+// instruction covers 64 consecutive entries of one worker, whose (chunk,
+// index) pairs are distinct.
+__device__ __forceinline__ void scatter_slab(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0, int nc,
+                                             int lane) {
+  const int keff = p.keff1;
+  const int n = nc * keff;
+  for (int w = 0; w < p.workers; ++w) {
+    const float* __restrict__ pv = p.pay_val + int64_t(w) * p.entries + e0;
+    const uint16_t* __restrict__ pi = p.pay_idx + int64_t(w) * p.entries + e0;
+    for (int f0 = 0; f0 < n; f0 += 64 * 8) {
+      float val[8];
+      uint32_t ix[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int f = f0 + 64 * j + lane;
+        val[j] = f < n ? pv[f] : 0.f;
+        ix[j] = f < n ? pi[f] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int f = f0 + 64 * j + lane;
+        if (f < n) accumulate(acc, cntw, uint32_t(f / keff), ix[j] & 63u, val[j]);
+      }
+    }
+  }
+}
+
+// Row `lane` of the average into q (row layout).
 __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, const uint32_t* cntw,
                                             const DecodeParams& p, int lane) {
   if (p.avg_workers) {
@@ -273,29 +344,28 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
 }
 
 template <class Basis>
-__global__ __launch_bounds__(64) void decode2d_kernel(LaunchTable tab, DecodeParams p, Basis basis) {
-  __shared__ float acc[64 * kLd];
-  __shared__ uint32_t cntw[64 * kCntLd];
+__device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
+                                              float* acc, uint32_t* cntw) {
   const int lane = threadIdx.x;
-  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
   const ChunkPos c = chunk_pos(ts, blockIdx.x);
 
-  clear_acc(acc, cntw, lane);
-  __syncthreads();
-  scatter_chunk(acc, cntw, p, ts.entry_begin + int64_t(c.local) * p.keff, lane);
-  __syncthreads();
-
-  // parameters are fetched now; they land while the average and the inverse transform run
+  // Parameters are fetched first: they land while the payloads are averaged
+  // and inverse-transformed.
   const int64_t ld = ts.cols;
   float* __restrict__ xp = ts.dst + c.base;
   float x[64];
   if (c.full) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = xp[i * ld + lane];
+    for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[i * ld + lane]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = (lane < c.vc && i < c.vr) ? xp[i * ld + lane] : 0.f;
+    for (int i = 0; i < 64; ++i) x[i] = (lane < c.vc && i < c.vr) ? stream_load(&xp[i * ld + lane]) : 0.f;
   }
+
+  clear_acc(acc, cntw, lane);
+  __syncthreads();
+  scatter_chunk(acc, cntw, p, ts.entry_begin + int64_t(c.local) * p.keff2, lane);
+  __syncthreads();
 
   float q[64];
   average_row(q, acc, cntw, p, lane);
@@ -313,32 +383,17 @@ __global__ __launch_bounds__(64) void decode2d_kernel(LaunchTable tab, DecodePar
 }
 
 template <class Basis>
-__global__ __launch_bounds__(64) void decode1d_kernel(LaunchTable tab, DecodeParams p, Basis basis) {
-  __shared__ float acc[64 * kLd];
-  __shared__ uint32_t cntw[64 * kCntLd];
+__device__ __forceinline__ void decode_vector(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
+                                              float* acc, uint32_t* cntw) {
   const int lane = threadIdx.x;
-  const int item = blockIdx.x;
-  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
-  const int slab = item - ts.item_begin;
-  const int64_t first = int64_t(slab) * 64 * 64;
-  const int64_t len = ts.rows;
+  const int slab = blockIdx.x - ts.item_begin;
+  const int64_t first = int64_t(slab) * 64 * 64 + lane;  // this lane's element of the slab's chunk 0
+  const int64_t rem = int64_t(ts.rows) - first;          // elements c * 64 < rem exist
+  const int nc = min(64, int((uint32_t(ts.rows) + 63u) >> 6) - slab * 64);  // chunks in this slab
 
   clear_acc(acc, cntw, lane);
   __syncthreads();
-  // lane c gathers the payload entries of its own chunk into LDS row c
-  const int chunk = slab * 64 + lane;
-  if (chunk < ts.grid1) {
-    const int64_t e0 = ts.entry_begin + int64_t(chunk) * p.keff;
-    for (int w = 0; w < p.workers; ++w) {
-      const float* __restrict__ pv = p.pay_val + w * p.entries + e0;
-      const uint16_t* __restrict__ pi = p.pay_idx + w * p.entries + e0;
-      for (int e = 0; e < p.keff; ++e) {
-        const uint32_t id = pi[e] & 63u;
-        acc[lane * kLd + id] += pv[e];
-        cntw[lane * kCntLd + (id >> 2)] += 1u << ((id & 3u) * 8u);
-      }
-    }
-  }
+  scatter_slab(acc, cntw, p, ts.entry_begin + int64_t(slab) * 64 * p.keff1, nc, lane);
   __syncthreads();
   float q[64];
   average_row(q, acc, cntw, p, lane);
@@ -346,75 +401,66 @@ __global__ __launch_bounds__(64) void decode1d_kernel(LaunchTable tab, DecodePar
   basis.inv0(q);
   row_to_col(acc, q, lane);
 
-  float* __restrict__ x = ts.dst;
+  float* __restrict__ x = ts.dst + first;
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
-    const int64_t off = first + int64_t(c) * 64 + lane;
-    if (off < len) x[off] = update(x[off], q[c], p);
+    if (c * 64 < rem) stream_store(update(stream_load(&x[c * 64]), q[c], p), &x[c * 64]);
   }
+}
+
+template <class Basis>
+__device__ __forceinline__ void decode_item(const LaunchTable& tab, const DecodeParams& p, const Basis& basis,
+                                            float* acc, uint32_t* cntw) {
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  if (ts.cols == 0)
+    decode_vector<Basis>(ts, p, basis, acc, cntw);
+  else
+    decode_matrix<Basis>(ts, p, basis, acc, cntw);
+}
+
+__global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParams p) {
+  __shared__ float acc[64 * kLd];
+  __shared__ uint32_t cntw[64 * kCntLd];
+  decode_item<DctBasis>(tab, p, DctBasis{}, acc, cntw);
+}
+
+__global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
+  __shared__ float acc[64 * kLd];
+  __shared__ uint32_t cntw[64 * kCntLd];
+  decode_item<DenseBasis>(tab, p, basis, acc, cntw);
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------- host-side launchers
 
-hipError_t launch_encode2d(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, const float* basis_p0,
-                           const float* basis_p1, hipStream_t stream) {
+hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, const float* basis_p0,
+                         const float* basis_p1, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
   const dim3 grid(tab.items), block(64);
   if (basis_p0 == nullptr) {
     if (g_bf16)
-      encode2d_kernel<DctBasis, true><<<grid, block, 0, stream>>>(tab, p, DctBasis{});
+      encode_kernel<true><<<grid, block, 0, stream>>>(tab, p);
     else
-      encode2d_kernel<DctBasis, false><<<grid, block, 0, stream>>>(tab, p, DctBasis{});
+      encode_kernel<false><<<grid, block, 0, stream>>>(tab, p);
   } else {
     const DenseBasis b{basis_p0, basis_p1};
     if (g_bf16)
-      encode2d_kernel<DenseBasis, true><<<grid, block, 0, stream>>>(tab, p, b);
+      encode_dense_kernel<true><<<grid, block, 0, stream>>>(tab, p, b);
     else
-      encode2d_kernel<DenseBasis, false><<<grid, block, 0, stream>>>(tab, p, b);
+      encode_dense_kernel<false><<<grid, block, 0, stream>>>(tab, p, b);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_encode1d(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, const float* basis_p0,
-                           hipStream_t stream) {
-  if (tab.items <= 0) return hipSuccess;
-  const dim3 grid(tab.items), block(64);
-  if (basis_p0 == nullptr) {
-    if (g_bf16)
-      encode1d_kernel<DctBasis, true><<<grid, block, 0, stream>>>(tab, p, DctBasis{});
-    else
-      encode1d_kernel<DctBasis, false><<<grid, block, 0, stream>>>(tab, p, DctBasis{});
-  } else {
-    const DenseBasis b{basis_p0, basis_p0};
-    if (g_bf16)
-      encode1d_kernel<DenseBasis, true><<<grid, block, 0, stream>>>(tab, p, b);
-    else
-      encode1d_kernel<DenseBasis, false><<<grid, block, 0, stream>>>(tab, p, b);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_decode2d(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0,
-                           const float* basis_p1, hipStream_t stream) {
+hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0, const float* basis_p1,
+                         hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
   const dim3 grid(tab.items), block(64);
   if (basis_p0 == nullptr)
-    decode2d_kernel<DctBasis><<<grid, block, 0, stream>>>(tab, p, DctBasis{});
+    decode_kernel<<<grid, block, 0, stream>>>(tab, p);
   else
-    decode2d_kernel<DenseBasis><<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
-  return hipGetLastError();
-}
-
-hipError_t launch_decode1d(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0,
-                           hipStream_t stream) {
-  if (tab.items <= 0) return hipSuccess;
-  const dim3 grid(tab.items), block(64);
-  if (basis_p0 == nullptr)
-    decode1d_kernel<DctBasis><<<grid, block, 0, stream>>>(tab, p, DctBasis{});
-  else
-    decode1d_kernel<DenseBasis><<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p0});
+    decode_dense_kernel<<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
   return hipGetLastError();
 }
 

@@ -1,11 +1,11 @@
 // Kernel-argument layout shared by the host side (codec.cpp) and the kernels.
 //
-// A launch covers up to kMaxTensorsPerLaunch tensors of one kind (2-D
-// matrices, or 1-D vectors).  The tensor table travels by value in the kernel
-// arguments, so no device-side table is allocated or copied.  A work item is
-// one 64x64 chunk (2-D) or one slab of up to 64 consecutive 64-element chunks
-// of a vector (1-D); items are numbered consecutively over the launch's
-// tensors in list order.
+// A launch covers up to kMaxTensorsPerLaunch tensors of both kinds.  The
+// tensor table travels by value in the kernel arguments, so no device-side
+// table is allocated or copied.  A work item is one 64x64 chunk of a matrix,
+// or one slab of up to 64 consecutive 64-element chunks of a vector; items
+// are numbered consecutively over the launch's tensors in table order (the
+// host lists the vectors first).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,7 +15,7 @@
 namespace demo {
 
 constexpr int kChunk = 64;
-constexpr int kMaxTensorsPerLaunch = 64;
+constexpr int kMaxTensorsPerLaunch = 96;
 constexpr int kMaxWorkers = 255;  // counts are kept in 8 bits
 
 struct TensorSlot {
@@ -23,9 +23,8 @@ struct TensorSlot {
   float* dst;           // encode: momentum (in/out); decode: parameters (in/out)
   int64_t entry_begin;  // payload entry of the tensor's first chunk
   int32_t rows;         // 2-D: dim 0; 1-D: length
-  int32_t cols;         // 2-D: dim 1; 1-D: 1
+  int32_t cols;         // 2-D: dim 1 (>= 1); 1-D: 0, which marks a vector
   int32_t item_begin;   // first work item of this tensor within the launch
-  int32_t grid1;        // 2-D: chunks along dim 1; 1-D: number of 64-element chunks
 };
 
 struct LaunchTable {
@@ -33,6 +32,10 @@ struct LaunchTable {
   int32_t items;
   TensorSlot t[kMaxTensorsPerLaunch];
 };
+// Kernel arguments are limited to 4 KiB; the table leaves room for the
+// parameter structs and the basis pointers.
+static_assert(sizeof(TensorSlot) == 40, "tensor slot layout");
+static_assert(sizeof(LaunchTable) <= 3856, "launch table too large for the kernel argument segment");
 
 struct EncodeParams {
   float* pay_val;
@@ -40,7 +43,8 @@ struct EncodeParams {
   float beta;
   float gcoef;  // (1 - beta) or 1
   float alpha;
-  int32_t keff;
+  int32_t keff2;  // entries per 64x64 chunk
+  int32_t keff1;  // entries per 64-element chunk
 };
 
 struct DecodeParams {
@@ -48,7 +52,8 @@ struct DecodeParams {
   const uint16_t* pay_idx;
   int64_t entries;  // entries per worker payload
   int32_t workers;
-  int32_t keff;
+  int32_t keff2;  // entries per 64x64 chunk
+  int32_t keff1;  // entries per 64-element chunk
   float eta;
   float lam;
   float inv_workers;
@@ -58,13 +63,9 @@ struct DecodeParams {
 
 // Host entry points into the kernels (kernels.hip).  basis_p0/p1 are null for
 // the DCT basis.  Return the hipError_t of the launch.
-hipError_t launch_encode2d(const LaunchTable& tab, const EncodeParams& p, bool g_bf16,
-                           const float* basis_p0, const float* basis_p1, hipStream_t stream);
-hipError_t launch_encode1d(const LaunchTable& tab, const EncodeParams& p, bool g_bf16,
-                           const float* basis_p0, hipStream_t stream);
-hipError_t launch_decode2d(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0,
-                           const float* basis_p1, hipStream_t stream);
-hipError_t launch_decode1d(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0,
-                           hipStream_t stream);
+hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, const float* basis_p0,
+                         const float* basis_p1, hipStream_t stream);
+hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0, const float* basis_p1,
+                         hipStream_t stream);
 
 }  // namespace demo

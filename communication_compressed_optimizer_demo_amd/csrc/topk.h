@@ -52,48 +52,51 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t mag_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
-
 // Bitwise search over all 4096 magnitudes: K = largest T with #(|q| >= T) >= keff.
+// Magnitudes are compared as floats through the |x| operand modifier (the
+// order of non-negative floats is the order of their bit patterns), so no
+// second copy of the block is held in registers.
 __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int lane, float alpha,
                                                  float* __restrict__ outv, uint16_t* __restrict__ outi) {
-  uint32_t lmax = 0;
+  float lmax = 0.f;
 #pragma unroll
-  for (int v = 0; v < 64; ++v) lmax = max(lmax, mag_bits(q[v]));
-  uint32_t hi = lmax;
+  for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(q[v]));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
+  for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
+  const uint32_t hi = __float_as_uint(lmax);
   uint32_t T = 0;
+#pragma unroll 1
   for (int b = 30; b >= 0; --b) {
     const uint32_t cand = T | (1u << b);
     if (cand > hi) continue;
+    const float cf = __uint_as_float(cand);
     int c = 0;
 #pragma unroll
-    for (int v = 0; v < 64; ++v) c += mag_bits(q[v]) >= cand ? 1 : 0;
+    for (int v = 0; v < 64; ++v) c += fabsf(q[v]) >= cf ? 1 : 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
     if (c >= keff) T = cand;
   }
+  const float kf = __uint_as_float(T);
   int gt = 0, eq = 0;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    const uint32_t a = mag_bits(q[v]);
-    gt += a > T ? 1 : 0;
-    eq += a == T ? 1 : 0;
+    gt += fabsf(q[v]) > kf ? 1 : 0;
+    eq += fabsf(q[v]) == kf ? 1 : 0;
   }
   int gt_all = gt;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) gt_all += __shfl_xor(gt_all, o);
-  const int quota = keff - gt_all;  // ties at T still to take, in index order
+  const int quota = keff - gt_all;  // ties at K still to take, in index order
   const int eq_before = wave_incl_scan(eq, lane) - eq;
   const int kept = gt + min(max(quota - eq_before, 0), eq);
   int off = wave_incl_scan(kept, lane) - kept;
   int eqr = eq_before;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    const uint32_t a = mag_bits(q[v]);
-    const bool is_eq = a == T;
-    const bool keep = a > T || (is_eq && eqr < quota);
+    const float a = fabsf(q[v]);
+    const bool is_eq = a == kf;
+    const bool keep = a > kf || (is_eq && eqr < quota);
     eqr += is_eq ? 1 : 0;
     if (keep) {
       outv[off] = q[v];
@@ -245,27 +248,31 @@ __device__ __forceinline__ void topk_lane(float (&q)[64], int keff, bool write, 
     }
     return;
   }
-  uint32_t hi = 0;
+  float lmax = 0.f;
 #pragma unroll
-  for (int v = 0; v < 64; ++v) hi = max(hi, mag_bits(q[v]));
+  for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(q[v]));
+  const uint32_t hi = __float_as_uint(lmax);
   uint32_t T = 0;
+#pragma unroll 1
   for (int b = 30; b >= 0; --b) {
     const uint32_t cand = T | (1u << b);
+    const float cf = __uint_as_float(cand);
     int c = 0;
 #pragma unroll
-    for (int v = 0; v < 64; ++v) c += mag_bits(q[v]) >= cand ? 1 : 0;
+    for (int v = 0; v < 64; ++v) c += fabsf(q[v]) >= cf ? 1 : 0;
     if (cand <= hi && c >= keff) T = cand;
   }
+  const float kf = __uint_as_float(T);
   int gt = 0;
 #pragma unroll
-  for (int v = 0; v < 64; ++v) gt += mag_bits(q[v]) > T ? 1 : 0;
+  for (int v = 0; v < 64; ++v) gt += fabsf(q[v]) > kf ? 1 : 0;
   const int quota = keff - gt;
   int eqr = 0, off = 0;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    const uint32_t a = mag_bits(q[v]);
-    const bool is_eq = a == T;
-    const bool keep = a > T || (is_eq && eqr < quota);
+    const float a = fabsf(q[v]);
+    const bool is_eq = a == kf;
+    const bool keep = a > kf || (is_eq && eqr < quota);
     eqr += is_eq ? 1 : 0;
     if (keep) {
       if (write) {

@@ -49,6 +49,7 @@ extern "C" {
 
 #define DEMO_CHUNK 64        /* the only chunk size built (pages' default s = 64) */
 #define DEMO_MAX_WORKERS 255 /* decode keeps per-coefficient contributor counts in 8 bits */
+#define DEMO_MAX_TENSORS_PER_LAUNCH 96 /* longer lists are split into several launches per call */
 
 typedef enum demo_status {
   DEMO_OK = 0,

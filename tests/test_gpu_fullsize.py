@@ -1,9 +1,9 @@
 """Parity at the full OLMo-shaped sizes, sampled, in the launch configuration bench.py times.
 
 The whole tensor list runs on the GPU: W workers each hold their own
-momentum for every tensor, encode with one call for the matrices and one
-for the vectors (as bench.py does), and all W payloads are decoded and
-applied to the shared parameters.  Inputs are drawn on the device with
+momentum for every tensor, encode the whole list in one call (as bench.py
+does), and all W payloads are decoded and applied to the shared parameters
+in one call.  Inputs are drawn on the device with
 seeded generators (demo_inputs.device_*).
 
 The oracle cannot run 800M parameters, so it recomputes sampled chunks one
@@ -58,13 +58,13 @@ def chunk_block(t: torch.Tensor, shape, c: int) -> np.ndarray:
     return t[cr * 64:(cr + 1) * 64, cc * 64:(cc + 1) * 64].cpu().numpy()
 
 
-def check_payload_properties(vals: torch.Tensor, idx: torch.Tensor, layout, limit: int, where: str):
-    """Indices ascending and below ``limit`` (chunk element count) inside every chunk; values finite."""
+def check_payload_properties(vals: torch.Tensor, idx: torch.Tensor, layout, limits, where: str):
+    """Indices ascending and below the chunk element count (``limits``, per tensor) inside every chunk; values finite."""
     assert torch.isfinite(vals).all(), f"{where}: non-finite payload value"
     iv = idx.to(torch.int32) & 0xFFFF
     for t, (n, keff, e0) in enumerate(layout):
         ix = iv[e0:e0 + n * keff].view(n, keff)
-        assert int(ix.max()) < limit, f"{where}: tensor {t} index out of range"
+        assert int(ix.max()) < limits[t], f"{where}: tensor {t} index out of range"
         if keff > 1:
             assert bool((ix[:, 1:] > ix[:, :-1]).all()), f"{where}: tensor {t} indices not ascending"
 
@@ -77,14 +77,11 @@ def test_full_size_sampled(dev, name):
     P = O.dct_basis()
     rng = np.random.default_rng(7 + w.config_id)
 
-    groups = []  # as bench.py: matrices in one call, vectors in another
-    for want in (2, 1):
-        ids = [i for i, s in enumerate(w.shapes) if len(s) == want]
-        shapes = [w.shapes[i] for i in ids]
-        codec = B.Codec(shapes, w.k, w.beta, w.alpha)
-        vals, pidx = codec.alloc_payload(W)
-        groups.append({"ids": ids, "shapes": shapes, "codec": codec, "vals": vals, "pidx": pidx,
-                       "lay": PR.layout(shapes, w.k)})
+    shapes = [tuple(s) for s in w.shapes]
+    groups = [{"ids": list(range(len(shapes))), "shapes": shapes, "codec": B.Codec(shapes, w.k, w.beta, w.alpha),
+               "lay": PR.layout(shapes, w.k)}]
+    for gr in groups:
+        gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
     say(f"[{name}] {len(w.shapes)} tensors, {w.n_params} params, W={W}: allocating momenta")
     M = {i: [torch.zeros(w.shapes[i], device=dev) for _ in range(W)] for i in range(len(w.shapes))}
     X = {i: DI.device_initial_params(w, i, dev) for i in range(len(w.shapes))}
@@ -110,7 +107,7 @@ def test_full_size_sampled(dev, name):
                 ne = gr["codec"].n_entries
                 gv = gr["vals"][wk * ne:(wk + 1) * ne]
                 gi = gr["pidx"][wk * ne:(wk + 1) * ne]
-                check_payload_properties(gv, gi, gr["lay"], 4096 if len(gr["shapes"][0]) == 2 else 64,
+                check_payload_properties(gv, gi, gr["lay"], [4096 if len(s) == 2 else 64 for s in gr["shapes"]],
                                          f"{name} step {t} worker {wk}")
                 gv_h = gv.cpu().numpy()
                 gi_h = gi.cpu().numpy().view(np.uint16)

@@ -204,3 +204,12 @@ def test_deterministic_repeat(dev):
         results.append([t.cpu().numpy() for t in [v, ix] + X + M[0] + M[1] + M[2]])
     for a, b in zip(*results):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_list_longer_than_one_launch(dev):
+    """More tensors than one launch's table holds: the call splits into launches, vectors first in each."""
+    shapes = []
+    for i in range(B.DEMO_MAX_TENSORS_PER_LAUNCH + 7):
+        shapes.append([(64, 64), (100,), (65, 3), (1,), (70, 130)][i % 5])
+    w = DI.WORKLOADS["tiny_256"].replace(name="long_list", shapes=tuple(shapes), workers=2, k=5)
+    Sim(w).run(2)
