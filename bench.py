@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one untimed 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="print the HBM rates plain torch streaming kernels reach on this device and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into profiles/traffic_<kernel>_<workload>.json and exit")
@@ -190,6 +192,40 @@ def pmc_summary(w: DI.Workload, fetch_csv: str, write_csv: str):
     return recs
 
 
+def hbm_probe(w: DI.Workload):
+    """Rates of plain streaming torch kernels over the workload's matrices (the achievable mixes)."""
+    import torch
+    dev = torch.device("cuda:0")
+    mats = [s for s in w.shapes if len(s) == 2]
+    A = [torch.ones(s, device=dev) for s in mats]
+    Bm = [torch.ones(s, device=dev) for s in mats]
+    n = sum(a.numel() for a in A)
+    big = torch.ones(1 << 28, device=dev)
+    big2 = torch.empty_like(big)
+
+    def med(fn, reps=7):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return sorted(ts)[reps // 2]
+    out = {}
+    for name, fn, nbytes in (
+            ("read 2, write 1 (lerp over the matrices)", lambda: [b.lerp_(a, 0.001) for a, b in zip(A, Bm)], 12 * n),
+            ("read 1, write 1 (scale over the matrices)", lambda: [b.mul_(0.999) for b in Bm], 8 * n),
+            ("read 1, write 1 (1 GiB device copy)", lambda: big2.copy_(big), 2 << 30),
+            ("write only (1 GiB fill)", lambda: big.fill_(1.0), 1 << 30)):
+        ms = med(fn)
+        out[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(nbytes / ms / 1e6, 1)}
+    return out
+
+
 def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False):
     import torch
 
@@ -295,6 +331,9 @@ def main():
               "codec on one GPU's share; collectives across GPUs are not part of it.", file=sys.stderr)
         sys.exit(2)
     w = DI.WORKLOADS[args.workload]
+    if args.hbm_probe:
+        print(json.dumps({"device": "cuda:0", "workload": w.name, "rates": hbm_probe(w)}))
+        return
     if args.pmc_summary:
         for name, rec in pmc_summary(w, *args.pmc_summary).items():
             print(json.dumps(rec))
