@@ -5,8 +5,9 @@ The codec runs in hand-written HIP kernels behind the C ABI declared in
 in-tree build (``build.py``) and a thin ctypes binding (``binding.py``).
 """
 from .binding import (  # noqa: F401
-    DEMO_AVG_CONTRIBUTORS, DEMO_AVG_WORKERS, DEMO_BASIS_DCT, DEMO_BASIS_USER, DEMO_BF16, DEMO_CHUNK, DEMO_F32,
-    DEMO_MAX_WORKERS, DEMO_MOMENTUM_DAMPED, DEMO_MOMENTUM_PLAIN, DEMO_PHI_IDENTITY, DEMO_PHI_SIGN, Codec,
-    DemoError, LIB_PATH, demo_ctx_create, demo_ctx_destroy, demo_decode_apply, demo_encode, demo_plan,
+    DEMO_AVG_CONTRIBUTORS, DEMO_AVG_WORKERS, DEMO_BASIS_DCT, DEMO_BASIS_IDENTITY, DEMO_BASIS_USER, DEMO_BF16,
+    DEMO_CHUNK, DEMO_F32, DEMO_MAX_TENSORS_PER_LAUNCH, DEMO_MAX_WORKERS, DEMO_MOMENTUM_DAMPED, DEMO_MOMENTUM_PLAIN,
+    DEMO_PHI_IDENTITY, DEMO_PHI_SIGN, DEMO_SUBTRACT_AGGREGATED, DEMO_SUBTRACT_LOCAL, Codec, DemoError, LIB_PATH,
+    demo_ctx_create, demo_ctx_destroy, demo_decode_apply, demo_decode_apply_subtract, demo_encode, demo_plan,
     load_library, make_cfg,
 )

@@ -26,9 +26,10 @@ STATUS_NAMES = {0: "DEMO_OK", 1: "DEMO_ERR_INVALID", 2: "DEMO_ERR_SHAPE", 3: "DE
 # enums
 DEMO_F32, DEMO_BF16 = 0, 1
 DEMO_MOMENTUM_DAMPED, DEMO_MOMENTUM_PLAIN = 0, 1
-DEMO_BASIS_DCT, DEMO_BASIS_USER = 0, 1
+DEMO_BASIS_DCT, DEMO_BASIS_USER, DEMO_BASIS_IDENTITY = 0, 1, 2
 DEMO_PHI_SIGN, DEMO_PHI_IDENTITY = 0, 1
 DEMO_AVG_CONTRIBUTORS, DEMO_AVG_WORKERS = 0, 1
+DEMO_SUBTRACT_LOCAL, DEMO_SUBTRACT_AGGREGATED = 0, 1
 
 
 class DemoError(RuntimeError):
@@ -44,7 +45,7 @@ class demo_shape(ctypes.Structure):
 class demo_codec_cfg(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int32), ("k", ctypes.c_int32), ("beta", ctypes.c_float),
                 ("alpha", ctypes.c_float), ("momentum_form", ctypes.c_int32), ("basis", ctypes.c_int32),
-                ("P0", ctypes.c_void_p), ("P1", ctypes.c_void_p)]
+                ("P0", ctypes.c_void_p), ("P1", ctypes.c_void_p), ("subtraction", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -75,6 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.demo_decode_apply.restype = i32
     lib.demo_decode_apply.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32,
                                       vp, vp, i64, i32, f32, f32, i32, vp]
+    lib.demo_decode_apply_subtract.restype = i32
+    lib.demo_decode_apply_subtract.argtypes = [vp, i32, P(demo_shape), P(vp), P(vp), P(demo_codec_cfg), i32,
+                                               vp, vp, i64, i32, f32, f32, i32, vp]
     _lib = lib
     return lib
 
@@ -110,15 +114,24 @@ def _stream_handle(stream) -> Optional[int]:
 
 
 def make_cfg(k: int, beta: float = 0.999, alpha: float = 0.2, plain: bool = False,
-             P0=None, P1=None, chunk: int = DEMO_CHUNK) -> demo_codec_cfg:
-    """Codec configuration; P0/P1 (device float32 64x64 tensors) select the user basis."""
+             P0=None, P1=None, chunk: int = DEMO_CHUNK, identity: bool = False,
+             aggregated: bool = False) -> demo_codec_cfg:
+    """Codec configuration; P0/P1 (device float32 64x64 tensors) select the user basis,
+    ``identity`` the identity basis (top-k in the parameter domain), ``aggregated``
+    the subtraction of the averaged coefficients on the decode side."""
     cfg = demo_codec_cfg()
     cfg.chunk = chunk
     cfg.k = int(k)
     cfg.beta = float(beta)
     cfg.alpha = float(alpha)
     cfg.momentum_form = DEMO_MOMENTUM_PLAIN if plain else DEMO_MOMENTUM_DAMPED
-    if P0 is None:
+    cfg.subtraction = DEMO_SUBTRACT_AGGREGATED if aggregated else DEMO_SUBTRACT_LOCAL
+    if identity:
+        if P0 is not None:
+            raise ValueError("the identity basis takes no P0/P1")
+        cfg.basis = DEMO_BASIS_IDENTITY
+        cfg.P0 = cfg.P1 = None
+    elif P0 is None:
         cfg.basis = DEMO_BASIS_DCT
         cfg.P0 = cfg.P1 = None
     else:
@@ -210,16 +223,44 @@ def demo_decode_apply(ctx: int, params, cfg: demo_codec_cfg, workers: int, pay_v
                                  float(eta), float(lam), int(avg), _stream_handle(stream)))
 
 
+def demo_decode_apply_subtract(ctx: int, params, moms, cfg: demo_codec_cfg, workers: int, pay_values, pay_idx,
+                               phi: int = DEMO_PHI_SIGN, eta: float = 1e-3, lam: float = 0.0,
+                               avg: int = DEMO_AVG_CONTRIBUTORS, stream=None) -> None:
+    """Aggregated-subtraction decode: params (or None) get the update, moms (or None) M - alpha M*."""
+    lib = load_library()
+    import torch
+    lists = [t for t in (params, moms) if t is not None]
+    if not lists:
+        raise ValueError("give params, moms or both")
+    ref = lists[0]
+    for lst in lists:
+        if len(lst) != len(ref) or any(tuple(a.shape) != tuple(b.shape) for a, b in zip(lst, ref)):
+            raise ValueError("params and moms must match in count and shape")
+        if any(t.dtype != torch.float32 for t in lst):
+            raise ValueError("parameters and momenta must be float32")
+    if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
+        raise ValueError("payload arrays must hold workers x entries elements")
+    per = pay_values.numel() // workers
+    pp = None if params is None else _ptrs([_device_ptr(x, 4) for x in params])
+    mp = None if moms is None else _ptrs([_device_ptr(m, 4) for m in moms])
+    _check(lib.demo_decode_apply_subtract(ctx, len(ref), _shapes([tuple(x.shape) for x in ref]), pp, mp,
+                                          ctypes.byref(cfg), int(workers), _device_ptr(pay_values, 4),
+                                          _device_ptr(pay_idx, 2), per, int(phi), float(eta), float(lam), int(avg),
+                                          _stream_handle(stream)))
+
+
 class Codec:
     """A context bound to one device plus the codec configuration of a tensor list."""
 
     def __init__(self, shapes: Sequence[Sequence[int]], k: int, beta: float = 0.999, alpha: float = 0.2,
-                 plain: bool = False, device: int = 0):
+                 plain: bool = False, device: int = 0, identity: bool = False, aggregated: bool = False):
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         self.k = int(k)
         self.beta = float(beta)
         self.alpha = float(alpha)
         self.plain = bool(plain)
+        self.identity = bool(identity)
+        self.aggregated = bool(aggregated)
         self.n_chunks, self.n_entries, self.entry_begin = demo_plan(self.shapes, self.k)
         self.ctx = demo_ctx_create(device)
 
@@ -235,7 +276,8 @@ class Codec:
             pass
 
     def cfg(self, P0=None, P1=None) -> demo_codec_cfg:
-        return make_cfg(self.k, self.beta, self.alpha, self.plain, P0, P1)
+        return make_cfg(self.k, self.beta, self.alpha, self.plain, P0, P1, identity=self.identity,
+                        aggregated=self.aggregated)
 
     def alloc_payload(self, workers: int = 1, device="cuda"):
         """Empty payload buffers: float32 values and 16-bit indices (int16 storage of uint16)."""
@@ -251,3 +293,8 @@ class Codec:
                      avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
         demo_decode_apply(self.ctx, params, self.cfg(P0, P1), workers, pay_values, pay_idx, phi, eta, lam,
                           avg, stream)
+
+    def decode_apply_subtract(self, params, moms, workers, pay_values, pay_idx, phi=DEMO_PHI_SIGN, eta=1e-3,
+                              lam=0.0, avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
+        demo_decode_apply_subtract(self.ctx, params, moms, self.cfg(P0, P1), workers, pay_values, pay_idx, phi,
+                                   eta, lam, avg, stream)

@@ -96,17 +96,25 @@ demo_status check_device(const demo_ctx* ctx) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-demo_status check_basis(const demo_codec_cfg* cfg, const std::vector<TensorPlan>& plan, const float** p0,
-                        const float** p1) {
+demo_status check_basis(const demo_codec_cfg* cfg, const std::vector<TensorPlan>& plan, demo::BasisKind* kind,
+                        const float** p0, const float** p1) {
   *p0 = nullptr;
   *p1 = nullptr;
-  if (cfg->basis == DEMO_BASIS_DCT) return DEMO_OK;
+  if (cfg->basis == DEMO_BASIS_DCT) {
+    *kind = demo::BasisKind::kDct;
+    return DEMO_OK;
+  }
+  if (cfg->basis == DEMO_BASIS_IDENTITY) {
+    *kind = demo::BasisKind::kIdentity;
+    return DEMO_OK;
+  }
   if (cfg->basis != DEMO_BASIS_USER) return fail(DEMO_ERR_INVALID, "unknown basis");
   bool any2d = false;
   for (const auto& t : plan) any2d = any2d || t.ndim == 2;
   if (cfg->P0 == nullptr) return fail(DEMO_ERR_INVALID, "user basis without P0");
   if (any2d && cfg->P1 == nullptr) return fail(DEMO_ERR_INVALID, "user basis without P1 for a matrix");
   if (!aligned(cfg->P0, 4) || (cfg->P1 && !aligned(cfg->P1, 4))) return fail(DEMO_ERR_ALIGN, "basis misaligned");
+  *kind = demo::BasisKind::kUser;
   *p0 = cfg->P0;
   *p1 = cfg->P1 ? cfg->P1 : cfg->P0;
   return DEMO_OK;
@@ -143,6 +151,62 @@ demo_status for_each_batch(const std::vector<TensorPlan>& plan, Fill&& fill, Lau
     }
   }
   return flush();
+}
+
+// Shared body of the decode entry points: params and/or moms (either may be
+// NULL) receive X - eta (phi(M*) + lambda X) and M - alpha M*.
+demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                          float* const* moms, const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                          const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
+                          demo_average avg, hipStream_t stream) {
+  if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
+  std::vector<TensorPlan> plan;
+  int64_t entries = 0;
+  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr);
+  if (s != DEMO_OK) return s;
+  if (workers < 1 || workers > demo::kMaxWorkers) return fail(DEMO_ERR_RANGE, "workers must be in 1..255");
+  if (phi != DEMO_PHI_SIGN && phi != DEMO_PHI_IDENTITY) return fail(DEMO_ERR_INVALID, "unknown phi");
+  if (avg != DEMO_AVG_CONTRIBUTORS && avg != DEMO_AVG_WORKERS) return fail(DEMO_ERR_INVALID, "unknown average");
+  if (!std::isfinite(eta) || !std::isfinite(lambda)) return fail(DEMO_ERR_INVALID, "eta/lambda not finite");
+  if (moms != nullptr && !std::isfinite(cfg->alpha)) return fail(DEMO_ERR_INVALID, "alpha not finite");
+  if (n_entries != entries)
+    return fail(DEMO_ERR_PAYLOAD, "payload holds " + std::to_string(n_entries) + " entries per worker, plan needs " +
+                                      std::to_string(entries));
+  for (float* const* list : {params, moms}) {
+    if (list == nullptr) continue;
+    for (int32_t i = 0; i < n; ++i) {
+      if (list[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
+      if (!aligned(list[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
+    }
+  }
+  if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr)) return fail(DEMO_ERR_INVALID, "payload is NULL");
+  if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
+  const float *p0, *p1;
+  demo::BasisKind kind;
+  if ((s = check_basis(cfg, plan, &kind, &p0, &p1)) != DEMO_OK) return s;
+  if ((s = check_device(ctx)) != DEMO_OK) return s;
+
+  demo::DecodeParams p{};
+  p.pay_val = pay_values;
+  p.pay_idx = pay_idx;
+  p.entries = entries;
+  p.workers = workers;
+  p.eta = eta;
+  p.lam = lambda;
+  p.inv_workers = float(1.0 / double(workers));
+  p.phi_sign = phi == DEMO_PHI_SIGN ? 1 : 0;
+  p.avg_workers = avg == DEMO_AVG_WORKERS ? 1 : 0;
+  p.update_x = params != nullptr ? 1 : 0;
+  p.update_m = moms != nullptr ? 1 : 0;
+  p.alpha = cfg->alpha;
+  auto fill = [&](demo::TensorSlot& slot, size_t i) {
+    slot.aux = moms != nullptr ? moms[i] : nullptr;
+    slot.dst = params != nullptr ? params[i] : nullptr;
+  };
+  p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
+  p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
+  return for_each_batch(plan, fill,
+                        [&](const LaunchTable& t) { return demo::launch_decode(t, p, kind, p0, p1, stream); });
 }
 
 }  // namespace
@@ -196,6 +260,8 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
   if (grad_dtype != DEMO_F32 && grad_dtype != DEMO_BF16) return fail(DEMO_ERR_INVALID, "unknown gradient dtype");
   if (cfg->momentum_form != DEMO_MOMENTUM_DAMPED && cfg->momentum_form != DEMO_MOMENTUM_PLAIN)
     return fail(DEMO_ERR_INVALID, "unknown momentum form");
+  if (cfg->subtraction != DEMO_SUBTRACT_LOCAL && cfg->subtraction != DEMO_SUBTRACT_AGGREGATED)
+    return fail(DEMO_ERR_INVALID, "unknown subtraction mode");
   if (!std::isfinite(cfg->beta) || !std::isfinite(cfg->alpha)) return fail(DEMO_ERR_INVALID, "beta/alpha not finite");
   if (n_entries != entries)
     return fail(DEMO_ERR_PAYLOAD, "payload holds " + std::to_string(n_entries) + " entries, plan needs " +
@@ -211,7 +277,8 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
   if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr)) return fail(DEMO_ERR_INVALID, "payload is NULL");
   if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
   const float *p0, *p1;
-  if ((s = check_basis(cfg, plan, &p0, &p1)) != DEMO_OK) return s;
+  demo::BasisKind kind;
+  if ((s = check_basis(cfg, plan, &kind, &p0, &p1)) != DEMO_OK) return s;
   if ((s = check_device(ctx)) != DEMO_OK) return s;
 
   demo::EncodeParams p{};
@@ -220,61 +287,34 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
   p.beta = cfg->beta;
   p.gcoef = cfg->momentum_form == DEMO_MOMENTUM_PLAIN ? 1.0f : float(1.0 - double(cfg->beta));
   p.alpha = cfg->alpha;
+  p.subtract_local = cfg->subtraction == DEMO_SUBTRACT_LOCAL ? 1 : 0;
   const bool bf16 = grad_dtype == DEMO_BF16;
   auto fill = [&](demo::TensorSlot& slot, size_t i) {
-    slot.src = grads[i];
+    slot.aux = const_cast<void*>(grads[i]);  // read only in the kernels
     slot.dst = moms[i];
   };
   p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
   p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
   return for_each_batch(plan, fill,
-                        [&](const LaunchTable& t) { return demo::launch_encode(t, p, bf16, p0, p1, stream); });
+                        [&](const LaunchTable& t) { return demo::launch_encode(t, p, bf16, kind, p0, p1, stream); });
 }
 
 demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                               const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
                               const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
                               demo_average avg, hipStream_t stream) {
-  if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
-  std::vector<TensorPlan> plan;
-  int64_t entries = 0;
-  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr);
-  if (s != DEMO_OK) return s;
-  if (workers < 1 || workers > demo::kMaxWorkers) return fail(DEMO_ERR_RANGE, "workers must be in 1..255");
-  if (phi != DEMO_PHI_SIGN && phi != DEMO_PHI_IDENTITY) return fail(DEMO_ERR_INVALID, "unknown phi");
-  if (avg != DEMO_AVG_CONTRIBUTORS && avg != DEMO_AVG_WORKERS) return fail(DEMO_ERR_INVALID, "unknown average");
-  if (!std::isfinite(eta) || !std::isfinite(lambda)) return fail(DEMO_ERR_INVALID, "eta/lambda not finite");
-  if (n_entries != entries)
-    return fail(DEMO_ERR_PAYLOAD, "payload holds " + std::to_string(n_entries) + " entries per worker, plan needs " +
-                                      std::to_string(entries));
   if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
-  for (int32_t i = 0; i < n; ++i) {
-    if (params[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
-    if (!aligned(params[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
-  }
-  if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr)) return fail(DEMO_ERR_INVALID, "payload is NULL");
-  if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
-  const float *p0, *p1;
-  if ((s = check_basis(cfg, plan, &p0, &p1)) != DEMO_OK) return s;
-  if ((s = check_device(ctx)) != DEMO_OK) return s;
+  return decode_common(ctx, n, shapes, params, nullptr, cfg, workers, pay_values, pay_idx, n_entries, phi, eta,
+                       lambda, avg, stream);
+}
 
-  demo::DecodeParams p{};
-  p.pay_val = pay_values;
-  p.pay_idx = pay_idx;
-  p.entries = entries;
-  p.workers = workers;
-  p.eta = eta;
-  p.lam = lambda;
-  p.inv_workers = float(1.0 / double(workers));
-  p.phi_sign = phi == DEMO_PHI_SIGN ? 1 : 0;
-  p.avg_workers = avg == DEMO_AVG_WORKERS ? 1 : 0;
-  auto fill = [&](demo::TensorSlot& slot, size_t i) {
-    slot.src = nullptr;
-    slot.dst = params[i];
-  };
-  p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
-  p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
-  return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_decode(t, p, p0, p1, stream); });
+demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                       float* const* moms, const demo_codec_cfg* cfg, int32_t workers,
+                                       const float* pay_values, const uint16_t* pay_idx, int64_t n_entries,
+                                       demo_phi phi, float eta, float lambda, demo_average avg, hipStream_t stream) {
+  if (params == nullptr && moms == nullptr) return fail(DEMO_ERR_INVALID, "neither parameters nor momenta given");
+  return decode_common(ctx, n, shapes, params, moms, cfg, workers, pay_values, pay_idx, n_entries, phi, eta, lambda,
+                       avg, stream);
 }
 
 }  // extern "C"

@@ -40,6 +40,7 @@ namespace {
 
 using xf::DctBasis;
 using xf::DenseBasis;
+using xf::IdentityBasis;
 
 constexpr int kLd = 65;     // LDS tile row stride in floats
 constexpr int kCntLd = 17;  // count rows: 16 words of 8-bit counts + 1 pad word
@@ -134,7 +135,7 @@ __device__ __forceinline__ void load_momentum(float (&q)[64], const TensorSlot& 
                                               float beta, float gcoef) {
   const int64_t ld = ts.cols;
   const float* __restrict__ m = ts.dst + c.base;
-  const char* __restrict__ g = static_cast<const char*>(ts.src) + c.base * (kBf16 ? 2 : 4);
+  const char* __restrict__ g = static_cast<const char*>(ts.aux) + c.base * (kBf16 ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     float gv = 0.f, mv = 0.f;
@@ -157,6 +158,12 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
     load_momentum<true, kBf16>(q, ts, c, lane, p.beta, p.gcoef);
   else
     load_momentum<false, kBf16>(q, ts, c, lane, p.beta, p.gcoef);
+  if (!p.subtract_local) {  // aggregated subtraction: M = M' now, the decode side subtracts
+    if (c.full)
+      store_rows<true>(q, ts.dst + c.base, ts.cols, c, lane);
+    else
+      store_rows<false>(q, ts.dst + c.base, ts.cols, c, lane);
+  }
 
   basis.fwd0(q);
   col_to_row(tile, q, lane);
@@ -164,6 +171,7 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
   tk::topk_chunk(q, p.keff2, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
+  if (!p.subtract_local) return;
   __syncthreads();
 
   basis.inv1(q);
@@ -190,7 +198,7 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
   const int64_t first = int64_t(slab) * 64 * 64 + lane;  // this lane's element of the slab's chunk 0
   const int64_t rem = int64_t(ts.rows) - first;          // elements c * 64 < rem exist
   float* __restrict__ m = ts.dst + first;
-  const char* __restrict__ g = static_cast<const char*>(ts.src) + first * (kBf16 ? 2 : 4);
+  const char* __restrict__ g = static_cast<const char*>(ts.aux) + first * (kBf16 ? 2 : 4);
 
   float q[64];
 #pragma unroll
@@ -202,6 +210,12 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
     }
     q[c] = fmaf(p.beta, mv, p.gcoef * gv);
   }
+  if (!p.subtract_local) {  // aggregated subtraction: M = M' now, the decode side subtracts
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      if (c * 64 < rem) stream_store(q[c], &m[c * 64]);
+    }
+  }
   col_to_row(tile, q, lane);
   basis.fwd0(q);
 
@@ -209,6 +223,7 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
   const bool live = chunk < int((uint32_t(ts.rows) + 63u) >> 6);
   const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff1;
   tk::topk_lane(q, p.keff1, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
+  if (!p.subtract_local) return;
 
   basis.inv0(q);
   row_to_col(tile, q, lane);
@@ -228,13 +243,13 @@ __device__ __forceinline__ void encode_item(const LaunchTable& tab, const Encode
     encode_matrix<Basis, kBf16>(ts, p, basis, tile);
 }
 
-// The DCT kernel fits 168 VGPRs, i.e. three waves per SIMD; the dense
-// (caller-basis) kernel needs more and is left to the compiler.
-template <bool kBf16>
+// The DCT and identity kernels fit 168 VGPRs, i.e. three waves per SIMD; the
+// dense (caller-basis) kernel needs more and is left to the compiler.
+template <class Basis, bool kBf16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void encode_kernel(LaunchTable tab,
                                                                                              EncodeParams p) {
   __shared__ float tile[64 * kLd];
-  encode_item<DctBasis, kBf16>(tab, p, DctBasis{}, tile);
+  encode_item<Basis, kBf16>(tab, p, Basis{}, tile);
 }
 
 template <bool kBf16>
@@ -352,14 +367,16 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   // Parameters are fetched first: they land while the payloads are averaged
   // and inverse-transformed.
   const int64_t ld = ts.cols;
-  float* __restrict__ xp = ts.dst + c.base;
+  float* __restrict__ xp = p.update_x ? ts.dst + c.base : nullptr;
   float x[64];
-  if (c.full) {
+  if (p.update_x) {
+    if (c.full) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[i * ld + lane]);
-  } else {
+      for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[i * ld + lane]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = (lane < c.vc && i < c.vr) ? stream_load(&xp[i * ld + lane]) : 0.f;
+      for (int i = 0; i < 64; ++i) x[i] = (lane < c.vc && i < c.vr) ? stream_load(&xp[i * ld + lane]) : 0.f;
+    }
   }
 
   clear_acc(acc, cntw, lane);
@@ -374,12 +391,24 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   row_to_col(acc, q, lane);
   basis.inv0(q);
 
+  if (p.update_x) {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
-  if (c.full)
-    store_rows<true>(x, xp, ld, c, lane);
-  else
-    store_rows<false>(x, xp, ld, c, lane);
+    for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
+    if (c.full)
+      store_rows<true>(x, xp, ld, c, lane);
+    else
+      store_rows<false>(x, xp, ld, c, lane);
+  }
+  if (p.update_m) {  // aggregated subtraction: M = M - alpha M*
+    float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (c.full || (lane < c.vc && i < c.vr)) {
+        const int64_t off = i * ld + lane;
+        stream_store(fmaf(-p.alpha, q[i], stream_load(&mp[off])), &mp[off]);
+      }
+    }
+  }
 }
 
 template <class Basis>
@@ -401,10 +430,19 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   basis.inv0(q);
   row_to_col(acc, q, lane);
 
-  float* __restrict__ x = ts.dst + first;
+  if (p.update_x) {
+    float* __restrict__ x = ts.dst + first;
 #pragma unroll
-  for (int c = 0; c < 64; ++c) {
-    if (c * 64 < rem) stream_store(update(stream_load(&x[c * 64]), q[c], p), &x[c * 64]);
+    for (int c = 0; c < 64; ++c) {
+      if (c * 64 < rem) stream_store(update(stream_load(&x[c * 64]), q[c], p), &x[c * 64]);
+    }
+  }
+  if (p.update_m) {  // aggregated subtraction: M = M - alpha M*
+    float* __restrict__ m = static_cast<float*>(ts.aux) + first;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      if (c * 64 < rem) stream_store(fmaf(-p.alpha, q[c], stream_load(&m[c * 64])), &m[c * 64]);
+    }
   }
 }
 
@@ -418,10 +456,11 @@ __device__ __forceinline__ void decode_item(const LaunchTable& tab, const Decode
     decode_matrix<Basis>(ts, p, basis, acc, cntw);
 }
 
+template <class Basis>
 __global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParams p) {
   __shared__ float acc[64 * kLd];
   __shared__ uint32_t cntw[64 * kCntLd];
-  decode_item<DctBasis>(tab, p, DctBasis{}, acc, cntw);
+  decode_item<Basis>(tab, p, Basis{}, acc, cntw);
 }
 
 __global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
@@ -434,33 +473,50 @@ __global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, Decod
 
 // ---------------------------------------------------------------- host-side launchers
 
-hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, const float* basis_p0,
-                         const float* basis_p1, hipStream_t stream) {
+hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, BasisKind kind,
+                         const float* basis_p0, const float* basis_p1, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
   const dim3 grid(tab.items), block(64);
-  if (basis_p0 == nullptr) {
-    if (g_bf16)
-      encode_kernel<true><<<grid, block, 0, stream>>>(tab, p);
-    else
-      encode_kernel<false><<<grid, block, 0, stream>>>(tab, p);
-  } else {
-    const DenseBasis b{basis_p0, basis_p1};
-    if (g_bf16)
-      encode_dense_kernel<true><<<grid, block, 0, stream>>>(tab, p, b);
-    else
-      encode_dense_kernel<false><<<grid, block, 0, stream>>>(tab, p, b);
+  switch (kind) {
+    case BasisKind::kDct:
+      if (g_bf16)
+        encode_kernel<DctBasis, true><<<grid, block, 0, stream>>>(tab, p);
+      else
+        encode_kernel<DctBasis, false><<<grid, block, 0, stream>>>(tab, p);
+      break;
+    case BasisKind::kIdentity:
+      if (g_bf16)
+        encode_kernel<IdentityBasis, true><<<grid, block, 0, stream>>>(tab, p);
+      else
+        encode_kernel<IdentityBasis, false><<<grid, block, 0, stream>>>(tab, p);
+      break;
+    case BasisKind::kUser: {
+      const DenseBasis b{basis_p0, basis_p1};
+      if (g_bf16)
+        encode_dense_kernel<true><<<grid, block, 0, stream>>>(tab, p, b);
+      else
+        encode_dense_kernel<false><<<grid, block, 0, stream>>>(tab, p, b);
+      break;
+    }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0, const float* basis_p1,
-                         hipStream_t stream) {
+hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
+                         const float* basis_p1, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
   const dim3 grid(tab.items), block(64);
-  if (basis_p0 == nullptr)
-    decode_kernel<<<grid, block, 0, stream>>>(tab, p);
-  else
-    decode_dense_kernel<<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
+  switch (kind) {
+    case BasisKind::kDct:
+      decode_kernel<DctBasis><<<grid, block, 0, stream>>>(tab, p);
+      break;
+    case BasisKind::kIdentity:
+      decode_kernel<IdentityBasis><<<grid, block, 0, stream>>>(tab, p);
+      break;
+    case BasisKind::kUser:
+      decode_dense_kernel<<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@ constexpr int kMaxTensorsPerLaunch = 96;
 constexpr int kMaxWorkers = 255;  // counts are kept in 8 bits
 
 struct TensorSlot {
-  const void* src;      // encode: gradient (fp32 or bf16); unused by decode
-  float* dst;           // encode: momentum (in/out); decode: parameters (in/out)
+  void* aux;            // encode: gradient (fp32 or bf16, read only); decode: momentum (in/out) or null
+  float* dst;           // encode: momentum (in/out); decode: parameters (in/out) or null
   int64_t entry_begin;  // payload entry of the tensor's first chunk
   int32_t rows;         // 2-D: dim 0; 1-D: length
   int32_t cols;         // 2-D: dim 1 (>= 1); 1-D: 0, which marks a vector
@@ -43,8 +43,9 @@ struct EncodeParams {
   float beta;
   float gcoef;  // (1 - beta) or 1
   float alpha;
-  int32_t keff2;  // entries per 64x64 chunk
-  int32_t keff1;  // entries per 64-element chunk
+  int32_t keff2;           // entries per 64x64 chunk
+  int32_t keff1;           // entries per 64-element chunk
+  int32_t subtract_local;  // 1: M = M' - alpha (own part); 0: M = M'
 };
 
 struct DecodeParams {
@@ -59,13 +60,18 @@ struct DecodeParams {
   float inv_workers;
   int32_t phi_sign;     // 1: sign, 0: identity
   int32_t avg_workers;  // 1: divide by W, 0: by contributor count
+  int32_t update_x;     // 1: X = X - eta (phi(M*) + lambda X)
+  int32_t update_m;     // 1: M = M - alpha M* (aggregated subtraction)
+  float alpha;
 };
 
-// Host entry points into the kernels (kernels.hip).  basis_p0/p1 are null for
-// the DCT basis.  Return the hipError_t of the launch.
-hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, const float* basis_p0,
+enum class BasisKind { kDct, kUser, kIdentity };
+
+// Host entry points into the kernels (kernels.hip).  basis_p0/p1 are used
+// for BasisKind::kUser only.  Return the hipError_t of the launch.
+hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, BasisKind kind,
+                         const float* basis_p0, const float* basis_p1, hipStream_t stream);
+hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream);
-hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, const float* basis_p0, const float* basis_p1,
-                         hipStream_t stream);
 
 }  // namespace demo

@@ -265,6 +265,14 @@ struct DctBasis {
   __host__ __device__ __forceinline__ void inv1(float (&x)[64]) const { dct3<64, Ortho<64>>(x); }
 };
 
+// P0 = P1 = I: the chunk is ranked and sparsified in the parameter domain.
+struct IdentityBasis {
+  __host__ __device__ __forceinline__ void fwd0(float (&)[64]) const {}
+  __host__ __device__ __forceinline__ void fwd1(float (&)[64]) const {}
+  __host__ __device__ __forceinline__ void inv0(float (&)[64]) const {}
+  __host__ __device__ __forceinline__ void inv1(float (&)[64]) const {}
+};
+
 // Caller-supplied orthonormal P0 / P1 (64 x 64, row-major, rows are basis vectors).
 struct DenseBasis {
   const float* __restrict__ p0;

@@ -71,10 +71,12 @@ typedef enum demo_dtype { DEMO_F32 = 0, DEMO_BF16 = 1 } demo_dtype;
 typedef enum demo_momentum_form { DEMO_MOMENTUM_DAMPED = 0, DEMO_MOMENTUM_PLAIN = 1 } demo_momentum_form;
 
 /* Projection, DeMo summary §3.4 Blockwise Linear Projection (DCT):
- * DCT   orthonormal DCT-II on both chunk dimensions (P0 = P1 = P, P^T = P^-1)
- * USER  caller-supplied orthonormal P0, P1 (e.g. the random orthonormal
- *       projection re-drawn every step, identical on all workers) */
-typedef enum demo_basis { DEMO_BASIS_DCT = 0, DEMO_BASIS_USER = 1 } demo_basis;
+ * DCT       orthonormal DCT-II on both chunk dimensions (P0 = P1 = P, P^T = P^-1)
+ * USER      caller-supplied orthonormal P0, P1 (e.g. the random orthonormal
+ *           projection re-drawn every step, identical on all workers)
+ * IDENTITY  P0 = P1 = I: top-k in the parameter domain (the identity choice
+ *           that section compares against) */
+typedef enum demo_basis { DEMO_BASIS_DCT = 0, DEMO_BASIS_USER = 1, DEMO_BASIS_IDENTITY = 2 } demo_basis;
 
 /* phi of DeMo summary §3.4 Base Optimizer Update: sign (Signum) or identity (SGD). */
 typedef enum demo_phi { DEMO_PHI_SIGN = 0, DEMO_PHI_IDENTITY = 1 } demo_phi;
@@ -83,6 +85,17 @@ typedef enum demo_phi { DEMO_PHI_SIGN = 0, DEMO_PHI_IDENTITY = 1 } demo_phi;
  * CONTRIBUTORS  number of workers whose payload holds the index (default)
  * WORKERS       W (a worker without the index contributes a zero) */
 typedef enum demo_average { DEMO_AVG_CONTRIBUTORS = 0, DEMO_AVG_WORKERS = 1 } demo_average;
+
+/* What the momentum subtraction removes (DeMo summary §3.4 Momentum
+ * Subtraction as Implicit Error Feedback, which writes the aggregated
+ * coefficients; the papernotes.org note's 关键设计 3 subtracts what the worker
+ * itself sent, before the all-gather):
+ * LOCAL       demo_encode leaves M' - alpha * unchunk(P0^T Q_hat P1), Q_hat the
+ *             worker's own selected coefficients (default)
+ * AGGREGATED  demo_encode leaves M' untouched; demo_decode_apply_subtract then
+ *             removes alpha * unchunk(P0^T Q_bar P1) = alpha * M*, Q_bar the
+ *             average of all W payloads */
+typedef enum demo_subtraction { DEMO_SUBTRACT_LOCAL = 0, DEMO_SUBTRACT_AGGREGATED = 1 } demo_subtraction;
 
 typedef struct demo_shape {
   int32_t ndim;    /* 1 or 2 */
@@ -99,6 +112,7 @@ typedef struct demo_codec_cfg {
   const float* P0;       /* DEMO_BASIS_USER: device 64x64 fp32 row-major, rows are the basis
                             vectors; acts on dimension 0 and on vectors */
   const float* P1;       /* DEMO_BASIS_USER with any matrix: device 64x64, acts on dimension 1 */
+  int32_t subtraction;   /* demo_subtraction */
 } demo_codec_cfg;
 
 typedef struct demo_ctx demo_ctx;
@@ -126,6 +140,7 @@ demo_status demo_plan(const demo_shape* shapes, int32_t n, int32_t chunk, int32_
  *   moms[i]:   device float32, shapes[i]; read and overwritten with
  *              M' - alpha * unchunk(P0^T Q_hat P1), where M' is the updated
  *              momentum and Q_hat this worker's own selected coefficients
+ *              (with cfg->subtraction == DEMO_SUBTRACT_AGGREGATED: with M')
  *   pay_values / pay_idx: device arrays of n_entries entries, written
  * Top-k ranks float32 magnitudes; equal magnitudes go to the lower index. */
 demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, const void* const* grads,
@@ -139,12 +154,28 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
  *               X - eta * (phi(M*) + lambda * X), X the pre-update value
  *   pay_values / pay_idx: device, workers x n_entries entries (worker-major, as
  *               an all-gather lays them out); read only
- * cfg supplies chunk, k and the basis; its beta, alpha and momentum_form are unused.
- * Coefficients are summed in worker order 0..W-1; the result is deterministic. */
+ * cfg supplies chunk, k and the basis; its beta, alpha, momentum_form and
+ * subtraction are unused.  Coefficients are summed in worker order 0..W-1;
+ * the result is deterministic. */
 demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                               const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
                               const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
                               demo_average avg, hipStream_t stream);
+
+/* The decode of DEMO_SUBTRACT_AGGREGATED (DeMo summary §3.4 Momentum
+ * Subtraction as Implicit Error Feedback, with the aggregated coefficients):
+ * the same M* as demo_decode_apply, applied to the parameters and/or to one
+ * worker's momentum in one pass.
+ *   params: as for demo_decode_apply, or NULL to leave the parameters alone
+ *   moms:   NULL, or device float32 tensors (shapes[i]) overwritten with
+ *           M - cfg->alpha * M*
+ * At least one of params and moms must be given.  A worker runs it once with
+ * both; a single-device simulation of W workers passes the parameters with
+ * one worker's momenta and then each other worker's momenta alone. */
+demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                       float* const* moms, const demo_codec_cfg* cfg, int32_t workers,
+                                       const float* pay_values, const uint16_t* pay_idx, int64_t n_entries,
+                                       demo_phi phi, float eta, float lambda, demo_average avg, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,9 @@ Pages followed (cited below by these tags):
 Readings taken where the pages are silent or disagree (each is listed in
 the design doc with its reason):
   * momentum form: (1-beta)*G by default, plain G behind ``plain=True``;
-  * momentum subtraction uses the worker's OWN selected coefficients;
+  * momentum subtraction uses the worker's OWN selected coefficients
+    (``subtract="aggregated"`` with ``subtract_aggregated`` gives the
+    summary page's aggregated reading);
   * averaging divides by the number of workers whose payload holds the
     index (membership, even for a 0.0 value); ``mode="workers"`` divides by W;
   * dims not divisible by s are zero-padded; the full s x s block is
@@ -199,11 +201,14 @@ def subtract_selected(Mp_chunks: np.ndarray, Q: np.ndarray, S: np.ndarray, alpha
 
 def encode(M: np.ndarray, G: np.ndarray, *, beta: float, alpha: float, k: int,
            plain: bool = False, P0: Optional[np.ndarray] = None, P1: Optional[np.ndarray] = None,
-           s: int = 64) -> Dict[str, np.ndarray]:
+           s: int = 64, subtract: str = "local") -> Dict[str, np.ndarray]:
     """One worker's encode of one tensor.
 
     Steps in the pages' order: local momentum update, chunking, projection,
     per-chunk top-k, payload (value, index), momentum subtraction.
+    ``subtract="aggregated"`` leaves M' in place: [S] Momentum Subtraction
+    writes the subtraction with the server's averaged coefficients, which
+    only exist after the exchange (see ``subtract_aggregated``).
     Returns float32 ``M`` (new momentum), float32 ``values`` [n_chunks, keff],
     uint16 ``idx`` [n_chunks, keff] (ascending per chunk), and the float64
     intermediates ``Mp_chunks`` and ``Q`` for the tests.
@@ -219,7 +224,12 @@ def encode(M: np.ndarray, G: np.ndarray, *, beta: float, alpha: float, k: int,
     keff = k_effective(k, numel)
     S = select_topk(Q.reshape(n, numel), keff)
     vals = np.take_along_axis(Q.reshape(n, numel), S, axis=1)
-    new_chunks = subtract_selected(chunks, Q, S, alpha, P0, P1)
+    if subtract == "local":
+        new_chunks = subtract_selected(chunks, Q, S, alpha, P0, P1)
+    elif subtract == "aggregated":
+        new_chunks = chunks
+    else:
+        raise ValueError(subtract)
     M_new = merge_chunks(new_chunks, M.shape, s).astype(F32)
     return {
         "M": M_new,
@@ -295,6 +305,16 @@ def decode_apply(X: np.ndarray, values: np.ndarray, idx: np.ndarray, *, phi: str
     X64 = X.astype(F64)
     X_new = X64 - float(eta) * (phi_map(Mstar, phi) + float(lam) * X64)
     return {"X": X_new.astype(F32), "Mstar": Mstar}
+
+
+def subtract_aggregated(M: np.ndarray, Mstar: np.ndarray, alpha: float) -> np.ndarray:
+    """Momentum subtraction with the aggregated coefficients.
+
+    [S] Momentum Subtraction as Implicit Error Feedback: M <- M - alpha *
+    B^-1(T^-1(Q_bar)), Q_bar the server's average, i.e. M - alpha * M* with
+    M* from ``decode_apply``.  Returns float32.
+    """
+    return (np.asarray(M, dtype=F64) - float(alpha) * np.asarray(Mstar, dtype=F64)).astype(F32)
 
 
 # ---------------------------------------------------------------------------

@@ -187,3 +187,18 @@ def compare_decode(dec: dict, shape, phi: str, eta: float, gpu_X: np.ndarray, ch
         raise AssertionError(f"{where}: parameters differ at flat {i}: gpu {gpu_X.ravel()[i]!r} "
                              f"ref {ref.ravel()[i]!r} M* {Mstar.ravel()[i]!r} ({int(bad.sum())} elements)")
     return new_elem
+
+
+def compare_momentum(ref_M: np.ndarray, gpu_M: np.ndarray, shape, chunk_diverged: np.ndarray, where: str = ""):
+    """Check a momentum tensor after the aggregated subtraction, chunks not diverged only."""
+    ref = ref_M.astype(np.float64)
+    n = chunk_diverged.shape[0]
+    norms = np.linalg.norm(O.split_chunks(ref).reshape(n, -1), axis=1)
+    atol = chunk_values_to_elements(np.maximum(ATOL, NOISE * norms), shape)
+    live = ~chunk_mask_to_elements(chunk_diverged, shape)
+    diff = np.abs(gpu_M.astype(np.float64) - ref)
+    bad = (diff > _tol(ref, atol)) & live
+    if bad.any():
+        i = np.argmax(np.where(bad, diff, 0))
+        raise AssertionError(f"{where}: momentum differs at flat {i}: gpu {gpu_M.ravel()[i]!r} "
+                             f"ref {ref.ravel()[i]!r} ({int(bad.sum())} elements)")

@@ -73,8 +73,8 @@ def test_plan_olmo_sizes(lib):
 
 
 def _call_encode(lib, shapes, k=8, chunk=64, grad_dtype=0, beta=0.9, alpha=0.2, form=0, basis=0,
-                 P0=None, P1=None, entries=None, grads=0x1000, moms=0x2000, vals=0x3000, idx=0x4000):
-    cfg = B.demo_codec_cfg(chunk, k, beta, alpha, form, basis, P0, P1)
+                 P0=None, P1=None, entries=None, grads=0x1000, moms=0x2000, vals=0x3000, idx=0x4000, subtraction=0):
+    cfg = B.demo_codec_cfg(chunk, k, beta, alpha, form, basis, P0, P1, subtraction)
     n = len(shapes)
     sh = B._shapes(shapes)
     if entries is None:
@@ -92,6 +92,18 @@ def _call_decode(lib, shapes, k=8, workers=2, phi=0, avg=0, eta=1e-3, lam=0.0, e
         entries = O.payload_entries(shapes, k)
     return lib.demo_decode_apply(None, n, B._shapes(shapes), B._ptrs([params] * n), ctypes.byref(cfg), workers,
                                  vals, idx, entries, phi, eta, lam, avg, None)
+
+
+def _call_decode_subtract(lib, shapes, params=0x1000, moms=0x2000, alpha=0.2, k=8, workers=2, vals=0x3000,
+                          idx=0x4000, bad_index=None):
+    cfg = B.demo_codec_cfg(64, k, 0.9, alpha, 0, 0, None, None, 1)
+    n = len(shapes)
+    pl = None if params is None else B._ptrs([params] * n)
+    ml = None if moms is None else B._ptrs([moms] * n)
+    if bad_index is not None:
+        ml[bad_index] = None
+    return lib.demo_decode_apply_subtract(None, n, B._shapes(shapes), pl, ml, ctypes.byref(cfg), workers, vals, idx,
+                                          O.payload_entries(shapes, k), 0, 1e-3, 0.0, 0, None)
 
 
 def _msg(lib):
@@ -128,6 +140,9 @@ def test_valid_arguments_reach_the_context_check(lib):
     (dict(basis=1), 1),
     (dict(basis=1, P0=0x5000), 1),
     (dict(basis=1, P0=0x5002, P1=0x6000), 7),
+    (dict(basis=3), 1),
+    (dict(subtraction=2), 1),
+    (dict(subtraction=-1), 1),
 ])
 def test_encode_rejects_bad_arguments(lib, kw, status):
     shapes = kw.pop("shapes", [(128, 64), (100,)])
@@ -150,6 +165,26 @@ def test_encode_rejects_bad_arguments(lib, kw, status):
 ])
 def test_decode_rejects_bad_arguments(lib, kw, status):
     assert _call_decode(lib, [(128, 64), (100,)], **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(subtraction=1), dict(basis=2), dict(basis=2, subtraction=1, k=4096)])
+def test_identity_basis_and_aggregated_subtraction_are_valid(lib, kw):
+    assert _call_encode(lib, [(128, 64), (100,)], **kw) == 1 and "context" in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(), 1, "context"),
+    (dict(params=None), 1, "context"),
+    (dict(moms=None), 1, "context"),
+    (dict(params=None, moms=None), 1, "neither"),
+    (dict(moms=0x2002), 7, "misaligned"),
+    (dict(bad_index=1), 1, "NULL"),
+    (dict(alpha=float("nan")), 1, "alpha"),
+    (dict(workers=0), 3, "workers"),
+])
+def test_decode_apply_subtract_arguments(lib, kw, status, text):
+    assert _call_decode_subtract(lib, [(128, 64), (100,)], **kw) == status
+    assert text in _msg(lib)
 
 
 def test_vectors_only_user_basis_needs_no_p1(lib):

@@ -32,13 +32,15 @@ def dev():
 class Sim:
     """W workers of one workload, GPU next to the oracle."""
 
-    def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None):
+    def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None, identity=False, aggregated=False):
         self.w = w
         self.plain = plain
+        self.identity = identity
+        self.aggregated = aggregated
         self.avg = avg
         self.inputs = inputs  # optional callable (worker, step, tensor) -> float32 gradient
         self.shapes = [tuple(s) for s in w.shapes]
-        self.codec = B.Codec(self.shapes, w.k, w.beta, w.alpha, plain)
+        self.codec = B.Codec(self.shapes, w.k, w.beta, w.alpha, plain, identity=identity, aggregated=aggregated)
         self.lay = PR.layout(self.shapes, w.k)
         nc, ne, eb = B.demo_plan(self.shapes, w.k)
         assert ne == sum(n * k for n, k, _ in self.lay)
@@ -60,6 +62,9 @@ class Sim:
         return DI.gradient(self.w, worker, step, i)
 
     def basis(self, step):
+        if self.identity:
+            eye = np.eye(64)
+            return eye, eye, None, None
         if not self.w.random_basis:
             return None, None, None, None
         P0 = O.orthonormal_rows(DI.gaussian_matrix(self.w, step, 0)).astype(np.float32)
@@ -89,10 +94,10 @@ class Sim:
             for i, shp in enumerate(self.shapes):
                 n, keff, e0 = self.lay[i]
                 out = O.encode(self.M_or[wk][i], G[i], beta=w.beta, alpha=w.alpha, k=w.k, plain=self.plain,
-                               P0=P0, P1=P1)
+                               P0=P0, P1=P1, subtract="aggregated" if self.aggregated else "local")
                 gM = self.M_gpu[wk][i].cpu().numpy()
                 self.cdiv[wk][i] = PR.compare_encode(
-                    out, shp, keff, w.alpha, O.dct_basis() if P0 is None else P0,
+                    out, shp, keff, 0.0 if self.aggregated else w.alpha, O.dct_basis() if P0 is None else P0,
                     O.dct_basis() if P1 is None else P1, gM, gv[e0:e0 + n * keff].reshape(n, keff),
                     gi[e0:e0 + n * keff].reshape(n, keff), self.cdiv[wk][i], self.report,
                     where=f"{w.name} step {t} worker {wk} tensor {i} {shp}")
@@ -100,7 +105,15 @@ class Sim:
                 or_vals[i][wk] = out["values"]
                 or_idx[i][wk] = out["idx"]
         say(f"  [{w.name}] step {t}: GPU decode/apply over {W} payloads")
-        self.codec.decode_apply(self.X_gpu, W, self.vals, self.idx, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
+        if self.aggregated:
+            # worker 0 updates the parameters and its momentum in one pass, the others their momentum only
+            self.codec.decode_apply_subtract(self.X_gpu, self.M_gpu[0], W, self.vals, self.idx, phi_c, w.eta, w.lam,
+                                             avg_c, P0d, P1d)
+            for wk in range(1, W):
+                self.codec.decode_apply_subtract(None, self.M_gpu[wk], W, self.vals, self.idx, phi_c, w.eta, w.lam,
+                                                 avg_c, P0d, P1d)
+        else:
+            self.codec.decode_apply(self.X_gpu, W, self.vals, self.idx, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
         torch.cuda.synchronize()
         for i, shp in enumerate(self.shapes):
             dec = O.decode_apply(self.X_or[i], np.stack(or_vals[i]), np.stack(or_idx[i]), phi=w.phi, eta=w.eta,
@@ -111,6 +124,12 @@ class Sim:
             self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
                                              where=f"{w.name} step {t} tensor {i} {shp}")
             self.X_or[i] = dec["X"]
+            if self.aggregated:
+                for wk in range(W):
+                    self.M_or[wk][i] = O.subtract_aggregated(self.M_or[wk][i], dec["Mstar"], w.alpha)
+                    PR.compare_momentum(self.M_or[wk][i], self.M_gpu[wk][i].cpu().numpy(), shp, cd,
+                                        where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (aggregated)")
+                    self.cdiv[wk][i] = self.cdiv[wk][i] | cd
 
     def run(self, steps, max_tie_fraction=0.02):
         for t in range(steps):
@@ -213,3 +232,18 @@ def test_list_longer_than_one_launch(dev):
         shapes.append([(64, 64), (100,), (65, 3), (1,), (70, 130)][i % 5])
     w = DI.WORKLOADS["tiny_256"].replace(name="long_list", shapes=tuple(shapes), workers=2, k=5)
     Sim(w).run(2)
+
+
+@pytest.mark.parametrize("k,alpha", [(8, 0.2), (1, 1.0), (4096, 0.5)])
+def test_identity_basis(dev, k, alpha):
+    """P0 = P1 = I: top-k and subtraction act on the momentum itself (padded chunks and vectors included)."""
+    w = DI.WORKLOADS["edge_mix"].replace(name=f"identity_k{k}", k=k, alpha=alpha)
+    Sim(w, identity=True).run(w.steps)
+
+
+@pytest.mark.parametrize("name,k,alpha,rand", [("tiny_256", 8, 0.2, False), ("edge_mix", 4, 0.5, False),
+                                                ("edge_mix", 4096, 1.0, True)])
+def test_aggregated_subtraction(dev, name, k, alpha, rand):
+    """The summary page's reading of the momentum subtraction: every worker removes alpha * M*."""
+    w = DI.WORKLOADS[name].replace(name=f"aggregated_{name}_k{k}", k=k, alpha=alpha, random_basis=rand, workers=3)
+    Sim(w, aggregated=True).run(3)

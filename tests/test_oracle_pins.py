@@ -390,3 +390,50 @@ def test_tiny_and_ragged_shapes_run_and_keep_payload_sorted(shape):
         assert o["idx"].shape == (int(np.prod(O.chunk_grid(shape))), min(k, numel))
         assert np.all(np.diff(o["idx"].astype(np.int64), axis=1) > 0)
         assert o["M"].shape == shape and o["M"].dtype == np.float32
+
+
+def test_identity_basis_ranks_and_subtracts_in_parameter_space():
+    """P0 = P1 = I (the identity choice of the projection): Q is the block itself, the payload is the
+    block's own largest entries, and the residual scales exactly those entries by (1 - alpha)."""
+    rng = _rng(11)
+    G = rng.standard_normal((70, 130)).astype(np.float32)
+    eye = np.eye(64)
+    out = O.encode(np.zeros_like(G), G, beta=0.5, alpha=0.25, k=3, P0=eye, P1=eye)
+    Mp = 0.5 * G.astype(np.float64)
+    chunks = O.split_chunks(Mp)
+    assert np.array_equal(out["Q"], chunks)
+    for c in range(chunks.shape[0]):
+        flat = chunks[c].ravel()
+        want = np.sort(np.argsort(-np.abs(flat).astype(np.float32), kind="stable")[:3])
+        assert np.array_equal(out["idx"][c], want)
+        assert np.array_equal(out["values"][c], flat[want].astype(np.float32))
+    expect = chunks.copy().reshape(chunks.shape[0], -1)
+    rows = np.arange(chunks.shape[0])[:, None]
+    expect[rows, out["idx"].astype(np.int64)] *= 0.75
+    assert np.array_equal(out["M"], O.merge_chunks(expect.reshape(chunks.shape), G.shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("W", [1, 3])
+def test_aggregated_subtraction_lossless_closed_form(W):
+    """k = numel: Q_bar is the mean of the workers' full coefficients, so M* is the mean of the
+    M'_w and the aggregated subtraction leaves M'_w - alpha * mean(M'); with identical workers
+    and alpha = 1 that is exactly zero."""
+    rng = _rng(12)
+    alpha = 0.3
+    Gs = [rng.standard_normal((70, 100)).astype(np.float32) for _ in range(W)]
+    outs = [O.encode(np.zeros_like(g), g, beta=0.9, alpha=alpha, k=4096, subtract="aggregated") for g in Gs]
+    for g, o in zip(Gs, outs):
+        assert np.array_equal(o["M"], (0.1 * g.astype(np.float64)).astype(np.float32))  # M' kept as is
+    dec = O.decode_apply(np.zeros((70, 100), np.float32), np.stack([o["values"] for o in outs]),
+                         np.stack([o["idx"] for o in outs]), phi="identity", eta=1.0, lam=0.0)
+    mean = np.mean([0.1 * g.astype(np.float64) for g in Gs], axis=0)
+    assert np.abs(dec["Mstar"] - mean).max() <= 1e-6 * np.abs(mean).max()
+    for o in outs:
+        new = O.subtract_aggregated(o["M"], dec["Mstar"], alpha)
+        ref = o["M"].astype(np.float64) - alpha * mean
+        assert np.abs(new - ref).max() <= 1e-6 * np.abs(ref).max()
+    same = [O.encode(np.zeros_like(Gs[0]), Gs[0], beta=0.9, alpha=1.0, k=4096, subtract="aggregated")
+            for _ in range(W)]
+    dec = O.decode_apply(np.zeros((70, 100), np.float32), np.stack([o["values"] for o in same]),
+                         np.stack([o["idx"] for o in same]), phi="identity", eta=1.0, lam=0.0)
+    assert np.abs(O.subtract_aggregated(same[0]["M"], dec["Mstar"], 1.0)).max() <= 1e-7 * np.abs(same[0]["M"]).max()
