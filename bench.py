@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmo_1b", choices=sorted(DI.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--basis", default="dct", choices=("dct", "identity"),
+                    help="projection (identity: the ablation that ranks in the parameter domain)")
+    ap.add_argument("--subtraction", default="local", choices=("local", "aggregated"),
+                    help="momentum subtraction of the worker's own coefficients, or of the averaged ones")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one untimed 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -226,7 +230,8 @@ def hbm_probe(w: DI.Workload):
     return out
 
 
-def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False):
+def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False, basis: str = "dct",
+              subtraction: str = "local"):
     import torch
 
     from communication_compressed_optimizer_demo_amd import binding as B
@@ -239,7 +244,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
     W = w.workers
     # the whole list in one call per half, as a training step would pass it
     shapes = [tuple(s) for s in w.shapes]
-    codec = B.Codec(shapes, w.k, w.beta, w.alpha)
+    aggregated = subtraction == "aggregated"
+    codec = B.Codec(shapes, w.k, w.beta, w.alpha, identity=basis == "identity", aggregated=aggregated)
     launches = -(-len(shapes) // B.DEMO_MAX_TENSORS_PER_LAUNCH)
     G = [DI.device_gradient(w, 0, 0, i, dev) for i in range(len(shapes))]
     M = [torch.zeros(s, device=dev) for s in shapes]
@@ -276,7 +282,10 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
         codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream)
         if ev:
             ev[1].record(stream)
-        codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream)
+        if aggregated:  # this worker's parameters and momentum, one pass
+            codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam, stream=stream)
+        else:
+            codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream)
         if ev:
             ev[2].record(stream)
 
@@ -298,7 +307,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
     gbytes = 2 if w.grad_bf16 else 4
     numel = w.n_params
     kern = {}
-    for name, b in (("encode", numel * (gbytes + 8) + ne * 6), ("decode", numel * 8 + W * ne * 6)):
+    dec_bytes = numel * (16 if aggregated else 8) + W * ne * 6  # X (and M) read and written, W payloads
+    for name, b in (("encode", numel * (gbytes + 8) + ne * 6), ("decode", dec_bytes)):
         ms = per[name]
         kern[name] = {"ms": round(ms, 4), "launches": launches, "algorithmic_bytes": int(b),
                       "GBps": round(b / ms / 1e6, 1), "params": numel}
@@ -319,7 +329,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False)
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": _traffic(f"{dom}_kernel", w.name) if launches == 1 else None,
+            "traffic": (_traffic(f"{dom}_kernel", w.name)
+                        if launches == 1 and basis == "dct" and subtraction == "local" else None),
         },
     }
 
@@ -339,7 +350,7 @@ def main():
             print(json.dumps(rec))
         return
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
-    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe)
+    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction)
     line = {
         "metric": METRIC,
         "value": g["value"],
@@ -366,6 +377,8 @@ def main():
             "beta": w.beta,
             "phi": w.phi,
             "grad_dtype": "bf16" if w.grad_bf16 else "fp32",
+            "basis": args.basis,
+            "subtraction": args.subtraction,
         },
         "step_GBps": round(g["step_GBps"], 1),
         "kernels": g["kernels"],

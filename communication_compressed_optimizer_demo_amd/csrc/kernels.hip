@@ -260,6 +260,11 @@ __global__ __launch_bounds__(64) void encode_dense_kernel(LaunchTable tab, Encod
 
 // ---------------------------------------------------------------- decode / apply
 
+// What a decode launch writes: the parameters, a momentum (aggregated
+// subtraction), or both.
+constexpr int kToParams = 1;
+constexpr int kToMomentum = 2;
+
 __device__ __forceinline__ float update(float x, float m, const DecodeParams& p) {
   const float ph = p.phi_sign ? sign_of(m) : m;
   return fmaf(-p.eta, fmaf(p.lam, x, ph), x);
@@ -358,24 +363,30 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
   }
 }
 
-template <class Basis>
+template <class Basis, int kTargets>
 __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
                                               float* acc, uint32_t* cntw) {
   const int lane = threadIdx.x;
   const ChunkPos c = chunk_pos(ts, blockIdx.x);
 
-  // Parameters are fetched first: they land while the payloads are averaged
-  // and inverse-transformed.
+  // The tensors to update are fetched first: they land while the payloads
+  // are averaged and inverse-transformed.
   const int64_t ld = ts.cols;
-  float* __restrict__ xp = p.update_x ? ts.dst + c.base : nullptr;
-  float x[64];
-  if (p.update_x) {
-    if (c.full) {
+  float* __restrict__ xp = ts.dst + c.base;
+  float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
+  float x[64], m[64];
+  if (c.full) {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[i * ld + lane]);
-    } else {
+    for (int i = 0; i < 64; ++i) {
+      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[i * ld + lane]);
+      if constexpr ((kTargets & kToMomentum) != 0) m[i] = stream_load(&mp[i * ld + lane]);
+    }
+  } else {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = (lane < c.vc && i < c.vr) ? stream_load(&xp[i * ld + lane]) : 0.f;
+    for (int i = 0; i < 64; ++i) {
+      const bool in = lane < c.vc && i < c.vr;
+      if constexpr ((kTargets & kToParams) != 0) x[i] = in ? stream_load(&xp[i * ld + lane]) : 0.f;
+      if constexpr ((kTargets & kToMomentum) != 0) m[i] = in ? stream_load(&mp[i * ld + lane]) : 0.f;
     }
   }
 
@@ -391,7 +402,7 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   row_to_col(acc, q, lane);
   basis.inv0(q);
 
-  if (p.update_x) {
+  if constexpr ((kTargets & kToParams) != 0) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
     if (c.full)
@@ -399,19 +410,17 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
     else
       store_rows<false>(x, xp, ld, c, lane);
   }
-  if (p.update_m) {  // aggregated subtraction: M = M - alpha M*
-    float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
+  if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if (c.full || (lane < c.vc && i < c.vr)) {
-        const int64_t off = i * ld + lane;
-        stream_store(fmaf(-p.alpha, q[i], stream_load(&mp[off])), &mp[off]);
-      }
-    }
+    for (int i = 0; i < 64; ++i) m[i] = fmaf(-p.alpha, q[i], m[i]);
+    if (c.full)
+      store_rows<true>(m, mp, ld, c, lane);
+    else
+      store_rows<false>(m, mp, ld, c, lane);
   }
 }
 
-template <class Basis>
+template <class Basis, int kTargets>
 __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
                                               float* acc, uint32_t* cntw) {
   const int lane = threadIdx.x;
@@ -430,14 +439,14 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   basis.inv0(q);
   row_to_col(acc, q, lane);
 
-  if (p.update_x) {
+  if constexpr ((kTargets & kToParams) != 0) {
     float* __restrict__ x = ts.dst + first;
 #pragma unroll
     for (int c = 0; c < 64; ++c) {
       if (c * 64 < rem) stream_store(update(stream_load(&x[c * 64]), q[c], p), &x[c * 64]);
     }
   }
-  if (p.update_m) {  // aggregated subtraction: M = M - alpha M*
+  if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
     float* __restrict__ m = static_cast<float*>(ts.aux) + first;
 #pragma unroll
     for (int c = 0; c < 64; ++c) {
@@ -446,27 +455,45 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   }
 }
 
-template <class Basis>
+template <class Basis, int kTargets>
 __device__ __forceinline__ void decode_item(const LaunchTable& tab, const DecodeParams& p, const Basis& basis,
                                             float* acc, uint32_t* cntw) {
   const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
   if (ts.cols == 0)
-    decode_vector<Basis>(ts, p, basis, acc, cntw);
+    decode_vector<Basis, kTargets>(ts, p, basis, acc, cntw);
   else
-    decode_matrix<Basis>(ts, p, basis, acc, cntw);
+    decode_matrix<Basis, kTargets>(ts, p, basis, acc, cntw);
 }
 
-template <class Basis>
+template <class Basis, int kTargets>
 __global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParams p) {
   __shared__ float acc[64 * kLd];
   __shared__ uint32_t cntw[64 * kCntLd];
-  decode_item<Basis>(tab, p, Basis{}, acc, cntw);
+  decode_item<Basis, kTargets>(tab, p, Basis{}, acc, cntw);
 }
 
+template <int kTargets>
 __global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
   __shared__ float acc[64 * kLd];
   __shared__ uint32_t cntw[64 * kCntLd];
-  decode_item<DenseBasis>(tab, p, basis, acc, cntw);
+  decode_item<DenseBasis, kTargets>(tab, p, basis, acc, cntw);
+}
+
+template <int kTargets>
+void launch_decode_targets(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
+                           const float* basis_p1, hipStream_t stream) {
+  const dim3 grid(tab.items), block(64);
+  switch (kind) {
+    case BasisKind::kDct:
+      decode_kernel<DctBasis, kTargets><<<grid, block, 0, stream>>>(tab, p);
+      break;
+    case BasisKind::kIdentity:
+      decode_kernel<IdentityBasis, kTargets><<<grid, block, 0, stream>>>(tab, p);
+      break;
+    case BasisKind::kUser:
+      decode_dense_kernel<kTargets><<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
+      break;
+  }
 }
 
 }  // namespace
@@ -505,18 +532,12 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
-  const dim3 grid(tab.items), block(64);
-  switch (kind) {
-    case BasisKind::kDct:
-      decode_kernel<DctBasis><<<grid, block, 0, stream>>>(tab, p);
-      break;
-    case BasisKind::kIdentity:
-      decode_kernel<IdentityBasis><<<grid, block, 0, stream>>>(tab, p);
-      break;
-    case BasisKind::kUser:
-      decode_dense_kernel<<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
-      break;
-  }
+  if (p.update_x && p.update_m)
+    launch_decode_targets<kToParams | kToMomentum>(tab, p, kind, basis_p0, basis_p1, stream);
+  else if (p.update_m)
+    launch_decode_targets<kToMomentum>(tab, p, kind, basis_p0, basis_p1, stream);
+  else
+    launch_decode_targets<kToParams>(tab, p, kind, basis_p0, basis_p1, stream);
   return hipGetLastError();
 }
 

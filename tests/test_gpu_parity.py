@@ -247,3 +247,10 @@ def test_aggregated_subtraction(dev, name, k, alpha, rand):
     """The summary page's reading of the momentum subtraction: every worker removes alpha * M*."""
     w = DI.WORKLOADS[name].replace(name=f"aggregated_{name}_k{k}", k=k, alpha=alpha, random_basis=rand, workers=3)
     Sim(w, aggregated=True).run(3)
+
+
+@pytest.mark.parametrize("avg", ["count", "workers"])
+def test_more_workers_than_one_batch(dev, avg):
+    """W = 20 (> 16 payloads per register batch): the decode's general averaging path."""
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"w20_{avg}", shapes=((128, 192), (130,)), workers=20, k=16)
+    Sim(w, avg=avg).run(2)
