@@ -369,30 +369,53 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   const int lane = threadIdx.x;
   const ChunkPos c = chunk_pos(ts, blockIdx.x);
 
-  // The tensors to update are fetched first: they land while the payloads
-  // are averaged and inverse-transformed.
+  // Memory order matters: a wave's loads complete in issue order, so the
+  // payload entries (needed first) are requested before the tensors to
+  // update, which then land while the payloads are averaged and
+  // inverse-transformed.  Both sets of loads are issued without branches
+  // (addresses clamped into the valid range, results of clamped lanes
+  // unused), so no wait separates them.  With both X and M to update the
+  // registers for early payloads would halve occupancy, so that form reads
+  // the payloads after its tensor loads.
+  constexpr bool kEarlyPayload = kTargets != (kToParams | kToMomentum);
+  const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
+  const bool one_batch = kEarlyPayload && p.keff2 <= 64 && p.workers <= kWorkerBatch;
+  float val[kWorkerBatch];
+  uint32_t ix[kWorkerBatch];
+  if (one_batch) {
+    const int64_t e = e0 + min(lane, p.keff2 - 1);
+#pragma unroll
+    for (int j = 0; j < kWorkerBatch; ++j) {
+      const int64_t off = int64_t(min(j, p.workers - 1)) * p.entries + e;
+      val[j] = p.pay_val[off];
+      ix[j] = p.pay_idx[off];
+    }
+  }
   const int64_t ld = ts.cols;
   float* __restrict__ xp = ts.dst + c.base;
   float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
+  const int col = min(lane, c.vc - 1);
   float x[64], m[64];
-  if (c.full) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[i * ld + lane]);
-      if constexpr ((kTargets & kToMomentum) != 0) m[i] = stream_load(&mp[i * ld + lane]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const bool in = lane < c.vc && i < c.vr;
-      if constexpr ((kTargets & kToParams) != 0) x[i] = in ? stream_load(&xp[i * ld + lane]) : 0.f;
-      if constexpr ((kTargets & kToMomentum) != 0) m[i] = in ? stream_load(&mp[i * ld + lane]) : 0.f;
-    }
+  for (int i = 0; i < 64; ++i) {
+    const int64_t off = min(i, c.vr - 1) * ld + col;
+    if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
+    if constexpr ((kTargets & kToMomentum) != 0) m[i] = stream_load(&mp[off]);
   }
 
   clear_acc(acc, cntw, lane);
   __syncthreads();
-  scatter_chunk(acc, cntw, p, ts.entry_begin + int64_t(c.local) * p.keff2, lane);
+  if (one_batch) {
+#pragma unroll
+    for (int j = 0; j < kWorkerBatch; ++j) {
+      if (lane < p.keff2 && j < p.workers) {
+        const uint32_t id = ix[j] & 4095u;
+        accumulate(acc, cntw, id >> 6, id & 63u, val[j]);
+      }
+    }
+  } else {
+    scatter_chunk(acc, cntw, p, e0, lane);
+  }
   __syncthreads();
 
   float q[64];
