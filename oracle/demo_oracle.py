@@ -33,7 +33,9 @@ the design doc with its reason):
   * k larger than a chunk is clamped to the chunk's element count;
   * ties in float32 magnitude go to the lower chunk-local index
     idx = u*s + v (u: dimension-0 frequency, v: dimension-1 frequency);
-  * sign(0) = 0; weight decay uses the pre-update X on every tensor.
+  * sign(0) = 0; weight decay uses the pre-update X on every tensor;
+  * the one-bit download (``pack_signs``) sets a bit where M* < 0, so a
+    zero reads as +1 there.
 
 Pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, SciPy's DCT routines, brute force over all index
@@ -315,6 +317,48 @@ def subtract_aggregated(M: np.ndarray, Mstar: np.ndarray, alpha: float) -> np.nd
     M* from ``decode_apply``.  Returns float32.
     """
     return (np.asarray(M, dtype=F64) - float(alpha) * np.asarray(Mstar, dtype=F64)).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Signum download path: one bit per parameter
+# ---------------------------------------------------------------------------
+
+def sign_words(shapes: Sequence[Sequence[int]], s: int = 64) -> int:
+    """64-bit words of the packed sign of a tensor list: one bit per element of every (padded) chunk."""
+    total = 0
+    for shp in shapes:
+        numel = s if len(shp) == 1 else s * s
+        total += int(np.prod(chunk_grid(shp, s))) * (numel // 64)
+    return total
+
+
+def pack_signs(Mstar: np.ndarray, s: int = 64) -> np.ndarray:
+    """The download of the Signum variant: sign(M*) as one bit per parameter.
+
+    [S] Base Optimizer Update: with phi = sign the server broadcasts only the
+    sign of the reconstructed momentum, one bit per parameter.  Layout (the
+    pages fix none): chunk after chunk in chunk order; inside a chunk the
+    elements in row-major order, 64 to a little-endian uint64 word (bit j of a
+    word is the j-th of its 64 elements).  A bit is set where M* < 0.  One bit
+    cannot carry sign(0) = 0: a zero reads as +1.  Padding positions hold 0.
+    Returns uint64 words.
+    """
+    chunks = split_chunks(np.asarray(Mstar, dtype=F64), s)
+    bits = (chunks < 0.0).reshape(-1, 64)
+    return np.packbits(bits, axis=1, bitorder="little").view("<u8").reshape(-1).astype(np.uint64)
+
+
+def apply_signs(X: np.ndarray, words: np.ndarray, *, eta: float, lam: float, s: int = 64) -> np.ndarray:
+    """Worker side of the download: X <- X - eta * (phi + lambda * X), phi = -1 where
+    the bit is set, else +1 ([S] Base Optimizer Update).  Returns float32."""
+    X = np.asarray(X)
+    grid = chunk_grid(X.shape, s)
+    cshape = (int(np.prod(grid)), s) if X.ndim == 1 else (int(np.prod(grid)), s, s)
+    by = np.ascontiguousarray(np.asarray(words, dtype="<u8")).view(np.uint8).reshape(-1, 8)
+    bits = np.unpackbits(by, axis=1, bitorder="little").reshape(cshape)
+    phi = merge_chunks(np.where(bits != 0, -1.0, 1.0), X.shape, s)
+    X64 = X.astype(F64)
+    return (X64 - float(eta) * (phi + float(lam) * X64)).astype(F32)
 
 
 # ---------------------------------------------------------------------------

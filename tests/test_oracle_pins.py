@@ -437,3 +437,71 @@ def test_aggregated_subtraction_lossless_closed_form(W):
     dec = O.decode_apply(np.zeros((70, 100), np.float32), np.stack([o["values"] for o in same]),
                          np.stack([o["idx"] for o in same]), phi="identity", eta=1.0, lam=0.0)
     assert np.abs(O.subtract_aggregated(same[0]["M"], dec["Mstar"], 1.0)).max() <= 1e-7 * np.abs(same[0]["M"]).max()
+
+
+# --------------------------------------------------------------------------- the one-bit sign download
+
+def test_pack_signs_hand_built_words():
+    """Words written out by hand from the layout: chunk after chunk, row-major inside a chunk,
+    bit j of a word = the j-th of its 64 elements, set where M* < 0, padding 0."""
+    v = np.ones(70)
+    v[[0, 3, 63]] = -1.0
+    v[66] = -3.0
+    v[69] = 0.0  # zero reads as +1: no bit
+    assert O.pack_signs(v).tolist() == [1 + 8 + (1 << 63), 4]
+    m = np.ones((2, 65))
+    m[0, 0] = -1.0    # chunk 0, row 0, column 0
+    m[1, 5] = -1.0    # chunk 0, row 1, column 5
+    m[0, 64] = -2.0   # chunk 1 (columns 64..127), row 0, column 0
+    m[1, 64] = -0.5   # chunk 1, row 1, column 0
+    w = O.pack_signs(m)
+    assert w.shape == (128,) and O.sign_words([(2, 65)]) == 128
+    want = np.zeros(128, np.uint64)
+    want[0], want[1], want[64], want[65] = 1, 1 << 5, 1, 1
+    assert np.array_equal(w, want)
+
+
+@pytest.mark.parametrize("shape", [(130, 70), (64, 64), (3, 200), (777,), (1,)])
+def test_pack_signs_bit_address_formula(shape):
+    """Every element's bit, looked up with the address written out per element: matrix
+    element (r, c) sits in chunk (r // 64) * ceil(cols / 64) + c // 64, word r % 64 of that
+    chunk, bit c % 64; vector element e in word e // 64, bit e % 64.  Padding bits stay 0."""
+    rng = _rng(40)
+    M = rng.standard_normal(shape)
+    w = O.pack_signs(M)
+    assert w.shape == (O.sign_words([shape]),)
+    seen = np.zeros(w.shape[0] * 64, bool)
+    for pos in np.ndindex(*shape):
+        if len(shape) == 2:
+            r, c = pos
+            word = ((r // 64) * -(-shape[1] // 64) + c // 64) * 64 + r % 64
+            bit = c % 64
+        else:
+            word, bit = pos[0] // 64, pos[0] % 64
+        assert bool((int(w[word]) >> bit) & 1) == (M[pos] < 0)
+        seen[word * 64 + bit] = True
+    for word in range(w.shape[0]):
+        for bit in range(64):
+            if not seen[word * 64 + bit]:
+                assert (int(w[word]) >> bit) & 1 == 0
+
+
+def test_apply_signs_closed_forms_and_agreement_with_signum_decode():
+    rng = _rng(41)
+    X = rng.standard_normal((70, 130)).astype(np.float32)
+    X64 = X.astype(np.float64)
+    n = O.sign_words([X.shape])
+    for fill, phi in ((0, 1.0), (~np.uint64(0), -1.0)):
+        got = O.apply_signs(X, np.full(n, fill, np.uint64), eta=0.01, lam=0.1)
+        ref = X64 - 0.01 * (phi + 0.1 * X64)
+        assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
+    # the bit path reproduces the Signum decode wherever M* != 0
+    G = rng.standard_normal(X.shape).astype(np.float32)
+    o = O.encode(np.zeros_like(G), G, beta=0.9, alpha=0.2, k=37)
+    d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="sign", eta=0.01, lam=0.1)
+    assert np.all(d["Mstar"] != 0)
+    got = O.apply_signs(X, O.pack_signs(d["Mstar"]), eta=0.01, lam=0.1)
+    assert np.array_equal(got, d["X"])
+    # zero M* (no coefficient kept anywhere) reads as +1
+    z = O.apply_signs(X, O.pack_signs(np.zeros(X.shape)), eta=0.01, lam=0.0)
+    assert np.all(np.abs(z - (X64 - 0.01)) <= np.spacing(np.abs(X64 - 0.01).astype(np.float32)))
