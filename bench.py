@@ -52,6 +52,9 @@ def parse():
                     help="projection (identity: the ablation that ranks in the parameter domain)")
     ap.add_argument("--subtraction", default="local", choices=("local", "aggregated"),
                     help="momentum subtraction of the worker's own coefficients, or of the averaged ones")
+    ap.add_argument("--download", default="apply", choices=("apply", "signs"),
+                    help="apply: decode/apply in one kernel; signs: the Signum variant's one-bit download, "
+                         "decode to packed sign bits then apply them (phi = sign)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one untimed 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -231,7 +234,7 @@ def hbm_probe(w: DI.Workload):
 
 
 def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False, basis: str = "dct",
-              subtraction: str = "local"):
+              subtraction: str = "local", download: str = "apply"):
     import torch
 
     from communication_compressed_optimizer_demo_amd import binding as B
@@ -275,26 +278,33 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
 
     phi = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
     stream = torch.cuda.current_stream()
+    signs = codec.alloc_signs() if download == "signs" else None
+
+    # the step's calls in order; HIP events between them time each one
+    calls = [("encode", lambda: codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream))]
+    if download == "signs":  # server: packed sign(M*); worker: apply the bits
+        calls.append(("decode", lambda: codec.decode_signs(W, vals, pidx, signs, stream=stream)))
+        calls.append(("apply", lambda: codec.apply_signs(X, signs, w.eta, w.lam, stream=stream)))
+    elif aggregated:  # this worker's parameters and momentum, one pass
+        calls.append(("decode", lambda: codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam,
+                                                                    stream=stream)))
+    else:
+        calls.append(("decode", lambda: codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream)))
 
     def one_step(ev):
+        for j, (_, fn) in enumerate(calls):
+            if ev:
+                ev[j].record(stream)
+            fn()
         if ev:
-            ev[0].record(stream)
-        codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream)
-        if ev:
-            ev[1].record(stream)
-        if aggregated:  # this worker's parameters and momentum, one pass
-            codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam, stream=stream)
-        else:
-            codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream)
-        if ev:
-            ev[2].record(stream)
+            ev[len(calls)].record(stream)
 
     log(f"warmup {warmup} steps")
     for _ in range(warmup):
         one_step(None)
     torch.cuda.synchronize()
     log(f"timing {steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
@@ -302,13 +312,17 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per = {"encode": sum(ev[0].elapsed_time(ev[1]) for ev in events) / steps,
-           "decode": sum(ev[1].elapsed_time(ev[2]) for ev in events) / steps}
+    per = {name: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j, (name, _) in enumerate(calls)}
     gbytes = 2 if w.grad_bf16 else 4
     numel = w.n_params
     kern = {}
-    dec_bytes = numel * (16 if aggregated else 8) + W * ne * 6  # X (and M) read and written, W payloads
-    for name, b in (("encode", numel * (gbytes + 8) + ne * 6), ("decode", dec_bytes)):
+    algo = {"encode": numel * (gbytes + 8) + ne * 6}
+    if download == "signs":
+        algo["decode"] = W * ne * 6 + codec.n_sign_words * 8  # W payloads read, packed signs written
+        algo["apply"] = numel * 8 + codec.n_sign_words * 8    # X read and written, packed signs read
+    else:
+        algo["decode"] = numel * (16 if aggregated else 8) + W * ne * 6  # X (and M) read and written, W payloads
+    for name, b in algo.items():
         ms = per[name]
         kern[name] = {"ms": round(ms, 4), "launches": launches, "algorithmic_bytes": int(b),
                       "GBps": round(b / ms / 1e6, 1), "params": numel}
@@ -330,7 +344,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": (_traffic(f"{dom}_kernel", w.name)
-                        if launches == 1 and basis == "dct" and subtraction == "local" else None),
+                        if launches == 1 and basis == "dct" and subtraction == "local" and download == "apply"
+                        else None),
         },
     }
 
@@ -349,8 +364,13 @@ def main():
         for name, rec in pmc_summary(w, *args.pmc_summary).items():
             print(json.dumps(rec))
         return
+    if args.download == "signs":
+        if args.subtraction != "local":
+            print("--download signs pairs with the local subtraction only", file=sys.stderr)
+            sys.exit(2)
+        w = w.replace(phi="sign")  # the one-bit download exists for the Signum variant only
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
-    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction)
+    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction, args.download)
     line = {
         "metric": METRIC,
         "value": g["value"],
@@ -379,6 +399,7 @@ def main():
             "grad_dtype": "bf16" if w.grad_bf16 else "fp32",
             "basis": args.basis,
             "subtraction": args.subtraction,
+            "download": args.download,
         },
         "step_GBps": round(g["step_GBps"], 1),
         "kernels": g["kernels"],

@@ -79,6 +79,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.demo_decode_apply_subtract.restype = i32
     lib.demo_decode_apply_subtract.argtypes = [vp, i32, P(demo_shape), P(vp), P(vp), P(demo_codec_cfg), i32,
                                                vp, vp, i64, i32, f32, f32, i32, vp]
+    lib.demo_plan_signs.restype = i32
+    lib.demo_plan_signs.argtypes = [P(demo_shape), i32, i32, P(i64), P(i64)]
+    lib.demo_decode_signs.restype = i32
+    lib.demo_decode_signs.argtypes = [vp, i32, P(demo_shape), P(demo_codec_cfg), i32, vp, vp, i64, i32, vp, i64,
+                                      vp]
+    lib.demo_apply_signs.restype = i32
+    lib.demo_apply_signs.argtypes = [vp, i32, P(demo_shape), P(vp), i32, vp, i64, f32, f32, vp]
     _lib = lib
     return lib
 
@@ -249,6 +256,41 @@ def demo_decode_apply_subtract(ctx: int, params, moms, cfg: demo_codec_cfg, work
                                           _stream_handle(stream)))
 
 
+def demo_plan_signs(shapes: Sequence[Sequence[int]], chunk: int = DEMO_CHUNK) -> Tuple[int, List[int]]:
+    """(n_words, word_begin[n+1]) of the packed one-bit sign of a tensor list; host-only."""
+    lib = load_library()
+    n = len(shapes)
+    nw = ctypes.c_int64()
+    wb = (ctypes.c_int64 * (n + 1))()
+    _check(lib.demo_plan_signs(_shapes(shapes), n, chunk, ctypes.byref(nw), wb))
+    return nw.value, list(wb)
+
+
+def demo_decode_signs(ctx: int, shapes: Sequence[Sequence[int]], cfg: demo_codec_cfg, workers: int, pay_values,
+                      pay_idx, signs, avg: int = DEMO_AVG_CONTRIBUTORS, stream=None) -> None:
+    """Average ``workers`` payloads and pack sign(M*) into ``signs`` (64-bit words, int64 storage)."""
+    lib = load_library()
+    if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
+        raise ValueError("payload arrays must hold workers x entries elements")
+    per = pay_values.numel() // workers
+    _check(lib.demo_decode_signs(ctx, len(shapes), _shapes(shapes), ctypes.byref(cfg), int(workers),
+                                 _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per, int(avg),
+                                 _device_ptr(signs, 8), signs.numel(), _stream_handle(stream)))
+
+
+def demo_apply_signs(ctx: int, params, signs, eta: float = 1e-3, lam: float = 0.0, chunk: int = DEMO_CHUNK,
+                     stream=None) -> None:
+    """X <- X - eta * (s + lam * X) with s = -1 where the packed bit is set, else +1."""
+    lib = load_library()
+    import torch
+    for x in params:
+        if x.dtype != torch.float32:
+            raise ValueError("parameters must be float32")
+    _check(lib.demo_apply_signs(ctx, len(params), _shapes([tuple(x.shape) for x in params]),
+                                _ptrs([_device_ptr(x, 4) for x in params]), int(chunk), _device_ptr(signs, 8),
+                                signs.numel(), float(eta), float(lam), _stream_handle(stream)))
+
+
 class Codec:
     """A context bound to one device plus the codec configuration of a tensor list."""
 
@@ -262,6 +304,7 @@ class Codec:
         self.identity = bool(identity)
         self.aggregated = bool(aggregated)
         self.n_chunks, self.n_entries, self.entry_begin = demo_plan(self.shapes, self.k)
+        self.n_sign_words, self.sign_word_begin = demo_plan_signs(self.shapes)
         self.ctx = demo_ctx_create(device)
 
     def close(self) -> None:
@@ -298,3 +341,16 @@ class Codec:
                               lam=0.0, avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
         demo_decode_apply_subtract(self.ctx, params, moms, self.cfg(P0, P1), workers, pay_values, pay_idx, phi,
                                    eta, lam, avg, stream)
+
+    def alloc_signs(self, device="cuda"):
+        """Empty packed-sign buffer: one 64-bit word per 64 elements of every chunk (int64 storage)."""
+        import torch
+        return torch.empty(self.n_sign_words, dtype=torch.int64, device=device)
+
+    def decode_signs(self, workers, pay_values, pay_idx, signs, avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None,
+                     stream=None) -> None:
+        demo_decode_signs(self.ctx, self.shapes, self.cfg(P0, P1), workers, pay_values, pay_idx, signs, avg,
+                          stream)
+
+    def apply_signs(self, params, signs, eta=1e-3, lam=0.0, stream=None) -> None:
+        demo_apply_signs(self.ctx, params, signs, eta, lam, stream=stream)

@@ -39,15 +39,20 @@ struct TensorPlan {
   int32_t keff;         // entries per chunk
   int64_t entry_begin;  // payload offset of the first chunk
   int64_t items;        // work items: chunks (2-D) or 64-chunk slabs (1-D)
+  int64_t word_begin;   // first 64-bit word of the tensor's packed sign
 };
 
+// Packed-sign words per chunk: one per 64 elements of the (padded) chunk.
+constexpr int64_t kWordsPerMatrixChunk = kChunk * kChunk / 64;
+constexpr int64_t kWordsPerVectorChunk = kChunk / 64;
+
 demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_t k, std::vector<TensorPlan>* out,
-                      int64_t* entries, int64_t* chunks) {
+                      int64_t* entries, int64_t* chunks, int64_t* words = nullptr) {
   if (n < 0) return fail(DEMO_ERR_RANGE, "tensor count is negative");
   if (n > 0 && shapes == nullptr) return fail(DEMO_ERR_INVALID, "shapes is NULL");
   if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "chunk size must be 64");
   if (k < 1) return fail(DEMO_ERR_RANGE, "k must be >= 1");
-  int64_t e = 0, c = 0;
+  int64_t e = 0, c = 0, w = 0;
   if (out) out->clear();
   for (int32_t i = 0; i < n; ++i) {
     const demo_shape& s = shapes[i];
@@ -75,12 +80,15 @@ demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_
     }
     if (t.items > INT32_MAX) return fail(DEMO_ERR_SHAPE, "tensor " + std::to_string(i) + ": too many chunks");
     t.entry_begin = e;
+    t.word_begin = w;
     e += t.chunks * t.keff;
     c += t.chunks;
+    w += t.chunks * (t.ndim == 2 ? kWordsPerMatrixChunk : kWordsPerVectorChunk);
     if (out) out->push_back(t);
   }
   if (entries) *entries = e;
   if (chunks) *chunks = c;
+  if (words) *words = w;
   return DEMO_OK;
 }
 
@@ -154,16 +162,25 @@ demo_status for_each_batch(const std::vector<TensorPlan>& plan, Fill&& fill, Lau
 }
 
 // Shared body of the decode entry points: params and/or moms (either may be
-// NULL) receive X - eta (phi(M*) + lambda X) and M - alpha M*.
+// NULL) receive X - eta (phi(M*) + lambda X) and M - alpha M*; or, with
+// `signs` given (params and moms NULL), sign(M*) is packed into n_words words.
 demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                           float* const* moms, const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
                           const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
-                          demo_average avg, hipStream_t stream) {
+                          demo_average avg, hipStream_t stream, uint64_t* signs = nullptr, int64_t n_words = 0) {
   if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
   std::vector<TensorPlan> plan;
-  int64_t entries = 0;
-  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr);
+  int64_t entries = 0, words = 0;
+  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr, &words);
   if (s != DEMO_OK) return s;
+  const bool to_signs = params == nullptr && moms == nullptr;
+  if (to_signs) {
+    if (n_words != words)
+      return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +
+                                        std::to_string(words));
+    if (words > 0 && signs == nullptr) return fail(DEMO_ERR_INVALID, "sign buffer is NULL");
+    if (!aligned(signs, 8)) return fail(DEMO_ERR_ALIGN, "sign buffer misaligned");
+  }
   if (workers < 1 || workers > demo::kMaxWorkers) return fail(DEMO_ERR_RANGE, "workers must be in 1..255");
   if (phi != DEMO_PHI_SIGN && phi != DEMO_PHI_IDENTITY) return fail(DEMO_ERR_INVALID, "unknown phi");
   if (avg != DEMO_AVG_CONTRIBUTORS && avg != DEMO_AVG_WORKERS) return fail(DEMO_ERR_INVALID, "unknown average");
@@ -198,9 +215,11 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   p.avg_workers = avg == DEMO_AVG_WORKERS ? 1 : 0;
   p.update_x = params != nullptr ? 1 : 0;
   p.update_m = moms != nullptr ? 1 : 0;
+  p.pack_signs = to_signs ? 1 : 0;
   p.alpha = cfg->alpha;
   auto fill = [&](demo::TensorSlot& slot, size_t i) {
-    slot.aux = moms != nullptr ? moms[i] : nullptr;
+    slot.aux = moms != nullptr ? static_cast<void*>(moms[i])
+                               : (to_signs ? static_cast<void*>(signs + plan[i].word_begin) : nullptr);
     slot.dst = params != nullptr ? params[i] : nullptr;
   };
   p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
@@ -315,6 +334,54 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
   if (params == nullptr && moms == nullptr) return fail(DEMO_ERR_INVALID, "neither parameters nor momenta given");
   return decode_common(ctx, n, shapes, params, moms, cfg, workers, pay_values, pay_idx, n_entries, phi, eta, lambda,
                        avg, stream);
+}
+
+demo_status demo_plan_signs(const demo_shape* shapes, int32_t n, int32_t chunk, int64_t* n_words,
+                            int64_t* word_begin) {
+  std::vector<TensorPlan> plan;
+  int64_t w = 0;
+  const demo_status s = plan_list(shapes, n, chunk, 1, &plan, nullptr, nullptr, &w);
+  if (s != DEMO_OK) return s;
+  if (n_words) *n_words = w;
+  if (word_begin) {
+    for (int32_t i = 0; i < n; ++i) word_begin[i] = plan[i].word_begin;
+    word_begin[n] = w;
+  }
+  return DEMO_OK;
+}
+
+demo_status demo_decode_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes, const demo_codec_cfg* cfg,
+                              int32_t workers, const float* pay_values, const uint16_t* pay_idx, int64_t n_entries,
+                              demo_average avg, uint64_t* signs, int64_t n_words, hipStream_t stream) {
+  return decode_common(ctx, n, shapes, nullptr, nullptr, cfg, workers, pay_values, pay_idx, n_entries,
+                       DEMO_PHI_SIGN, 0.0f, 0.0f, avg, stream, signs, n_words);
+}
+
+demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                             int32_t chunk, const uint64_t* signs, int64_t n_words, float eta, float lambda,
+                             hipStream_t stream) {
+  std::vector<TensorPlan> plan;
+  int64_t words = 0;
+  demo_status s = plan_list(shapes, n, chunk, 1, &plan, nullptr, nullptr, &words);
+  if (s != DEMO_OK) return s;
+  if (!std::isfinite(eta) || !std::isfinite(lambda)) return fail(DEMO_ERR_INVALID, "eta/lambda not finite");
+  if (n_words != words)
+    return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +
+                                      std::to_string(words));
+  if (words > 0 && signs == nullptr) return fail(DEMO_ERR_INVALID, "sign buffer is NULL");
+  if (!aligned(signs, 8)) return fail(DEMO_ERR_ALIGN, "sign buffer misaligned");
+  if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    if (params[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
+    if (!aligned(params[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
+  }
+  if ((s = check_device(ctx)) != DEMO_OK) return s;
+  const demo::ApplyParams p{eta, lambda};
+  auto fill = [&](demo::TensorSlot& slot, size_t i) {
+    slot.aux = const_cast<uint64_t*>(signs) + plan[i].word_begin;  // read only in the kernel
+    slot.dst = params[i];
+  };
+  return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_apply_signs(t, p, stream); });
 }
 
 }  // extern "C"

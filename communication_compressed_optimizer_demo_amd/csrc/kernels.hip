@@ -261,9 +261,12 @@ __global__ __launch_bounds__(64) void encode_dense_kernel(LaunchTable tab, Encod
 // ---------------------------------------------------------------- decode / apply
 
 // What a decode launch writes: the parameters, a momentum (aggregated
-// subtraction), or both.
+// subtraction), both, or the packed sign of M* (one-bit download).
 constexpr int kToParams = 1;
 constexpr int kToMomentum = 2;
+constexpr int kToSigns = 4;
+
+__device__ __forceinline__ void stream_store(uint64_t v, uint64_t* p) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ float update(float x, float m, const DecodeParams& p) {
   const float ph = p.phi_sign ? sign_of(m) : m;
@@ -441,6 +444,17 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
     else
       store_rows<false>(m, mp, ld, c, lane);
   }
+  if constexpr ((kTargets & kToSigns) != 0) {
+    // Row i of the chunk is one ballot (bit j = lane j = column j); lane i
+    // keeps it, and the 64 words go out as one coalesced 512-byte store.
+    uint64_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const uint64_t b = __ballot(lane < c.vc && q[i] < 0.f);
+      word = (lane == i && i < c.vr) ? b : word;
+    }
+    stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(c.local) * 64 + lane);
+  }
 }
 
 template <class Basis, int kTargets>
@@ -475,6 +489,15 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
     for (int c = 0; c < 64; ++c) {
       if (c * 64 < rem) stream_store(fmaf(-p.alpha, q[c], stream_load(&m[c * 64])), &m[c * 64]);
     }
+  }
+  if constexpr ((kTargets & kToSigns) != 0) {  // one word per vector chunk: chunk c's ballot goes to lane c
+    uint64_t word = 0;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      const uint64_t b = __ballot(c * 64 < rem && q[c] < 0.f);
+      word = lane == c ? b : word;
+    }
+    if (lane < nc) stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(slab) * 64 + lane);
   }
 }
 
@@ -519,6 +542,51 @@ void launch_decode_targets(const LaunchTable& tab, const DecodeParams& p, BasisK
   }
 }
 
+// ---------------------------------------------------------------- one-bit sign apply
+
+// X = X - eta (s + lambda X), s = -1 where the element's bit is set, else +1.
+__device__ __forceinline__ float apply_bit(float x, uint64_t word, int bit, const ApplyParams& p) {
+  const float s = ((word >> bit) & 1u) ? -1.f : 1.f;
+  return fmaf(-p.eta, fmaf(p.lam, x, s), x);
+}
+
+// Same work items as the decode: a 64x64 chunk (word i = row i, bit j =
+// column j = lane j) or a slab of 64 vector chunks (word c = chunk c, bit j =
+// element j = lane j).  The word index is wave-uniform, so the words arrive
+// through scalar loads while the rows stream through vector loads.
+__global__ __launch_bounds__(64) void apply_signs_kernel(LaunchTable tab, ApplyParams p) {
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const int lane = threadIdx.x;
+  const uint64_t* __restrict__ words = static_cast<const uint64_t*>(ts.aux);
+  if (ts.cols == 0) {
+    const int slab = blockIdx.x - ts.item_begin;
+    const int64_t first = int64_t(slab) * 64 * 64 + lane;
+    const int64_t rem = int64_t(ts.rows) - first;
+    const int nc = min(64, int((uint32_t(ts.rows) + 63u) >> 6) - slab * 64);
+    const uint64_t* __restrict__ wp = words + int64_t(slab) * 64;
+    float* __restrict__ x = ts.dst + first;
+    for (int c = 0; c < nc; ++c) {
+      const uint64_t w = wp[c];
+      if (c * 64 < rem) stream_store(apply_bit(stream_load(&x[c * 64]), w, lane, p), &x[c * 64]);
+    }
+    return;
+  }
+  const ChunkPos c = chunk_pos(ts, blockIdx.x);
+  const uint64_t* __restrict__ wp = words + int64_t(c.local) * 64;
+  float* __restrict__ xp = ts.dst + c.base;
+  const int64_t ld = ts.cols;
+  const int col = min(lane, c.vc - 1);
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[min(i, c.vr - 1) * ld + col]);
+#pragma unroll
+  for (int i = 0; i < 64; ++i) x[i] = apply_bit(x[i], wp[i], lane, p);
+  if (c.full)
+    store_rows<true>(x, xp, ld, c, lane);
+  else
+    store_rows<false>(x, xp, ld, c, lane);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- host-side launchers
@@ -555,12 +623,20 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
-  if (p.update_x && p.update_m)
+  if (p.pack_signs)
+    launch_decode_targets<kToSigns>(tab, p, kind, basis_p0, basis_p1, stream);
+  else if (p.update_x && p.update_m)
     launch_decode_targets<kToParams | kToMomentum>(tab, p, kind, basis_p0, basis_p1, stream);
   else if (p.update_m)
     launch_decode_targets<kToMomentum>(tab, p, kind, basis_p0, basis_p1, stream);
   else
     launch_decode_targets<kToParams>(tab, p, kind, basis_p0, basis_p1, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream) {
+  if (tab.items <= 0) return hipSuccess;
+  apply_signs_kernel<<<dim3(tab.items), dim3(64), 0, stream>>>(tab, p);
   return hipGetLastError();
 }
 

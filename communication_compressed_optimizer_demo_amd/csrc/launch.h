@@ -19,8 +19,9 @@ constexpr int kMaxTensorsPerLaunch = 96;
 constexpr int kMaxWorkers = 255;  // counts are kept in 8 bits
 
 struct TensorSlot {
-  void* aux;            // encode: gradient (fp32 or bf16, read only); decode: momentum (in/out) or null
-  float* dst;           // encode: momentum (in/out); decode: parameters (in/out) or null
+  void* aux;            // encode: gradient (fp32 or bf16, read only); decode: momentum (in/out), the
+                        // tensor's packed sign words (out), or null; sign apply: sign words (in)
+  float* dst;           // encode: momentum (in/out); decode, sign apply: parameters (in/out) or null
   int64_t entry_begin;  // payload entry of the tensor's first chunk
   int32_t rows;         // 2-D: dim 0; 1-D: length
   int32_t cols;         // 2-D: dim 1 (>= 1); 1-D: 0, which marks a vector
@@ -62,7 +63,13 @@ struct DecodeParams {
   int32_t avg_workers;  // 1: divide by W, 0: by contributor count
   int32_t update_x;     // 1: X = X - eta (phi(M*) + lambda X)
   int32_t update_m;     // 1: M = M - alpha M* (aggregated subtraction)
+  int32_t pack_signs;   // 1: write sign(M*) as bits (no parameter or momentum update)
   float alpha;
+};
+
+struct ApplyParams {
+  float eta;
+  float lam;
 };
 
 enum class BasisKind { kDct, kUser, kIdentity };
@@ -73,5 +80,6 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
                          const float* basis_p0, const float* basis_p1, hipStream_t stream);
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream);
+hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream);
 
 }  // namespace demo

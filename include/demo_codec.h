@@ -11,6 +11,9 @@
  *                      subtraction.
  *   demo_decode_apply  after communication: sparse averaging of W payloads,
  *                      inverse DCT, phi, parameter update.
+ *   demo_decode_signs / demo_apply_signs
+ *                      the same decode split once more for the Signum
+ *                      variant's one-bit download (server side / worker side).
  *
  * Conventions for every call:
  *   - Tensors are dense, row-major, contiguous device buffers.  Matrices
@@ -176,6 +179,38 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
                                        float* const* moms, const demo_codec_cfg* cfg, int32_t workers,
                                        const float* pay_values, const uint16_t* pay_idx, int64_t n_entries,
                                        demo_phi phi, float eta, float lambda, demo_average avg, hipStream_t stream);
+
+/* ---- One-bit download of the Signum variant (DeMo summary §3.4 Base Optimizer
+ * Update: with phi = sign the server broadcasts only sign(M*), one bit per
+ * parameter, and every worker applies it to its own copy of X).
+ * Packed-sign layout: uint64 words, chunk after chunk in the chunk order of the
+ * payload.  A 64x64 chunk takes 64 words (word i = chunk row i, bit j = column
+ * j), a 64-element vector chunk one word (bit j = element j).  A bit is set
+ * where M* < 0; M* = 0 reads as +1, since one bit cannot carry sign(0) = 0.
+ * Padding positions hold 0. */
+
+/* Host-only: words of the packed sign of a list (n_words, may be NULL) and, if
+ * word_begin is not NULL, the first word of every tensor (n+1 entries, the
+ * total at [n]). */
+demo_status demo_plan_signs(const demo_shape* shapes, int32_t n, int32_t chunk, int64_t* n_words,
+                            int64_t* word_begin);
+
+/* Server side: the sparse average of W payloads, inverse transform and
+ * unchunking of demo_decode_apply, then sign(M*) packed as above.
+ *   signs: device, n_words uint64 words (8-byte aligned); every word is written
+ * cfg supplies chunk, k and the basis; the other fields are unused. */
+demo_status demo_decode_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes, const demo_codec_cfg* cfg,
+                              int32_t workers, const float* pay_values, const uint16_t* pay_idx, int64_t n_entries,
+                              demo_average avg, uint64_t* signs, int64_t n_words, hipStream_t stream);
+
+/* Worker side: X <- X - eta * (s + lambda * X) with the pre-update X, s = -1
+ * where the tensor's bit is set and +1 elsewhere.
+ *   params[i]: device float32, shapes[i]; read and overwritten
+ *   signs:     device, n_words words laid out as demo_decode_signs writes them;
+ *              read only */
+demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                             int32_t chunk, const uint64_t* signs, int64_t n_words, float eta, float lambda,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

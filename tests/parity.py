@@ -202,3 +202,31 @@ def compare_momentum(ref_M: np.ndarray, gpu_M: np.ndarray, shape, chunk_diverged
         i = np.argmax(np.where(bad, diff, 0))
         raise AssertionError(f"{where}: momentum differs at flat {i}: gpu {gpu_M.ravel()[i]!r} "
                              f"ref {ref.ravel()[i]!r} ({int(bad.sum())} elements)")
+
+
+def _bits(words: np.ndarray, n_chunks: int) -> np.ndarray:
+    by = np.ascontiguousarray(np.asarray(words).astype("<u8")).view(np.uint8).reshape(-1, 8)
+    return np.unpackbits(by, axis=1, bitorder="little").reshape(n_chunks, -1).astype(bool)
+
+
+def compare_signs(Mstar: np.ndarray, shape, gpu_words: np.ndarray, chunk_diverged: np.ndarray, where: str = ""):
+    """Check one tensor's packed sign words against the oracle's packing of its M*.
+
+    Bit-exact on every valid element except where |M*| is within RTOL of its
+    chunk's largest |M*| (float rounding may flip such a sign, as for Signum)
+    and in chunks whose top-k legitimately diverged; padding bits must be 0."""
+    n = chunk_diverged.shape[0]
+    ref = _bits(O.pack_signs(Mstar), n)
+    got = _bits(gpu_words, n)
+    valid = O.split_chunks(np.ones(shape)).reshape(n, -1) != 0
+    pad = got & ~valid
+    assert not pad.any(), f"{where}: {int(pad.sum())} padding bits set"
+    a = O.split_chunks(np.abs(Mstar)).reshape(n, -1)
+    near0 = a <= RTOL * a.max(axis=1, keepdims=True)
+    live = valid & ~near0 & ~chunk_diverged[:, None]
+    bad = (got != ref) & live
+    if bad.any():
+        c, e = np.argwhere(bad)[0]
+        raise AssertionError(f"{where}: sign bit differs in chunk {c} element {e} "
+                             f"({int(bad.sum())} bits; M* there {O.split_chunks(Mstar).reshape(n, -1)[c, e]!r})")
+    return int(((got != ref) & valid).sum())

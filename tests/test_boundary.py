@@ -204,3 +204,74 @@ def test_ctx_create_without_gpu_fails_cleanly(lib):
         pytest.skip("a GPU is present")
     with pytest.raises(B.DemoError):
         B.demo_ctx_create(0)
+
+
+# --------------------------------------------------------------------------- one-bit sign download
+
+@pytest.mark.parametrize("name", sorted(DI.WORKLOADS))
+def test_plan_signs_matches_oracle_word_count(lib, name):
+    import numpy as np
+    w = DI.WORKLOADS[name]
+    n_words, begin = B.demo_plan_signs(w.shapes)
+    assert n_words == O.sign_words(w.shapes)
+    acc = 0
+    for i, s in enumerate(w.shapes):
+        assert begin[i] == acc
+        acc += O.sign_words([s])
+    assert begin[len(w.shapes)] == acc == n_words
+    if name == "olmo_1b":
+        assert n_words * 64 == w.n_params  # no padding in the OLMo shapes: exactly one bit per parameter
+        assert np.isclose(n_words * 8 / (4 * w.n_params), 1 / 32)
+
+
+def _call_decode_signs(lib, shapes, k=8, workers=2, avg=0, vals=0x3000, idx=0x4000, signs=0x5000, words=None,
+                       entries=None, chunk=64):
+    cfg = B.demo_codec_cfg(chunk, k, 0.9, 0.2, 0, 0, None, None, 0)
+    n = len(shapes)
+    if words is None:
+        words = O.sign_words(shapes)
+    if entries is None:
+        entries = O.payload_entries(shapes, k)
+    return lib.demo_decode_signs(None, n, B._shapes(shapes), ctypes.byref(cfg), workers, vals, idx, entries, avg,
+                                 signs, words, None)
+
+
+def _call_apply_signs(lib, shapes, params=0x1000, signs=0x5000, words=None, eta=1e-3, lam=0.0, chunk=64,
+                      null_list=False):
+    n = len(shapes)
+    if words is None:
+        words = O.sign_words(shapes)
+    pl = None if null_list else B._ptrs([params] * n)
+    return lib.demo_apply_signs(None, n, B._shapes(shapes), pl, chunk, signs, words, eta, lam, None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(), 1, "context"),
+    (dict(words=3), 4, "sign buffer"),
+    (dict(signs=0), 1, "sign buffer is NULL"),
+    (dict(signs=0x5004), 7, "misaligned"),
+    (dict(entries=2), 4, "payload"),
+    (dict(workers=0), 3, "workers"),
+    (dict(avg=5), 1, "average"),
+    (dict(chunk=128), 3, "chunk"),
+    (dict(vals=0), 1, "payload is NULL"),
+])
+def test_decode_signs_arguments(lib, kw, status, text):
+    assert _call_decode_signs(lib, [(128, 64), (100,)], **kw) == status
+    assert text in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(), 1, "context"),
+    (dict(words=129), 4, "sign buffer"),
+    (dict(signs=0), 1, "sign buffer is NULL"),
+    (dict(signs=0x5002), 7, "misaligned"),
+    (dict(params=0), 1, "NULL device pointer"),
+    (dict(params=0x1002), 7, "misaligned"),
+    (dict(null_list=True), 1, "pointer list"),
+    (dict(eta=float("nan")), 1, "eta"),
+    (dict(chunk=32), 3, "chunk"),
+])
+def test_apply_signs_arguments(lib, kw, status, text):
+    assert _call_apply_signs(lib, [(128, 64), (100,)], **kw) == status
+    assert text in _msg(lib)

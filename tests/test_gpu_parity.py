@@ -32,8 +32,11 @@ def dev():
 class Sim:
     """W workers of one workload, GPU next to the oracle."""
 
-    def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None, identity=False, aggregated=False):
+    def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None, identity=False, aggregated=False,
+                 signs=False):
         self.w = w
+        self.signs = signs  # one-bit download: decode_signs, then apply_signs (phi = sign)
+        assert not (signs and (aggregated or w.phi != "sign"))
         self.plain = plain
         self.identity = identity
         self.aggregated = aggregated
@@ -52,6 +55,7 @@ class Sim:
         self.X_gpu = [torch.from_numpy(x.copy()).cuda() for x in X0]
         self.X_or = [x.copy() for x in X0]
         self.vals, self.idx = self.codec.alloc_payload(W)
+        self.sign_words = self.codec.alloc_signs() if signs else None
         self.cdiv = [[np.zeros(n, dtype=bool) for n, _, _ in self.lay] for _ in range(W)]
         self.ediv = [None for _ in self.shapes]
         self.report = PR.EncodeReport()
@@ -112,6 +116,12 @@ class Sim:
             for wk in range(1, W):
                 self.codec.decode_apply_subtract(None, self.M_gpu[wk], W, self.vals, self.idx, phi_c, w.eta, w.lam,
                                                  avg_c, P0d, P1d)
+        elif self.signs:
+            self.sign_words.fill_(-1)  # every word must be rewritten, padding bits included
+            self.codec.decode_signs(W, self.vals, self.idx, self.sign_words, avg_c, P0d, P1d)
+            torch.cuda.synchronize()
+            words = self.sign_words.cpu().numpy().view(np.uint64)
+            self.codec.apply_signs(self.X_gpu, self.sign_words, w.eta, w.lam)
         else:
             self.codec.decode_apply(self.X_gpu, W, self.vals, self.idx, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
         torch.cuda.synchronize()
@@ -121,6 +131,12 @@ class Sim:
             cd = np.zeros_like(self.cdiv[0][i])
             for wk in range(W):
                 cd |= self.cdiv[wk][i]
+            if self.signs:
+                wb = self.codec.sign_word_begin
+                PR.compare_signs(dec["Mstar"], shp, words[wb[i]:wb[i + 1]], cd,
+                                 where=f"{w.name} step {t} tensor {i} {shp} (signs)")
+                dec = {"X": O.apply_signs(self.X_or[i], O.pack_signs(dec["Mstar"]), eta=w.eta, lam=w.lam),
+                       "Mstar": dec["Mstar"]}
             self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
                                              where=f"{w.name} step {t} tensor {i} {shp}")
             self.X_or[i] = dec["X"]
@@ -254,3 +270,47 @@ def test_more_workers_than_one_batch(dev, avg):
     """W = 20 (> 16 payloads per register batch): the decode's general averaging path."""
     w = DI.WORKLOADS["tiny_256"].replace(name=f"w20_{avg}", shapes=((128, 192), (130,)), workers=20, k=16)
     Sim(w, avg=avg).run(2)
+
+
+@pytest.mark.parametrize("name,k,avg,rand", [("tiny_256", 8, "count", False), ("edge_mix", 4, "workers", False),
+                                              ("edge_mix", 37, "count", True)])
+def test_one_bit_sign_download(dev, name, k, avg, rand):
+    """Server packs sign(M*) into bits, workers apply them: bits against the oracle's packing,
+    parameters against the oracle's apply (padded chunks, vectors and a random basis included)."""
+    w = DI.WORKLOADS[name].replace(name=f"signs_{name}_k{k}", k=k, random_basis=rand, workers=3, phi="sign")
+    Sim(w, avg=avg, signs=True).run(3)
+
+
+def test_one_bit_sign_download_ragged_and_zero(dev):
+    """Tiny and ragged shapes plus an all-zero tensor (M* = 0 reads as +1 on both sides)."""
+    w = DI.WORKLOADS["tiny_256"].replace(
+        name="signs_ragged", shapes=((1, 1), (2, 3), (65, 65), (64, 64), (1,), (63,), (130,)), k=5, workers=2)
+
+    def inputs(worker, step, i):
+        if i == 3:
+            return np.zeros((64, 64), np.float32)
+        return DI.gradient(w, worker, step, i)
+
+    Sim(w, inputs=inputs, signs=True).run(2)
+
+
+def test_sign_download_matches_signum_decode(dev):
+    """apply_signs(decode_signs(payloads)) equals decode_apply with phi = sign wherever M* != 0."""
+    w = DI.WORKLOADS["tiny_256"].replace(name="signs_vs_signum", shapes=((192, 256), (300,)), workers=3, k=12)
+    codec = B.Codec(w.shapes, w.k, w.beta, w.alpha)
+    v, ix = codec.alloc_payload(w.workers)
+    ne = codec.n_entries
+    for wk in range(w.workers):
+        g = [torch.from_numpy(DI.gradient(w, wk, 0, i)).cuda() for i in range(len(w.shapes))]
+        codec.encode(g, [torch.zeros(s, device="cuda") for s in w.shapes], v[wk * ne:(wk + 1) * ne],
+                     ix[wk * ne:(wk + 1) * ne])
+    X0 = [torch.from_numpy(DI.initial_params(w, i)).cuda() for i in range(len(w.shapes))]
+    Xa = [x.clone() for x in X0]
+    Xb = [x.clone() for x in X0]
+    codec.decode_apply(Xa, w.workers, v, ix, B.DEMO_PHI_SIGN, w.eta, w.lam)
+    words = codec.alloc_signs()
+    codec.decode_signs(w.workers, v, ix, words)
+    codec.apply_signs(Xb, words, w.eta, w.lam)
+    torch.cuda.synchronize()
+    for a, b in zip(Xa, Xb):
+        assert torch.equal(a, b)
