@@ -273,10 +273,17 @@ __device__ __forceinline__ float update(float x, float m, const DecodeParams& p)
   return fmaf(-p.eta, fmaf(p.lam, x, ph), x);
 }
 
-// Zero the accumulator tile and the count rows.
-__device__ __forceinline__ void clear_acc(float* acc, uint32_t* cntw, int lane) {
-  for (int i = lane; i < 64 * kLd; i += 64) acc[i] = 0.f;
-  for (int i = lane; i < 64 * kCntLd; i += 64) cntw[i] = 0u;
+// The decode's LDS: the 64 x kLd fp32 accumulator, then 64 x kCntLd words of
+// 8-bit counts, rounded up so that 64 lanes x 16 bytes clear it in whole
+// instructions.
+constexpr int kDecodeLdsWords = ((64 * kLd + 64 * kCntLd) + 255) / 256 * 256;
+
+// Zero the accumulator tile and the count rows: unguarded 16-byte stores.
+__device__ __forceinline__ void clear_acc(uint32_t* lds, int lane) {
+  uint4* l4 = reinterpret_cast<uint4*>(lds);
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int i = 0; i < kDecodeLdsWords / 256; ++i) l4[i * 64 + lane] = z;
 }
 
 // Add one payload entry (value v at coefficient (u, col)) to the accumulator.
@@ -386,27 +393,28 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   float val[kWorkerBatch];
   uint32_t ix[kWorkerBatch];
   if (one_batch) {
-    const int64_t e = e0 + min(lane, p.keff2 - 1);
+    // wave-uniform worker pointers plus a 32-bit lane index
+    const uint32_t e = uint32_t(min(lane, p.keff2 - 1));
 #pragma unroll
     for (int j = 0; j < kWorkerBatch; ++j) {
-      const int64_t off = int64_t(min(j, p.workers - 1)) * p.entries + e;
-      val[j] = p.pay_val[off];
-      ix[j] = p.pay_idx[off];
+      const int64_t w0 = int64_t(min(j, p.workers - 1)) * p.entries + e0;
+      val[j] = (p.pay_val + w0)[e];
+      ix[j] = (p.pay_idx + w0)[e];
     }
   }
   const int64_t ld = ts.cols;
   float* __restrict__ xp = ts.dst + c.base;
   float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
-  const int col = min(lane, c.vc - 1);
+  const uint32_t col = uint32_t(min(lane, c.vc - 1));
   float x[64], m[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    const int64_t off = min(i, c.vr - 1) * ld + col;
-    if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
-    if constexpr ((kTargets & kToMomentum) != 0) m[i] = stream_load(&mp[off]);
+    const int64_t row = int64_t(min(i, c.vr - 1)) * ld;
+    if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&(xp + row)[col]);
+    if constexpr ((kTargets & kToMomentum) != 0) m[i] = stream_load(&(mp + row)[col]);
   }
 
-  clear_acc(acc, cntw, lane);
+  clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
   __syncthreads();
   if (one_batch) {
 #pragma unroll
@@ -445,12 +453,13 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
       store_rows<false>(m, mp, ld, c, lane);
   }
   if constexpr ((kTargets & kToSigns) != 0) {
-    // Row i of the chunk is one ballot (bit j = lane j = column j); lane i
-    // keeps it, and the 64 words go out as one coalesced 512-byte store.
+    // Row i of the chunk is one ballot (bit j = lane j = column j), kept by
+    // lane i; the 64 words go out as one coalesced 512-byte store.
+    const uint64_t cols = __builtin_amdgcn_ballot_w64(lane < c.vc);
     uint64_t word = 0;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
-      const uint64_t b = __ballot(lane < c.vc && q[i] < 0.f);
+      const uint64_t b = __builtin_amdgcn_ballot_w64(q[i] < 0.f) & cols;
       word = (lane == i && i < c.vr) ? b : word;
     }
     stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(c.local) * 64 + lane);
@@ -466,7 +475,7 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   const int64_t rem = int64_t(ts.rows) - first;          // elements c * 64 < rem exist
   const int nc = min(64, int((uint32_t(ts.rows) + 63u) >> 6) - slab * 64);  // chunks in this slab
 
-  clear_acc(acc, cntw, lane);
+  clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
   __syncthreads();
   scatter_slab(acc, cntw, p, ts.entry_begin + int64_t(slab) * 64 * p.keff1, nc, lane);
   __syncthreads();
@@ -494,7 +503,7 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
     uint64_t word = 0;
 #pragma unroll
     for (int c = 0; c < 64; ++c) {
-      const uint64_t b = __ballot(c * 64 < rem && q[c] < 0.f);
+      const uint64_t b = __builtin_amdgcn_ballot_w64(c * 64 < rem && q[c] < 0.f);
       word = lane == c ? b : word;
     }
     if (lane < nc) stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(slab) * 64 + lane);
@@ -513,16 +522,14 @@ __device__ __forceinline__ void decode_item(const LaunchTable& tab, const Decode
 
 template <class Basis, int kTargets>
 __global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParams p) {
-  __shared__ float acc[64 * kLd];
-  __shared__ uint32_t cntw[64 * kCntLd];
-  decode_item<Basis, kTargets>(tab, p, Basis{}, acc, cntw);
+  __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
+  decode_item<Basis, kTargets>(tab, p, Basis{}, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }
 
 template <int kTargets>
 __global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
-  __shared__ float acc[64 * kLd];
-  __shared__ uint32_t cntw[64 * kCntLd];
-  decode_item<DenseBasis, kTargets>(tab, p, basis, acc, cntw);
+  __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
+  decode_item<DenseBasis, kTargets>(tab, p, basis, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }
 
 template <int kTargets>
