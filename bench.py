@@ -52,6 +52,8 @@ def parse():
                     help="projection (identity: the ablation that ranks in the parameter domain)")
     ap.add_argument("--subtraction", default="local", choices=("local", "aggregated"),
                     help="momentum subtraction of the worker's own coefficients, or of the averaged ones")
+    ap.add_argument("--chunk", type=int, default=64, choices=(64, 128),
+                    help="chunk edge s (128: DCT basis, apply download)")
     ap.add_argument("--download", default="apply", choices=("apply", "signs"),
                     help="apply: decode/apply in one kernel; signs: the Signum variant's one-bit download, "
                          "decode to packed sign bits then apply them (phi = sign)")
@@ -234,7 +236,7 @@ def hbm_probe(w: DI.Workload):
 
 
 def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False, basis: str = "dct",
-              subtraction: str = "local", download: str = "apply"):
+              subtraction: str = "local", download: str = "apply", chunk: int = 64):
     import torch
 
     from communication_compressed_optimizer_demo_amd import binding as B
@@ -248,7 +250,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     # the whole list in one call per half, as a training step would pass it
     shapes = [tuple(s) for s in w.shapes]
     aggregated = subtraction == "aggregated"
-    codec = B.Codec(shapes, w.k, w.beta, w.alpha, identity=basis == "identity", aggregated=aggregated)
+    codec = B.Codec(shapes, w.k, w.beta, w.alpha, identity=basis == "identity", aggregated=aggregated, chunk=chunk)
     launches = -(-len(shapes) // B.DEMO_MAX_TENSORS_PER_LAUNCH)
     G = [DI.device_gradient(w, 0, 0, i, dev) for i in range(len(shapes))]
     M = [torch.zeros(s, device=dev) for s in shapes]
@@ -345,7 +347,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": (_traffic(f"{dom}_kernel", w.name)
                         if launches == 1 and basis == "dct" and subtraction == "local" and download == "apply"
-                        else None),
+                        and chunk == 64 else None),
         },
     }
 
@@ -364,13 +366,17 @@ def main():
         for name, rec in pmc_summary(w, *args.pmc_summary).items():
             print(json.dumps(rec))
         return
+    if args.chunk == 128 and (args.basis != "dct" or args.download != "apply"):
+        print("--chunk 128 is built for the DCT basis and the apply download", file=sys.stderr)
+        sys.exit(2)
     if args.download == "signs":
         if args.subtraction != "local":
             print("--download signs pairs with the local subtraction only", file=sys.stderr)
             sys.exit(2)
         w = w.replace(phi="sign")  # the one-bit download exists for the Signum variant only
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
-    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction, args.download)
+    g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction, args.download,
+                  args.chunk)
     line = {
         "metric": METRIC,
         "value": g["value"],
@@ -390,7 +396,7 @@ def main():
             "workload": w.name,
             "tensors": len(w.shapes),
             "params": w.n_params,
-            "chunk": 64,
+            "chunk": args.chunk,
             "k": w.k,
             "workers": w.workers,
             "alpha": w.alpha,

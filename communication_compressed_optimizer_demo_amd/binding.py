@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdemo_codec.so")
 
 DEMO_CHUNK = 64
+DEMO_CHUNK_LARGE = 128  # the other chunk edge built (DCT basis, no one-bit download)
 DEMO_MAX_WORKERS = 255
 DEMO_MAX_TENSORS_PER_LAUNCH = 96  # one kernel launch per this many tensors of a call
 
@@ -295,16 +296,21 @@ class Codec:
     """A context bound to one device plus the codec configuration of a tensor list."""
 
     def __init__(self, shapes: Sequence[Sequence[int]], k: int, beta: float = 0.999, alpha: float = 0.2,
-                 plain: bool = False, device: int = 0, identity: bool = False, aggregated: bool = False):
+                 plain: bool = False, device: int = 0, identity: bool = False, aggregated: bool = False,
+                 chunk: int = DEMO_CHUNK):
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.chunk = int(chunk)
         self.k = int(k)
         self.beta = float(beta)
         self.alpha = float(alpha)
         self.plain = bool(plain)
         self.identity = bool(identity)
         self.aggregated = bool(aggregated)
-        self.n_chunks, self.n_entries, self.entry_begin = demo_plan(self.shapes, self.k)
-        self.n_sign_words, self.sign_word_begin = demo_plan_signs(self.shapes)
+        self.n_chunks, self.n_entries, self.entry_begin = demo_plan(self.shapes, self.k, self.chunk)
+        if self.chunk == DEMO_CHUNK:
+            self.n_sign_words, self.sign_word_begin = demo_plan_signs(self.shapes)
+        else:
+            self.n_sign_words, self.sign_word_begin = 0, None
         self.ctx = demo_ctx_create(device)
 
     def close(self) -> None:
@@ -319,8 +325,8 @@ class Codec:
             pass
 
     def cfg(self, P0=None, P1=None) -> demo_codec_cfg:
-        return make_cfg(self.k, self.beta, self.alpha, self.plain, P0, P1, identity=self.identity,
-                        aggregated=self.aggregated)
+        return make_cfg(self.k, self.beta, self.alpha, self.plain, P0, P1, chunk=self.chunk,
+                        identity=self.identity, aggregated=self.aggregated)
 
     def alloc_payload(self, workers: int = 1, device="cuda"):
         """Empty payload buffers: float32 values and 16-bit indices (int16 storage of uint16)."""

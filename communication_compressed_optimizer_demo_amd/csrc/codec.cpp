@@ -20,6 +20,7 @@ struct demo_ctx {
 namespace {
 
 using demo::kChunk;
+using demo::kChunkLarge;
 using demo::kMaxTensorsPerLaunch;
 static_assert(kMaxTensorsPerLaunch == DEMO_MAX_TENSORS_PER_LAUNCH, "header and launch table disagree");
 static_assert(demo::kMaxWorkers == DEMO_MAX_WORKERS, "header and kernels disagree");
@@ -42,15 +43,19 @@ struct TensorPlan {
   int64_t word_begin;   // first 64-bit word of the tensor's packed sign
 };
 
-// Packed-sign words per chunk: one per 64 elements of the (padded) chunk.
+// Packed-sign words per chunk (chunk edge 64): one per 64 elements of the (padded) chunk.
 constexpr int64_t kWordsPerMatrixChunk = kChunk * kChunk / 64;
 constexpr int64_t kWordsPerVectorChunk = kChunk / 64;
+
+// Vector chunks per work item: 64 (one wave, one chunk per lane) at chunk
+// edge 64, 128 (four waves, one chunk per lane pair) at chunk edge 128.
+int64_t vector_chunks_per_item(int32_t chunk) { return chunk == kChunk ? 64 : 128; }
 
 demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_t k, std::vector<TensorPlan>* out,
                       int64_t* entries, int64_t* chunks, int64_t* words = nullptr) {
   if (n < 0) return fail(DEMO_ERR_RANGE, "tensor count is negative");
   if (n > 0 && shapes == nullptr) return fail(DEMO_ERR_INVALID, "shapes is NULL");
-  if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "chunk size must be 64");
+  if (chunk != kChunk && chunk != kChunkLarge) return fail(DEMO_ERR_RANGE, "chunk size must be 64 or 128");
   if (k < 1) return fail(DEMO_ERR_RANGE, "k must be >= 1");
   int64_t e = 0, c = 0, w = 0;
   if (out) out->clear();
@@ -67,16 +72,17 @@ demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_
     if (s.ndim == 2) {
       t.rows = s.dims[0];
       t.cols = s.dims[1];
-      const int64_t g0 = (t.rows + kChunk - 1) / kChunk, g1 = (t.cols + kChunk - 1) / kChunk;
+      const int64_t g0 = (t.rows + chunk - 1) / chunk, g1 = (t.cols + chunk - 1) / chunk;
       t.chunks = g0 * g1;
-      t.keff = k < kChunk * kChunk ? k : kChunk * kChunk;
+      t.keff = k < chunk * chunk ? k : chunk * chunk;
       t.items = t.chunks;
     } else {
       t.rows = s.dims[0];
       t.cols = 1;
-      t.chunks = (t.rows + kChunk - 1) / kChunk;
-      t.keff = k < kChunk ? k : kChunk;
-      t.items = (t.chunks + kChunk - 1) / kChunk;
+      t.chunks = (t.rows + chunk - 1) / chunk;
+      t.keff = k < chunk ? k : chunk;
+      const int64_t per = vector_chunks_per_item(chunk);
+      t.items = (t.chunks + per - 1) / per;
     }
     if (t.items > INT32_MAX) return fail(DEMO_ERR_SHAPE, "tensor " + std::to_string(i) + ": too many chunks");
     t.entry_begin = e;
@@ -174,6 +180,7 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr, &words);
   if (s != DEMO_OK) return s;
   const bool to_signs = params == nullptr && moms == nullptr;
+  if (to_signs && cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
   if (to_signs) {
     if (n_words != words)
       return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +
@@ -201,6 +208,8 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   const float *p0, *p1;
   demo::BasisKind kind;
   if ((s = check_basis(cfg, plan, &kind, &p0, &p1)) != DEMO_OK) return s;
+  if (cfg->chunk == kChunkLarge && kind != demo::BasisKind::kDct)
+    return fail(DEMO_ERR_RANGE, "chunk 128 is built for the DCT basis");
   if ((s = check_device(ctx)) != DEMO_OK) return s;
 
   demo::DecodeParams p{};
@@ -222,8 +231,11 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
                                : (to_signs ? static_cast<void*>(signs + plan[i].word_begin) : nullptr);
     slot.dst = params != nullptr ? params[i] : nullptr;
   };
-  p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
-  p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
+  const int32_t S = cfg->chunk;
+  p.keff2 = cfg->k < S * S ? cfg->k : S * S;
+  p.keff1 = cfg->k < S ? cfg->k : S;
+  if (S == kChunkLarge)
+    return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_decode128(t, p, stream); });
   return for_each_batch(plan, fill,
                         [&](const LaunchTable& t) { return demo::launch_decode(t, p, kind, p0, p1, stream); });
 }
@@ -298,6 +310,8 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
   const float *p0, *p1;
   demo::BasisKind kind;
   if ((s = check_basis(cfg, plan, &kind, &p0, &p1)) != DEMO_OK) return s;
+  if (cfg->chunk == kChunkLarge && kind != demo::BasisKind::kDct)
+    return fail(DEMO_ERR_RANGE, "chunk 128 is built for the DCT basis");
   if ((s = check_device(ctx)) != DEMO_OK) return s;
 
   demo::EncodeParams p{};
@@ -312,8 +326,12 @@ demo_status demo_encode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, cons
     slot.aux = const_cast<void*>(grads[i]);  // read only in the kernels
     slot.dst = moms[i];
   };
-  p.keff2 = cfg->k < kChunk * kChunk ? cfg->k : kChunk * kChunk;
-  p.keff1 = cfg->k < kChunk ? cfg->k : kChunk;
+  const int32_t S = cfg->chunk;
+  p.keff2 = cfg->k < S * S ? cfg->k : S * S;
+  p.keff1 = cfg->k < S ? cfg->k : S;
+  if (S == kChunkLarge)
+    return for_each_batch(plan, fill,
+                          [&](const LaunchTable& t) { return demo::launch_encode128(t, p, bf16, stream); });
   return for_each_batch(plan, fill,
                         [&](const LaunchTable& t) { return demo::launch_encode(t, p, bf16, kind, p0, p1, stream); });
 }
@@ -338,6 +356,7 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
 
 demo_status demo_plan_signs(const demo_shape* shapes, int32_t n, int32_t chunk, int64_t* n_words,
                             int64_t* word_begin) {
+  if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
   std::vector<TensorPlan> plan;
   int64_t w = 0;
   const demo_status s = plan_list(shapes, n, chunk, 1, &plan, nullptr, nullptr, &w);
@@ -364,6 +383,7 @@ demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes,
   int64_t words = 0;
   demo_status s = plan_list(shapes, n, chunk, 1, &plan, nullptr, nullptr, &words);
   if (s != DEMO_OK) return s;
+  if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
   if (!std::isfinite(eta) || !std::isfinite(lambda)) return fail(DEMO_ERR_INVALID, "eta/lambda not finite");
   if (n_words != words)
     return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +

@@ -31,6 +31,7 @@
 //   (indices are distinct within one payload, so the lanes of one
 //   instruction never collide and the sum order is fixed); average;
 //   M* = P0^T Q_bar P1; X = X - eta (phi(M*) + lambda X).
+#include "common.h"
 #include "launch.h"
 #include "topk.h"
 #include "xform.h"
@@ -46,38 +47,6 @@ constexpr int kLd = 65;     // LDS tile row stride in floats
 constexpr int kCntLd = 17;  // count rows: 16 words of 8-bit counts + 1 pad word
 constexpr int kWorkerBatch = 16;
 
-// ---------------------------------------------------------------- helpers
-
-__device__ __forceinline__ int find_tensor(const LaunchTable& tab, int item) {
-  int lo = 0, hi = tab.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tab.t[mid].item_begin <= item)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
-template <class T>
-__device__ __forceinline__ T stream_load(const T* p) {
-  return __builtin_nontemporal_load(p);
-}
-
-__device__ __forceinline__ void stream_store(float v, float* p) { __builtin_nontemporal_store(v, p); }
-
-template <bool kBf16>
-__device__ __forceinline__ float load_src(const void* p, int64_t off) {
-  if constexpr (kBf16) {
-    const uint32_t b = stream_load(static_cast<const uint16_t*>(p) + off);
-    return __uint_as_float(b << 16);
-  } else {
-    return stream_load(static_cast<const float*>(p) + off);
-  }
-}
-
-__device__ __forceinline__ float sign_of(float m) { return m > 0.f ? 1.f : (m < 0.f ? -1.f : 0.f); }
 
 // column layout -> row layout through the LDS tile
 __device__ __forceinline__ void col_to_row(float* tile, float (&x)[64], int lane) {
@@ -259,19 +228,6 @@ __global__ __launch_bounds__(64) void encode_dense_kernel(LaunchTable tab, Encod
 }
 
 // ---------------------------------------------------------------- decode / apply
-
-// What a decode launch writes: the parameters, a momentum (aggregated
-// subtraction), both, or the packed sign of M* (one-bit download).
-constexpr int kToParams = 1;
-constexpr int kToMomentum = 2;
-constexpr int kToSigns = 4;
-
-__device__ __forceinline__ void stream_store(uint64_t v, uint64_t* p) { __builtin_nontemporal_store(v, p); }
-
-__device__ __forceinline__ float update(float x, float m, const DecodeParams& p) {
-  const float ph = p.phi_sign ? sign_of(m) : m;
-  return fmaf(-p.eta, fmaf(p.lam, x, ph), x);
-}
 
 // The decode's LDS: the 64 x kLd fp32 accumulator, then 64 x kCntLd words of
 // 8-bit counts, rounded up so that 64 lanes x 16 bytes clear it in whole

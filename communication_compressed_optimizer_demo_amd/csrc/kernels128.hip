@@ -1,0 +1,871 @@
+// HIP kernels of the DeMo codec for chunk edge s = 128 on CDNA4 (gfx950).
+//
+// The pages run DeMo with 64x64 and with 128x128 chunks ("DeMo: Decoupled
+// Momentum Optimization", summary §3.4 Tensor Chunking; extended results,
+// chunk size s = 64 vs s = 128).  The method is the same as for s = 64 (see
+// kernels.hip); only the transform length and the chunk size change.
+//
+// Transform.  The orthonormal 128-point DCT-II splits into two 64-point
+// halves: the even frequencies 2m are a 64-point DCT-II of the sums
+// x[n] + x[127-n], the odd frequencies 2m+1 a 64-point DCT-IV of the
+// differences x[n] - x[127-n], both scaled by sqrt(2/128).  On both
+// dimensions of a 128x128 block this makes four independent 64x64
+// transforms: sub-block (a, b) holds the coefficients Q[2u+a][2v+b] and is
+// the (C_a x C_b) transform (C_0 = DCT-II, C_1 = DCT-IV) of
+//   S_ab[i][j] = sum over quadrants (qa, qb) of (-1)^(a qa + b qb) B_q[i][j],
+// where B_q[i][j] is chunk element (qa ? 127-i : i, qb ? 127-j : j).  The
+// inverse applies the transposed halves and the same sign combination (the
+// factor 1/2 of the butterfly's inverse is inside the sqrt(2/128) scaling).
+//
+// Work split.  A 256-thread workgroup (four wave64) owns one 128x128 chunk.
+// Wave q loads quadrant q already in those (i, j) coordinates (row and lane
+// order reversed in the second halves; each row segment is still one
+// contiguous 256-byte access), the waves exchange quadrants through LDS to
+// form S_ab (wave w = 2a + b takes sub-block (a, b)), and each wave then runs
+// its 64x64 sub-block exactly like a 64x64 chunk: column pass in registers,
+// LDS transpose, row pass.  Top-k is workgroup-wide over the 16384
+// coefficients of the chunk; decode scatters the W payloads into a 128x128
+// LDS accumulator (one wave, in worker order, so sums are deterministic).
+//
+// A vector is cut into 128-element chunks; a workgroup item is 128 chunks,
+// 32 per wave.  A lane pair holds one chunk (lane 2g + h: half h of chunk g),
+// the halves are exchanged between the two lanes with DPP, and lane h runs
+// the 64-point half transform h.
+#include "common.h"
+#include "launch.h"
+#include "xform.h"
+
+namespace demo {
+namespace {
+
+using xf::Ortho;
+using xf::Unit;
+
+constexpr int kS = 128;
+constexpr int kLd = 65;             // per-wave transpose tile row stride (floats)
+constexpr int kTile = 64 * kLd;     // floats of one wave's transpose tile
+constexpr int kQuad = 64 * 64;      // floats of one quadrant in the butterfly exchange
+constexpr int kWorkerBatch = 16;
+constexpr int kMaxCand = 256;       // top-k candidates held in LDS
+constexpr int kVecChunksPerWave = 32;
+constexpr int kVecChunksPerItem = 4 * kVecChunksPerWave;
+
+// encode LDS: four transpose tiles (the butterfly exchange reuses them), then
+// the top-k scratch
+constexpr int kTilesWords = 4 * kTile;
+constexpr int kScrWords = 256 + 8 + 8 + 512 + 2 * kMaxCand;
+constexpr int kEncLdsWords = kTilesWords + kScrWords;
+// decode LDS: 128 x 128 fp32 accumulator + 128 x 32 words of 8-bit counts;
+// the tiles, the butterfly exchange and the vector path reuse it
+constexpr int kAccWords = kS * kS;
+constexpr int kDecLdsWords = kAccWords + kS * kS / 4;
+static_assert(kTilesWords <= kDecLdsWords && 4 * kQuad <= kTilesWords, "LDS regions");
+static_assert(kDecLdsWords * 4 <= 81920, "two decode workgroups per CU");
+static_assert((kEncLdsWords * 4) * 2 <= 160 * 1024, "two encode workgroups per CU");
+
+// ---------------------------------------------------------------- halves of the 128-point DCT
+
+// h = 0: even frequencies from the sums; h = 1: odd frequencies from the differences.
+__device__ __forceinline__ void fwd_half(float (&x)[64], int h) {
+  if (h == 0)
+    xf::dct2<64, Ortho<128>>(x);
+  else
+    xf::dct4<64, Unit, Ortho<128>>(x);
+}
+
+__device__ __forceinline__ void inv_half(float (&x)[64], int h) {
+  if (h == 0)
+    xf::dct3<64, Ortho<128>>(x);
+  else
+    xf::dct4<64, Ortho<128>, Unit>(x);
+}
+
+// ---------------------------------------------------------------- wave / workgroup helpers
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int ballot_count(bool p) { return __popcll(__builtin_amdgcn_ballot_w64(p)); }
+
+// Sum over the four waves of one wave-uniform value.  `buf` holds two sets of
+// four words used alternately (`parity`), so one barrier per call suffices: a
+// wave can only overwrite a set after every wave has passed the next call's
+// barrier, i.e. after all of them have read it.
+__device__ __forceinline__ int wg_sum(int v, uint32_t* buf, int& parity, int w, int lane) {
+  uint32_t* b = buf + parity * 4;
+  if (lane == 0) b[w] = uint32_t(v);
+  __syncthreads();
+  parity ^= 1;
+  return int(b[0] + b[1] + b[2] + b[3]);
+}
+
+// value of the other lane of this lane's pair (lanes 2g and 2g+1)
+__device__ __forceinline__ float pair_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ int pair_swap(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint64_t pair_swap(uint64_t v) {
+  return (uint64_t(uint32_t(pair_swap(int(v >> 32)))) << 32) | uint32_t(pair_swap(int(uint32_t(v))));
+}
+
+__device__ __forceinline__ int popc64(uint64_t v) { return __popcll(v); }
+
+// bits below position n (n in 0..64)
+__device__ __forceinline__ uint64_t below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
+
+// per-wave LDS transposes (every wave of the workgroup calls them together)
+__device__ __forceinline__ void col_to_row(float* tile, float (&x)[64], int lane) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) tile[i * kLd + lane] = x[i];
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 64; ++v) x[v] = tile[lane * kLd + v];
+  __syncthreads();
+}
+
+__device__ __forceinline__ void row_to_col(float* tile, float (&x)[64], int lane) {
+#pragma unroll
+  for (int v = 0; v < 64; ++v) tile[lane * kLd + v] = x[v];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 64; ++i) x[i] = tile[i * kLd + lane];
+  __syncthreads();
+}
+
+// x <- sum over the four waves' x (same i, same lane) with sign (-1)^(a qa + b qb),
+// (a, b) the bits of this wave, (qa, qb) those of the other.  Forward: quadrants ->
+// S_ab; inverse: S'_ab -> quadrants.  Leaves the exchange area free.
+__device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) xq[w * kQuad + i * 64 + lane] = x[i];
+  __syncthreads();
+  const int a = w >> 1, b = w & 1;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float t = xq[q * kQuad + i * 64 + lane];
+      s = (((a & (q >> 1)) ^ (b & q)) & 1) ? s - t : s + t;
+    }
+    x[i] = s;
+  }
+  __syncthreads();
+}
+
+struct Chunk128 {
+  int local;     // chunk ordinal within its tensor
+  int vr, vc;    // valid rows / columns
+  int64_t base;  // element offset of the chunk's (0, 0)
+  bool full;
+};
+
+__device__ __forceinline__ Chunk128 chunk_pos128(const TensorSlot& ts, int item) {
+  Chunk128 c;
+  c.local = item - ts.item_begin;
+  const int grid1 = int((uint32_t(ts.cols) + 127u) >> 7);
+  const int cr = c.local / grid1;
+  const int cc = c.local - cr * grid1;
+  c.vr = min(kS, ts.rows - cr * kS);
+  c.vc = min(kS, ts.cols - cc * kS);
+  c.base = int64_t(cr) * kS * ts.cols + int64_t(cc) * kS;
+  c.full = (c.vr == kS) && (c.vc == kS);
+  return c;
+}
+
+// quadrant coordinates -> chunk coordinates
+__device__ __forceinline__ int quad_row(int qa, int i) { return qa ? (kS - 1 - i) : i; }
+
+// ---------------------------------------------------------------- top-k over a 128x128 chunk
+
+// Wave w = 2a + b holds sub-block (a, b) in row layout: lane u, q[v] =
+// Q[2u+a][2v+b], chunk-local index (2u+a)*128 + 2v + b.  Keeps the keff
+// largest magnitudes (float32; equal magnitudes: lower index first), writes
+// them in index order and scales them by (1 - alpha) in place.
+//   Fast path (keff <= 64): T0 = keff-th largest of the 256 lane maxima (so at
+//   least keff coefficients are >= T0); the coefficients >= T0 go to LDS; wave 0
+//   finds the threshold K and the tie cut over them.  Otherwise (or with more
+//   than kMaxCand candidates) the same bitwise searches run over all 16384.
+//   Either way: kept = |q| > K, or |q| == K with index <= the tie cut.
+__device__ __forceinline__ void topk128(float (&q)[64], int keff, int w, int lane, float alpha,
+                                        float* __restrict__ outv, uint16_t* __restrict__ outi, uint32_t* scr) {
+  const int a = w >> 1, b = w & 1;
+  const uint32_t idx0 = uint32_t((2 * lane + a) * kS + b);  // index of q[0]; q[v] sits at idx0 + 2v
+  uint32_t* rmax = scr;
+  uint32_t* red = scr + 256;
+  uint32_t* bc = scr + 264;
+  uint32_t* kmask = scr + 272;
+  uint32_t* cmag = scr + 784;
+  uint32_t* cid = cmag + kMaxCand;
+
+  if (keff >= kS * kS) {  // lossless: every coefficient, at its own index
+#pragma unroll
+    for (int v = 0; v < 64; ++v) {
+      const uint32_t id = idx0 + 2 * v;
+      outv[id] = q[v];
+      outi[id] = static_cast<uint16_t>(id);
+      q[v] = fmaf(-alpha, q[v], q[v]);
+    }
+    return;
+  }
+
+  float lm = 0.f;
+#pragma unroll
+  for (int v = 0; v < 64; ++v) lm = fmaxf(lm, fabsf(q[v]));
+  uint32_t K = 0, cut = 0xffffffffu;  // cut: largest index admitted among |q| == K
+  int parity = 0;
+  bool fast = keff <= 64;
+  if (fast) {
+    rmax[w * 64 + lane] = __float_as_uint(lm);
+    __syncthreads();
+    uint32_t mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx[r] = rmax[r * 64 + lane];
+    uint32_t T0 = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t c = T0 | (1u << bit);
+      const int n = ballot_count(mx[0] >= c) + ballot_count(mx[1] >= c) + ballot_count(mx[2] >= c) +
+                    ballot_count(mx[3] >= c);
+      if (n >= keff) T0 = c;
+    }
+    int cnt = 0;
+    if (T0 != 0) {
+      const float t0 = __uint_as_float(T0);
+#pragma unroll
+      for (int v = 0; v < 64; ++v) cnt += fabsf(q[v]) >= t0 ? 1 : 0;
+    }
+    const int incl = wave_incl_scan(cnt, lane);
+    if (lane == 63) red[w] = uint32_t(incl);
+    __syncthreads();
+    int total = 0, base = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = int(red[r]);
+      total += t;
+      base += r < w ? t : 0;
+    }
+    fast = T0 != 0 && total <= kMaxCand;  // the same for every wave
+    if (fast) {
+      const float t0 = __uint_as_float(T0);
+      int pos = base + incl - cnt;
+#pragma unroll
+      for (int v = 0; v < 64; ++v) {
+        if (fabsf(q[v]) >= t0) {
+          const uint32_t bits = __float_as_uint(q[v]);
+          cmag[pos] = bits & 0x7fffffffu;
+          cid[pos] = idx0 + 2 * v;
+          ++pos;
+        }
+      }
+      __syncthreads();
+      if (w == 0) {
+        uint32_t m[4], id[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = r * 64 + lane;
+          const bool live = s < total;
+          m[r] = live ? cmag[s] : 0u;  // empty slots: 0 < T0 <= K, never counted
+          id[r] = live ? cid[s] : 0xffffffffu;
+        }
+        for (int bit = 30; bit >= 0; --bit) {
+          const uint32_t c = K | (1u << bit);
+          const int n = ballot_count(m[0] >= c) + ballot_count(m[1] >= c) + ballot_count(m[2] >= c) +
+                        ballot_count(m[3] >= c);
+          if (n >= keff) K = c;
+        }
+        const int gt = ballot_count(m[0] > K) + ballot_count(m[1] > K) + ballot_count(m[2] > K) +
+                       ballot_count(m[3] > K);
+        const int eq = ballot_count(m[0] == K) + ballot_count(m[1] == K) + ballot_count(m[2] == K) +
+                       ballot_count(m[3] == K);
+        const int quota = keff - gt;
+        if (eq > quota) {  // the quota-th smallest index among the ties
+          uint32_t L = 0;
+          for (int bit = 13; bit >= 0; --bit) {
+            const uint32_t c = L | (1u << bit);
+            const int n = ballot_count(m[0] == K && id[0] < c) + ballot_count(m[1] == K && id[1] < c) +
+                          ballot_count(m[2] == K && id[2] < c) + ballot_count(m[3] == K && id[3] < c);
+            if (n < quota) L = c;
+          }
+          cut = L;
+        }
+        if (lane == 0) {
+          bc[0] = K;
+          bc[1] = cut;
+        }
+      }
+      __syncthreads();
+      K = bc[0];
+      cut = bc[1];
+    }
+  }
+  if (!fast) {
+    // bitwise searches over all 16384 magnitudes, counted across the workgroup
+    float hmax = lm;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+    if (lane == 0) rmax[w] = __float_as_uint(hmax);
+    __syncthreads();
+    const uint32_t hi = max(max(rmax[0], rmax[1]), max(rmax[2], rmax[3]));
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      if (c > hi) continue;  // the same for every wave
+      const float cf = __uint_as_float(c);
+      int n = 0;
+#pragma unroll
+      for (int v = 0; v < 64; ++v) n += fabsf(q[v]) >= cf ? 1 : 0;
+      if (wg_sum(wave_sum(n), red, parity, w, lane) >= keff) T = c;
+    }
+    K = T;
+    const float kf = __uint_as_float(K);
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int v = 0; v < 64; ++v) {
+      gt += fabsf(q[v]) > kf ? 1 : 0;
+      eq += fabsf(q[v]) == kf ? 1 : 0;
+    }
+    const int quota = keff - wg_sum(wave_sum(gt), red, parity, w, lane);
+    if (wg_sum(wave_sum(eq), red, parity, w, lane) > quota) {
+      uint32_t L = 0;
+      for (int bit = 13; bit >= 0; --bit) {
+        const uint32_t c = L | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int v = 0; v < 64; ++v) n += (fabsf(q[v]) == kf && idx0 + 2 * v < c) ? 1 : 0;
+        if (wg_sum(wave_sum(n), red, parity, w, lane) < quota) L = c;
+      }
+      cut = L;
+    }
+  }
+
+  // kept masks; the payload position of a kept coefficient is the number of
+  // kept coefficients of smaller index: rows before its row (rows 2u and
+  // 2u+1 belong to lane u of waves 0,1 and 2,3), plus, in its row, its own
+  // wave's kept entries of smaller v and its partner wave's (other b) ones
+  // of smaller column.
+  const float kf = __uint_as_float(K);
+  uint64_t mine = 0;
+#pragma unroll
+  for (int v = 0; v < 64; ++v) {
+    const float m = fabsf(q[v]);
+    const bool keep = m > kf || (m == kf && idx0 + 2 * v <= cut);
+    mine |= keep ? (1ull << v) : 0ull;
+  }
+  kmask[(w * 64 + lane) * 2] = uint32_t(mine);
+  kmask[(w * 64 + lane) * 2 + 1] = uint32_t(mine >> 32);
+  __syncthreads();
+  uint64_t mk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    mk[r] = (uint64_t(kmask[(r * 64 + lane) * 2 + 1]) << 32) | kmask[(r * 64 + lane) * 2];
+  const int c0 = popc64(mk[0]) + popc64(mk[1]);  // row 2u
+  const int c1 = popc64(mk[2]) + popc64(mk[3]);  // row 2u + 1
+  const int tot = c0 + c1;
+  const int rbase = wave_incl_scan(tot, lane) - tot + (a ? c0 : 0);
+  const uint64_t partner = mk[w ^ 1];
+#pragma unroll
+  for (int v = 0; v < 64; ++v) {
+    if ((mine >> v) & 1ull) {
+      const int pos = rbase + popc64(mine & below(v)) + popc64(partner & below(v + b));
+      outv[pos] = q[v];
+      outi[pos] = static_cast<uint16_t>(idx0 + 2 * v);
+      q[v] = fmaf(-alpha, q[v], q[v]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k over a 128-element vector chunk
+
+// The chunk is held by a lane pair: lane h has y[m] = coefficient 2m + h.
+// Same rule as above over the pair; `write` is false for lanes past the
+// tensor's last chunk.
+__device__ __forceinline__ void topk_pair(float (&y)[64], int keff, int h, bool write, float alpha,
+                                          float* __restrict__ outv, uint16_t* __restrict__ outi) {
+  float lm = 0.f;
+#pragma unroll
+  for (int m = 0; m < 64; ++m) lm = fmaxf(lm, fabsf(y[m]));
+  const uint32_t hi = max(__float_as_uint(lm), __float_as_uint(pair_swap(lm)));
+  uint32_t T = 0;
+#pragma unroll 1
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    const float cf = __uint_as_float(c);
+    int n = 0;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) n += fabsf(y[m]) >= cf ? 1 : 0;
+    n += pair_swap(n);
+    if (c <= hi && n >= keff) T = c;
+  }
+  const float kf = __uint_as_float(T);
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    gt += fabsf(y[m]) > kf ? 1 : 0;
+    eq += fabsf(y[m]) == kf ? 1 : 0;
+  }
+  gt += pair_swap(gt);
+  eq += pair_swap(eq);
+  const int quota = keff - gt;
+  uint32_t cut = 0xffffffffu;
+  if (eq > quota) {
+    uint32_t L = 0;
+#pragma unroll 1
+    for (int bit = 6; bit >= 0; --bit) {
+      const uint32_t c = L | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int m = 0; m < 64; ++m) n += (fabsf(y[m]) == kf && uint32_t(2 * m + h) < c) ? 1 : 0;
+      n += pair_swap(n);
+      if (n < quota) L = c;
+    }
+    cut = L;
+  }
+  uint64_t mine = 0;
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    const float v = fabsf(y[m]);
+    const bool keep = v > kf || (v == kf && uint32_t(2 * m + h) <= cut);
+    mine |= keep ? (1ull << m) : 0ull;
+  }
+  const uint64_t partner = pair_swap(mine);
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    if ((mine >> m) & 1ull) {
+      if (write) {
+        const int pos = popc64(mine & below(m)) + popc64(partner & below(m + h));
+        outv[pos] = y[m];
+        outi[pos] = static_cast<uint16_t>(2 * m + h);
+      }
+      y[m] = fmaf(-alpha, y[m], y[m]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- encode
+
+template <bool kFull, bool kBf16>
+__device__ __forceinline__ void load_quadrant(float (&x)[64], const TensorSlot& ts, const Chunk128& c, int q,
+                                              int lane, float beta, float gcoef) {
+  const int64_t ld = ts.cols;
+  const int col = (q & 1) ? kS - 1 - lane : lane;
+  const float* __restrict__ m = ts.dst + c.base;
+  const char* __restrict__ g = static_cast<const char*>(ts.aux) + c.base * (kBf16 ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int row = quad_row(q >> 1, i);
+    float gv = 0.f, mv = 0.f;
+    if (kFull || (row < c.vr && col < c.vc)) {
+      gv = load_src<kBf16>(g, row * ld + col);
+      mv = stream_load(&m[row * ld + col]);
+    }
+    x[i] = fmaf(beta, mv, gcoef * gv);
+  }
+}
+
+template <bool kFull>
+__device__ __forceinline__ void store_quadrant(const float (&x)[64], float* __restrict__ dst, int64_t ld,
+                                               const Chunk128& c, int q, int lane) {
+  const int col = (q & 1) ? kS - 1 - lane : lane;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int row = quad_row(q >> 1, i);
+    if (kFull || (row < c.vr && col < c.vc)) stream_store(x[i], &dst[row * ld + col]);
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const EncodeParams& p, float* lds,
+                                                 uint32_t* scr) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int a = w >> 1, b = w & 1;
+  const Chunk128 c = chunk_pos128(ts, blockIdx.x);
+  float* __restrict__ mdst = ts.dst + c.base;
+
+  float x[64];
+  if (c.full)
+    load_quadrant<true, kBf16>(x, ts, c, w, lane, p.beta, p.gcoef);
+  else
+    load_quadrant<false, kBf16>(x, ts, c, w, lane, p.beta, p.gcoef);
+  if (!p.subtract_local) {  // aggregated subtraction: M = M' now, the decode side subtracts
+    if (c.full)
+      store_quadrant<true>(x, mdst, ts.cols, c, w, lane);
+    else
+      store_quadrant<false>(x, mdst, ts.cols, c, w, lane);
+  }
+
+  butterfly(x, lds, w, lane);  // quadrants -> S_ab
+  fwd_half(x, a);
+  col_to_row(lds + w * kTile, x, lane);
+  fwd_half(x, b);
+
+  const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
+  topk128(x, p.keff2, w, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, scr);
+  if (!p.subtract_local) return;
+
+  inv_half(x, b);
+  row_to_col(lds + w * kTile, x, lane);
+  inv_half(x, a);
+  butterfly(x, lds, w, lane);  // S'_ab -> quadrants
+
+  if (c.full)
+    store_quadrant<true>(x, mdst, ts.cols, c, w, lane);
+  else
+    store_quadrant<false>(x, mdst, ts.cols, c, w, lane);
+}
+
+// Lane pair (2g, 2g+1) holds chunk g of this wave's 32: x[e] = position 64h + e.
+// In place, x becomes the sums x_n + x_{127-n} (h = 0) or the differences
+// x_n - x_{127-n} (h = 1), n = 0..63.
+__device__ __forceinline__ void pair_butterfly(float (&x)[64], int h) {
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    const float on = x[n], om = x[63 - n];
+    const float pn = pair_swap(on), pm = pair_swap(om);
+    x[n] = h ? pn - om : on + pm;
+    x[63 - n] = h ? pm - on : om + pn;
+  }
+}
+
+// Inverse of pair_butterfly after the inverse half transforms (lane h holds
+// the even part a_n or the odd part b_n): in place, lane h gets positions
+// 64h + e of its chunk, x_n = a_n + b_n and x_{127-n} = a_n - b_n.
+__device__ __forceinline__ void pair_unbutterfly(float (&y)[64], int h) {
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const float ye = y[e], ym = y[63 - e];
+    const float pe = pair_swap(ye), pm = pair_swap(ym);
+    y[e] = h ? pm - ym : ye + pe;
+    y[63 - e] = h ? pe - ye : ym + pm;
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void encode_vector128(const TensorSlot& ts, const EncodeParams& p, float* lds) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slab = blockIdx.x - ts.item_begin;
+  const int chunk0 = slab * kVecChunksPerItem + w * kVecChunksPerWave;  // this wave's first chunk
+  const int64_t first = int64_t(chunk0) * kS + lane;  // column layout: x[r] = element first + 64 r
+  const int64_t rem = int64_t(ts.rows) - first;       // element r exists iff 64 r < rem
+  float* __restrict__ m = ts.dst + first;
+  const char* __restrict__ g = static_cast<const char*>(ts.aux) + first * (kBf16 ? 2 : 4);
+
+  float x[64];
+#pragma unroll
+  for (int r = 0; r < 64; ++r) {
+    float gv = 0.f, mv = 0.f;
+    if (r * 64 < rem) {
+      gv = load_src<kBf16>(g, r * 64);
+      mv = stream_load(&m[r * 64]);
+    }
+    x[r] = fmaf(p.beta, mv, p.gcoef * gv);
+  }
+  if (!p.subtract_local) {
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      if (r * 64 < rem) stream_store(x[r], &m[r * 64]);
+    }
+  }
+  float* tile = lds + w * kTile;
+  col_to_row(tile, x, lane);  // lane 2g + h: positions 64h + e of chunk g
+  const int h = lane & 1;
+  pair_butterfly(x, h);
+  fwd_half(x, h);  // lane h: coefficients 2m + h
+
+  const int chunk = chunk0 + (lane >> 1);
+  const int nchunks = int((uint32_t(ts.rows) + 127u) >> 7);
+  const bool live = chunk < nchunks;
+  const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff1;
+  topk_pair(x, p.keff1, h, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
+  if (!p.subtract_local) return;
+
+  inv_half(x, h);
+  pair_unbutterfly(x, h);
+  row_to_col(tile, x, lane);
+#pragma unroll
+  for (int r = 0; r < 64; ++r) {
+    if (r * 64 < rem) stream_store(x[r], &m[r * 64]);
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void encode128_kernel(LaunchTable tab,
+                                                                                               EncodeParams p) {
+  __shared__ __align__(16) uint32_t lds[kEncLdsWords];
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  if (ts.cols == 0)
+    encode_vector128<kBf16>(ts, p, reinterpret_cast<float*>(lds));
+  else
+    encode_matrix128<kBf16>(ts, p, reinterpret_cast<float*>(lds), lds + kTilesWords);
+}
+
+// ---------------------------------------------------------------- decode
+
+// Matrix accumulator: coefficient (r, c) at r*128 + (c ^ ((r >> 1) & 31)); its
+// 8-bit count in byte c & 3 of word r*32 + ((c >> 2) ^ ((r >> 1) & 31)).  The
+// XOR spreads one column of rows 2u + a (the averaging reads) over the banks.
+__device__ __forceinline__ void accumulate128(float* acc, uint32_t* cntw, uint32_t id, float v) {
+  const uint32_t r = id >> 7, c = id & 127u, s = (r >> 1) & 31u;
+  atomicAdd(&acc[r * 128 + (c ^ s)], v);
+  atomicAdd(&cntw[r * 32 + ((c >> 2) ^ s)], 1u << ((c & 3u) * 8u));
+}
+
+__device__ __forceinline__ void clear_lds(uint32_t* lds, int tid) {
+  uint4* l4 = reinterpret_cast<uint4*>(lds);
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  static_assert(kDecLdsWords % (256 * 4) == 0, "whole 16-byte stores");
+#pragma unroll
+  for (int i = 0; i < kDecLdsWords / (256 * 4); ++i) l4[i * 256 + tid] = z;
+}
+
+__device__ __forceinline__ float avg_scale(uint32_t n, const DecodeParams& p) {
+  // n == 0: no worker sent the coefficient and its sum is 0 as well
+  return p.avg_workers ? p.inv_workers : __builtin_amdgcn_rcpf(fmaxf(float(n), 1.f));
+}
+
+template <int kTargets>
+__device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int a = w >> 1, b = w & 1;
+  const Chunk128 c = chunk_pos128(ts, blockIdx.x);
+  float* acc = reinterpret_cast<float*>(lds);
+  uint32_t* cntw = lds + kAccWords;
+
+  // wave 0 requests the payload entries first
+  // (with both X and M to update there are no registers to spare for early payloads)
+  constexpr bool kEarlyPayload = kTargets != (kToParams | kToMomentum);
+  const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
+  const bool one_batch = kEarlyPayload && p.keff2 <= 64 && p.workers <= kWorkerBatch;
+  float val[kWorkerBatch];
+  uint32_t ix[kWorkerBatch];
+  if (w == 0 && one_batch) {
+    const uint32_t e = uint32_t(min(lane, p.keff2 - 1));
+#pragma unroll
+    for (int j = 0; j < kWorkerBatch; ++j) {
+      const int64_t w0 = int64_t(min(j, p.workers - 1)) * p.entries + e0;
+      val[j] = (p.pay_val + w0)[e];
+      ix[j] = (p.pay_idx + w0)[e];
+    }
+  }
+  const int64_t ld = ts.cols;
+  float* __restrict__ xp = ts.dst + c.base;
+  float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
+  const int col = min((w & 1) ? kS - 1 - lane : lane, c.vc - 1);
+  float x[64], m[64];
+
+  clear_lds(lds, threadIdx.x);
+  __syncthreads();
+  if (w == 0) {  // one wave, worker order 0..W-1: a fixed summation order
+    if (one_batch) {
+#pragma unroll
+      for (int j = 0; j < kWorkerBatch; ++j) {
+        if (lane < p.keff2 && j < p.workers) accumulate128(acc, cntw, ix[j] & 16383u, val[j]);
+      }
+    } else {
+      for (int eb = 0; eb < p.keff2; eb += 64) {
+        const int e = eb + lane;
+        const bool on = e < p.keff2;
+        for (int w0 = 0; w0 < p.workers; w0 += kWorkerBatch) {
+          float v2[kWorkerBatch];
+          uint32_t i2[kWorkerBatch];
+#pragma unroll
+          for (int j = 0; j < kWorkerBatch; ++j) {
+            const int64_t off = int64_t(w0 + j) * p.entries + e0 + e;
+            const bool ok = on && (w0 + j) < p.workers;
+            v2[j] = ok ? p.pay_val[off] : 0.f;
+            i2[j] = ok ? p.pay_idx[off] : 0u;
+          }
+#pragma unroll
+          for (int j = 0; j < kWorkerBatch; ++j) {
+            if (on && (w0 + j) < p.workers) accumulate128(acc, cntw, i2[j] & 16383u, v2[j]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // this wave's sub-block (a, b) in row layout: lane u, q[v] = Q_bar[2u+a][2v+b]
+  float q[64];
+  {
+    const uint32_t r = uint32_t(2 * lane + a), s = uint32_t(lane) & 31u;
+#pragma unroll
+    for (int v2 = 0; v2 < 32; ++v2) {  // one count word covers columns 4 v2 .. 4 v2 + 3
+      const uint32_t cw = cntw[r * 32 + (uint32_t(v2) ^ s)];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t col2 = uint32_t(4 * v2 + 2 * t + b);
+        q[2 * v2 + t] = acc[r * 128 + (col2 ^ s)] * avg_scale((cw >> (8 * (2 * t + b))) & 255u, p);
+      }
+    }
+  }
+  __syncthreads();  // the accumulator area is reused from here on
+  inv_half(q, b);
+  row_to_col(reinterpret_cast<float*>(lds) + w * kTile, q, lane);
+  // the rows to update (clamped addresses; clamped lanes are not stored) land
+  // during the column pass and the butterfly exchange; with both targets the
+  // momentum rows follow the exchange (registers)
+  constexpr bool kEarlyM = kTargets == kToMomentum;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int64_t off = int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col;
+    if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
+    if constexpr (kEarlyM) m[i] = stream_load(&mp[off]);
+  }
+  inv_half(q, a);
+  butterfly(q, reinterpret_cast<float*>(lds), w, lane);  // -> M* of quadrant w
+
+  if constexpr ((kTargets & kToParams) != 0) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
+    if (c.full)
+      store_quadrant<true>(x, xp, ld, c, w, lane);
+    else
+      store_quadrant<false>(x, xp, ld, c, w, lane);
+  }
+  if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
+    if constexpr (!kEarlyM) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) m[i] = stream_load(&mp[int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col]);
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) m[i] = fmaf(-p.alpha, q[i], m[i]);
+    if (c.full)
+      store_quadrant<true>(m, mp, ld, c, w, lane);
+    else
+      store_quadrant<false>(m, mp, ld, c, w, lane);
+  }
+}
+
+// Vector item: each wave owns 32 chunks and its own fifth of the LDS:
+// accumulator (chunk g, coefficient c) at g*128 + (c ^ g), counts in byte
+// c & 3 of word g*32 + ((c >> 2) ^ g).
+template <int kTargets>
+__device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kWaveWords = kDecLdsWords / 4;
+  static_assert(kVecChunksPerWave * kS + kVecChunksPerWave * kS / 4 <= kWaveWords && kTile <= kWaveWords,
+                "per-wave vector LDS");
+  uint32_t* my = lds + w * kWaveWords;
+  float* acc = reinterpret_cast<float*>(my);
+  uint32_t* cntw = my + kVecChunksPerWave * kS;
+  const int slab = blockIdx.x - ts.item_begin;
+  const int chunk0 = slab * kVecChunksPerItem + w * kVecChunksPerWave;
+  const int nchunks = int((uint32_t(ts.rows) + 127u) >> 7);
+  const int nc = max(0, min(kVecChunksPerWave, nchunks - chunk0));  // chunks of this wave
+  const int64_t first = int64_t(chunk0) * kS + lane;
+  const int64_t rem = int64_t(ts.rows) - first;
+
+  uint4* l4 = reinterpret_cast<uint4*>(my);
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int i = 0; i < kWaveWords / 256; ++i) l4[i * 64 + lane] = z4;
+  __syncthreads();
+  const int keff = p.keff1;
+  const int n = nc * keff;
+  const int64_t e0 = ts.entry_begin + int64_t(chunk0) * keff;
+  for (int wk = 0; wk < p.workers; ++wk) {
+    const float* __restrict__ pv = p.pay_val + int64_t(wk) * p.entries + e0;
+    const uint16_t* __restrict__ pi = p.pay_idx + int64_t(wk) * p.entries + e0;
+    for (int f0 = 0; f0 < n; f0 += 64 * 8) {
+      float vv[8];
+      uint32_t ii[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int f = f0 + 64 * j + lane;
+        vv[j] = f < n ? pv[f] : 0.f;
+        ii[j] = f < n ? pi[f] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int f = f0 + 64 * j + lane;
+        if (f < n) {
+          const uint32_t g = uint32_t(f / keff), cc = ii[j] & 127u;
+          atomicAdd(&acc[g * 128 + (cc ^ g)], vv[j]);
+          atomicAdd(&cntw[g * 32 + ((cc >> 2) ^ g)], 1u << ((cc & 3u) * 8u));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int h = lane & 1;
+  const uint32_t g = uint32_t(lane >> 1);
+  float y[64];  // lane h: coefficients 2m + h of chunk g
+#pragma unroll
+  for (int m2 = 0; m2 < 32; ++m2) {
+    const uint32_t cw = cntw[g * 32 + (uint32_t(m2) ^ g)];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t cc = uint32_t(4 * m2 + 2 * t + h);
+      y[2 * m2 + t] = acc[g * 128 + (cc ^ g)] * avg_scale((cw >> (8 * (2 * t + h))) & 255u, p);
+    }
+  }
+  __syncthreads();
+  inv_half(y, h);
+  pair_unbutterfly(y, h);
+  float (&x)[64] = y;
+  row_to_col(reinterpret_cast<float*>(my), x, lane);  // column layout: x[r] = M* at element first + 64 r
+
+  if constexpr ((kTargets & kToParams) != 0) {
+    float* __restrict__ xp = ts.dst + first;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      if (r * 64 < rem) stream_store(update(stream_load(&xp[r * 64]), x[r], p), &xp[r * 64]);
+    }
+  }
+  if constexpr ((kTargets & kToMomentum) != 0) {
+    float* __restrict__ mp = static_cast<float*>(ts.aux) + first;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      if (r * 64 < rem) stream_store(fmaf(-p.alpha, x[r], stream_load(&mp[r * 64])), &mp[r * 64]);
+    }
+  }
+}
+
+template <int kTargets>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode128_kernel(LaunchTable tab,
+                                                                                               DecodeParams p) {
+  __shared__ __align__(16) uint32_t lds[kDecLdsWords];
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  if (ts.cols == 0)
+    decode_vector128<kTargets>(ts, p, lds);
+  else
+    decode_matrix128<kTargets>(ts, p, lds);
+}
+
+}  // namespace
+
+hipError_t launch_encode128(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, hipStream_t stream) {
+  if (tab.items <= 0) return hipSuccess;
+  const dim3 grid(tab.items), block(256);
+  if (g_bf16)
+    encode128_kernel<true><<<grid, block, 0, stream>>>(tab, p);
+  else
+    encode128_kernel<false><<<grid, block, 0, stream>>>(tab, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode128(const LaunchTable& tab, const DecodeParams& p, hipStream_t stream) {
+  if (tab.items <= 0) return hipSuccess;
+  const dim3 grid(tab.items), block(256);
+  if (p.update_x && p.update_m)
+    decode128_kernel<kToParams | kToMomentum><<<grid, block, 0, stream>>>(tab, p);
+  else if (p.update_m)
+    decode128_kernel<kToMomentum><<<grid, block, 0, stream>>>(tab, p);
+  else
+    decode128_kernel<kToParams><<<grid, block, 0, stream>>>(tab, p);
+  return hipGetLastError();
+}
+
+}  // namespace demo

@@ -14,7 +14,8 @@
 
 namespace demo {
 
-constexpr int kChunk = 64;
+constexpr int kChunk = 64;       // default chunk edge
+constexpr int kChunkLarge = 128;  // the other chunk edge built
 constexpr int kMaxTensorsPerLaunch = 96;
 constexpr int kMaxWorkers = 255;  // counts are kept in 8 bits
 
@@ -44,8 +45,8 @@ struct EncodeParams {
   float beta;
   float gcoef;  // (1 - beta) or 1
   float alpha;
-  int32_t keff2;           // entries per 64x64 chunk
-  int32_t keff1;           // entries per 64-element chunk
+  int32_t keff2;           // entries per s x s chunk
+  int32_t keff1;           // entries per s-element chunk
   int32_t subtract_local;  // 1: M = M' - alpha (own part); 0: M = M'
 };
 
@@ -54,8 +55,8 @@ struct DecodeParams {
   const uint16_t* pay_idx;
   int64_t entries;  // entries per worker payload
   int32_t workers;
-  int32_t keff2;  // entries per 64x64 chunk
-  int32_t keff1;  // entries per 64-element chunk
+  int32_t keff2;  // entries per s x s chunk
+  int32_t keff1;  // entries per s-element chunk
   float eta;
   float lam;
   float inv_workers;
@@ -81,5 +82,9 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream);
 hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream);
+// Chunk edge 128 (kernels128.hip): DCT basis; a work item is one 128x128
+// chunk or 128 vector chunks, 256 threads each.
+hipError_t launch_encode128(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, hipStream_t stream);
+hipError_t launch_decode128(const LaunchTable& tab, const DecodeParams& p, hipStream_t stream);
 
 }  // namespace demo

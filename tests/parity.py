@@ -86,7 +86,7 @@ class EncodeReport:
 
 def compare_encode(out: dict, shape, keff: int, alpha: float, P0, P1, gpu_M: np.ndarray,
                    gpu_vals: np.ndarray, gpu_idx: np.ndarray, diverged: np.ndarray,
-                   report: EncodeReport, where: str = "") -> np.ndarray:
+                   report: EncodeReport, where: str = "", s: int = 64) -> np.ndarray:
     """Check one tensor's encode; returns the updated diverged-chunk mask.
 
     out: oracle.encode(...) result (float64 Mp_chunks and Q included).
@@ -114,7 +114,7 @@ def compare_encode(out: dict, shape, keff: int, alpha: float, P0, P1, gpu_M: np.
         report.ties += 1
         new_div[c] = True
         if expect_chunks is None:
-            expect_chunks = O.split_chunks(out["M"].astype(np.float64))
+            expect_chunks = O.split_chunks(out["M"].astype(np.float64), s)
         if comb(window.size, quota) <= MAX_ALTERNATIVES:
             alts = [np.sort(np.concatenate([forced, np.array(sub, dtype=np.int64)]))
                     for sub in itertools.combinations(window.tolist(), quota)]
@@ -127,7 +127,7 @@ def compare_encode(out: dict, shape, keff: int, alpha: float, P0, P1, gpu_M: np.
             # huge window: coefficients in it are near the noise floor; bound the residual difference
             kth = np.abs(Qf[c][oidx[c]]).min()
             tol = RTOL * kth + NOISE * norms[c]
-            extra_atol[c] = 2.0 * quota * (kth + tol) * abs(alpha) * (2.0 / 64.0) * 1.01
+            extra_atol[c] = 2.0 * quota * (kth + tol) * abs(alpha) * (2.0 / s) * 1.01
     report.chunks += n
     report.exact += int(np.sum(same & ~diverged))
     report.skipped += int(np.sum(diverged))
@@ -141,10 +141,10 @@ def compare_encode(out: dict, shape, keff: int, alpha: float, P0, P1, gpu_M: np.
     assert not bad.any(), f"{where}: payload values differ (chunk {np.nonzero(bad.any(axis=1))[0][:5]})"
 
     # new momentum, per element, chunks not diverged before this step
-    ref_M = out["M"].astype(np.float64) if expect_chunks is None else O.merge_chunks(expect_chunks, shape)
+    ref_M = out["M"].astype(np.float64) if expect_chunks is None else O.merge_chunks(expect_chunks, shape, s)
     mp_norm = np.linalg.norm(out["Mp_chunks"].reshape(n, -1), axis=1)
-    atol_e = chunk_values_to_elements(np.maximum(ATOL, NOISE * mp_norm) + extra_atol, shape)
-    emask = chunk_mask_to_elements(live, shape)
+    atol_e = chunk_values_to_elements(np.maximum(ATOL, NOISE * mp_norm) + extra_atol, shape, s)
+    emask = chunk_mask_to_elements(live, shape, s)
     diff = np.abs(gpu_M.astype(np.float64) - ref_M)
     bad = (diff > _tol(ref_M, atol_e)) & emask
     if bad.any():
@@ -162,20 +162,20 @@ def chunk_values_to_elements(vals: np.ndarray, shape, s: int = 64) -> np.ndarray
 
 
 def compare_decode(dec: dict, shape, phi: str, eta: float, gpu_X: np.ndarray, chunk_diverged: np.ndarray,
-                   elem_diverged: Optional[np.ndarray], where: str = "") -> np.ndarray:
+                   elem_diverged: Optional[np.ndarray], where: str = "", s: int = 64) -> np.ndarray:
     """Check one tensor's decode/apply; returns the updated diverged-element mask."""
     ref = dec["X"].astype(np.float64)
     Mstar = dec["Mstar"]
-    emask = ~chunk_mask_to_elements(chunk_diverged, shape)
+    emask = ~chunk_mask_to_elements(chunk_diverged, shape, s)
     if elem_diverged is not None:
         emask &= ~elem_diverged
     new_elem = np.zeros(shape, dtype=bool) if elem_diverged is None else elem_diverged.copy()
     diff = np.abs(gpu_X.astype(np.float64) - ref)
     tol = _tol(ref, ATOL)
     if phi == "sign":
-        ch = O.split_chunks(np.abs(Mstar))
+        ch = O.split_chunks(np.abs(Mstar), s)
         cmax = ch.reshape(ch.shape[0], -1).max(axis=1)
-        thresh = chunk_values_to_elements(RTOL * cmax, shape)
+        thresh = chunk_values_to_elements(RTOL * cmax, shape, s)
         near0 = np.abs(Mstar) <= thresh
         flip = near0 & (diff > tol)
         assert not np.any(flip & emask & (diff > 2 * eta + tol)), f"{where}: near-zero sign element off by > 2 eta"
@@ -189,13 +189,14 @@ def compare_decode(dec: dict, shape, phi: str, eta: float, gpu_X: np.ndarray, ch
     return new_elem
 
 
-def compare_momentum(ref_M: np.ndarray, gpu_M: np.ndarray, shape, chunk_diverged: np.ndarray, where: str = ""):
+def compare_momentum(ref_M: np.ndarray, gpu_M: np.ndarray, shape, chunk_diverged: np.ndarray, where: str = "",
+                     s: int = 64):
     """Check a momentum tensor after the aggregated subtraction, chunks not diverged only."""
     ref = ref_M.astype(np.float64)
     n = chunk_diverged.shape[0]
-    norms = np.linalg.norm(O.split_chunks(ref).reshape(n, -1), axis=1)
-    atol = chunk_values_to_elements(np.maximum(ATOL, NOISE * norms), shape)
-    live = ~chunk_mask_to_elements(chunk_diverged, shape)
+    norms = np.linalg.norm(O.split_chunks(ref, s).reshape(n, -1), axis=1)
+    atol = chunk_values_to_elements(np.maximum(ATOL, NOISE * norms), shape, s)
+    live = ~chunk_mask_to_elements(chunk_diverged, shape, s)
     diff = np.abs(gpu_M.astype(np.float64) - ref)
     bad = (diff > _tol(ref, atol)) & live
     if bad.any():

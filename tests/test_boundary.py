@@ -78,7 +78,7 @@ def _call_encode(lib, shapes, k=8, chunk=64, grad_dtype=0, beta=0.9, alpha=0.2, 
     n = len(shapes)
     sh = B._shapes(shapes)
     if entries is None:
-        entries = O.payload_entries(shapes, max(k, 1)) if k >= 1 and chunk == 64 else 0
+        entries = O.payload_entries(shapes, max(k, 1), chunk) if k >= 1 and chunk in (64, 128) else 0
     gp = B._ptrs([grads] * n)
     mp = B._ptrs([moms] * n)
     return lib.demo_encode(None, n, sh, gp, grad_dtype, mp, ctypes.byref(cfg), vals, idx, entries, None)
@@ -122,7 +122,10 @@ def test_valid_arguments_reach_the_context_check(lib):
     (dict(shapes=[(2 ** 31, 4)]), 2),
     (dict(k=0), 3),
     (dict(k=-3), 3),
-    (dict(chunk=128), 3),
+    (dict(chunk=96), 3),
+    (dict(chunk=128, basis=2), 3),
+    (dict(chunk=128, basis=1, P0=0x5000, P1=0x6000), 3),
+    (dict(chunk=128, entries=O.payload_entries([(128, 64), (100,)], 8)), 4),
     (dict(grad_dtype=7), 1),
     (dict(form=2), 1),
     (dict(beta=float("nan")), 1),
@@ -275,3 +278,29 @@ def test_decode_signs_arguments(lib, kw, status, text):
 def test_apply_signs_arguments(lib, kw, status, text):
     assert _call_apply_signs(lib, [(128, 64), (100,)], **kw) == status
     assert text in _msg(lib)
+
+
+@pytest.mark.parametrize("name", sorted(DI.WORKLOADS))
+def test_plan_chunk128_matches_oracle(lib, name):
+    import numpy as np
+    w = DI.WORKLOADS[name]
+    for k in (1, w.k, 64, 128, 16384, 20000):
+        n_chunks, n_entries, begin = B.demo_plan(w.shapes, k, 128)
+        assert n_entries == O.payload_entries(w.shapes, k, 128)
+        assert n_chunks == sum(int(np.prod(O.chunk_grid(s, 128))) for s in w.shapes)
+        assert begin[-1] == n_entries
+
+
+def test_chunk128_valid_arguments_reach_the_context_check(lib):
+    assert _call_encode(lib, [(300, 200), (1000,)], chunk=128, k=16) == 1 and "context" in _msg(lib)
+    assert _call_encode(lib, [(300, 200)], chunk=128, k=16, subtraction=1) == 1 and "context" in _msg(lib)
+    cfg = B.demo_codec_cfg(128, 16, 0.9, 0.2, 0, 0, None, None, 0)
+    sh = [(300, 200), (1000,)]
+    e = O.payload_entries(sh, 16, 128)
+    assert lib.demo_decode_apply(None, 2, B._shapes(sh), B._ptrs([0x1000] * 2), ctypes.byref(cfg), 3, 0x3000,
+                                 0x4000, e, 0, 1e-3, 0.0, 0, None) == 1 and "context" in _msg(lib)
+    # the one-bit download is built for chunk 64 only
+    assert lib.demo_decode_signs(None, 2, B._shapes(sh), ctypes.byref(cfg), 3, 0x3000, 0x4000, e, 0, 0x5000, 8,
+                                 None) == 3 and "chunk 64" in _msg(lib)
+    nw = ctypes.c_int64()
+    assert lib.demo_plan_signs(B._shapes(sh), 2, 128, ctypes.byref(nw), None) == 3

@@ -42,20 +42,20 @@ def dev():
     return torch.device("cuda:0")
 
 
-def sample_chunks(shape, rng):
+def sample_chunks(shape, rng, s=64):
     """Chunk ordinals to check: first, last, and one seeded random chunk."""
-    n = int(np.prod(O.chunk_grid(shape)))
+    n = int(np.prod(O.chunk_grid(shape, s)))
     picks = {0, n - 1, int(rng.integers(n))}
     return sorted(picks)
 
 
-def chunk_block(t: torch.Tensor, shape, c: int) -> np.ndarray:
+def chunk_block(t: torch.Tensor, shape, c: int, s: int = 64) -> np.ndarray:
     """The (unpadded) sub-block of chunk c, copied to the host."""
     if len(shape) == 1:
-        return t[c * 64:(c + 1) * 64].cpu().numpy()
-    g1 = O.chunk_grid(shape)[1]
+        return t[c * s:(c + 1) * s].cpu().numpy()
+    g1 = O.chunk_grid(shape, s)[1]
     cr, cc = divmod(c, g1)
-    return t[cr * 64:(cr + 1) * 64, cc * 64:(cc + 1) * 64].cpu().numpy()
+    return t[cr * s:(cr + 1) * s, cc * s:(cc + 1) * s].cpu().numpy()
 
 
 def check_payload_properties(vals: torch.Tensor, idx: torch.Tensor, layout, limits, where: str):
@@ -69,26 +69,27 @@ def check_payload_properties(vals: torch.Tensor, idx: torch.Tensor, layout, limi
             assert bool((ix[:, 1:] > ix[:, :-1]).all()), f"{where}: tensor {t} indices not ascending"
 
 
-@pytest.mark.parametrize("name", ["olmo_300m", "olmo_1b"])
-def test_full_size_sampled(dev, name):
+@pytest.mark.parametrize("name,s", [("olmo_300m", 64), ("olmo_1b", 64), ("olmo_1b", 128)])
+def test_full_size_sampled(dev, name, s):
     w = DI.WORKLOADS[name]
     W, steps = w.workers, 2
     phi_c = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
-    P = O.dct_basis()
+    P = O.dct_basis(s)
     rng = np.random.default_rng(7 + w.config_id)
+    name = f"{name} s={s}"
 
-    shapes = [tuple(s) for s in w.shapes]
-    groups = [{"ids": list(range(len(shapes))), "shapes": shapes, "codec": B.Codec(shapes, w.k, w.beta, w.alpha),
-               "lay": PR.layout(shapes, w.k)}]
+    shapes = [tuple(d) for d in w.shapes]
+    groups = [{"ids": list(range(len(shapes))), "shapes": shapes,
+               "codec": B.Codec(shapes, w.k, w.beta, w.alpha, chunk=s), "lay": PR.layout(shapes, w.k, s)}]
     for gr in groups:
         gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
     say(f"[{name}] {len(w.shapes)} tensors, {w.n_params} params, W={W}: allocating momenta")
     M = {i: [torch.zeros(w.shapes[i], device=dev) for _ in range(W)] for i in range(len(w.shapes))}
     X = {i: DI.device_initial_params(w, i, dev) for i in range(len(w.shapes))}
-    samples = {i: sample_chunks(w.shapes[i], rng) for i in range(len(w.shapes))}
+    samples = {i: sample_chunks(w.shapes[i], rng, s) for i in range(len(w.shapes))}
     # oracle state of every sampled chunk: momentum per worker, parameters
     M_or = {(i, c): [None] * W for i in samples for c in samples[i]}
-    X_or = {(i, c): chunk_block(X[i], w.shapes[i], c).copy() for i in samples for c in samples[i]}
+    X_or = {(i, c): chunk_block(X[i], w.shapes[i], c, s).copy() for i in samples for c in samples[i]}
     cdiv = {(i, c, wk): np.zeros(1, bool) for i in samples for c in samples[i] for wk in range(W)}
     ediv = {}
     report = PR.EncodeReport()
@@ -107,7 +108,7 @@ def test_full_size_sampled(dev, name):
                 ne = gr["codec"].n_entries
                 gv = gr["vals"][wk * ne:(wk + 1) * ne]
                 gi = gr["pidx"][wk * ne:(wk + 1) * ne]
-                check_payload_properties(gv, gi, gr["lay"], [4096 if len(s) == 2 else 64 for s in gr["shapes"]],
+                check_payload_properties(gv, gi, gr["lay"], [s * s if len(d) == 2 else s for d in gr["shapes"]],
                                          f"{name} step {t} worker {wk}")
                 gv_h = gv.cpu().numpy()
                 gi_h = gi.cpu().numpy().view(np.uint16)
@@ -116,16 +117,16 @@ def test_full_size_sampled(dev, name):
                     shape = w.shapes[i]
                     assert torch.isfinite(M[i][wk]).all(), f"{name}: non-finite momentum, tensor {i}"
                     for c in samples[i]:
-                        g_blk = chunk_block(G[i], shape, c)
+                        g_blk = chunk_block(G[i], shape, c, s)
                         m_prev = M_or[(i, c)][wk]
                         if m_prev is None:
                             m_prev = np.zeros_like(g_blk)
-                        out = O.encode(m_prev, g_blk, beta=w.beta, alpha=w.alpha, k=w.k)
+                        out = O.encode(m_prev, g_blk, beta=w.beta, alpha=w.alpha, k=w.k, s=s)
                         s0 = e0 + c * keff
                         cdiv[(i, c, wk)] = PR.compare_encode(
-                            out, g_blk.shape, keff, w.alpha, P, P, chunk_block(M[i][wk], shape, c),
+                            out, g_blk.shape, keff, w.alpha, P, P, chunk_block(M[i][wk], shape, c, s),
                             gv_h[s0:s0 + keff].reshape(1, keff), gi_h[s0:s0 + keff].reshape(1, keff),
-                            cdiv[(i, c, wk)], report, where=f"{name} step {t} worker {wk} tensor {i} chunk {c}")
+                            cdiv[(i, c, wk)], report, where=f"{name} step {t} worker {wk} tensor {i} chunk {c}", s=s)
                         M_or[(i, c)][wk] = out["M"]
                         or_vals[(i, c)][wk] = out["values"]
                         or_idx[(i, c)][wk] = out["idx"]
@@ -137,12 +138,12 @@ def test_full_size_sampled(dev, name):
         for (i, c), xo in X_or.items():
             assert torch.isfinite(X[i]).all(), f"{name}: non-finite parameters, tensor {i}"
             dec = O.decode_apply(xo, np.stack(or_vals[(i, c)]), np.stack(or_idx[(i, c)]), phi=w.phi,
-                                 eta=w.eta, lam=w.lam)
+                                 eta=w.eta, lam=w.lam, s=s)
             div = np.zeros(1, bool)
             for wk in range(W):
                 div |= cdiv[(i, c, wk)]
-            ediv[(i, c)] = PR.compare_decode(dec, xo.shape, w.phi, w.eta, chunk_block(X[i], w.shapes[i], c), div,
-                                             ediv.get((i, c)), where=f"{name} step {t} tensor {i} chunk {c}")
+            ediv[(i, c)] = PR.compare_decode(dec, xo.shape, w.phi, w.eta, chunk_block(X[i], w.shapes[i], c, s), div,
+                                             ediv.get((i, c)), where=f"{name} step {t} tensor {i} chunk {c}", s=s)
             X_or[(i, c)] = dec["X"]
     say(f"[{name}] sampled chunks checked {report.chunks}: exact {report.exact}, near-tie {report.ties}, "
         f"skipped {report.skipped}")

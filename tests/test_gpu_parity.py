@@ -33,8 +33,9 @@ class Sim:
     """W workers of one workload, GPU next to the oracle."""
 
     def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None, identity=False, aggregated=False,
-                 signs=False):
+                 signs=False, chunk=64):
         self.w = w
+        self.s = chunk
         self.signs = signs  # one-bit download: decode_signs, then apply_signs (phi = sign)
         assert not (signs and (aggregated or w.phi != "sign"))
         self.plain = plain
@@ -43,9 +44,10 @@ class Sim:
         self.avg = avg
         self.inputs = inputs  # optional callable (worker, step, tensor) -> float32 gradient
         self.shapes = [tuple(s) for s in w.shapes]
-        self.codec = B.Codec(self.shapes, w.k, w.beta, w.alpha, plain, identity=identity, aggregated=aggregated)
-        self.lay = PR.layout(self.shapes, w.k)
-        nc, ne, eb = B.demo_plan(self.shapes, w.k)
+        self.codec = B.Codec(self.shapes, w.k, w.beta, w.alpha, plain, identity=identity, aggregated=aggregated,
+                             chunk=chunk)
+        self.lay = PR.layout(self.shapes, w.k, chunk)
+        nc, ne, eb = B.demo_plan(self.shapes, w.k, chunk)
         assert ne == sum(n * k for n, k, _ in self.lay)
         assert eb[:-1] == [e for _, _, e in self.lay]
         W = w.workers
@@ -98,13 +100,13 @@ class Sim:
             for i, shp in enumerate(self.shapes):
                 n, keff, e0 = self.lay[i]
                 out = O.encode(self.M_or[wk][i], G[i], beta=w.beta, alpha=w.alpha, k=w.k, plain=self.plain,
-                               P0=P0, P1=P1, subtract="aggregated" if self.aggregated else "local")
+                               P0=P0, P1=P1, s=self.s, subtract="aggregated" if self.aggregated else "local")
                 gM = self.M_gpu[wk][i].cpu().numpy()
                 self.cdiv[wk][i] = PR.compare_encode(
-                    out, shp, keff, 0.0 if self.aggregated else w.alpha, O.dct_basis() if P0 is None else P0,
-                    O.dct_basis() if P1 is None else P1, gM, gv[e0:e0 + n * keff].reshape(n, keff),
-                    gi[e0:e0 + n * keff].reshape(n, keff), self.cdiv[wk][i], self.report,
-                    where=f"{w.name} step {t} worker {wk} tensor {i} {shp}")
+                    out, shp, keff, 0.0 if self.aggregated else w.alpha,
+                    O.dct_basis(self.s) if P0 is None else P0, O.dct_basis(self.s) if P1 is None else P1, gM,
+                    gv[e0:e0 + n * keff].reshape(n, keff), gi[e0:e0 + n * keff].reshape(n, keff),
+                    self.cdiv[wk][i], self.report, where=f"{w.name} step {t} worker {wk} tensor {i} {shp}", s=self.s)
                 self.M_or[wk][i] = out["M"]
                 or_vals[i][wk] = out["values"]
                 or_idx[i][wk] = out["idx"]
@@ -127,7 +129,7 @@ class Sim:
         torch.cuda.synchronize()
         for i, shp in enumerate(self.shapes):
             dec = O.decode_apply(self.X_or[i], np.stack(or_vals[i]), np.stack(or_idx[i]), phi=w.phi, eta=w.eta,
-                                 lam=w.lam, mode=self.avg, P0=P0, P1=P1)
+                                 lam=w.lam, mode=self.avg, P0=P0, P1=P1, s=self.s)
             cd = np.zeros_like(self.cdiv[0][i])
             for wk in range(W):
                 cd |= self.cdiv[wk][i]
@@ -138,13 +140,13 @@ class Sim:
                 dec = {"X": O.apply_signs(self.X_or[i], O.pack_signs(dec["Mstar"]), eta=w.eta, lam=w.lam),
                        "Mstar": dec["Mstar"]}
             self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
-                                             where=f"{w.name} step {t} tensor {i} {shp}")
+                                             where=f"{w.name} step {t} tensor {i} {shp}", s=self.s)
             self.X_or[i] = dec["X"]
             if self.aggregated:
                 for wk in range(W):
                     self.M_or[wk][i] = O.subtract_aggregated(self.M_or[wk][i], dec["Mstar"], w.alpha)
                     PR.compare_momentum(self.M_or[wk][i], self.M_gpu[wk][i].cpu().numpy(), shp, cd,
-                                        where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (aggregated)")
+                                        where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (aggregated)", s=self.s)
                     self.cdiv[wk][i] = self.cdiv[wk][i] | cd
 
     def run(self, steps, max_tie_fraction=0.02):
@@ -314,3 +316,57 @@ def test_sign_download_matches_signum_decode(dev):
     torch.cuda.synchronize()
     for a, b in zip(Xa, Xb):
         assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- chunk edge 128
+
+@pytest.mark.parametrize("k", [1, 8, 32, 64])
+def test_chunk128_single_chunk(dev, k):
+    """One 128x128 chunk, two workers: the fast top-k path (keff <= 64)."""
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"s128_one_k{k}", shapes=((128, 128),), k=k, workers=2)
+    Sim(w, chunk=128).run(2)
+
+
+@pytest.mark.parametrize("k", [65, 500, 16384])
+def test_chunk128_large_k(dev, k):
+    """keff > 64 (workgroup-wide bitwise search) and the lossless k = 16384."""
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"s128_bigk{k}", shapes=((128, 256), (300,)), k=k, workers=2)
+    Sim(w, chunk=128).run(2)
+
+
+@pytest.mark.parametrize("k", [1, 4, 37])
+def test_chunk128_ragged_and_vectors(dev, k):
+    """Padded chunks, tiny matrices and vectors of awkward lengths at s = 128."""
+    w = DI.WORKLOADS["tiny_256"].replace(
+        name=f"s128_ragged_k{k}",
+        shapes=((1, 1), (2, 3), (129, 130), (300, 77), (1,), (127,), (129,), (5000,)), k=k, workers=3)
+    Sim(w, chunk=128).run(2)
+
+
+@pytest.mark.parametrize("plain,avg,phi", [(False, "count", "sign"), (True, "workers", "identity")])
+def test_chunk128_modes(dev, plain, avg, phi):
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"s128_modes_{plain}_{avg}_{phi}", shapes=((256, 384), (1000,)),
+                                         phi=phi, workers=3, k=16)
+    Sim(w, chunk=128, plain=plain, avg=avg).run(3)
+
+
+def test_chunk128_aggregated_and_many_workers(dev):
+    w = DI.WORKLOADS["tiny_256"].replace(name="s128_agg", shapes=((256, 128), (200,)), workers=3, k=8)
+    Sim(w, chunk=128, aggregated=True).run(3)
+    w = DI.WORKLOADS["tiny_256"].replace(name="s128_w20", shapes=((128, 256), (130,)), workers=20, k=16)
+    Sim(w, chunk=128).run(2)
+
+
+def test_chunk128_degenerate(dev):
+    """All-zero and constant gradients: exact ties in the workgroup-wide top-k."""
+    w = DI.WORKLOADS["tiny_256"].replace(name="s128_degenerate", shapes=((128, 128), (128, 256), (300,)), k=8,
+                                         workers=2)
+
+    def inputs(worker, step, i):
+        if i == 0:
+            return np.zeros((128, 128), np.float32)
+        if i == 1:
+            return np.full((128, 256), 1e-3 * (worker + 1), np.float32)
+        return np.full((300,), -2e-3, np.float32)
+
+    Sim(w, inputs=inputs, chunk=128).run(2, max_tie_fraction=1.0)
