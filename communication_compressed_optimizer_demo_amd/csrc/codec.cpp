@@ -24,6 +24,7 @@ using demo::kChunkLarge;
 using demo::kMaxTensorsPerLaunch;
 static_assert(kMaxTensorsPerLaunch == DEMO_MAX_TENSORS_PER_LAUNCH, "header and launch table disagree");
 static_assert(demo::kMaxWorkers == DEMO_MAX_WORKERS, "header and kernels disagree");
+static_assert(kChunk == DEMO_CHUNK && kChunkLarge == DEMO_CHUNK_LARGE, "header and kernels disagree on chunk edges");
 using demo::LaunchTable;
 
 thread_local std::string g_last_error;

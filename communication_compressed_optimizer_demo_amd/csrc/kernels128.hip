@@ -46,14 +46,17 @@ constexpr int kLd = 65;             // per-wave transpose tile row stride (float
 constexpr int kTile = 64 * kLd;     // floats of one wave's transpose tile
 constexpr int kQuad = 64 * 64;      // floats of one quadrant in the butterfly exchange
 constexpr int kWorkerBatch = 16;
-constexpr int kMaxCand = 256;       // top-k candidates held in LDS
 constexpr int kVecChunksPerWave = 32;
 constexpr int kVecChunksPerItem = 4 * kVecChunksPerWave;
 
 // encode LDS: four transpose tiles (the butterfly exchange reuses them), then
 // the top-k scratch
 constexpr int kTilesWords = 4 * kTile;
-constexpr int kScrWords = 256 + 8 + 8 + 512 + 2 * kMaxCand;
+constexpr int kSlots = 1;                 // top-k candidate slots per lane and wave
+constexpr int kCandPerWave = 64 * kSlots;  // candidates each wave may put in LDS
+// top-k scratch: 16 header words, 512 kept-mask words, candidate values and
+// indices, the kept list (64 values, 64 indices)
+constexpr int kScrWords = 16 + 512 + 2 * 4 * kCandPerWave + 128;
 constexpr int kEncLdsWords = kTilesWords + kScrWords;
 // decode LDS: 128 x 128 fp32 accumulator + 128 x 32 words of 8-bit counts;
 // the tiles, the butterfly exchange and the vector path reuse it
@@ -144,25 +147,27 @@ __device__ __forceinline__ void row_to_col(float* tile, float (&x)[64], int lane
   __syncthreads();
 }
 
-// x <- sum over the four waves' x (same i, same lane) with sign (-1)^(a qa + b qb),
-// (a, b) the bits of this wave, (qa, qb) those of the other.  Forward: quadrants ->
-// S_ab; inverse: S'_ab -> quadrants.  Leaves the exchange area free.
-__device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int lane) {
+// One butterfly stage between wave w and wave w ^ bit: the wave without `bit`
+// keeps own + partner, the one with it partner - own.
+__device__ __forceinline__ void butterfly_stage(float (&x)[64], float* xq, int w, int lane, int bit) {
 #pragma unroll
   for (int i = 0; i < 64; ++i) xq[w * kQuad + i * 64 + lane] = x[i];
   __syncthreads();
-  const int a = w >> 1, b = w & 1;
+  const float sg = (w & bit) ? -1.f : 1.f;
+  const float* __restrict__ px = xq + (w ^ bit) * kQuad + lane;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float t = xq[q * kQuad + i * 64 + lane];
-      s = (((a & (q >> 1)) ^ (b & q)) & 1) ? s - t : s + t;
-    }
-    x[i] = s;
-  }
+  for (int i = 0; i < 64; ++i) x[i] = fmaf(sg, x[i], px[i * 64]);
   __syncthreads();
+}
+
+// x <- sum over the four waves' x (same i, same lane) with sign (-1)^(a qa + b qb),
+// (a, b) the bits of this wave, (qa, qb) those of the other: the two-point
+// butterfly along dimension 1 (bit 1), then along dimension 0 (bit 2).
+// Forward: quadrants -> S_ab; inverse: S'_ab -> quadrants.  Leaves the
+// exchange area free.
+__device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int lane) {
+  butterfly_stage(x, xq, w, lane, 1);
+  butterfly_stage(x, xq, w, lane, 2);
 }
 
 struct Chunk128 {
@@ -194,21 +199,32 @@ __device__ __forceinline__ int quad_row(int qa, int i) { return qa ? (kS - 1 - i
 // Q[2u+a][2v+b], chunk-local index (2u+a)*128 + 2v + b.  Keeps the keff
 // largest magnitudes (float32; equal magnitudes: lower index first), writes
 // them in index order and scales them by (1 - alpha) in place.
-//   Fast path (keff <= 64): T0 = keff-th largest of the 256 lane maxima (so at
-//   least keff coefficients are >= T0); the coefficients >= T0 go to LDS; wave 0
-//   finds the threshold K and the tie cut over them.  Otherwise (or with more
-//   than kMaxCand candidates) the same bitwise searches run over all 16384.
-//   Either way: kept = |q| > K, or |q| == K with index <= the tie cut.
-__device__ __forceinline__ void topk128(float (&q)[64], int keff, int w, int lane, float alpha,
+//
+// Fast path (keff <= 64), one workgroup barrier:
+//   1. each wave finds T_w = the keff-th largest of its 64 lane maxima (wave
+//      ballots, as for a 64x64 chunk) and puts its coefficients >= T_w (the
+//      candidates) into its own LDS region;
+//   2. every wave reads all four regions and finds, redundantly, the
+//      threshold K and the tie cut over the union.  The union holds every
+//      coefficient >= K: K >= each wave's own keff-th largest >= T_w;
+//   3. wave 0 ranks the keff kept candidates by index and writes the payload;
+//      every wave scales its own kept coefficients.
+// Otherwise (keff > 64, or a region overflows, e.g. a block of equal
+// magnitudes) the same bitwise searches run over all 16384 coefficients with
+// workgroup-wide counts, and the payload positions come from kept-bit masks.
+
+// Returns true when the payload is still to be written by emit_kept (fast
+// path: wave 0 holds the kept list in LDS scratch that nothing else reuses).
+__device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lane, float alpha,
                                         float* __restrict__ outv, uint16_t* __restrict__ outi, uint32_t* scr) {
   const int a = w >> 1, b = w & 1;
   const uint32_t idx0 = uint32_t((2 * lane + a) * kS + b);  // index of q[0]; q[v] sits at idx0 + 2v
-  uint32_t* rmax = scr;
-  uint32_t* red = scr + 256;
-  uint32_t* bc = scr + 264;
-  uint32_t* kmask = scr + 272;
-  uint32_t* cmag = scr + 784;
-  uint32_t* cid = cmag + kMaxCand;
+  uint32_t* hdr = scr;                             // [0, 4): candidates per wave (~0u: none)
+  uint32_t* red = scr + 8;                         // two sets of four words: workgroup sums
+  uint32_t* kmask = scr + 16;                      // kept bits, 2 words per lane and wave
+  uint32_t* cval = scr + 528;                      // candidate value bits, kCandPerWave per wave
+  uint32_t* cid = cval + 4 * kCandPerWave;         // candidate indices
+  uint32_t* kl = cid + 4 * kCandPerWave;           // wave 0: kept list (64 values, 64 indices)
 
   if (keff >= kS * kS) {  // lossless: every coefficient, at its own index
 #pragma unroll
@@ -218,118 +234,139 @@ __device__ __forceinline__ void topk128(float (&q)[64], int keff, int w, int lan
       outi[id] = static_cast<uint16_t>(id);
       q[v] = fmaf(-alpha, q[v], q[v]);
     }
-    return;
+    return false;
   }
 
   float lm = 0.f;
 #pragma unroll
   for (int v = 0; v < 64; ++v) lm = fmaxf(lm, fabsf(q[v]));
   uint32_t K = 0, cut = 0xffffffffu;  // cut: largest index admitted among |q| == K
-  int parity = 0;
   bool fast = keff <= 64;
   if (fast) {
-    rmax[w * 64 + lane] = __float_as_uint(lm);
-    __syncthreads();
-    uint32_t mx[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mx[r] = rmax[r * 64 + lane];
-    uint32_t T0 = 0;
+    const uint32_t lmb = __float_as_uint(lm);
+    uint32_t T = 0;
     for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t c = T0 | (1u << bit);
-      const int n = ballot_count(mx[0] >= c) + ballot_count(mx[1] >= c) + ballot_count(mx[2] >= c) +
-                    ballot_count(mx[3] >= c);
-      if (n >= keff) T0 = c;
+      const uint32_t c = T | (1u << bit);
+      if (ballot_count(lmb >= c) >= keff) T = c;
     }
     int cnt = 0;
-    if (T0 != 0) {
-      const float t0 = __uint_as_float(T0);
+    if (T != 0) {
+      const float t = __uint_as_float(T);
 #pragma unroll
-      for (int v = 0; v < 64; ++v) cnt += fabsf(q[v]) >= t0 ? 1 : 0;
+      for (int v = 0; v < 64; ++v) cnt += fabsf(q[v]) >= t ? 1 : 0;
     }
     const int incl = wave_incl_scan(cnt, lane);
-    if (lane == 63) red[w] = uint32_t(incl);
-    __syncthreads();
-    int total = 0, base = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = int(red[r]);
-      total += t;
-      base += r < w ? t : 0;
-    }
-    fast = T0 != 0 && total <= kMaxCand;  // the same for every wave
-    if (fast) {
-      const float t0 = __uint_as_float(T0);
-      int pos = base + incl - cnt;
+    const int cw = __shfl(incl, 63);
+    if (T != 0 && cw <= kCandPerWave) {
+      const float t = __uint_as_float(T);
+      int pos = w * kCandPerWave + incl - cnt;
 #pragma unroll
       for (int v = 0; v < 64; ++v) {
-        if (fabsf(q[v]) >= t0) {
-          const uint32_t bits = __float_as_uint(q[v]);
-          cmag[pos] = bits & 0x7fffffffu;
+        if (fabsf(q[v]) >= t) {
+          cval[pos] = __float_as_uint(q[v]);
           cid[pos] = idx0 + 2 * v;
           ++pos;
         }
       }
-      __syncthreads();
-      if (w == 0) {
-        uint32_t m[4], id[4];
+    }
+    if (lane == 0) hdr[w] = T != 0 ? uint32_t(cw) : 0xffffffffu;
+    __syncthreads();
+    uint32_t C[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = r * 64 + lane;
-          const bool live = s < total;
-          m[r] = live ? cmag[s] : 0u;  // empty slots: 0 < T0 <= K, never counted
-          id[r] = live ? cid[s] : 0xffffffffu;
-        }
-        for (int bit = 30; bit >= 0; --bit) {
-          const uint32_t c = K | (1u << bit);
-          const int n = ballot_count(m[0] >= c) + ballot_count(m[1] >= c) + ballot_count(m[2] >= c) +
-                        ballot_count(m[3] >= c);
-          if (n >= keff) K = c;
-        }
-        const int gt = ballot_count(m[0] > K) + ballot_count(m[1] > K) + ballot_count(m[2] > K) +
-                       ballot_count(m[3] > K);
-        const int eq = ballot_count(m[0] == K) + ballot_count(m[1] == K) + ballot_count(m[2] == K) +
-                       ballot_count(m[3] == K);
-        const int quota = keff - gt;
-        if (eq > quota) {  // the quota-th smallest index among the ties
-          uint32_t L = 0;
-          for (int bit = 13; bit >= 0; --bit) {
-            const uint32_t c = L | (1u << bit);
-            const int n = ballot_count(m[0] == K && id[0] < c) + ballot_count(m[1] == K && id[1] < c) +
-                          ballot_count(m[2] == K && id[2] < c) + ballot_count(m[3] == K && id[3] < c);
-            if (n < quota) L = c;
+    for (int r = 0; r < 4; ++r) {
+      C[r] = hdr[r];
+      fast = fast && C[r] <= uint32_t(kCandPerWave);
+    }
+    if (fast) {  // the same decision in every wave
+      // slot j = (region r = j / kSlots, entry (j % kSlots) * 64 + lane); empty slots hold 0, never counted
+      uint32_t mg[4 * kSlots];
+#pragma unroll
+      for (int j = 0; j < 4 * kSlots; ++j) {
+        const uint32_t e = uint32_t((j % kSlots) * 64 + lane);
+        mg[j] = e < C[j / kSlots] ? (cval[(j / kSlots) * kCandPerWave + e] & 0x7fffffffu) : 0u;
+      }
+      for (int bit = 30; bit >= 0; --bit) {
+        const uint32_t c = K | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < 4 * kSlots; ++j) n += ballot_count(mg[j] >= c);
+        if (n >= keff) K = c;
+      }
+      int gt = 0, eq = 0;
+#pragma unroll
+      for (int j = 0; j < 4 * kSlots; ++j) {
+        gt += ballot_count(mg[j] > K);
+        eq += ballot_count(mg[j] == K);
+      }
+      const int quota = keff - gt;
+      if (eq > quota) {  // the quota-th smallest index among the ties
+        uint32_t L = 0;
+        for (int bit = 13; bit >= 0; --bit) {
+          const uint32_t c = L | (1u << bit);
+          int n = 0;
+#pragma unroll
+          for (int j = 0; j < 4 * kSlots; ++j) {
+            const uint32_t e = uint32_t((j % kSlots) * 64 + lane);
+            const uint32_t id = e < C[j / kSlots] ? cid[(j / kSlots) * kCandPerWave + e] : 0xffffffffu;
+            n += ballot_count(mg[j] == K && id < c);
           }
-          cut = L;
+          if (n < quota) L = c;
         }
-        if (lane == 0) {
-          bc[0] = K;
-          bc[1] = cut;
+        cut = L;
+      }
+      if (w == 0) {
+        // compact the keff kept candidates into the kept list; emit_kept ranks
+        // and writes them at the end of the chunk (the other waves do not wait)
+        int off = 0;
+#pragma unroll
+        for (int j = 0; j < 4 * kSlots; ++j) {
+          const int r = j / kSlots;
+          const uint32_t e = uint32_t((j % kSlots) * 64 + lane);
+          const bool live = e < C[r];
+          const uint32_t id = live ? cid[r * kCandPerWave + e] : 0u;
+          const bool keep = live && (mg[j] > K || (mg[j] == K && id <= cut));
+          const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+          if (keep) {
+            const int o = off + lanes_below_mask(km);
+            kl[o] = cval[r * kCandPerWave + e];
+            kl[64 + o] = id;
+          }
+          off += __popcll(km);
         }
       }
-      __syncthreads();
-      K = bc[0];
-      cut = bc[1];
+      const float kf = __uint_as_float(K);
+#pragma unroll
+      for (int v = 0; v < 64; ++v) {
+        const float m = fabsf(q[v]);
+        const bool keep = m > kf || (m == kf && idx0 + 2 * v <= cut);
+        q[v] = keep ? fmaf(-alpha, q[v], q[v]) : q[v];
+      }
+      return true;
     }
   }
-  if (!fast) {
-    // bitwise searches over all 16384 magnitudes, counted across the workgroup
-    float hmax = lm;
+
+  // bitwise searches over all 16384 magnitudes, counted across the workgroup
+  int parity = 0;
+  float hmax = lm;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
-    if (lane == 0) rmax[w] = __float_as_uint(hmax);
-    __syncthreads();
-    const uint32_t hi = max(max(rmax[0], rmax[1]), max(rmax[2], rmax[3]));
-    uint32_t T = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      if (c > hi) continue;  // the same for every wave
-      const float cf = __uint_as_float(c);
-      int n = 0;
+  for (int o = 32; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+  if (lane == 0) red[w] = __float_as_uint(hmax);
+  __syncthreads();
+  const uint32_t hi = max(max(red[0], red[1]), max(red[2], red[3]));
+  parity = 1;  // set 0 of `red` is still being read
+  uint32_t T = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    if (c > hi) continue;  // the same for every wave
+    const float cf = __uint_as_float(c);
+    int n = 0;
 #pragma unroll
-      for (int v = 0; v < 64; ++v) n += fabsf(q[v]) >= cf ? 1 : 0;
-      if (wg_sum(wave_sum(n), red, parity, w, lane) >= keff) T = c;
-    }
-    K = T;
-    const float kf = __uint_as_float(K);
+    for (int v = 0; v < 64; ++v) n += fabsf(q[v]) >= cf ? 1 : 0;
+    if (wg_sum(wave_sum(n), red, parity, w, lane) >= keff) T = c;
+  }
+  K = T;
+  const float kf = __uint_as_float(K);
+  {
     int gt = 0, eq = 0;
 #pragma unroll
     for (int v = 0; v < 64; ++v) {
@@ -338,13 +375,14 @@ __device__ __forceinline__ void topk128(float (&q)[64], int keff, int w, int lan
     }
     const int quota = keff - wg_sum(wave_sum(gt), red, parity, w, lane);
     if (wg_sum(wave_sum(eq), red, parity, w, lane) > quota) {
+      uint64_t eqm = 0;  // ties of this lane; q[v] has index idx0 + 2v
+#pragma unroll
+      for (int v = 0; v < 64; ++v) eqm |= fabsf(q[v]) == kf ? (1ull << v) : 0ull;
       uint32_t L = 0;
       for (int bit = 13; bit >= 0; --bit) {
         const uint32_t c = L | (1u << bit);
-        int n = 0;
-#pragma unroll
-        for (int v = 0; v < 64; ++v) n += (fabsf(q[v]) == kf && idx0 + 2 * v < c) ? 1 : 0;
-        if (wg_sum(wave_sum(n), red, parity, w, lane) < quota) L = c;
+        const int nv = min(64, max(0, (int(c) - int(idx0) + 1) >> 1));  // v with idx0 + 2v < c
+        if (wg_sum(wave_sum(popc64(eqm & below(nv))), red, parity, w, lane) < quota) L = c;
       }
       cut = L;
     }
@@ -355,7 +393,6 @@ __device__ __forceinline__ void topk128(float (&q)[64], int keff, int w, int lan
   // 2u+1 belong to lane u of waves 0,1 and 2,3), plus, in its row, its own
   // wave's kept entries of smaller v and its partner wave's (other b) ones
   // of smaller column.
-  const float kf = __uint_as_float(K);
   uint64_t mine = 0;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
@@ -383,6 +420,23 @@ __device__ __forceinline__ void topk128(float (&q)[64], int keff, int w, int lan
       outi[pos] = static_cast<uint16_t>(idx0 + 2 * v);
       q[v] = fmaf(-alpha, q[v], q[v]);
     }
+  }
+  return false;
+}
+
+// Wave 0, after the fast path: the keff (<= 64) kept candidates of the kept
+// list, ranked by index, into the payload.
+__device__ __forceinline__ void emit_kept(int keff, int lane, float* __restrict__ outv, uint16_t* __restrict__ outi,
+                                          const uint32_t* scr) {
+  const uint32_t* kl = scr + 528 + 2 * 4 * kCandPerWave;
+  const bool mine = lane < keff;
+  const uint32_t myv = mine ? kl[lane] : 0u;
+  const uint32_t myid = mine ? kl[64 + lane] : 0xffffffffu;
+  int rank = 0;
+  for (int j = 0; j < keff; ++j) rank += uint32_t(__builtin_amdgcn_readlane(int(myid), j)) < myid ? 1 : 0;
+  if (mine) {
+    outv[rank] = __uint_as_float(myv);
+    outi[rank] = static_cast<uint16_t>(myid);
   }
 }
 
@@ -420,13 +474,14 @@ __device__ __forceinline__ void topk_pair(float (&y)[64], int keff, int h, bool 
   const int quota = keff - gt;
   uint32_t cut = 0xffffffffu;
   if (eq > quota) {
+    uint64_t eqm = 0;  // ties of this lane; y[m] is coefficient 2m + h
+#pragma unroll
+    for (int m = 0; m < 64; ++m) eqm |= fabsf(y[m]) == kf ? (1ull << m) : 0ull;
     uint32_t L = 0;
 #pragma unroll 1
     for (int bit = 6; bit >= 0; --bit) {
       const uint32_t c = L | (1u << bit);
-      int n = 0;
-#pragma unroll
-      for (int m = 0; m < 64; ++m) n += (fabsf(y[m]) == kf && uint32_t(2 * m + h) < c) ? 1 : 0;
+      int n = popc64(eqm & below(min(64, max(0, (int(c) - h + 1) >> 1))));  // m with 2m + h < c
       n += pair_swap(n);
       if (n < quota) L = c;
     }
@@ -455,20 +510,26 @@ __device__ __forceinline__ void topk_pair(float (&y)[64], int keff, int h, bool 
 
 // ---------------------------------------------------------------- encode
 
+// Element offset of quadrant q's (0, lane) inside the chunk, and the
+// (wave-uniform) offset from one quadrant row to the next.
+__device__ __forceinline__ int64_t quad_origin(int q, int lane, int64_t ld) {
+  return int64_t((q >> 1) ? kS - 1 : 0) * ld + ((q & 1) ? kS - 1 - lane : lane);
+}
+__device__ __forceinline__ int64_t quad_step(int q, int64_t ld) { return (q >> 1) ? -ld : ld; }
+
 template <bool kFull, bool kBf16>
 __device__ __forceinline__ void load_quadrant(float (&x)[64], const TensorSlot& ts, const Chunk128& c, int q,
                                               int lane, float beta, float gcoef) {
-  const int64_t ld = ts.cols;
+  const int64_t ld = ts.cols, step = quad_step(q, ld), o = c.base + quad_origin(q, lane, ld);
   const int col = (q & 1) ? kS - 1 - lane : lane;
-  const float* __restrict__ m = ts.dst + c.base;
-  const char* __restrict__ g = static_cast<const char*>(ts.aux) + c.base * (kBf16 ? 2 : 4);
+  const float* __restrict__ m = ts.dst + o;
+  const char* __restrict__ g = static_cast<const char*>(ts.aux) + o * (kBf16 ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    const int row = quad_row(q >> 1, i);
     float gv = 0.f, mv = 0.f;
-    if (kFull || (row < c.vr && col < c.vc)) {
-      gv = load_src<kBf16>(g, row * ld + col);
-      mv = stream_load(&m[row * ld + col]);
+    if (kFull || (quad_row(q >> 1, i) < c.vr && col < c.vc)) {
+      gv = load_src<kBf16>(g, i * step);
+      mv = stream_load(&m[i * step]);
     }
     x[i] = fmaf(beta, mv, gcoef * gv);
   }
@@ -477,11 +538,12 @@ __device__ __forceinline__ void load_quadrant(float (&x)[64], const TensorSlot& 
 template <bool kFull>
 __device__ __forceinline__ void store_quadrant(const float (&x)[64], float* __restrict__ dst, int64_t ld,
                                                const Chunk128& c, int q, int lane) {
+  const int64_t step = quad_step(q, ld);
   const int col = (q & 1) ? kS - 1 - lane : lane;
+  float* __restrict__ d = dst + quad_origin(q, lane, ld);
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    const int row = quad_row(q >> 1, i);
-    if (kFull || (row < c.vr && col < c.vc)) stream_store(x[i], &dst[row * ld + col]);
+    if (kFull || (quad_row(q >> 1, i) < c.vr && col < c.vc)) stream_store(x[i], &d[i * step]);
   }
 }
 
@@ -511,8 +573,11 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
   fwd_half(x, b);
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  topk128(x, p.keff2, w, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, scr);
-  if (!p.subtract_local) return;
+  const bool deferred = topk128(x, p.keff2, w, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, scr);
+  if (!p.subtract_local) {
+    if (deferred && w == 0) emit_kept(p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, scr);
+    return;
+  }
 
   inv_half(x, b);
   row_to_col(lds + w * kTile, x, lane);
@@ -523,6 +588,7 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
     store_quadrant<true>(x, mdst, ts.cols, c, w, lane);
   else
     store_quadrant<false>(x, mdst, ts.cols, c, w, lane);
+  if (deferred && w == 0) emit_kept(p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, scr);
 }
 
 // Lane pair (2g, 2g+1) holds chunk g of this wave's 32: x[e] = position 64h + e.
@@ -717,11 +783,20 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   // during the column pass and the butterfly exchange; with both targets the
   // momentum rows follow the exchange (registers)
   constexpr bool kEarlyM = kTargets == kToMomentum;
+  if (c.full) {
+    const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const int64_t off = int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col;
-    if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
-    if constexpr (kEarlyM) m[i] = stream_load(&mp[off]);
+    for (int i = 0; i < 64; ++i) {
+      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[o + i * step]);
+      if constexpr (kEarlyM) m[i] = stream_load(&mp[o + i * step]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int64_t off = int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col;
+      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
+      if constexpr (kEarlyM) m[i] = stream_load(&mp[off]);
+    }
   }
   inv_half(q, a);
   butterfly(q, reinterpret_cast<float*>(lds), w, lane);  // -> M* of quadrant w
@@ -736,8 +811,14 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   }
   if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
     if constexpr (!kEarlyM) {
+      if (c.full) {
+        const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
 #pragma unroll
-      for (int i = 0; i < 64; ++i) m[i] = stream_load(&mp[int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col]);
+        for (int i = 0; i < 64; ++i) m[i] = stream_load(&mp[o + i * step]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) m[i] = stream_load(&mp[int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 64; ++i) m[i] = fmaf(-p.alpha, q[i], m[i]);

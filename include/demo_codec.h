@@ -17,13 +17,14 @@
  *
  * Conventions for every call:
  *   - Tensors are dense, row-major, contiguous device buffers.  Matrices
- *     (ndim 2) are cut into 64x64 chunks, vectors (ndim 1) into 64-element
- *     chunks; trailing chunks are zero-padded for the transform and cropped
- *     on store.  Chunks are numbered tensor by tensor in list order,
- *     row-major inside a matrix.
+ *     (ndim 2) are cut into s x s chunks, vectors (ndim 1) into s-element
+ *     chunks, s = 64 (default) or 128 (DeMo summary §3.4 Tensor Chunking;
+ *     the extended results run both); trailing chunks are zero-padded for the
+ *     transform and cropped on store.  Chunks are numbered tensor by tensor in
+ *     list order, row-major inside a matrix.
  *   - A payload holds, for every chunk in that order, keff = min(k, chunk
  *     element count) entries: a float32 value array and a uint16 index array
- *     (index = u*64 + v inside a 64x64 chunk, u the dimension-0 frequency;
+ *     (index = u*s + v inside an s x s chunk, u the dimension-0 frequency;
  *     the frequency itself for a vector chunk), entries of a chunk in
  *     ascending index order.  demo_plan gives the entry count and offsets.
  *   - The caller owns every buffer.  Device pointers must be device memory of
@@ -50,7 +51,8 @@
 extern "C" {
 #endif
 
-#define DEMO_CHUNK 64        /* the only chunk size built (pages' default s = 64) */
+#define DEMO_CHUNK 64        /* default chunk edge s (the pages' default) */
+#define DEMO_CHUNK_LARGE 128 /* the other chunk edge built: DCT basis only, no one-bit download */
 #define DEMO_MAX_WORKERS 255 /* decode keeps per-coefficient contributor counts in 8 bits */
 #define DEMO_MAX_TENSORS_PER_LAUNCH 96 /* longer lists are split into several launches per call */
 
@@ -58,7 +60,7 @@ typedef enum demo_status {
   DEMO_OK = 0,
   DEMO_ERR_INVALID = 1, /* null pointer, unknown enum value, non-finite scalar */
   DEMO_ERR_SHAPE = 2,   /* ndim not 1 or 2, a zero or too large dimension */
-  DEMO_ERR_RANGE = 3,   /* k < 1, chunk != 64, workers outside 1..255, n < 0 */
+  DEMO_ERR_RANGE = 3,   /* k < 1, chunk not 64 or 128 (or 128 where not built), workers outside 1..255, n < 0 */
   DEMO_ERR_PAYLOAD = 4, /* payload entry count differs from the plan */
   DEMO_ERR_DEVICE = 5,  /* no gfx950 device, or the current device is not the context's */
   DEMO_ERR_HIP = 6,     /* a HIP runtime call or launch failed */
@@ -106,7 +108,7 @@ typedef struct demo_shape {
 } demo_shape;
 
 typedef struct demo_codec_cfg {
-  int32_t chunk;         /* chunk edge s; must be DEMO_CHUNK */
+  int32_t chunk;         /* chunk edge s: DEMO_CHUNK, or DEMO_CHUNK_LARGE with the DCT basis */
   int32_t k;             /* coefficients kept per chunk, >= 1; clamped to the chunk's element count */
   float beta;            /* momentum decay (DeMo summary §3.4 Decoupled Local Momentum Updates) */
   float alpha;           /* momentum-subtraction coefficient (§3.4 Momentum Subtraction) */
@@ -183,6 +185,7 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
 /* ---- One-bit download of the Signum variant (DeMo summary §3.4 Base Optimizer
  * Update: with phi = sign the server broadcasts only sign(M*), one bit per
  * parameter, and every worker applies it to its own copy of X).
+ * Built for chunk edge 64 (other chunk edges return DEMO_ERR_RANGE).
  * Packed-sign layout: uint64 words, chunk after chunk in the chunk order of the
  * payload.  A 64x64 chunk takes 64 words (word i = chunk row i, bit j = column
  * j), a 64-element vector chunk one word (bit j = element j).  A bit is set
