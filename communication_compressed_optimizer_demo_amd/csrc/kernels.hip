@@ -340,12 +340,9 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   // update, which then land while the payloads are averaged and
   // inverse-transformed.  Both sets of loads are issued without branches
   // (addresses clamped into the valid range, results of clamped lanes
-  // unused), so no wait separates them.  With both X and M to update the
-  // registers for early payloads would halve occupancy, so that form reads
-  // the payloads after its tensor loads.
-  constexpr bool kEarlyPayload = kTargets != (kToParams | kToMomentum);
+  // unused), so no wait separates them.
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  const bool one_batch = kEarlyPayload && p.keff2 <= 64 && p.workers <= kWorkerBatch;
+  const bool one_batch = p.keff2 <= 64 && p.workers <= kWorkerBatch;
   float val[kWorkerBatch];
   uint32_t ix[kWorkerBatch];
   if (one_batch) {
@@ -362,12 +359,15 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   float* __restrict__ xp = ts.dst + c.base;
   float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
   const uint32_t col = uint32_t(min(lane, c.vc - 1));
+  // with both targets the momentum rows are fetched after the transforms
+  // (registers: X, M and the transform together would halve occupancy)
+  constexpr bool kEarlyM = kTargets == kToMomentum;
   float x[64], m[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     const int64_t row = int64_t(min(i, c.vr - 1)) * ld;
     if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&(xp + row)[col]);
-    if constexpr ((kTargets & kToMomentum) != 0) m[i] = stream_load(&(mp + row)[col]);
+    if constexpr (kEarlyM) m[i] = stream_load(&(mp + row)[col]);
   }
 
   clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
@@ -401,6 +401,10 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
       store_rows<false>(x, xp, ld, c, lane);
   }
   if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
+    if constexpr (!kEarlyM) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) m[i] = stream_load(&(mp + int64_t(min(i, c.vr - 1)) * ld)[col]);
+    }
 #pragma unroll
     for (int i = 0; i < 64; ++i) m[i] = fmaf(-p.alpha, q[i], m[i]);
     if (c.full)
