@@ -1,9 +1,10 @@
 // HIP kernels of the DeMo codec for chunk edge s = 128 on CDNA4 (gfx950).
 //
 // The pages run DeMo with 64x64 and with 128x128 chunks ("DeMo: Decoupled
-// Momentum Optimization", summary §3.4 Tensor Chunking; extended results,
-// chunk size s = 64 vs s = 128).  The method is the same as for s = 64 (see
-// kernels.hip); only the transform length and the chunk size change.
+// Momentum Optimization", summary §3.4 Tensor Chunking; Ablation Studies and
+// Robustness Checks, chunk size s = 64 vs s = 128).  The method is the same
+// as for s = 64 (see kernels.hip); only the transform length and the chunk
+// size change.
 //
 // Transform.  The orthonormal 128-point DCT-II splits into two 64-point
 // halves: the even frequencies 2m are a 64-point DCT-II of the sums

@@ -19,7 +19,7 @@
  *   - Tensors are dense, row-major, contiguous device buffers.  Matrices
  *     (ndim 2) are cut into s x s chunks, vectors (ndim 1) into s-element
  *     chunks, s = 64 (default) or 128 (DeMo summary §3.4 Tensor Chunking;
- *     the extended results run both); trailing chunks are zero-padded for the
+ *     Ablation Studies, chunk size s = 64 vs 128); trailing chunks are zero-padded for the
  *     transform and cropped on store.  Chunks are numbered tensor by tensor in
  *     list order, row-major inside a matrix.
  *   - A payload holds, for every chunk in that order, keff = min(k, chunk

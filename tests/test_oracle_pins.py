@@ -505,3 +505,44 @@ def test_apply_signs_closed_forms_and_agreement_with_signum_decode():
     # zero M* (no coefficient kept anywhere) reads as +1
     z = O.apply_signs(X, O.pack_signs(np.zeros(X.shape)), eta=0.01, lam=0.0)
     assert np.all(np.abs(z - (X64 - 0.01)) <= np.spacing(np.abs(X64 - 0.01).astype(np.float32)))
+
+
+# --------------------------------------------------------------------------- chunk edge 128
+
+def test_chunk128_projection_matches_scipy_and_round_trips():
+    rng = _rng(50)
+    P = O.dct_basis(128)
+    B = rng.standard_normal((2, 128, 128))
+    Q = O.project(B, P, P)
+    assert np.abs(Q - scipy.fft.dctn(B, type=2, norm="ortho", axes=(1, 2))).max() < 1e-11
+    assert np.abs(O.unproject(Q, P, P) - B).max() < 1e-12
+    b = rng.standard_normal((3, 128))
+    assert np.abs(O.project(b, P, P) - scipy.fft.dct(b, type=2, norm="ortho", axis=1)).max() < 1e-12
+
+
+def test_chunk128_payload_sizes_printed_on_the_page():
+    gold = json.load(open(GOLDEN))
+    r = gold["chunk_size_payload_ratio"]
+    shapes = [(2048, 6144), (2048, 2048), (8192, 2048)]
+    for k in (1, 8, 32):
+        small = O.payload_entries(shapes, k, r["s_small"])
+        large = O.payload_entries(shapes, k, r["s_large"])
+        assert small == r["ratio"] * large
+    f = gold["chunk_size_fraction_kept"]
+    assert O.payload_entries([(f["s"], f["s"])], f["k"], f["s"]) == f["k"]
+    assert O.k_effective(10 ** 6, f["s"] * f["s"]) == f["numel"]
+
+
+def test_chunk128_encode_closed_forms():
+    """s = 128: lossless k with alpha = 1 leaves a zero residual; a single basis function is found
+    at its index u*128 + v and removed exactly by alpha = 1."""
+    rng = _rng(51)
+    G = rng.standard_normal((130, 300)).astype(np.float32)
+    out = O.encode(np.zeros_like(G), G, beta=0.5, alpha=1.0, k=128 * 128, s=128)
+    assert np.abs(out["M"]).max() <= 1e-6 * np.abs(G).max()
+    P = O.dct_basis(128)
+    blk = (np.outer(P[5], P[77]) * 3.0).astype(np.float32)
+    out = O.encode(np.zeros_like(blk), blk, beta=0.0, alpha=1.0, k=1, plain=True, s=128)
+    assert out["idx"].tolist() == [[5 * 128 + 77]]
+    assert abs(float(out["values"][0, 0]) - 3.0) < 1e-5
+    assert np.abs(out["M"]).max() < 1e-5
