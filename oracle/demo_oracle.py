@@ -34,6 +34,8 @@ the design doc with its reason):
   * ties in float32 magnitude go to the lower chunk-local index
     idx = u*s + v (u: dimension-0 frequency, v: dimension-1 frequency);
   * sign(0) = 0; weight decay uses the pre-update X on every tensor;
+  * Muon's phi acts on each whole tensor (a vector as one column) with the
+    caller's eps, the formula the pages print;
   * the one-bit download (``pack_signs``) sets a bit where M* < 0, so a
     zero reads as +1 there.
 
@@ -276,18 +278,39 @@ def aggregate(values: np.ndarray, idx: np.ndarray, numel: int, mode: str = "coun
     return out.reshape(n, numel)
 
 
-def phi_map(M: np.ndarray, phi: str) -> np.ndarray:
-    """[S] Base Optimizer Update: phi = sign (Signum) or identity (SGD); sign(0) = 0."""
+def phi_muon(M: np.ndarray, eps: float) -> np.ndarray:
+    """[S] Base Optimizer Update, Muon: phi(M) = M (M^T M + eps I)^(-1/2) on the whole tensor.
+
+    Computed through the smaller Gram matrix: for a wide M (rows <= cols)
+    (M M^T + eps I)^(-1/2) M, which is the same matrix (both equal
+    U diag(s / sqrt(s^2 + eps)) V^T for M = U diag(s) V^T).  The inverse
+    square root is taken from the symmetric eigendecomposition in float64.  A
+    vector is a one-column matrix: m / sqrt(m.m + eps).
+    """
+    M = np.asarray(M, dtype=F64)
+    if M.ndim == 1:
+        return M / np.sqrt(M @ M + float(eps))
+    wide = M.shape[0] <= M.shape[1]
+    G = M @ M.T if wide else M.T @ M
+    lam, V = np.linalg.eigh(G + float(eps) * np.eye(G.shape[0]))
+    inv_sqrt = (V / np.sqrt(lam)) @ V.T
+    return inv_sqrt @ M if wide else M @ inv_sqrt
+
+
+def phi_map(M: np.ndarray, phi: str, eps: float = 0.0) -> np.ndarray:
+    """[S] Base Optimizer Update: phi = sign (Signum), identity (SGD) or Muon; sign(0) = 0."""
     if phi == "sign":
         return np.sign(M)
     if phi == "identity":
         return M
+    if phi == "muon":
+        return phi_muon(M, eps)
     raise ValueError(phi)
 
 
 def decode_apply(X: np.ndarray, values: np.ndarray, idx: np.ndarray, *, phi: str, eta: float,
                  lam: float, mode: str = "count", P0: Optional[np.ndarray] = None,
-                 P1: Optional[np.ndarray] = None, s: int = 64) -> Dict[str, np.ndarray]:
+                 P1: Optional[np.ndarray] = None, s: int = 64, eps: float = 0.0) -> Dict[str, np.ndarray]:
     """Aggregate W payloads of one tensor, reconstruct M*, apply phi and the update.
 
     [S] Server-Side Aggregation and Momentum Reconstruction, Inverse DCT and
@@ -305,7 +328,7 @@ def decode_apply(X: np.ndarray, values: np.ndarray, idx: np.ndarray, *, phi: str
     cshape = (n, s) if X.ndim == 1 else (n, s, s)
     Mstar = merge_chunks(unproject(Qbar.reshape(cshape), P0, P1), X.shape, s)
     X64 = X.astype(F64)
-    X_new = X64 - float(eta) * (phi_map(Mstar, phi) + float(lam) * X64)
+    X_new = X64 - float(eta) * (phi_map(Mstar, phi, eps) + float(lam) * X64)
     return {"X": X_new.astype(F32), "Mstar": Mstar}
 
 

@@ -546,3 +546,41 @@ def test_chunk128_encode_closed_forms():
     assert out["idx"].tolist() == [[5 * 128 + 77]]
     assert abs(float(out["values"][0, 0]) - 3.0) < 1e-5
     assert np.abs(out["M"]).max() < 1e-5
+
+
+# --------------------------------------------------------------------------- phi = Muon
+
+@pytest.mark.parametrize("shape", [(7, 12), (12, 7), (9, 9), (1, 5), (5, 1)])
+def test_muon_phi_matches_svd_form(shape):
+    """M (M^T M + eps I)^(-1/2) = U diag(s / sqrt(s^2 + eps)) V^T, computed independently by SVD."""
+    rng = _rng(60)
+    M = rng.standard_normal(shape)
+    eps = 0.3
+    U, sv, Vt = np.linalg.svd(M, full_matrices=False)
+    ref = (U * (sv / np.sqrt(sv ** 2 + eps))) @ Vt
+    assert np.abs(O.phi_muon(M, eps) - ref).max() < 1e-12
+
+
+def test_muon_phi_limits_and_scaling():
+    rng = _rng(61)
+    M = rng.standard_normal((6, 10))
+    P = O.phi_muon(M, 0.0)                       # eps = 0: the polar factor, orthonormal rows
+    assert np.abs(P @ P.T - np.eye(6)).max() < 1e-12
+    c = 37.0                                     # phi(cM, c^2 eps) = phi(M, eps)
+    assert np.abs(O.phi_muon(c * M, c * c * 0.5) - O.phi_muon(M, 0.5)).max() < 1e-12
+    v = rng.standard_normal(11)                  # a vector is one column: m / sqrt(m.m + eps)
+    assert np.abs(O.phi_muon(v, 2.0) - v / np.sqrt(v @ v + 2.0)).max() < 1e-15
+    assert np.abs(O.phi_muon(v[:, None], 2.0)[:, 0] - O.phi_muon(v, 2.0)).max() < 1e-14
+    # large eps: phi ~ M / sqrt(eps)
+    assert np.abs(O.phi_muon(M, 1e12) * 1e6 - M).max() < 1e-6
+
+
+def test_muon_decode_apply_update():
+    rng = _rng(62)
+    X = rng.standard_normal((70, 90)).astype(np.float32)
+    G = rng.standard_normal((70, 90)).astype(np.float32)
+    o = O.encode(np.zeros_like(G), G, beta=0.5, alpha=0.2, k=4096)
+    d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="muon", eta=0.01, lam=0.1, eps=1e-3)
+    ref = X.astype(np.float64) - 0.01 * (O.phi_muon(d["Mstar"], 1e-3) + 0.1 * X.astype(np.float64))
+    assert np.all(np.abs(d["X"] - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
+    assert np.abs(d["Mstar"] - 0.5 * G.astype(np.float64)).max() < 1e-6  # lossless k: M* = M'
