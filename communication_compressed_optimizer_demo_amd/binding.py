@@ -87,6 +87,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp]
     lib.demo_apply_signs.restype = i32
     lib.demo_apply_signs.argtypes = [vp, i32, P(demo_shape), P(vp), i32, vp, i64, f32, f32, vp]
+    lib.demo_muon_workspace.restype = i32
+    lib.demo_muon_workspace.argtypes = [P(demo_shape), i32, P(i64)]
+    lib.demo_decode_apply_muon.restype = i32
+    lib.demo_decode_apply_muon.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32, vp, vp, i64, f32,
+                                           f32, f32, i32, i32, vp, i64, vp]
     _lib = lib
     return lib
 
@@ -292,6 +297,35 @@ def demo_apply_signs(ctx: int, params, signs, eta: float = 1e-3, lam: float = 0.
                                 signs.numel(), float(eta), float(lam), _stream_handle(stream)))
 
 
+def demo_muon_workspace(shapes: Sequence[Sequence[int]]) -> int:
+    """Bytes of device workspace demo_decode_apply_muon needs for a tensor list; host-only."""
+    lib = load_library()
+    out = ctypes.c_int64()
+    _check(lib.demo_muon_workspace(_shapes(shapes), len(shapes), ctypes.byref(out)))
+    return out.value
+
+
+def demo_decode_apply_muon(ctx: int, params, cfg: demo_codec_cfg, workers: int, pay_values, pay_idx, workspace,
+                           eta: float = 1e-3, lam: float = 0.0, eps: float = 1e-8, iters: int = 24,
+                           avg: int = DEMO_AVG_CONTRIBUTORS, stream=None) -> None:
+    """decode_apply with phi = Muon; ``workspace`` is a device buffer of demo_muon_workspace bytes."""
+    lib = load_library()
+    import torch
+    for x in params:
+        if x.dtype != torch.float32:
+            raise ValueError("parameters must be float32")
+    if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
+        raise ValueError("payload arrays must hold workers x entries elements")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    per = pay_values.numel() // workers
+    _check(lib.demo_decode_apply_muon(ctx, len(params), _shapes([tuple(x.shape) for x in params]),
+                                      _ptrs([_device_ptr(x, 4) for x in params]), ctypes.byref(cfg), int(workers),
+                                      _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per, float(eta),
+                                      float(lam), float(eps), int(iters), int(avg), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+
+
 class Codec:
     """A context bound to one device plus the codec configuration of a tensor list."""
 
@@ -360,3 +394,13 @@ class Codec:
 
     def apply_signs(self, params, signs, eta=1e-3, lam=0.0, stream=None) -> None:
         demo_apply_signs(self.ctx, params, signs, eta, lam, stream=stream)
+
+    def alloc_muon_workspace(self, device="cuda"):
+        """Device workspace of the Muon decode for this list (uint8 storage)."""
+        import torch
+        return torch.empty(demo_muon_workspace(self.shapes), dtype=torch.uint8, device=device)
+
+    def decode_apply_muon(self, params, workers, pay_values, pay_idx, workspace, eta=1e-3, lam=0.0, eps=1e-8,
+                          iters=24, avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
+        demo_decode_apply_muon(self.ctx, params, self.cfg(P0, P1), workers, pay_values, pay_idx, workspace, eta, lam,
+                               eps, iters, avg, stream)

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdemo_codec.so")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "kernels128.hip", "codec.cpp"]
+SOURCES = ["kernels.hip", "kernels128.hip", "kernels_muon.hip", "codec.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -3,6 +3,7 @@
 // the kernels themselves live in kernels.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -174,13 +175,14 @@ demo_status for_each_batch(const std::vector<TensorPlan>& plan, Fill&& fill, Lau
 demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                           float* const* moms, const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
                           const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
-                          demo_average avg, hipStream_t stream, uint64_t* signs = nullptr, int64_t n_words = 0) {
+                          demo_average avg, hipStream_t stream, uint64_t* signs = nullptr, int64_t n_words = 0,
+                          float* const* mstar = nullptr) {
   if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
   std::vector<TensorPlan> plan;
   int64_t entries = 0, words = 0;
   demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr, &words);
   if (s != DEMO_OK) return s;
-  const bool to_signs = params == nullptr && moms == nullptr;
+  const bool to_signs = params == nullptr && moms == nullptr && mstar == nullptr;
   if (to_signs && cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
   if (to_signs) {
     if (n_words != words)
@@ -226,10 +228,13 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   p.update_x = params != nullptr ? 1 : 0;
   p.update_m = moms != nullptr ? 1 : 0;
   p.pack_signs = to_signs ? 1 : 0;
+  p.write_mstar = mstar != nullptr ? 1 : 0;
   p.alpha = cfg->alpha;
   auto fill = [&](demo::TensorSlot& slot, size_t i) {
-    slot.aux = moms != nullptr ? static_cast<void*>(moms[i])
-                               : (to_signs ? static_cast<void*>(signs + plan[i].word_begin) : nullptr);
+    slot.aux = moms != nullptr    ? static_cast<void*>(moms[i])
+               : mstar != nullptr ? static_cast<void*>(mstar[i])
+               : to_signs         ? static_cast<void*>(signs + plan[i].word_begin)
+                                  : nullptr;
     slot.dst = params != nullptr ? params[i] : nullptr;
   };
   const int32_t S = cfg->chunk;
@@ -239,6 +244,34 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
     return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_decode128(t, p, stream); });
   return for_each_batch(plan, fill,
                         [&](const LaunchTable& t) { return demo::launch_decode(t, p, kind, p0, p1, stream); });
+}
+
+// Workspace of the Muon decode: M* of every tensor (offsets rounded up to 64
+// floats), then six n_max x n_max fp32 matrices for the Newton-Schulz
+// iteration (A, Y, Y', Z, Z', T), 256 doubles of partial sums and two floats.
+struct MuonLayout {
+  std::vector<int64_t> mstar;  // float offset of each tensor's M*
+  int64_t nmax = 0;
+  int64_t ns = 0, partial = 0, scal = 0, bytes = 0;  // float offsets / total bytes
+};
+
+MuonLayout muon_layout(const std::vector<TensorPlan>& plan) {
+  MuonLayout L;
+  int64_t off = 0;
+  for (const auto& t : plan) {
+    L.mstar.push_back(off);
+    off += (t.rows * t.cols + 63) / 64 * 64;
+    if (t.ndim == 2) L.nmax = std::max(L.nmax, std::min(t.rows, t.cols));
+  }
+  L.ns = off;
+  off += 6 * L.nmax * L.nmax;
+  off = (off + 63) / 64 * 64;
+  L.partial = off;
+  off += 2 * 256;  // 256 doubles
+  L.scal = off;
+  off += 64;
+  L.bytes = off * 4;
+  return L;
 }
 
 }  // namespace
@@ -403,6 +436,121 @@ demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes,
     slot.dst = params[i];
   };
   return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_apply_signs(t, p, stream); });
+}
+
+demo_status demo_muon_workspace(const demo_shape* shapes, int32_t n, int64_t* ws_bytes) {
+  std::vector<TensorPlan> plan;
+  const demo_status s = plan_list(shapes, n, kChunk, 1, &plan, nullptr, nullptr);
+  if (s != DEMO_OK) return s;
+  if (ws_bytes == nullptr) return fail(DEMO_ERR_INVALID, "ws_bytes is NULL");
+  *ws_bytes = muon_layout(plan).bytes;
+  return DEMO_OK;
+}
+
+demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                   const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                                   const uint16_t* pay_idx, int64_t n_entries, float eta, float lambda, float eps,
+                                   int32_t iters, demo_average avg, void* workspace, int64_t ws_bytes,
+                                   hipStream_t stream) {
+  if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
+  if (cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the Muon decode is built for chunk 64");
+  if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DEMO_ERR_INVALID, "eps must be finite and >= 0");
+  if (iters < 1 || iters > 64) return fail(DEMO_ERR_RANGE, "iters must be in 1..64");
+  std::vector<TensorPlan> plan;
+  demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, nullptr, nullptr);
+  if (s != DEMO_OK) return s;
+  const MuonLayout L = muon_layout(plan);
+  if (ws_bytes < L.bytes)
+    return fail(DEMO_ERR_RANGE, "workspace holds " + std::to_string(ws_bytes) + " bytes, the list needs " +
+                                    std::to_string(L.bytes));
+  if (L.bytes > 0 && workspace == nullptr) return fail(DEMO_ERR_INVALID, "workspace is NULL");
+  if (!aligned(workspace, 16)) return fail(DEMO_ERR_ALIGN, "workspace misaligned (16 bytes)");
+  float* ws = static_cast<float*>(workspace);
+  std::vector<float*> mstar(size_t(n > 0 ? n : 0));
+  for (int32_t i = 0; i < n; ++i) mstar[i] = ws + L.mstar[i];
+  // rows a7, a8: M* of every tensor into the workspace (validates the rest)
+  s = decode_common(ctx, n, shapes, nullptr, nullptr, cfg, workers, pay_values, pay_idx, n_entries, DEMO_PHI_IDENTITY,
+                    eta, lambda, avg, stream, nullptr, 0, mstar.data());
+  if (s != DEMO_OK) return s;
+  for (int32_t i = 0; i < n; ++i) {
+    if (params[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
+    if (!aligned(params[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
+  }
+  auto check = [&](hipError_t e) -> demo_status {
+    if (e != hipSuccess) return fail(DEMO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return DEMO_OK;
+  };
+  float* scal = ws + L.scal;
+  double* partial = reinterpret_cast<double*>(ws + L.partial);
+  for (int32_t i = 0; i < n; ++i) {
+    const TensorPlan& t = plan[i];
+    const float* Ms = mstar[i];
+    float* X = params[i];
+    if (t.ndim == 1) {
+      if ((s = check(demo::launch_muon_vector(Ms, X, t.rows, eps, eta, lambda, stream))) != DEMO_OK) return s;
+      continue;
+    }
+    const int32_t r = int32_t(t.rows), c = int32_t(t.cols);
+    const bool wide = r <= c;
+    const int32_t nn = wide ? r : c;
+    const int64_t sq = int64_t(nn) * nn;
+    float* A = ws + L.ns;
+    float *Y = A + sq, *Y2 = Y + sq, *Z = Y2 + sq, *Z2 = Z + sq, *T = Z2 + sq;
+    demo::GemmArgs g{};
+    // Gram: A = M M^T (wide) or M^T M
+    g.A = Ms;
+    g.B = Ms;
+    g.D = A;
+    g.M = g.N = nn;
+    g.K = wide ? c : r;
+    g.lda = g.ldb = c;
+    g.ldd = nn;
+    g.alpha = 1.f;
+    if ((s = check(demo::launch_gemm(g, !wide, wide, stream))) != DEMO_OK) return s;
+    if ((s = check(demo::launch_ns_prepare(A, nn, eps, partial, scal, Y, Z, stream))) != DEMO_OK) return s;
+    for (int32_t it = 0; it < iters; ++it) {
+      demo::GemmArgs h{};
+      h.M = h.N = h.K = nn;
+      h.lda = h.ldb = h.ldd = nn;
+      // T = 1.5 I - 0.5 Z Y
+      h.A = Z;
+      h.B = Y;
+      h.D = T;
+      h.alpha = -0.5f;
+      h.gamma = 1.5f;
+      if ((s = check(demo::launch_gemm(h, false, false, stream))) != DEMO_OK) return s;
+      h.gamma = 0.f;
+      h.alpha = 1.f;
+      h.A = Y;  // Y' = Y T
+      h.B = T;
+      h.D = Y2;
+      if ((s = check(demo::launch_gemm(h, false, false, stream))) != DEMO_OK) return s;
+      h.A = T;  // Z' = T Z
+      h.B = Z;
+      h.D = Z2;
+      if ((s = check(demo::launch_gemm(h, false, false, stream))) != DEMO_OK) return s;
+      std::swap(Y, Y2);
+      std::swap(Z, Z2);
+    }
+    // X = (1 - eta lambda) X - eta / sqrt(s) * (Z M  or  M Z), Z ~ (A + eps I)^(-1/2) sqrt(s)
+    demo::GemmArgs f{};
+    f.A = wide ? Z : Ms;
+    f.B = wide ? Ms : Z;
+    f.C = X;
+    f.D = X;
+    f.M = r;
+    f.N = c;
+    f.K = wide ? r : c;
+    f.lda = wide ? nn : c;
+    f.ldb = wide ? c : nn;
+    f.ldc = f.ldd = c;
+    f.alpha = -eta;
+    f.alpha_scale = scal + 1;
+    f.beta = 1.f - eta * lambda;
+    if ((s = check(demo::launch_gemm(f, false, false, stream))) != DEMO_OK) return s;
+  }
+  return DEMO_OK;
 }
 
 }  // extern "C"

@@ -45,10 +45,12 @@ __device__ __forceinline__ float sign_of(float m) { return m > 0.f ? 1.f : (m < 
 __device__ __forceinline__ void stream_store(uint64_t v, uint64_t* p) { __builtin_nontemporal_store(v, p); }
 
 // What a decode launch writes: the parameters, a momentum (aggregated
-// subtraction), both, or the packed sign of M* (one-bit download).
+// subtraction), both, the packed sign of M* (one-bit download), or M* itself
+// (Muon, whose phi needs whole tensors).
 constexpr int kToParams = 1;
 constexpr int kToMomentum = 2;
 constexpr int kToSigns = 4;
+constexpr int kToMstar = 8;
 
 __device__ __forceinline__ float update(float x, float m, const DecodeParams& p) {
   const float ph = p.phi_sign ? sign_of(m) : m;

@@ -412,6 +412,13 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
     else
       store_rows<false>(m, mp, ld, c, lane);
   }
+  if constexpr ((kTargets & kToMstar) != 0) {
+    float* __restrict__ sp = static_cast<float*>(ts.aux) + c.base;
+    if (c.full)
+      store_rows<true>(q, sp, ld, c, lane);
+    else
+      store_rows<false>(q, sp, ld, c, lane);
+  }
   if constexpr ((kTargets & kToSigns) != 0) {
     // Row i of the chunk is one ballot (bit j = lane j = column j), kept by
     // lane i; the 64 words go out as one coalesced 512-byte store.
@@ -457,6 +464,13 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
 #pragma unroll
     for (int c = 0; c < 64; ++c) {
       if (c * 64 < rem) stream_store(fmaf(-p.alpha, q[c], stream_load(&m[c * 64])), &m[c * 64]);
+    }
+  }
+  if constexpr ((kTargets & kToMstar) != 0) {
+    float* __restrict__ sp = static_cast<float*>(ts.aux) + first;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      if (c * 64 < rem) stream_store(q[c], &sp[c * 64]);
     }
   }
   if constexpr ((kTargets & kToSigns) != 0) {  // one word per vector chunk: chunk c's ballot goes to lane c
@@ -592,6 +606,8 @@ hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKin
   if (tab.items <= 0) return hipSuccess;
   if (p.pack_signs)
     launch_decode_targets<kToSigns>(tab, p, kind, basis_p0, basis_p1, stream);
+  else if (p.write_mstar)
+    launch_decode_targets<kToMstar>(tab, p, kind, basis_p0, basis_p1, stream);
   else if (p.update_x && p.update_m)
     launch_decode_targets<kToParams | kToMomentum>(tab, p, kind, basis_p0, basis_p1, stream);
   else if (p.update_m)

@@ -1,0 +1,243 @@
+// phi = Muon on CDNA4 (gfx950): phi(M) = M (M^T M + eps I)^(-1/2) on every
+// whole tensor ("DeMo: Decoupled Momentum Optimization", summary §3.4 Base
+// Optimizer Update, Muon), followed by X = X - eta (phi(M*) + lambda X).
+//
+// A matrix M (r x c, n = min(r, c)) goes through its smaller Gram matrix
+// A = M M^T (r <= c) or M^T M, n x n, since (M M^T + eps I)^(-1/2) M and
+// M (M^T M + eps I)^(-1/2) are the same matrix.  The inverse square root
+// comes from the coupled Newton-Schulz iteration
+//   Y0 = (A + eps I) / s,  Z0 = I,
+//   T = (3 I - Z Y) / 2,  Y <- Y T,  Z <- T Z,
+// with s = ||A + eps I||_F (so every eigenvalue of Y0 is in (0, 1]); Z then
+// converges to (A + eps I)^(-1/2) sqrt(s).  Every product is a dense fp32
+// GEMM on the matrix cores; the last one, Z M / sqrt(s) (or M Z / sqrt(s)),
+// carries the parameter update in its epilogue.  A vector is one column:
+// m / sqrt(m.m + eps).
+//
+// GEMM: 128 x 128 output tile per 256-thread workgroup, 2 x 2 waves of 64 x 64,
+// each wave 2 x 2 tiles of v_mfma_f32_32x32x2f32.  Operand layout of that
+// instruction: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the
+// accumulator holds D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v.
+// K advances 16 per LDS stage, double-buffered; global loads of the next
+// stage are issued before the current stage's MFMAs.
+#include "common.h"
+#include "launch.h"
+
+namespace demo {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 16, kPad = 4;
+
+template <bool kTA, bool kTB>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  __shared__ float As[2][kBK][kBM + kPad];
+  __shared__ float Bs[2][kBK][kBN + kPad];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int M = g.M, N = g.N, K = g.K;
+
+  float ra[8], rb[8];
+  // A(m, k): row-major M x K, or (kTA) the transpose of a row-major K x M matrix
+  auto load_a = [&](int k0) {
+    if constexpr (!kTA) {
+      const int m = m0 + (tid >> 1), kb = k0 + (tid & 1) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ra[q] = (m < M && kb + q < K) ? g.A[int64_t(m) * g.lda + kb + q] : 0.f;
+    } else {
+      const int k = k0 + (tid >> 4), mb = m0 + (tid & 15) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ra[q] = (k < K && mb + q < M) ? g.A[int64_t(k) * g.lda + mb + q] : 0.f;
+    }
+  };
+  // B(k, n): row-major K x N, or (kTB) the transpose of a row-major N x K matrix
+  auto load_b = [&](int k0) {
+    if constexpr (!kTB) {
+      const int k = k0 + (tid >> 4), nb = n0 + (tid & 15) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rb[q] = (k < K && nb + q < N) ? g.B[int64_t(k) * g.ldb + nb + q] : 0.f;
+    } else {
+      const int n = n0 + (tid >> 1), kb = k0 + (tid & 1) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rb[q] = (n < N && kb + q < K) ? g.B[int64_t(n) * g.ldb + kb + q] : 0.f;
+    }
+  };
+  auto store_ab = [&](int buf) {
+    if constexpr (!kTA) {
+      const int m = tid >> 1, kb = (tid & 1) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) As[buf][kb + q][m] = ra[q];
+    } else {
+      const int k = tid >> 4, mb = (tid & 15) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) As[buf][k][mb + q] = ra[q];
+    }
+    if constexpr (!kTB) {
+      const int k = tid >> 4, nb = (tid & 15) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Bs[buf][k][nb + q] = rb[q];
+    } else {
+      const int n = tid >> 1, kb = (tid & 1) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Bs[buf][kb + q][n] = rb[q];
+    }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = (K + kBK - 1) / kBK;
+  load_a(0);
+  load_b(0);
+  store_ab(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      load_a((kt + 1) * kBK);
+      load_b((kt + 1) * kBK);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK / 2; ++kk) {
+      const int kr = 2 * kk + (lane >> 5);
+      const float a0 = As[cur][kr][wm * 64 + (lane & 31)];
+      const float a1 = As[cur][kr][wm * 64 + 32 + (lane & 31)];
+      const float b0 = Bs[cur][kr][wn * 64 + (lane & 31)];
+      const float b1 = Bs[cur][kr][wn * 64 + 32 + (lane & 31)];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_ab(cur ^ 1);
+    __syncthreads();
+  }
+
+  // D = alpha * acc + beta * C + gamma * I (C may alias D: each element is
+  // read and written by the same lane)
+  const float alpha = g.alpha * (g.alpha_scale ? *g.alpha_scale : 1.f);
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+      const int col = n0 + wn * 64 + tj * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 64 + ti * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < M && col < N) {
+          float r = alpha * acc[ti][tj][v];
+          if (g.beta != 0.f) r = fmaf(g.beta, g.C[int64_t(row) * g.ldc + col], r);
+          if (row == col) r += g.gamma;
+          g.D[int64_t(row) * g.ldd + col] = r;
+        }
+      }
+    }
+  }
+}
+
+// ||A + eps I||_F^2, first level: per-block partial sums in float64 (a fixed
+// order, so the result does not change from run to run).
+constexpr int kNormBlocks = 256;
+
+__global__ __launch_bounds__(256) void fro_partial_kernel(const float* __restrict__ A, int n, float eps,
+                                                          double* __restrict__ partial) {
+  __shared__ double red[256];
+  const int64_t total = int64_t(n) * n;
+  double s = 0.0;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(kNormBlocks) * 256) {
+    double v = A[i];
+    if (i / n == i % n) v += eps;
+    s += v * v;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+// scal[0] = 1 / s, scal[1] = 1 / sqrt(s), s = ||A + eps I||_F
+__global__ __launch_bounds__(256) void fro_final_kernel(const double* __restrict__ partial,
+                                                        float* __restrict__ scal) {
+  __shared__ double red[256];
+  red[threadIdx.x] = threadIdx.x < kNormBlocks ? partial[threadIdx.x] : 0.0;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double s = sqrt(red[0]);
+    scal[0] = float(1.0 / s);
+    scal[1] = float(1.0 / sqrt(s));
+  }
+}
+
+// Y0 = (A + eps I) / s, Z0 = I
+__global__ __launch_bounds__(256) void ns_init_kernel(const float* __restrict__ A, int n, float eps,
+                                                      const float* __restrict__ scal, float* __restrict__ Y,
+                                                      float* __restrict__ Z) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(n) * n) return;
+  const bool diag = i / n == i % n;
+  Y[i] = (A[i] + (diag ? eps : 0.f)) * scal[0];
+  Z[i] = diag ? 1.f : 0.f;
+}
+
+// One vector: X = X - eta (m / sqrt(m.m + eps) + lambda X)
+__global__ __launch_bounds__(256) void muon_vector_kernel(const float* __restrict__ m, float* __restrict__ x,
+                                                          int64_t len, float eps, float eta, float lam) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < len; i += 256) s += double(m[i]) * double(m[i]);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float inv = float(1.0 / sqrt(red[0] + double(eps)));
+  for (int64_t i = threadIdx.x; i < len; i += 256) x[i] = fmaf(-eta, fmaf(lam, x[i], m[i] * inv), x[i]);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM), block(256);
+  if (!trans_a && !trans_b)
+    gemm_kernel<false, false><<<grid, block, 0, stream>>>(g);
+  else if (!trans_a && trans_b)
+    gemm_kernel<false, true><<<grid, block, 0, stream>>>(g);
+  else if (trans_a && !trans_b)
+    gemm_kernel<true, false><<<grid, block, 0, stream>>>(g);
+  else
+    gemm_kernel<true, true><<<grid, block, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_prepare(const float* A, int n, float eps, double* partial, float* scal, float* Y, float* Z,
+                             hipStream_t stream) {
+  fro_partial_kernel<<<kNormBlocks, 256, 0, stream>>>(A, n, eps, partial);
+  fro_final_kernel<<<1, 256, 0, stream>>>(partial, scal);
+  const int64_t total = int64_t(n) * n;
+  ns_init_kernel<<<dim3(unsigned((total + 255) / 256)), 256, 0, stream>>>(A, n, eps, scal, Y, Z);
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_vector(const float* m, float* x, int64_t len, float eps, float eta, float lam,
+                              hipStream_t stream) {
+  muon_vector_kernel<<<1, 256, 0, stream>>>(m, x, len, eps, eta, lam);
+  return hipGetLastError();
+}
+
+}  // namespace demo

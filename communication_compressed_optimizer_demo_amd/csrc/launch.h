@@ -21,7 +21,7 @@ constexpr int kMaxWorkers = 255;  // counts are kept in 8 bits
 
 struct TensorSlot {
   void* aux;            // encode: gradient (fp32 or bf16, read only); decode: momentum (in/out), the
-                        // tensor's packed sign words (out), or null; sign apply: sign words (in)
+                        // tensor's packed sign words or M* (out), or null; sign apply: sign words (in)
   float* dst;           // encode: momentum (in/out); decode, sign apply: parameters (in/out) or null
   int64_t entry_begin;  // payload entry of the tensor's first chunk
   int32_t rows;         // 2-D: dim 0; 1-D: length
@@ -65,6 +65,7 @@ struct DecodeParams {
   int32_t update_x;     // 1: X = X - eta (phi(M*) + lambda X)
   int32_t update_m;     // 1: M = M - alpha M* (aggregated subtraction)
   int32_t pack_signs;   // 1: write sign(M*) as bits (no parameter or momentum update)
+  int32_t write_mstar;  // 1: write M* itself (the Muon path applies phi afterwards)
   float alpha;
 };
 
@@ -82,6 +83,28 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream);
 hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream);
+// phi = Muon (kernels_muon.hip).  D = alpha * (*alpha_scale if given) *
+// op(A) op(B) + beta * C + gamma * I, fp32, row-major; op(A) is M x K (the
+// transpose of a row-major K x M matrix when trans_a), op(B) K x N.  C may
+// alias D.
+struct GemmArgs {
+  const float* A;
+  const float* B;
+  const float* C;
+  float* D;
+  int32_t M, N, K;
+  int64_t lda, ldb, ldc, ldd;
+  float alpha, beta, gamma;
+  const float* alpha_scale;
+};
+hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream);
+// partial: 256 doubles; scal: 2 floats (1/s, 1/sqrt(s)), s = ||A + eps I||_F;
+// Y = (A + eps I) / s, Z = I (all n x n)
+hipError_t launch_ns_prepare(const float* A, int n, float eps, double* partial, float* scal, float* Y, float* Z,
+                             hipStream_t stream);
+hipError_t launch_muon_vector(const float* m, float* x, int64_t len, float eps, float eta, float lam,
+                              hipStream_t stream);
+
 // Chunk edge 128 (kernels128.hip): DCT basis; a work item is one 128x128
 // chunk or 128 vector chunks, 256 threads each.
 hipError_t launch_encode128(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, hipStream_t stream);

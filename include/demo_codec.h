@@ -215,6 +215,30 @@ demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes,
                              int32_t chunk, const uint64_t* signs, int64_t n_words, float eta, float lambda,
                              hipStream_t stream);
 
+/* ---- phi = Muon (DeMo summary §3.4 Base Optimizer Update: phi(M) =
+ * M (M^T M + eps I)^(-1/2), Newton-Schulz normalization).  phi acts on each
+ * whole tensor, so the decode first writes M* of every tensor into a
+ * workspace; a matrix then goes through its smaller Gram matrix and the
+ * coupled Newton-Schulz iteration for the inverse square root (fp32 matrix
+ * cores), a vector (one column) through m / sqrt(m.m + eps).  Built for chunk
+ * edge 64. */
+
+/* Host-only: bytes of device workspace demo_decode_apply_muon needs for a list. */
+demo_status demo_muon_workspace(const demo_shape* shapes, int32_t n, int64_t* ws_bytes);
+
+/* demo_decode_apply with phi = Muon: X <- X - eta * (phi(M*) + lambda * X).
+ *   eps:       the eps of the formula (absolute), finite and >= 0
+ *   iters:     Newton-Schulz iterations, 1..64 (each costs three n x n x n
+ *              products, n the smaller dimension of the matrix)
+ *   workspace: device, at least demo_muon_workspace bytes, 16-byte aligned;
+ *              scratch owned by the caller, contents undefined afterwards
+ * Other arguments as for demo_decode_apply; cfg->chunk must be 64. */
+demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                   const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                                   const uint16_t* pay_idx, int64_t n_entries, float eta, float lambda, float eps,
+                                   int32_t iters, demo_average avg, void* workspace, int64_t ws_bytes,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -304,3 +304,42 @@ def test_chunk128_valid_arguments_reach_the_context_check(lib):
                                  None) == 3 and "chunk 64" in _msg(lib)
     nw = ctypes.c_int64()
     assert lib.demo_plan_signs(B._shapes(sh), 2, 128, ctypes.byref(nw), None) == 3
+
+
+# --------------------------------------------------------------------------- phi = Muon
+
+def test_muon_workspace_size(lib):
+    # M* of every tensor (64-float rounded), six n_max^2 matrices, 256 doubles, 64 floats
+    shapes = [(70, 90), (100,), (130, 200)]
+    mstar = (6336 + 128 + 26048)
+    ns = 6 * 130 * 130
+    want = (((mstar + ns) + 63) // 64 * 64 + 512 + 64) * 4
+    assert B.demo_muon_workspace(shapes) == want
+
+
+def _call_muon(lib, shapes, k=8, workers=2, eps=1e-6, iters=24, ws=0x7000, ws_bytes=None, chunk=64, params=0x1000,
+               eta=1e-3):
+    cfg = B.demo_codec_cfg(chunk, k, 0.9, 0.2, 0, 0, None, None, 0)
+    n = len(shapes)
+    if ws_bytes is None:
+        ws_bytes = B.demo_muon_workspace(shapes)
+    return lib.demo_decode_apply_muon(None, n, B._shapes(shapes), B._ptrs([params] * n), ctypes.byref(cfg), workers,
+                                      0x3000, 0x4000, O.payload_entries(shapes, k), eta, 0.0, eps, iters, 0, ws,
+                                      ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(), 1, "context"),
+    (dict(eps=-1.0), 1, "eps"),
+    (dict(eps=float("nan")), 1, "eps"),
+    (dict(iters=0), 3, "iters"),
+    (dict(iters=65), 3, "iters"),
+    (dict(ws_bytes=16), 3, "workspace"),
+    (dict(ws=0), 1, "workspace is NULL"),
+    (dict(ws=0x7004), 7, "misaligned"),
+    (dict(chunk=128), 3, "chunk 64"),
+    (dict(workers=0), 3, "workers"),
+])
+def test_muon_arguments(lib, kw, status, text):
+    assert _call_muon(lib, [(70, 90), (100,)], **kw) == status
+    assert text in _msg(lib)
