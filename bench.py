@@ -32,6 +32,7 @@ import demo_inputs as DI  # noqa: E402
 
 METRIC = "params/s for encode+decode/apply per step; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "communication_compressed_optimizer_demo_amd", "csrc")
 COPY_PROBE_BYTES = 1 << 30
@@ -54,6 +55,9 @@ def parse():
                     help="momentum subtraction of the worker's own coefficients, or of the averaged ones")
     ap.add_argument("--chunk", type=int, default=64, choices=(64, 128),
                     help="chunk edge s (128: DCT basis, apply download)")
+    ap.add_argument("--phi", default=None, choices=("muon",),
+                    help="override the workload's phi: muon runs decode + Newton-Schulz phi on every whole tensor")
+    ap.add_argument("--muon-iters", type=int, default=24, help="Newton-Schulz iterations of the Muon phi")
     ap.add_argument("--download", default="apply", choices=("apply", "signs"),
                     help="apply: decode/apply in one kernel; signs: the Signum variant's one-bit download, "
                          "decode to packed sign bits then apply them (phi = sign)")
@@ -235,8 +239,20 @@ def hbm_probe(w: DI.Workload):
     return out
 
 
+def muon_flops(shapes, iters: int) -> int:
+    """Matrix-core flops of one Muon decode: Gram, 3 n^3 products per iteration, final product."""
+    total = 0
+    for s in shapes:
+        if len(s) != 2:
+            continue
+        r, c = s
+        n, k = min(r, c), max(r, c)
+        total += 2 * n * n * k + iters * 3 * 2 * n ** 3 + 2 * r * c * n
+    return total
+
+
 def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False, basis: str = "dct",
-              subtraction: str = "local", download: str = "apply", chunk: int = 64):
+              subtraction: str = "local", download: str = "apply", chunk: int = 64, muon_iters: int = 0):
     import torch
 
     from communication_compressed_optimizer_demo_amd import binding as B
@@ -281,12 +297,19 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     phi = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
     stream = torch.cuda.current_stream()
     signs = codec.alloc_signs() if download == "signs" else None
+    muon_ws = codec.alloc_muon_workspace() if muon_iters else None
+    # Muon's eps does not change the work (a fixed iteration count); 1e-12 sits below the
+    # Gram eigenvalues of these M*
+    muon_eps = 1e-12
 
     # the step's calls in order; HIP events between them time each one
     calls = [("encode", lambda: codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream))]
     if download == "signs":  # server: packed sign(M*); worker: apply the bits
         calls.append(("decode", lambda: codec.decode_signs(W, vals, pidx, signs, stream=stream)))
         calls.append(("apply", lambda: codec.apply_signs(X, signs, w.eta, w.lam, stream=stream)))
+    elif muon_iters:
+        calls.append(("decode", lambda: codec.decode_apply_muon(X, W, vals, pidx, muon_ws, w.eta, w.lam, muon_eps,
+                                                                muon_iters, stream=stream)))
     elif aggregated:  # this worker's parameters and momentum, one pass
         calls.append(("decode", lambda: codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam,
                                                                     stream=stream)))
@@ -328,26 +351,31 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
         ms = per[name]
         kern[name] = {"ms": round(ms, 4), "launches": launches, "algorithmic_bytes": int(b),
                       "GBps": round(b / ms / 1e6, 1), "params": numel}
+    if muon_iters:
+        fl = muon_flops(shapes, muon_iters)
+        kern["decode"]["mfma_flops"] = fl
+        kern["decode"]["TFLOPs"] = round(fl / per["decode"] / 1e9, 2)
     dom = max(kern, key=lambda n: kern[n]["ms"])
     dk = kern[dom]
     achieved = dk["algorithmic_bytes"] / dk["ms"] / 1e6
     total_bytes = sum(k["algorithmic_bytes"] for k in kern.values())
     ms_per_step = elapsed / steps * 1e3
+    if muon_iters:  # the Muon decode is a chain of fp32 matrix-core products
+        roof = {"bound": "mfma", "kernel": "decode", "achieved": dk["TFLOPs"], "peak": FP32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dk["TFLOPs"] / FP32_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4)}
     return {
         "ms_per_step": ms_per_step,
         "value": w.n_params / (ms_per_step / 1e3),
         "step_GBps": total_bytes / (ms_per_step / 1e3) / 1e9,
         "kernels": kern,
         "roofline": {
-            "bound": "hbm",
-            "kernel": dom,
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            **roof,
             "traffic": (_traffic(f"{dom}_kernel", w.name)
                         if launches == 1 and basis == "dct" and subtraction == "local" and download == "apply"
-                        and chunk == 64 else None),
+                        and chunk == 64 and not muon_iters else None),
         },
     }
 
@@ -369,14 +397,19 @@ def main():
     if args.chunk == 128 and (args.basis != "dct" or args.download != "apply"):
         print("--chunk 128 is built for the DCT basis and the apply download", file=sys.stderr)
         sys.exit(2)
+    if args.phi == "muon":
+        if args.download != "apply" or args.subtraction != "local" or args.chunk != 64:
+            print("--phi muon runs with the apply download, the local subtraction and chunk 64", file=sys.stderr)
+            sys.exit(2)
+        w = w.replace(phi="muon")
     if args.download == "signs":
         if args.subtraction != "local":
             print("--download signs pairs with the local subtraction only", file=sys.stderr)
             sys.exit(2)
         w = w.replace(phi="sign")  # the one-bit download exists for the Signum variant only
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu = None if args.no_cpu_baseline or args.phi else cpu_baseline(w)
     g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction, args.download,
-                  args.chunk)
+                  args.chunk, args.muon_iters if args.phi == "muon" else 0)
     line = {
         "metric": METRIC,
         "value": g["value"],
@@ -406,6 +439,7 @@ def main():
             "basis": args.basis,
             "subtraction": args.subtraction,
             "download": args.download,
+            **({"muon_iters": args.muon_iters} if args.phi == "muon" else {}),
         },
         "step_GBps": round(g["step_GBps"], 1),
         "kernels": g["kernels"],

@@ -18,7 +18,7 @@
 // each wave 2 x 2 tiles of v_mfma_f32_32x32x2f32.  Operand layout of that
 // instruction: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the
 // accumulator holds D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v.
-// K advances 16 per LDS stage, double-buffered; global loads of the next
+// K advances kBK per LDS stage, double-buffered; global loads of the next
 // stage are issued before the current stage's MFMAs.
 #include "common.h"
 #include "launch.h"
@@ -28,68 +28,72 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 16, kPad = 4;
+constexpr int kBK = 16, kPad = 4;
 
-template <bool kTA, bool kTB>
+// kT: workgroup tile edge (128 or 64); the four waves form a 2 x 2 grid of
+// kT/2 x kT/2 wave tiles, each (kT/64) x (kT/64) MFMA tiles of 32 x 32.
+template <bool kTA, bool kTB, int kT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  __shared__ float As[2][kBK][kBM + kPad];
-  __shared__ float Bs[2][kBK][kBN + kPad];
+  constexpr int E = kT / 16;    // floats each thread stages per operand and K stage
+  constexpr int kMT = kT / 64;  // MFMA tiles per wave and dimension
+  __shared__ float As[2][kBK][kT + kPad];
+  __shared__ float Bs[2][kBK][kT + kPad];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   const int M = g.M, N = g.N, K = g.K;
 
-  float ra[8], rb[8];
-  // A(m, k): row-major M x K, or (kTA) the transpose of a row-major K x M matrix
+  // Staging: E consecutive elements per thread, along K for an operand whose
+  // rows run along M (N), along M (N) for a transposed one.
+  float ra[E], rb[E];
   auto load_a = [&](int k0) {
-    if constexpr (!kTA) {
-      const int m = m0 + (tid >> 1), kb = k0 + (tid & 1) * 8;
+    if constexpr (!kTA) {  // A row-major M x K
+      const int m = m0 + tid / (16 / E), kb = k0 + (tid % (16 / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) ra[q] = (m < M && kb + q < K) ? g.A[int64_t(m) * g.lda + kb + q] : 0.f;
-    } else {
-      const int k = k0 + (tid >> 4), mb = m0 + (tid & 15) * 8;
+      for (int q = 0; q < E; ++q) ra[q] = (m < M && kb + q < K) ? g.A[int64_t(m) * g.lda + kb + q] : 0.f;
+    } else {  // A = S^T, S row-major K x M
+      const int k = k0 + tid / (kT / E), mb = m0 + (tid % (kT / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) ra[q] = (k < K && mb + q < M) ? g.A[int64_t(k) * g.lda + mb + q] : 0.f;
+      for (int q = 0; q < E; ++q) ra[q] = (k < K && mb + q < M) ? g.A[int64_t(k) * g.lda + mb + q] : 0.f;
     }
   };
-  // B(k, n): row-major K x N, or (kTB) the transpose of a row-major N x K matrix
   auto load_b = [&](int k0) {
-    if constexpr (!kTB) {
-      const int k = k0 + (tid >> 4), nb = n0 + (tid & 15) * 8;
+    if constexpr (!kTB) {  // B row-major K x N
+      const int k = k0 + tid / (kT / E), nb = n0 + (tid % (kT / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rb[q] = (k < K && nb + q < N) ? g.B[int64_t(k) * g.ldb + nb + q] : 0.f;
-    } else {
-      const int n = n0 + (tid >> 1), kb = k0 + (tid & 1) * 8;
+      for (int q = 0; q < E; ++q) rb[q] = (k < K && nb + q < N) ? g.B[int64_t(k) * g.ldb + nb + q] : 0.f;
+    } else {  // B = S^T, S row-major N x K
+      const int n = n0 + tid / (16 / E), kb = k0 + (tid % (16 / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rb[q] = (n < N && kb + q < K) ? g.B[int64_t(n) * g.ldb + kb + q] : 0.f;
+      for (int q = 0; q < E; ++q) rb[q] = (n < N && kb + q < K) ? g.B[int64_t(n) * g.ldb + kb + q] : 0.f;
     }
   };
   auto store_ab = [&](int buf) {
     if constexpr (!kTA) {
-      const int m = tid >> 1, kb = (tid & 1) * 8;
+      const int m = tid / (16 / E), kb = (tid % (16 / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) As[buf][kb + q][m] = ra[q];
+      for (int q = 0; q < E; ++q) As[buf][kb + q][m] = ra[q];
     } else {
-      const int k = tid >> 4, mb = (tid & 15) * 8;
+      const int k = tid / (kT / E), mb = (tid % (kT / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) As[buf][k][mb + q] = ra[q];
+      for (int q = 0; q < E; ++q) As[buf][k][mb + q] = ra[q];
     }
     if constexpr (!kTB) {
-      const int k = tid >> 4, nb = (tid & 15) * 8;
+      const int k = tid / (kT / E), nb = (tid % (kT / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) Bs[buf][k][nb + q] = rb[q];
+      for (int q = 0; q < E; ++q) Bs[buf][k][nb + q] = rb[q];
     } else {
-      const int n = tid >> 1, kb = (tid & 1) * 8;
+      const int n = tid / (16 / E), kb = (tid % (16 / E)) * E;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) Bs[buf][kb + q][n] = rb[q];
+      for (int q = 0; q < E; ++q) Bs[buf][kb + q][n] = rb[q];
     }
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[kMT][kMT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kMT; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -107,14 +111,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 2; ++kk) {
       const int kr = 2 * kk + (lane >> 5);
-      const float a0 = As[cur][kr][wm * 64 + (lane & 31)];
-      const float a1 = As[cur][kr][wm * 64 + 32 + (lane & 31)];
-      const float b0 = Bs[cur][kr][wn * 64 + (lane & 31)];
-      const float b1 = Bs[cur][kr][wn * 64 + 32 + (lane & 31)];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      float a[kMT], b[kMT];
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) {
+        a[t] = As[cur][kr][wm * (kT / 2) + t * 32 + (lane & 31)];
+        b[t] = Bs[cur][kr][wn * (kT / 2) + t * 32 + (lane & 31)];
+      }
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kMT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) store_ab(cur ^ 1);
     __syncthreads();
@@ -124,13 +130,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // read and written by the same lane)
   const float alpha = g.alpha * (g.alpha_scale ? *g.alpha_scale : 1.f);
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
+  for (int ti = 0; ti < kMT; ++ti) {
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj) {
-      const int col = n0 + wn * 64 + tj * 32 + (lane & 31);
+    for (int tj = 0; tj < kMT; ++tj) {
+      const int col = n0 + wn * (kT / 2) + tj * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + ti * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int row = m0 + wm * (kT / 2) + ti * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < M && col < N) {
           float r = alpha * acc[ti][tj][v];
           if (g.beta != 0.f) r = fmaf(g.beta, g.C[int64_t(row) * g.ldc + col], r);
@@ -209,19 +215,30 @@ __global__ __launch_bounds__(256) void muon_vector_kernel(const float* __restric
   for (int64_t i = threadIdx.x; i < len; i += 256) x[i] = fmaf(-eta, fmaf(lam, x[i], m[i] * inv), x[i]);
 }
 
+template <int kT>
+void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream) {
+  const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT), block(256);
+  if (!trans_a && !trans_b)
+    gemm_kernel<false, false, kT><<<grid, block, 0, stream>>>(g);
+  else if (!trans_a && trans_b)
+    gemm_kernel<false, true, kT><<<grid, block, 0, stream>>>(g);
+  else if (trans_a && !trans_b)
+    gemm_kernel<true, false, kT><<<grid, block, 0, stream>>>(g);
+  else
+    gemm_kernel<true, true, kT><<<grid, block, 0, stream>>>(g);
+}
+
 }  // namespace
 
+// 128 x 128 workgroup tiles when they give at least one workgroup per CU,
+// 64 x 64 tiles otherwise (n x n products with n < 2048 on 256 CUs).
 hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM), block(256);
-  if (!trans_a && !trans_b)
-    gemm_kernel<false, false><<<grid, block, 0, stream>>>(g);
-  else if (!trans_a && trans_b)
-    gemm_kernel<false, true><<<grid, block, 0, stream>>>(g);
-  else if (trans_a && !trans_b)
-    gemm_kernel<true, false><<<grid, block, 0, stream>>>(g);
+  const int64_t big = int64_t((g.M + 127) / 128) * ((g.N + 127) / 128);
+  if (big >= 256)
+    launch_gemm_tile<128>(g, trans_a, trans_b, stream);
   else
-    gemm_kernel<true, true><<<grid, block, 0, stream>>>(g);
+    launch_gemm_tile<64>(g, trans_a, trans_b, stream);
   return hipGetLastError();
 }
 
