@@ -385,6 +385,45 @@ def apply_signs(X: np.ndarray, words: np.ndarray, *, eta: float, lam: float, s: 
 
 
 # ---------------------------------------------------------------------------
+# compact wire format: bfloat16 values, 12-bit indices
+# ---------------------------------------------------------------------------
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, rounding to nearest with ties to even (finite inputs)."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=F32)).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def pack_wire(values: np.ndarray, idx: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """A worker's payload as sent: [T] ("Training over Slow Links", top-k and DeMo
+    slides) counts a kept value as 2 bytes of bfloat16 plus its position, and a
+    64x64 chunk position needs 12 bits.  Values become bfloat16 (uint16 bits,
+    entry order kept); indices are packed two to three bytes: entries 2p and
+    2p+1 give bytes (i0 & 0xFF, (i0 >> 8) | (i1 & 0xF) << 4, i1 >> 4), an odd
+    last entry paired with 0."""
+    v = bf16_bits(np.asarray(values, dtype=F32).ravel())
+    i = np.asarray(idx).ravel().astype(np.uint32)
+    if np.any(i >= 4096):
+        raise ValueError("12-bit indices")
+    if i.size % 2:
+        i = np.concatenate([i, np.zeros(1, np.uint32)])
+    i0, i1 = i[0::2], i[1::2]
+    b = np.stack([i0 & 0xFF, (i0 >> 8) | ((i1 & 0xF) << 4), i1 >> 4], axis=1).astype(np.uint8)
+    return v, b.ravel()
+
+
+def unpack_wire(wv: np.ndarray, wi: np.ndarray, n: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Inverse of pack_wire for n entries: float32 values (bfloat16 widened) and indices."""
+    vals = (np.asarray(wv, dtype=np.uint16)[:n].astype(np.uint32) << 16).view(F32)
+    b = np.asarray(wi, dtype=np.uint8).reshape(-1, 3).astype(np.uint32)
+    i0 = b[:, 0] | ((b[:, 1] & 0xF) << 8)
+    i1 = (b[:, 1] >> 4) | (b[:, 2] << 4)
+    idx = np.stack([i0, i1], axis=1).ravel()[:n].astype(np.uint16)
+    return vals, idx
+
+
+# ---------------------------------------------------------------------------
 # payload accounting
 # ---------------------------------------------------------------------------
 

@@ -584,3 +584,31 @@ def test_muon_decode_apply_update():
     ref = X.astype(np.float64) - 0.01 * (O.phi_muon(d["Mstar"], 1e-3) + 0.1 * X.astype(np.float64))
     assert np.all(np.abs(d["X"] - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
     assert np.abs(d["Mstar"] - 0.5 * G.astype(np.float64)).max() < 1e-6  # lossless k: M* = M'
+
+
+# --------------------------------------------------------------------------- compact wire format
+
+def test_wire_format_hand_built():
+    one = np.float32(1.0)
+    v = np.array([1.0, -2.5, one + np.float32(2.0 ** -8), one + np.float32(3 * 2.0 ** -8), 0.0], np.float32)
+    # 1 + 2^-8 is a tie between 0x3F80 and 0x3F81: even wins; 1 + 3*2^-8 ties 0x3F81 / 0x3F82: even wins
+    wv, wi = O.pack_wire(v, np.array([0x123, 0xABC, 0xFFF, 0, 7]))
+    assert wv.tolist() == [0x3F80, 0xC020, 0x3F80, 0x3F82, 0x0000]
+    assert wi.tolist() == [0x23, 0xC1, 0xAB, 0xFF, 0x0F, 0x00, 0x07, 0x00, 0x00]
+    vals, idx = O.unpack_wire(wv, wi, 5)
+    assert idx.tolist() == [0x123, 0xABC, 0xFFF, 0, 7]
+    assert vals.tolist() == [1.0, -2.5, 1.0, 1.0 + 2 * 2.0 ** -7, 0.0]
+
+
+def test_wire_format_round_trip_and_rounding_bound():
+    rng = _rng(70)
+    v = (rng.standard_normal(1001) * 1e-3).astype(np.float32)
+    i = rng.integers(0, 4096, 1001)
+    wv, wi = O.pack_wire(v, i)
+    assert wi.size == 3 * 501
+    vals, idx = O.unpack_wire(wv, wi, 1001)
+    assert np.array_equal(idx, i.astype(np.uint16))
+    # round to nearest: at most half a bfloat16 ulp (2^-8 relative) away
+    assert np.all(np.abs(vals - v) <= np.abs(v) * 2.0 ** -8)
+    with pytest.raises(ValueError):
+        O.pack_wire(v[:2], np.array([1, 4096]))
