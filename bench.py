@@ -58,9 +58,11 @@ def parse():
     ap.add_argument("--phi", default=None, choices=("muon",),
                     help="override the workload's phi: muon runs decode + Newton-Schulz phi on every whole tensor")
     ap.add_argument("--muon-iters", type=int, default=24, help="Newton-Schulz iterations of the Muon phi")
-    ap.add_argument("--download", default="apply", choices=("apply", "signs"),
+    ap.add_argument("--download", default="apply", choices=("apply", "signs", "wire"),
                     help="apply: decode/apply in one kernel; signs: the Signum variant's one-bit download, "
-                         "decode to packed sign bits then apply them (phi = sign)")
+                         "decode to packed sign bits then apply them (phi = sign); wire: this worker's payload "
+                         "packed into the compact wire format (bfloat16 values, 12-bit indices), the decode "
+                         "reading all W payloads in that format")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one untimed 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -297,6 +299,11 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     phi = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
     stream = torch.cuda.current_stream()
     signs = codec.alloc_signs() if download == "signs" else None
+    if download == "wire":  # the other workers' payloads arrive packed; this worker packs its own in the step
+        wv, wi = codec.alloc_wire(W)
+        wb = B.demo_wire_size(ne)[1]
+        codec.pack_wire(W, vals, pidx, wv, wi)
+        torch.cuda.synchronize()
     muon_ws = codec.alloc_muon_workspace() if muon_iters else None
     # Muon's eps does not change the work (a fixed iteration count); 1e-12 sits below the
     # Gram eigenvalues of these M*
@@ -307,6 +314,9 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     if download == "signs":  # server: packed sign(M*); worker: apply the bits
         calls.append(("decode", lambda: codec.decode_signs(W, vals, pidx, signs, stream=stream)))
         calls.append(("apply", lambda: codec.apply_signs(X, signs, w.eta, w.lam, stream=stream)))
+    elif download == "wire":
+        calls.append(("pack", lambda: codec.pack_wire(1, vals[:ne], pidx[:ne], wv[:ne], wi[:wb], stream=stream)))
+        calls.append(("decode", lambda: codec.decode_apply_wire(X, W, wv, wi, phi, w.eta, w.lam, stream=stream)))
     elif muon_iters:
         calls.append(("decode", lambda: codec.decode_apply_muon(X, W, vals, pidx, muon_ws, w.eta, w.lam, muon_eps,
                                                                 muon_iters, stream=stream)))
@@ -345,6 +355,9 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     if download == "signs":
         algo["decode"] = W * ne * 6 + codec.n_sign_words * 8  # W payloads read, packed signs written
         algo["apply"] = numel * 8 + codec.n_sign_words * 8    # X read and written, packed signs read
+    elif download == "wire":
+        algo["pack"] = ne * 6 + ne * 2 + wb                   # own payload read, wire values and indices written
+        algo["decode"] = numel * 8 + W * (ne * 2 + wb)        # X read and written, W wire payloads read
     else:
         algo["decode"] = numel * (16 if aggregated else 8) + W * ne * 6  # X (and M) read and written, W payloads
     for name, b in algo.items():
@@ -402,6 +415,9 @@ def main():
             print("--phi muon runs with the apply download, the local subtraction and chunk 64", file=sys.stderr)
             sys.exit(2)
         w = w.replace(phi="muon")
+    if args.download == "wire" and (args.subtraction != "local" or args.chunk != 64):
+        print("--download wire runs with the local subtraction and chunk 64", file=sys.stderr)
+        sys.exit(2)
     if args.download == "signs":
         if args.subtraction != "local":
             print("--download signs pairs with the local subtraction only", file=sys.stderr)

@@ -92,6 +92,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.demo_decode_apply_muon.restype = i32
     lib.demo_decode_apply_muon.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32, vp, vp, i64, f32,
                                            f32, f32, i32, i32, vp, i64, vp]
+    lib.demo_wire_size.restype = i32
+    lib.demo_wire_size.argtypes = [i64, P(i64), P(i64)]
+    lib.demo_pack_wire.restype = i32
+    lib.demo_pack_wire.argtypes = [vp, i32, vp, vp, i64, vp, vp, vp]
+    lib.demo_decode_apply_wire.restype = i32
+    lib.demo_decode_apply_wire.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32,
+                                           vp, vp, i64, i32, f32, f32, i32, vp]
     _lib = lib
     return lib
 
@@ -326,6 +333,50 @@ def demo_decode_apply_muon(ctx: int, params, cfg: demo_codec_cfg, workers: int, 
                                       workspace.numel() * workspace.element_size(), _stream_handle(stream)))
 
 
+def demo_wire_size(n_entries: int) -> Tuple[int, int]:
+    """(value bytes, index bytes) of one worker's wire payload of n_entries entries; host-only."""
+    lib = load_library()
+    vb, ib = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.demo_wire_size(int(n_entries), ctypes.byref(vb), ctypes.byref(ib)))
+    return vb.value, ib.value
+
+
+def demo_pack_wire(ctx: int, workers: int, pay_values, pay_idx, wire_values, wire_idx, stream=None) -> None:
+    """``workers`` payloads (worker-major) -> wire values (int16 storage) and wire index bytes (uint8)."""
+    lib = load_library()
+    if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
+        raise ValueError("payload arrays must hold workers x entries elements")
+    per = pay_values.numel() // workers
+    vb, ib = demo_wire_size(per)
+    if wire_values.numel() * wire_values.element_size() != workers * vb:
+        raise ValueError("wire value buffer must hold workers x entries 16-bit values")
+    if wire_idx.numel() * wire_idx.element_size() != workers * ib:
+        raise ValueError("wire index buffer must hold workers x demo_wire_size index bytes")
+    _check(lib.demo_pack_wire(ctx, int(workers), _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per,
+                              _device_ptr(wire_values, 2), _device_ptr(wire_idx, wire_idx.element_size()), _stream_handle(stream)))
+
+
+def demo_decode_apply_wire(ctx: int, params, cfg: demo_codec_cfg, workers: int, wire_values, wire_idx,
+                           phi: int = DEMO_PHI_SIGN, eta: float = 1e-3, lam: float = 0.0,
+                           avg: int = DEMO_AVG_CONTRIBUTORS, stream=None) -> None:
+    """demo_decode_apply reading ``workers`` wire payloads (worker-major)."""
+    lib = load_library()
+    import torch
+    for x in params:
+        if x.dtype != torch.float32:
+            raise ValueError("parameters must be float32")
+    if wire_values.element_size() != 2 or wire_values.numel() % workers:
+        raise ValueError("wire values must hold workers x entries 16-bit values")
+    per = wire_values.numel() // workers
+    _, ib = demo_wire_size(per)
+    if wire_idx.numel() * wire_idx.element_size() != workers * ib:
+        raise ValueError("wire index buffer must hold workers x demo_wire_size index bytes")
+    _check(lib.demo_decode_apply_wire(ctx, len(params), _shapes([tuple(x.shape) for x in params]),
+                                      _ptrs([_device_ptr(x, 4) for x in params]), ctypes.byref(cfg), int(workers),
+                                      _device_ptr(wire_values, 2), _device_ptr(wire_idx, wire_idx.element_size()), per, int(phi),
+                                      float(eta), float(lam), int(avg), _stream_handle(stream)))
+
+
 class Codec:
     """A context bound to one device plus the codec configuration of a tensor list."""
 
@@ -394,6 +445,22 @@ class Codec:
 
     def apply_signs(self, params, signs, eta=1e-3, lam=0.0, stream=None) -> None:
         demo_apply_signs(self.ctx, params, signs, eta, lam, stream=stream)
+
+    def alloc_wire(self, workers: int = 1, device="cuda"):
+        """Empty wire buffers: bfloat16 bits (int16 storage) and packed 12-bit indices (uint8)."""
+        import torch
+        vb, ib = demo_wire_size(self.n_entries)
+        v = torch.empty(workers * vb // 2, dtype=torch.int16, device=device)
+        i = torch.empty(workers * ib, dtype=torch.uint8, device=device)
+        return v, i
+
+    def pack_wire(self, workers, pay_values, pay_idx, wire_values, wire_idx, stream=None) -> None:
+        demo_pack_wire(self.ctx, workers, pay_values, pay_idx, wire_values, wire_idx, stream)
+
+    def decode_apply_wire(self, params, workers, wire_values, wire_idx, phi=DEMO_PHI_SIGN, eta=1e-3, lam=0.0,
+                          avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
+        demo_decode_apply_wire(self.ctx, params, self.cfg(P0, P1), workers, wire_values, wire_idx, phi, eta, lam,
+                               avg, stream)
 
     def alloc_muon_workspace(self, device="cuda"):
         """Device workspace of the Muon decode for this list (uint8 storage)."""

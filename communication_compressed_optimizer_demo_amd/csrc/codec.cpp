@@ -169,14 +169,20 @@ demo_status for_each_batch(const std::vector<TensorPlan>& plan, Fill&& fill, Lau
   return flush();
 }
 
+// 32-bit words of one worker's wire indices: three per 8-entry group.
+int64_t wire_idx_words(int64_t entries) { return (entries + 7) / 8 * 3; }
+
 // Shared body of the decode entry points: params and/or moms (either may be
 // NULL) receive X - eta (phi(M*) + lambda X) and M - alpha M*; or, with
 // `signs` given (params and moms NULL), sign(M*) is packed into n_words words.
+// With `wire` the payload is read from the wire arrays instead of pay_values /
+// pay_idx (parameter update only).
 demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                           float* const* moms, const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
                           const uint16_t* pay_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
                           demo_average avg, hipStream_t stream, uint64_t* signs = nullptr, int64_t n_words = 0,
-                          float* const* mstar = nullptr) {
+                          float* const* mstar = nullptr, bool wire = false, const uint16_t* wire_values = nullptr,
+                          const void* wire_idx = nullptr) {
   if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
   std::vector<TensorPlan> plan;
   int64_t entries = 0, words = 0;
@@ -184,6 +190,7 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   if (s != DEMO_OK) return s;
   const bool to_signs = params == nullptr && moms == nullptr && mstar == nullptr;
   if (to_signs && cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
+  if (wire && cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the wire format is built for chunk 64");
   if (to_signs) {
     if (n_words != words)
       return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +
@@ -206,8 +213,15 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
       if (!aligned(list[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
     }
   }
-  if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr)) return fail(DEMO_ERR_INVALID, "payload is NULL");
-  if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
+  if (wire) {
+    if (entries > 0 && (wire_values == nullptr || wire_idx == nullptr))
+      return fail(DEMO_ERR_INVALID, "wire payload is NULL");
+    if (!aligned(wire_values, 2) || !aligned(wire_idx, 4)) return fail(DEMO_ERR_ALIGN, "wire payload misaligned");
+  } else {
+    if (entries > 0 && (pay_values == nullptr || pay_idx == nullptr))
+      return fail(DEMO_ERR_INVALID, "payload is NULL");
+    if (!aligned(pay_values, 4) || !aligned(pay_idx, 2)) return fail(DEMO_ERR_ALIGN, "payload misaligned");
+  }
   const float *p0, *p1;
   demo::BasisKind kind;
   if ((s = check_basis(cfg, plan, &kind, &p0, &p1)) != DEMO_OK) return s;
@@ -230,6 +244,10 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   p.pack_signs = to_signs ? 1 : 0;
   p.write_mstar = mstar != nullptr ? 1 : 0;
   p.alpha = cfg->alpha;
+  p.wire = wire ? 1 : 0;
+  p.wire_val = wire_values;
+  p.wire_idx = static_cast<const uint32_t*>(wire_idx);
+  p.wire_words = wire_idx_words(entries);
   auto fill = [&](demo::TensorSlot& slot, size_t i) {
     slot.aux = moms != nullptr    ? static_cast<void*>(moms[i])
                : mstar != nullptr ? static_cast<void*>(mstar[i])
@@ -377,6 +395,37 @@ demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes
   if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
   return decode_common(ctx, n, shapes, params, nullptr, cfg, workers, pay_values, pay_idx, n_entries, phi, eta,
                        lambda, avg, stream);
+}
+
+demo_status demo_wire_size(int64_t n_entries, int64_t* value_bytes, int64_t* idx_bytes) {
+  if (n_entries < 0 || n_entries > (int64_t(1) << 40)) return fail(DEMO_ERR_RANGE, "entry count out of range");
+  if (value_bytes != nullptr) *value_bytes = 2 * n_entries;
+  if (idx_bytes != nullptr) *idx_bytes = 4 * wire_idx_words(n_entries);
+  return DEMO_OK;
+}
+
+demo_status demo_pack_wire(demo_ctx* ctx, int32_t workers, const float* pay_values, const uint16_t* pay_idx,
+                           int64_t n_entries, uint16_t* wire_values, void* wire_idx, hipStream_t stream) {
+  if (workers < 1 || workers > demo::kMaxWorkers) return fail(DEMO_ERR_RANGE, "workers must be in 1..255");
+  if (n_entries < 0 || n_entries > (int64_t(1) << 40)) return fail(DEMO_ERR_RANGE, "entry count out of range");
+  if (n_entries > 0 && (pay_values == nullptr || pay_idx == nullptr || wire_values == nullptr || wire_idx == nullptr))
+    return fail(DEMO_ERR_INVALID, "payload or wire buffer is NULL");
+  if (!aligned(pay_values, 4) || !aligned(pay_idx, 2) || !aligned(wire_values, 2) || !aligned(wire_idx, 4))
+    return fail(DEMO_ERR_ALIGN, "payload or wire buffer misaligned");
+  demo_status s = check_device(ctx);
+  if (s != DEMO_OK) return s;
+  const hipError_t e = demo::launch_pack_wire(pay_values, pay_idx, n_entries, workers, wire_values,
+                                              static_cast<uint32_t*>(wire_idx), stream);
+  return e == hipSuccess ? DEMO_OK : fail(DEMO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+}
+
+demo_status demo_decode_apply_wire(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                   const demo_codec_cfg* cfg, int32_t workers, const uint16_t* wire_values,
+                                   const void* wire_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
+                                   demo_average avg, hipStream_t stream) {
+  if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
+  return decode_common(ctx, n, shapes, params, nullptr, cfg, workers, nullptr, nullptr, n_entries, phi, eta, lambda,
+                       avg, stream, nullptr, 0, nullptr, true, wire_values, wire_idx);
 }
 
 demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,

@@ -248,10 +248,32 @@ __device__ __forceinline__ void accumulate(float* acc, uint32_t* cntw, uint32_t 
   atomicAdd(&cntw[u * kCntLd + (col >> 2)], 1u << ((col & 3u) * 8u));
 }
 
+// Entry f of worker w's payload: the float32 arrays, or the compact wire
+// format (value = bfloat16 bits in the high half of a float; index = bits
+// 12f .. 12f + 11 of the worker's little-endian word string, which may
+// straddle two words of f's 8-entry, three-word group).
+template <bool kWire>
+__device__ __forceinline__ void load_entry(const DecodeParams& p, int64_t w, int64_t f, float& v, uint32_t& ix) {
+  if constexpr (kWire) {
+    v = __uint_as_float(uint32_t(p.wire_val[w * p.entries + f]) << 16);
+    const uint32_t* __restrict__ s = p.wire_idx + w * p.wire_words;
+    const int64_t bit = f * 12;
+    const int64_t d = bit >> 5;
+    const int64_t last = (f >> 3) * 3 + 2;
+    const uint64_t pair = (uint64_t(s[d < last ? d + 1 : d]) << 32) | s[d];
+    ix = uint32_t(pair >> (bit & 31)) & 4095u;
+  } else {
+    const int64_t off = w * p.entries + f;
+    v = p.pay_val[off];
+    ix = p.pay_idx[off];
+  }
+}
+
 // Scatter-add the W payload segments of one 64x64 chunk (entries e0 ..
 // e0 + keff of every worker).  One LDS atomic instruction per (worker, entry
 // block); within it the indices are distinct, so no lanes collide and every
 // coefficient receives its terms in worker order.
+template <bool kWire>
 __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0,
                                               int lane) {
   const int keff = p.keff2;
@@ -263,10 +285,9 @@ __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const 
       uint32_t ix[kWorkerBatch];
 #pragma unroll
       for (int j = 0; j < kWorkerBatch; ++j) {
-        const int64_t off = int64_t(w0 + j) * p.entries + e0 + e;
-        const bool ok = on && (w0 + j) < p.workers;
-        val[j] = ok ? p.pay_val[off] : 0.f;
-        ix[j] = ok ? p.pay_idx[off] : 0u;
+        val[j] = 0.f;
+        ix[j] = 0u;
+        if (on && (w0 + j) < p.workers) load_entry<kWire>(p, w0 + j, e0 + e, val[j], ix[j]);
       }
 #pragma unroll
       for (int j = 0; j < kWorkerBatch; ++j) {
@@ -284,21 +305,21 @@ __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const 
 // accumulator row r).  Entry f of a segment belongs to chunk f / keff; one
 // instruction covers 64 consecutive entries of one worker, whose (chunk,
 // index) pairs are distinct.
+template <bool kWire>
 __device__ __forceinline__ void scatter_slab(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0, int nc,
                                              int lane) {
   const int keff = p.keff1;
   const int n = nc * keff;
   for (int w = 0; w < p.workers; ++w) {
-    const float* __restrict__ pv = p.pay_val + int64_t(w) * p.entries + e0;
-    const uint16_t* __restrict__ pi = p.pay_idx + int64_t(w) * p.entries + e0;
     for (int f0 = 0; f0 < n; f0 += 64 * 8) {
       float val[8];
       uint32_t ix[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int f = f0 + 64 * j + lane;
-        val[j] = f < n ? pv[f] : 0.f;
-        ix[j] = f < n ? pi[f] : 0u;
+        val[j] = 0.f;
+        ix[j] = 0u;
+        if (f < n) load_entry<kWire>(p, w, e0 + f, val[j], ix[j]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -329,7 +350,7 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
   }
 }
 
-template <class Basis, int kTargets>
+template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
                                               float* acc, uint32_t* cntw) {
   const int lane = threadIdx.x;
@@ -350,9 +371,13 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
     const uint32_t e = uint32_t(min(lane, p.keff2 - 1));
 #pragma unroll
     for (int j = 0; j < kWorkerBatch; ++j) {
-      const int64_t w0 = int64_t(min(j, p.workers - 1)) * p.entries + e0;
-      val[j] = (p.pay_val + w0)[e];
-      ix[j] = (p.pay_idx + w0)[e];
+      if constexpr (kWire) {
+        load_entry<true>(p, min(j, p.workers - 1), e0 + e, val[j], ix[j]);
+      } else {
+        const int64_t w0 = int64_t(min(j, p.workers - 1)) * p.entries + e0;
+        val[j] = (p.pay_val + w0)[e];
+        ix[j] = (p.pay_idx + w0)[e];
+      }
     }
   }
   const int64_t ld = ts.cols;
@@ -381,7 +406,7 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
       }
     }
   } else {
-    scatter_chunk(acc, cntw, p, e0, lane);
+    scatter_chunk<kWire>(acc, cntw, p, e0, lane);
   }
   __syncthreads();
 
@@ -433,7 +458,7 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   }
 }
 
-template <class Basis, int kTargets>
+template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
                                               float* acc, uint32_t* cntw) {
   const int lane = threadIdx.x;
@@ -444,7 +469,7 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
 
   clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
   __syncthreads();
-  scatter_slab(acc, cntw, p, ts.entry_begin + int64_t(slab) * 64 * p.keff1, nc, lane);
+  scatter_slab<kWire>(acc, cntw, p, ts.entry_begin + int64_t(slab) * 64 * p.keff1, nc, lane);
   __syncthreads();
   float q[64];
   average_row(q, acc, cntw, p, lane);
@@ -484,43 +509,79 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   }
 }
 
-template <class Basis, int kTargets>
+template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_item(const LaunchTable& tab, const DecodeParams& p, const Basis& basis,
                                             float* acc, uint32_t* cntw) {
   const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
   if (ts.cols == 0)
-    decode_vector<Basis, kTargets>(ts, p, basis, acc, cntw);
+    decode_vector<Basis, kTargets, kWire>(ts, p, basis, acc, cntw);
   else
-    decode_matrix<Basis, kTargets>(ts, p, basis, acc, cntw);
+    decode_matrix<Basis, kTargets, kWire>(ts, p, basis, acc, cntw);
 }
 
-template <class Basis, int kTargets>
+template <class Basis, int kTargets, bool kWire = false>
 __global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParams p) {
   __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
-  decode_item<Basis, kTargets>(tab, p, Basis{}, reinterpret_cast<float*>(lds), lds + 64 * kLd);
+  decode_item<Basis, kTargets, kWire>(tab, p, Basis{}, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }
 
-template <int kTargets>
+template <int kTargets, bool kWire = false>
 __global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
   __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
-  decode_item<DenseBasis, kTargets>(tab, p, basis, reinterpret_cast<float*>(lds), lds + 64 * kLd);
+  decode_item<DenseBasis, kTargets, kWire>(tab, p, basis, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }
 
-template <int kTargets>
+template <int kTargets, bool kWire = false>
 void launch_decode_targets(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                            const float* basis_p1, hipStream_t stream) {
   const dim3 grid(tab.items), block(64);
   switch (kind) {
     case BasisKind::kDct:
-      decode_kernel<DctBasis, kTargets><<<grid, block, 0, stream>>>(tab, p);
+      decode_kernel<DctBasis, kTargets, kWire><<<grid, block, 0, stream>>>(tab, p);
       break;
     case BasisKind::kIdentity:
-      decode_kernel<IdentityBasis, kTargets><<<grid, block, 0, stream>>>(tab, p);
+      decode_kernel<IdentityBasis, kTargets, kWire><<<grid, block, 0, stream>>>(tab, p);
       break;
     case BasisKind::kUser:
-      decode_dense_kernel<kTargets><<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
+      decode_dense_kernel<kTargets, kWire><<<grid, block, 0, stream>>>(tab, p, DenseBasis{basis_p0, basis_p1});
       break;
   }
+}
+
+// ---------------------------------------------------------------- compact wire format
+
+// float32 -> bfloat16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// One thread per 8-entry group of one worker: eight bfloat16 values, and the
+// eight 12-bit indices as three little-endian words (entry j at bits 12j);
+// entries past the end count as index 0 and store no value.
+__global__ __launch_bounds__(256) void pack_wire_kernel(const float* __restrict__ pay_val,
+                                                        const uint16_t* __restrict__ pay_idx, int64_t entries,
+                                                        int64_t groups, int64_t total, uint16_t* __restrict__ wire_val,
+                                                        uint32_t* __restrict__ wire_idx) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t w = t / groups;
+  const int64_t g = t - w * groups;
+  const int64_t base = w * entries;
+  uint32_t f[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t e = g * 8 + j;
+    f[j] = 0u;
+    if (e < entries) {
+      f[j] = pay_idx[base + e] & 4095u;
+      wire_val[base + e] = uint16_t(bf16_rne(pay_val[base + e]));
+    }
+  }
+  uint32_t* __restrict__ out = wire_idx + t * 3;  // worker w's words start at w * groups * 3
+  out[0] = f[0] | (f[1] << 12) | (f[2] << 24);
+  out[1] = (f[2] >> 8) | (f[3] << 4) | (f[4] << 16) | (f[5] << 28);
+  out[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
 }
 
 // ---------------------------------------------------------------- one-bit sign apply
@@ -604,7 +665,9 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
-  if (p.pack_signs)
+  if (p.wire)
+    launch_decode_targets<kToParams, true>(tab, p, kind, basis_p0, basis_p1, stream);
+  else if (p.pack_signs)
     launch_decode_targets<kToSigns>(tab, p, kind, basis_p0, basis_p1, stream);
   else if (p.write_mstar)
     launch_decode_targets<kToMstar>(tab, p, kind, basis_p0, basis_p1, stream);
@@ -614,6 +677,16 @@ hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKin
     launch_decode_targets<kToMomentum>(tab, p, kind, basis_p0, basis_p1, stream);
   else
     launch_decode_targets<kToParams>(tab, p, kind, basis_p0, basis_p1, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_wire(const float* pay_val, const uint16_t* pay_idx, int64_t entries, int32_t workers,
+                            uint16_t* wire_val, uint32_t* wire_idx, hipStream_t stream) {
+  const int64_t groups = (entries + 7) / 8;
+  const int64_t total = groups * workers;
+  if (total <= 0) return hipSuccess;
+  pack_wire_kernel<<<dim3(uint32_t((total + 255) / 256)), dim3(256), 0, stream>>>(pay_val, pay_idx, entries, groups,
+                                                                                  total, wire_val, wire_idx);
   return hipGetLastError();
 }
 

@@ -67,6 +67,13 @@ struct DecodeParams {
   int32_t pack_signs;   // 1: write sign(M*) as bits (no parameter or momentum update)
   int32_t write_mstar;  // 1: write M* itself (the Muon path applies phi afterwards)
   float alpha;
+  // compact wire payload (read instead of pay_val / pay_idx when wire is 1):
+  // bfloat16 values and 12-bit indices in a little-endian bit string,
+  // wire_words 32-bit words per worker
+  int32_t wire;
+  const uint16_t* wire_val;
+  const uint32_t* wire_idx;
+  int64_t wire_words;
 };
 
 struct ApplyParams {
@@ -83,6 +90,10 @@ hipError_t launch_encode(const LaunchTable& tab, const EncodeParams& p, bool g_b
 hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKind kind, const float* basis_p0,
                          const float* basis_p1, hipStream_t stream);
 hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream);
+// workers x entries payload entries -> wire values (workers x entries) and
+// wire index words (workers x 3 * ceil(entries / 8))
+hipError_t launch_pack_wire(const float* pay_val, const uint16_t* pay_idx, int64_t entries, int32_t workers,
+                            uint16_t* wire_val, uint32_t* wire_idx, hipStream_t stream);
 // phi = Muon (kernels_muon.hip).  D = alpha * (*alpha_scale if given) *
 // op(A) op(B) + beta * C + gamma * I, fp32, row-major; op(A) is M x K (the
 // transpose of a row-major K x M matrix when trans_a), op(B) K x N.  C may

@@ -14,7 +14,8 @@ from its own stream.
 
 Seeding: every array comes from PCG64 seeded with
 ``SeedSequence([config_id, role, worker, step, tensor])`` where role 0 is a
-gradient, role 1 the initial parameters and role 2 a projection draw.
+gradient, role 1 the initial parameters, role 2 a projection draw and role 3
+a synthetic payload.
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ import numpy as np
 ROLE_GRAD = 0
 ROLE_PARAM = 1
 ROLE_BASIS = 2
+ROLE_PAYLOAD = 3
 
 PHI_SIGN = "sign"
 PHI_IDENTITY = "identity"
@@ -126,6 +128,41 @@ def gaussian_matrix(w: Workload, step: int, which: int, s: int = 64) -> np.ndarr
     dimension-0 matrix and 1 for the dimension-1 matrix.
     """
     return rng(w.config_id, ROLE_BASIS, which, step, 0).standard_normal((s, s))
+
+
+def synthetic_payload(chunks: Sequence[Tuple[int, int, int]], workers: int, seed: int, scale: float = 1e-5,
+                      specials: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Payloads of ``workers`` workers in the codec's layout, drawn directly.
+
+    ``chunks`` lists, per tensor, (chunk count, entries per chunk, index
+    range per chunk).  Every chunk gets distinct indices in ascending order
+    and N(0, scale^2) values.  With ``specials`` about one value in four is
+    replaced by a bit pattern that exercises float32 -> bfloat16 rounding:
+    exact halfway cases, one ulp either side of them, signed zeros,
+    subnormals, the largest finite float and the float32 maximum rounded.
+    Returns float32 values and uint16 indices, worker-major.
+    """
+    vals, idx = [], []
+    for wk in range(workers):
+        r = rng(seed, ROLE_PAYLOAD, wk, 0, 0)
+        for n, keff, numel in chunks:
+            for _ in range(n):
+                idx.append(np.sort(r.permutation(numel)[:keff]).astype(np.uint16))
+                vals.append((r.standard_normal(keff) * scale).astype(np.float32))
+    v = np.concatenate(vals) if vals else np.zeros(0, np.float32)
+    i = np.concatenate(idx) if idx else np.zeros(0, np.uint16)
+    if specials and v.size:
+        r = rng(seed, ROLE_PAYLOAD, workers, 1, 0)
+        pick = r.random(v.size) < 0.25
+        hi = r.integers(0, 0x7F7F, v.size, dtype=np.uint32) | (r.integers(0, 2, v.size, dtype=np.uint32) << 15)
+        low = r.choice(np.array([0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF], np.uint32), v.size)
+        bits = (hi << 16) | low
+        fixed = np.array([0x00000000, 0x80000000, 0x00000001, 0x807FFFFF, 0x7F7FFFFF, 0xFF7F7FFF,
+                          0x3F808000, 0x3F818000, 0x00008000, 0x80018000], np.uint32)
+        bits[:min(fixed.size, v.size)] = fixed[:min(fixed.size, v.size)]
+        pick[:min(fixed.size, v.size)] = True
+        v = np.where(pick, bits.view(np.float32), v).astype(np.float32)
+    return v, i
 
 
 # ---------------------------------------------------------------------------

@@ -14,6 +14,11 @@
  *   demo_decode_signs / demo_apply_signs
  *                      the same decode split once more for the Signum
  *                      variant's one-bit download (server side / worker side).
+ *   demo_pack_wire / demo_decode_apply_wire
+ *                      the payload in a compact wire format (bfloat16 values,
+ *                      12-bit indices) and the decode that reads it.
+ *   demo_decode_apply_muon
+ *                      the decode with phi = Muon.
  *
  * Conventions for every call:
  *   - Tensors are dense, row-major, contiguous device buffers.  Matrices
@@ -214,6 +219,41 @@ demo_status demo_decode_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes
 demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                              int32_t chunk, const uint64_t* signs, int64_t n_words, float eta, float lambda,
                              hipStream_t stream);
+
+/* ---- Compact wire format (teaching deck "Training over Slow Links", top-k
+ * and DeMo slides: a kept value travels as 2 bytes of bfloat16 plus its
+ * position, and a position inside a 64x64 chunk needs 12 bits).  Built for
+ * chunk edge 64 (other chunk edges return DEMO_ERR_RANGE).
+ * A worker's wire payload of E entries is two arrays:
+ *   values:  E uint16 bfloat16 bit patterns, entry order kept; float32 ->
+ *            bfloat16 rounds to nearest, ties to even
+ *   indices: 12 * ceil(E / 8) bytes: entry j's 12-bit index sits at bits
+ *            12j .. 12j + 11 of the array read as one little-endian bit
+ *            string (so entries 2p, 2p+1 fill bytes 3p .. 3p + 2, low bits
+ *            first); the bytes past 3 * ceil(E / 2) are zero.
+ * W wire payloads lie worker-major: values as W x E uint16, indices as
+ * W x demo_wire_size's idx_bytes. */
+
+/* Host-only: bytes of one worker's wire values (2E) and indices (12 ceil(E/8)). */
+demo_status demo_wire_size(int64_t n_entries, int64_t* value_bytes, int64_t* idx_bytes);
+
+/* Convert `workers` payloads (worker-major, n_entries each, as demo_encode
+ * writes them) into the wire format.  Indices are sent modulo 4096 (a 64x64
+ * chunk's indices are below that).
+ *   wire_values: device, workers x n_entries uint16 (2-byte aligned); written
+ *   wire_idx:    device, workers x idx_bytes bytes (4-byte aligned); written,
+ *                padding included */
+demo_status demo_pack_wire(demo_ctx* ctx, int32_t workers, const float* pay_values, const uint16_t* pay_idx,
+                           int64_t n_entries, uint16_t* wire_values, void* wire_idx, hipStream_t stream);
+
+/* demo_decode_apply reading W wire payloads directly (values widened from
+ * bfloat16, indices unpacked in the kernel; nothing is unpacked into memory).
+ * Arguments as for demo_decode_apply, the payload given as wire arrays
+ * (read only); cfg->chunk must be 64. */
+demo_status demo_decode_apply_wire(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                   const demo_codec_cfg* cfg, int32_t workers, const uint16_t* wire_values,
+                                   const void* wire_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,
+                                   demo_average avg, hipStream_t stream);
 
 /* ---- phi = Muon (DeMo summary §3.4 Base Optimizer Update: phi(M) =
  * M (M^T M + eps I)^(-1/2), Newton-Schulz normalization).  phi acts on each

@@ -231,3 +231,37 @@ def compare_signs(Mstar: np.ndarray, shape, gpu_words: np.ndarray, chunk_diverge
         raise AssertionError(f"{where}: sign bit differs in chunk {c} element {e} "
                              f"({int(bad.sum())} bits; M* there {O.split_chunks(Mstar).reshape(n, -1)[c, e]!r})")
     return int(((got != ref) & valid).sum())
+
+
+def _bf16_value(codes: np.ndarray) -> np.ndarray:
+    return (np.asarray(codes, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def compare_wire(values: np.ndarray, idx: np.ndarray, Q: np.ndarray, gpu_codes: np.ndarray, gpu_idx: np.ndarray,
+                 diverged: np.ndarray, where: str = "") -> np.ndarray:
+    """Check one tensor's wire entries; returns the chunks whose bfloat16 codes differ.
+
+    values / idx: the oracle's payload [n, keff] (float32 values); Q: its
+    coefficients [n, ...] (for the value tolerance); gpu_codes / gpu_idx: the
+    GPU wire entries unpacked [n, keff].  Chunks already diverged are skipped.
+    Indices must match exactly.  The bfloat16 code is a rounding decision
+    taken on a float32 value that may itself differ from the oracle's within
+    the payload tolerance, so a GPU code is valid iff it is the rounding of
+    some value within that tolerance of the oracle's: between the codes of
+    v - tol and v + tol (rounding is monotonic).  Chunks where it is valid
+    but not the oracle's own code are returned as diverged.
+    """
+    n = values.shape[0]
+    live = ~diverged
+    gi = np.asarray(gpu_idx).astype(np.int64)
+    assert np.array_equal(gi[live], np.asarray(idx).astype(np.int64)[live]), f"{where}: wire indices differ"
+    norms = np.linalg.norm(np.asarray(Q, dtype=np.float64).reshape(n, -1), axis=1)
+    v = np.asarray(values, dtype=np.float32)
+    tol = _tol(v.astype(np.float64), np.maximum(ATOL, NOISE * norms)[:, None])
+    lo = _bf16_value(O.bf16_bits((v - tol).astype(np.float32)))
+    hi = _bf16_value(O.bf16_bits((v + tol).astype(np.float32)))
+    g = _bf16_value(gpu_codes)
+    bad = ~((lo <= g) & (g <= hi)) & live[:, None]
+    assert not bad.any(), f"{where}: wire values outside the rounding of the tolerance (chunks " \
+                          f"{np.nonzero(bad.any(axis=1))[0][:5]})"
+    return ((np.asarray(gpu_codes) != O.bf16_bits(v)) & live[:, None]).any(axis=1)

@@ -343,3 +343,54 @@ def _call_muon(lib, shapes, k=8, workers=2, eps=1e-6, iters=24, ws=0x7000, ws_by
 def test_muon_arguments(lib, kw, status, text):
     assert _call_muon(lib, [(70, 90), (100,)], **kw) == status
     assert text in _msg(lib)
+
+
+# --------------------------------------------------------------------------- compact wire format
+
+@pytest.mark.parametrize("entries", [0, 1, 7, 8, 9, 1000, 6_291_456])
+def test_wire_size(lib, entries):
+    vb, ib = B.demo_wire_size(entries)
+    assert vb == 2 * entries
+    # whole 8-entry groups of 12 bytes, which hold the oracle's pair-packed bytes
+    assert ib == 12 * ((entries + 7) // 8)
+    if entries < 2000:
+        assert O.pack_wire([0.0] * entries, [0] * entries)[1].size <= ib
+
+
+def _call_wire_decode(lib, k=8, workers=2, chunk=64, wv=0x3000, wi=0x4000, entries=None, phi=0):
+    shapes = [(70, 90), (100,)]
+    cfg = B.demo_codec_cfg(chunk, k, 0.9, 0.2, 0, 0, None, None, 0)
+    e = O.payload_entries(shapes, k) if entries is None else entries
+    return lib.demo_decode_apply_wire(None, 2, B._shapes(shapes), B._ptrs([0x1000] * 2), ctypes.byref(cfg), workers,
+                                      wv, wi, e, phi, 1e-3, 0.0, 0, None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(), 1, "context"),
+    (dict(chunk=128), 3, "chunk 64"),
+    (dict(workers=0), 3, "workers"),
+    (dict(workers=256), 3, "workers"),
+    (dict(entries=5), 4, "entries"),
+    (dict(wv=0), 1, "wire payload is NULL"),
+    (dict(wi=0), 1, "wire payload is NULL"),
+    (dict(wv=0x3001), 7, "misaligned"),
+    (dict(wi=0x4002), 7, "misaligned"),
+    (dict(phi=9), 1, "phi"),
+])
+def test_wire_decode_arguments(lib, kw, status, text):
+    assert _call_wire_decode(lib, **kw) == status
+    assert text in _msg(lib)
+
+
+@pytest.mark.parametrize("args,status,text", [
+    ((2, 0x3000, 0x4000, 100, 0x5000, 0x6000), 1, "context"),
+    ((0, 0x3000, 0x4000, 100, 0x5000, 0x6000), 3, "workers"),
+    ((2, 0x3000, 0x4000, -1, 0x5000, 0x6000), 3, "entry count"),
+    ((2, 0, 0x4000, 100, 0x5000, 0x6000), 1, "NULL"),
+    ((2, 0x3000, 0x4000, 100, 0, 0x6000), 1, "NULL"),
+    ((2, 0x3002, 0x4000, 100, 0x5000, 0x6000), 7, "misaligned"),
+    ((2, 0x3000, 0x4000, 100, 0x5000, 0x6001), 7, "misaligned"),
+])
+def test_pack_wire_arguments(lib, args, status, text):
+    assert lib.demo_pack_wire(None, *args, None) == status
+    assert text in _msg(lib)

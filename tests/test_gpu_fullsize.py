@@ -69,20 +69,35 @@ def check_payload_properties(vals: torch.Tensor, idx: torch.Tensor, layout, limi
             assert bool((ix[:, 1:] > ix[:, :-1]).all()), f"{where}: tensor {t} indices not ascending"
 
 
-@pytest.mark.parametrize("name,s", [("olmo_300m", 64), ("olmo_1b", 64), ("olmo_1b", 128)])
-def test_full_size_sampled(dev, name, s):
+def wire_entries(wv: torch.Tensor, wi: torch.Tensor, wire_bytes: int, ne: int, worker: int, first: int, count: int):
+    """bfloat16 codes and indices of ``count`` wire entries of one worker from entry ``first``, on the host."""
+    codes = wv[worker * ne + first:worker * ne + first + count].cpu().numpy().view(np.uint16)
+    g0, g1 = first // 8, (first + count + 7) // 8
+    blk = wi[worker * wire_bytes + 12 * g0:worker * wire_bytes + 12 * g1].cpu().numpy()
+    skip = first - 8 * g0
+    idx = O.unpack_wire(np.zeros(skip + count, np.uint16), blk, skip + count)[1][skip:]
+    return codes, idx
+
+
+@pytest.mark.parametrize("name,s,wire", [("olmo_300m", 64, False), ("olmo_1b", 64, False), ("olmo_1b", 128, False),
+                                         ("olmo_1b", 64, True)])
+def test_full_size_sampled(dev, name, s, wire):
     w = DI.WORKLOADS[name]
     W, steps = w.workers, 2
     phi_c = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
     P = O.dct_basis(s)
     rng = np.random.default_rng(7 + w.config_id)
-    name = f"{name} s={s}"
+    name = f"{name} s={s}" + (" wire" if wire else "")
 
     shapes = [tuple(d) for d in w.shapes]
     groups = [{"ids": list(range(len(shapes))), "shapes": shapes,
                "codec": B.Codec(shapes, w.k, w.beta, w.alpha, chunk=s), "lay": PR.layout(shapes, w.k, s)}]
     for gr in groups:
         gr["vals"], gr["pidx"] = gr["codec"].alloc_payload(W)
+        if wire:
+            gr["wv"], gr["wi"] = gr["codec"].alloc_wire(W)
+            gr["wb"] = B.demo_wire_size(gr["codec"].n_entries)[1]
+    xdiv = {}  # sampled chunks whose parameters followed a bfloat16 code other than the oracle's
     say(f"[{name}] {len(w.shapes)} tensors, {w.n_params} params, W={W}: allocating momenta")
     M = {i: [torch.zeros(w.shapes[i], device=dev) for _ in range(W)] for i in range(len(w.shapes))}
     X = {i: DI.device_initial_params(w, i, dev) for i in range(len(w.shapes))}
@@ -97,6 +112,8 @@ def test_full_size_sampled(dev, name, s):
     for t in range(steps):
         or_vals = {key: [None] * W for key in M_or}
         or_idx = {key: [None] * W for key in M_or}
+        or_q = {key: [None] * W for key in M_or}
+        or_at = {}  # (tensor, chunk) -> first payload entry
         for wk in range(W):
             G = {i: DI.device_gradient(w, wk, t, i, dev) for i in range(len(w.shapes))}
             for gr in groups:
@@ -130,18 +147,36 @@ def test_full_size_sampled(dev, name, s):
                         M_or[(i, c)][wk] = out["M"]
                         or_vals[(i, c)][wk] = out["values"]
                         or_idx[(i, c)][wk] = out["idx"]
+                        or_q[(i, c)][wk] = out["Q"]
+                        or_at[(i, c)] = (s0, keff)
             del G
         say(f"[{name}] step {t}: encode of {W} workers checked; decode/apply")
         for gr in groups:
-            gr["codec"].decode_apply([X[i] for i in gr["ids"]], W, gr["vals"], gr["pidx"], phi_c, w.eta, w.lam)
+            if wire:  # the bench's wire variant: pack all W payloads, decode from the wire
+                gr["codec"].pack_wire(W, gr["vals"], gr["pidx"], gr["wv"], gr["wi"])
+                gr["codec"].decode_apply_wire([X[i] for i in gr["ids"]], W, gr["wv"], gr["wi"], phi_c, w.eta, w.lam)
+            else:
+                gr["codec"].decode_apply([X[i] for i in gr["ids"]], W, gr["vals"], gr["pidx"], phi_c, w.eta, w.lam)
         torch.cuda.synchronize()
         for (i, c), xo in X_or.items():
             assert torch.isfinite(X[i]).all(), f"{name}: non-finite parameters, tensor {i}"
-            dec = O.decode_apply(xo, np.stack(or_vals[(i, c)]), np.stack(or_idx[(i, c)]), phi=w.phi,
-                                 eta=w.eta, lam=w.lam, s=s)
-            div = np.zeros(1, bool)
+            div = xdiv.get((i, c), np.zeros(1, bool)).copy()
             for wk in range(W):
                 div |= cdiv[(i, c, wk)]
+            vals_in = or_vals[(i, c)]
+            if wire:
+                s0, keff = or_at[(i, c)]
+                gr = groups[0]
+                for wk in range(W):
+                    codes, gidx = wire_entries(gr["wv"], gr["wi"], gr["wb"], gr["codec"].n_entries, wk, s0, keff)
+                    xdiv[(i, c)] = xdiv.get((i, c), np.zeros(1, bool)) | PR.compare_wire(
+                        or_vals[(i, c)][wk], or_idx[(i, c)][wk], or_q[(i, c)][wk], codes.reshape(1, keff),
+                        gidx.reshape(1, keff), div, where=f"{name} step {t} worker {wk} tensor {i} chunk {c} (wire)")
+                div |= xdiv[(i, c)]
+                vals_in = [O.unpack_wire(*O.pack_wire(v, ix), v.size)[0].reshape(v.shape)
+                           for v, ix in zip(or_vals[(i, c)], or_idx[(i, c)])]
+            dec = O.decode_apply(xo, np.stack(vals_in), np.stack(or_idx[(i, c)]), phi=w.phi,
+                                 eta=w.eta, lam=w.lam, s=s)
             ediv[(i, c)] = PR.compare_decode(dec, xo.shape, w.phi, w.eta, chunk_block(X[i], w.shapes[i], c, s), div,
                                              ediv.get((i, c)), where=f"{name} step {t} tensor {i} chunk {c}", s=s)
             X_or[(i, c)] = dec["X"]

@@ -33,9 +33,11 @@ class Sim:
     """W workers of one workload, GPU next to the oracle."""
 
     def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None, identity=False, aggregated=False,
-                 signs=False, chunk=64):
+                 signs=False, chunk=64, wire=False):
         self.w = w
         self.s = chunk
+        self.wire = wire  # payloads go through the compact wire format: pack, then decode_apply_wire
+        assert not (wire and (signs or aggregated))
         self.signs = signs  # one-bit download: decode_signs, then apply_signs (phi = sign)
         assert not (signs and (aggregated or w.phi != "sign"))
         self.plain = plain
@@ -58,6 +60,10 @@ class Sim:
         self.X_or = [x.copy() for x in X0]
         self.vals, self.idx = self.codec.alloc_payload(W)
         self.sign_words = self.codec.alloc_signs() if signs else None
+        if wire:
+            self.wv, self.wi = self.codec.alloc_wire(W)
+            self.wire_bytes = B.demo_wire_size(self.codec.n_entries)[1]
+            self.xdiv = [np.zeros(n, dtype=bool) for n, _, _ in self.lay]  # chunks whose X follows other codes
         self.cdiv = [[np.zeros(n, dtype=bool) for n, _, _ in self.lay] for _ in range(W)]
         self.ediv = [None for _ in self.shapes]
         self.report = PR.EncodeReport()
@@ -86,6 +92,7 @@ class Sim:
         avg_c = B.DEMO_AVG_CONTRIBUTORS if self.avg == "count" else B.DEMO_AVG_WORKERS
         or_vals = [[None] * W for _ in self.shapes]
         or_idx = [[None] * W for _ in self.shapes]
+        or_q = [[None] * W for _ in self.shapes]
         for wk in range(W):
             G = [self.grad(wk, t, i) for i in range(len(self.shapes))]
             gd = [torch.from_numpy(g).cuda() for g in G]
@@ -110,6 +117,9 @@ class Sim:
                 self.M_or[wk][i] = out["M"]
                 or_vals[i][wk] = out["values"]
                 or_idx[i][wk] = out["idx"]
+                or_q[i][wk] = out["Q"]
+        if self.wire:
+            return self.step_wire(t, or_vals, or_idx, or_q, phi_c, avg_c, P0, P1, P0d, P1d)
         say(f"  [{w.name}] step {t}: GPU decode/apply over {W} payloads")
         if self.aggregated:
             # worker 0 updates the parameters and its momentum in one pass, the others their momentum only
@@ -148,6 +158,48 @@ class Sim:
                     PR.compare_momentum(self.M_or[wk][i], self.M_gpu[wk][i].cpu().numpy(), shp, cd,
                                         where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (aggregated)", s=self.s)
                     self.cdiv[wk][i] = self.cdiv[wk][i] | cd
+
+    def step_wire(self, t, or_vals, or_idx, or_q, phi_c, avg_c, P0, P1, P0d, P1d):
+        """Pack all W payloads into the wire format, check it, decode from it."""
+        w = self.w
+        W = w.workers
+        ne = self.codec.n_entries
+        say(f"  [{w.name}] step {t}: GPU wire pack + decode/apply over {W} payloads")
+        self.wv.fill_(-1)
+        self.wi.fill_(255)  # padding bytes must be rewritten as zero
+        self.codec.pack_wire(W, self.vals, self.idx, self.wv, self.wi)
+        torch.cuda.synchronize()
+        wv = self.wv.cpu().numpy().view(np.uint16)
+        wi = self.wi.cpu().numpy()
+        self.codec.decode_apply_wire(self.X_gpu, W, self.wv, self.wi, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
+        torch.cuda.synchronize()
+        wb = self.wire_bytes
+        used = 3 * ((ne + 1) // 2)
+        codes, gidx = [], []
+        for wk in range(W):
+            blk = wi[wk * wb:(wk + 1) * wb]
+            assert not blk[used:].any(), f"{w.name} step {t} worker {wk}: wire padding not zero"
+            codes.append(wv[wk * ne:(wk + 1) * ne])
+            gidx.append(O.unpack_wire(wv[wk * ne:(wk + 1) * ne], blk, ne)[1])
+        for i, shp in enumerate(self.shapes):
+            n, keff, e0 = self.lay[i]
+            cd = self.xdiv[i].copy()
+            for wk in range(W):
+                cd |= self.cdiv[wk][i]
+            for wk in range(W):
+                sl = slice(e0, e0 + n * keff)
+                self.xdiv[i] |= PR.compare_wire(or_vals[i][wk], or_idx[i][wk], or_q[i][wk],
+                                                codes[wk][sl].reshape(n, keff), gidx[wk][sl].reshape(n, keff), cd,
+                                                where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (wire)")
+            cd |= self.xdiv[i]
+            # the oracle decodes its own payload as the wire carries it: values rounded to bfloat16
+            vr = [O.unpack_wire(*O.pack_wire(or_vals[i][wk], or_idx[i][wk]), n * keff)[0].reshape(n, keff)
+                  for wk in range(W)]
+            dec = O.decode_apply(self.X_or[i], np.stack(vr), np.stack(or_idx[i]), phi=w.phi, eta=w.eta, lam=w.lam,
+                                 mode=self.avg, P0=P0, P1=P1, s=self.s)
+            self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
+                                             where=f"{w.name} step {t} tensor {i} {shp} (wire)", s=self.s)
+            self.X_or[i] = dec["X"]
 
     def run(self, steps, max_tie_fraction=0.02):
         for t in range(steps):
@@ -370,3 +422,97 @@ def test_chunk128_degenerate(dev):
         return np.full((300,), -2e-3, np.float32)
 
     Sim(w, inputs=inputs, chunk=128).run(2, max_tie_fraction=1.0)
+
+
+# --------------------------------------------------------------------------- compact wire format
+
+@pytest.mark.parametrize("case", ["tiny", "ragged_k3", "k100_w20", "unit_identity_workers", "user_basis"])
+def test_wire_end_to_end(dev, case):
+    """Encode, pack into the wire format, decode from it; the oracle decodes its own payload rounded the same way."""
+    base = DI.WORKLOADS["tiny_256"]
+    kw = {}
+    if case == "tiny":
+        w = base.replace(name="wire_tiny", workers=3)
+    elif case == "ragged_k3":
+        w = DI.WORKLOADS["edge_mix"].replace(name="wire_ragged", k=3)
+    elif case == "k100_w20":  # more than one worker batch and one entry block per chunk
+        w = base.replace(name="wire_k100_w20", shapes=((128, 192), (300,)), k=100, workers=20)
+    elif case == "unit_identity_workers":
+        w = base.replace(name="wire_unit", shapes=((192, 320), (129,)), grad_std=1.0, param_std=1.0, beta=0.9,
+                         k=16, workers=3, eta=0.01, phi="identity")
+        kw = dict(plain=True, avg="workers")
+    else:
+        w = base.replace(name="wire_user_basis", shapes=((128, 200), (65,)), k=4, workers=2, random_basis=True)
+    Sim(w, wire=True, **kw).run(3)
+
+
+def _lay_chunks(shapes, k):
+    return [(n, keff, 4096 if len(s) == 2 else 64) for (n, keff, _), s in zip(PR.layout(shapes, k), shapes)]
+
+
+@pytest.mark.parametrize("shapes,k,workers", [
+    (((256, 256),), 8, 2),
+    (((1000, 777), (3, 5000), (777,), (1,)), 3, 5),   # odd entry counts, vectors, ragged chunks
+    (((64, 64),), 1, 1),                               # one entry
+    (((130, 70), (63,)), 37, 17),
+])
+def test_wire_pack_bit_exact(dev, shapes, k, workers):
+    """The pack kernel against the oracle's format on drawn payloads full of rounding edge cases."""
+    codec = B.Codec(shapes, k)
+    ne = codec.n_entries
+    vals, idx = DI.synthetic_payload(_lay_chunks(shapes, k), workers, seed=40 + k, specials=True)
+    assert vals.size == workers * ne
+    wv, wi = codec.alloc_wire(workers)
+    wv.fill_(-1)
+    wi.fill_(255)
+    say(f"  wire pack {shapes} k={k} W={workers}: {ne} entries per worker")
+    codec.pack_wire(workers, torch.from_numpy(vals).cuda(), torch.from_numpy(idx.view(np.int16)).cuda(), wv, wi)
+    torch.cuda.synchronize()
+    gv = wv.cpu().numpy().view(np.uint16)
+    gb = wi.cpu().numpy()
+    ib = B.demo_wire_size(ne)[1]
+    for wk in range(workers):
+        ov, ob = O.pack_wire(vals[wk * ne:(wk + 1) * ne], idx[wk * ne:(wk + 1) * ne])
+        assert np.array_equal(gv[wk * ne:(wk + 1) * ne], ov), f"worker {wk}: value codes differ"
+        blk = gb[wk * ib:(wk + 1) * ib]
+        assert np.array_equal(blk[:ob.size], ob), f"worker {wk}: index bytes differ"
+        assert not blk[ob.size:].any(), f"worker {wk}: padding not zero"
+    codec.close()
+
+
+@pytest.mark.parametrize("phi,avg", [("sign", "count"), ("identity", "workers")])
+def test_wire_decode_synthetic(dev, phi, avg):
+    """decode_apply_wire on drawn payloads against the oracle's decode of the same wire; and bit-equal to
+    decode_apply given the same values rounded to bfloat16 (same arithmetic, same order)."""
+    shapes = ((200, 130), (1000,), (64, 64), (5,))
+    k, W = 12, 6
+    w = DI.WORKLOADS["tiny_256"].replace(name="wire_synth", shapes=shapes, k=k, workers=W, phi=phi)
+    codec = B.Codec(shapes, k)
+    ne = codec.n_entries
+    vals, idx = DI.synthetic_payload(_lay_chunks(shapes, k), W, seed=77)
+    vd, idd = torch.from_numpy(vals).cuda(), torch.from_numpy(idx.view(np.int16)).cuda()
+    wv, wi = codec.alloc_wire(W)
+    codec.pack_wire(W, vd, idd, wv, wi)
+    X0 = [DI.initial_params(w, i) for i in range(len(shapes))]
+    Xw = [torch.from_numpy(x.copy()).cuda() for x in X0]
+    Xf = [torch.from_numpy(x.copy()).cuda() for x in X0]
+    phi_c = B.DEMO_PHI_SIGN if phi == "sign" else B.DEMO_PHI_IDENTITY
+    avg_c = B.DEMO_AVG_CONTRIBUTORS if avg == "count" else B.DEMO_AVG_WORKERS
+    codec.decode_apply_wire(Xw, W, wv, wi, phi_c, w.eta, w.lam, avg_c)
+    vr = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).cuda()  # torch's own round-to-nearest-even
+    codec.decode_apply(Xf, W, vr, idd, phi_c, w.eta, w.lam, avg_c)
+    torch.cuda.synchronize()
+    lay = PR.layout(shapes, k)
+    for i, shp in enumerate(shapes):
+        n, keff, e0 = lay[i]
+        ov, oi = [], []
+        for wk in range(W):
+            sl = slice(wk * ne + e0, wk * ne + e0 + n * keff)
+            v_, i_ = O.unpack_wire(*O.pack_wire(vals[sl], idx[sl]), n * keff)
+            ov.append(v_.reshape(n, keff))
+            oi.append(i_.reshape(n, keff))
+        dec = O.decode_apply(X0[i], np.stack(ov), np.stack(oi), phi=phi, eta=w.eta, lam=w.lam, mode=avg)
+        gx = Xw[i].cpu().numpy()
+        PR.compare_decode(dec, shp, phi, w.eta, gx, np.zeros(n, bool), None, where=f"wire synthetic tensor {i} {shp}")
+        assert np.array_equal(gx, Xf[i].cpu().numpy()), f"tensor {i}: wire decode differs from the float32 decode"
+    codec.close()
