@@ -19,7 +19,8 @@
 // instruction: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the
 // accumulator holds D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v.
 // K advances kBK per LDS stage, double-buffered; global loads of the next
-// stage are issued before the current stage's MFMAs.
+// stage are issued before the current stage's MFMAs.  Whole tiles take a
+// second kernel (gemm_tile_kernel) with deeper prefetch and 16-byte moves.
 #include "common.h"
 #include "launch.h"
 
@@ -148,6 +149,180 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- whole-tile GEMM
+//
+// For products whose M and N are multiples of the tile edge and K of 2 kSK, with
+// 16-byte aligned operands.  Same 2 x 2 wave grid and MFMA tiles as above;
+// what differs is how operands reach the matrix cores:
+//  - K advances kSK = 32 per stage; each thread moves its share of a stage
+//    with 16-byte global loads, eight lanes per 128-byte row segment;
+//  - two register sets hold stages s+1 and s+2 while stage s is multiplied,
+//    so a global load has two stages of MFMA work to arrive;
+//  - MFMA k-slot h (lane half) takes the k values 16h .. 16h + 15 of a stage,
+//    so an operand whose rows run along K in memory is kept that way in LDS
+//    (pitch kSK + 4) and read with 16-byte LDS loads, and one whose rows run
+//    along M or N is kept k-major (pitch kT + 2: the two lane halves, 16 rows
+//    apart, fall on opposite halves of the banks).
+constexpr int kSK = 32;
+
+// Native vectors (not HIP's float4 struct) so the staging registers stay registers.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// One operand's stage: kT rows (along M for A, N for B) by kSK values of k.
+// kKc: element (row, k) sits at X[row * ld + k] (rows along K in memory);
+// otherwise at X[k * ld + row].
+template <bool kKc, int kT>
+struct TileOperand {
+  static constexpr int kV = kT / 32;  // f32x4 per thread and stage
+  static constexpr int kPitch = kKc ? kSK + 4 : kT + 2;
+  static constexpr int kFloats = kKc ? kT * kPitch : kSK * kPitch;
+
+  __device__ static void load(f32x4 (&r)[kV], const float* __restrict__ X, int64_t ld, int r0, int k0, int tid) {
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int f = tid + 256 * j;
+      if constexpr (kKc) {
+        const int c4 = f & 7, row = f >> 3;
+        r[j] = *reinterpret_cast<const f32x4*>(X + int64_t(r0 + row) * ld + k0 + 4 * c4);
+      } else {
+        const int c4 = f % (kT / 4), k = f / (kT / 4);
+        r[j] = *reinterpret_cast<const f32x4*>(X + int64_t(k0 + k) * ld + r0 + 4 * c4);
+      }
+    }
+  }
+
+  __device__ static void store(const f32x4 (&r)[kV], float* s, int tid) {
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int f = tid + 256 * j;
+      if constexpr (kKc) {
+        const int c4 = f & 7, row = f >> 3;
+        *reinterpret_cast<f32x4*>(s + row * kPitch + 4 * c4) = r[j];
+      } else {
+        const int c4 = f % (kT / 4), k = f / (kT / 4);
+        f32x2* p = reinterpret_cast<f32x2*>(s + k * kPitch + 4 * c4);
+        p[0] = r[j].xy;
+        p[1] = r[j].zw;
+      }
+    }
+  }
+};
+
+template <bool kTA, bool kTB, int kT>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
+  using OA = TileOperand<!kTA, kT>;
+  using OB = TileOperand<kTB, kT>;
+  constexpr int kMT = kT / 64;
+  constexpr int kAcc = kMT == 1 ? 2 : 1;  // a lone 32 x 32 tile alternates two accumulators
+  __shared__ __align__(16) float As[2][OA::kFloats];
+  __shared__ __align__(16) float Bs[2][OB::kFloats];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, i32 = lane & 31;
+  const int wm = w >> 1, wn = w & 1;
+  const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
+  const int nk = g.K / kSK;
+
+  floatx16 acc[kMT][kMT][kAcc];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+      for (int a = 0; a < kAcc; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][a][v] = 0.f;
+
+  // Multiply one LDS stage: 16 MFMA k-steps, step kk uses k = 16h + kk.
+  auto compute = [&](const float* sa, const float* sb) {
+    f32x4 av[kMT][4], bv[kMT][4];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      if constexpr (!kTA) {
+        const float* p = sa + (wm * (kT / 2) + t * 32 + i32) * OA::kPitch + 16 * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) av[t][q] = *reinterpret_cast<const f32x4*>(p + 4 * q);
+      }
+      if constexpr (kTB) {
+        const float* p = sb + (wn * (kT / 2) + t * 32 + i32) * OB::kPitch + 16 * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bv[t][q] = *reinterpret_cast<const f32x4*>(p + 4 * q);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[kMT], b[kMT];
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) {
+        if constexpr (!kTA)
+          a[t] = av[t][kk >> 2][kk & 3];
+        else
+          a[t] = sa[(16 * h + kk) * OA::kPitch + wm * (kT / 2) + t * 32 + i32];
+        if constexpr (kTB)
+          b[t] = bv[t][kk >> 2][kk & 3];
+        else
+          b[t] = sb[(16 * h + kk) * OB::kPitch + wn * (kT / 2) + t * 32 + i32];
+      }
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kMT; ++j)
+          acc[i][j][kk % kAcc] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j][kk % kAcc], 0, 0, 0);
+    }
+  };
+
+  f32x4 ra0[OA::kV], rb0[OB::kV], ra1[OA::kV], rb1[OB::kV];
+  auto load = [&](f32x4 (&ra)[OA::kV], f32x4 (&rb)[OB::kV], int kt) {
+    OA::load(ra, g.A, g.lda, m0, kt * kSK, tid);
+    OB::load(rb, g.B, g.ldb, n0, kt * kSK, tid);
+  };
+  auto store = [&](const f32x4 (&ra)[OA::kV], const f32x4 (&rb)[OB::kV], int buf) {
+    OA::store(ra, As[buf], tid);
+    OB::store(rb, Bs[buf], tid);
+  };
+
+  // nk is even and >= 2.  Loads past the last stage re-read the last stage
+  // and are never multiplied: with no branch around a load, the compiler's
+  // wait before a store counts only the younger register set.
+  load(ra0, rb0, 0);
+  store(ra0, rb0, 0);
+  load(ra0, rb0, 1);
+  load(ra1, rb1, min(2, nk - 1));
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    // stage kt from buffer 0; set 0 holds stage kt + 1, set 1 stage kt + 2
+    compute(As[0], Bs[0]);
+    store(ra0, rb0, 1);
+    load(ra0, rb0, min(kt + 3, nk - 1));
+    __syncthreads();
+    compute(As[1], Bs[1]);
+    store(ra1, rb1, 0);
+    load(ra1, rb1, min(kt + 4, nk - 1));
+    __syncthreads();
+  }
+
+  // D = alpha * acc + beta * C + gamma * I (C may alias D: each element is
+  // read and written by the same lane)
+  const float alpha = g.alpha * (g.alpha_scale ? *g.alpha_scale : 1.f);
+#pragma unroll
+  for (int ti = 0; ti < kMT; ++ti) {
+#pragma unroll
+    for (int tj = 0; tj < kMT; ++tj) {
+      const int col = n0 + wn * (kT / 2) + tj * 32 + i32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * (kT / 2) + ti * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        float sum = acc[ti][tj][0][v];
+        if constexpr (kAcc == 2) sum += acc[ti][tj][1][v];
+        float r = alpha * sum;
+        if (g.beta != 0.f) r = fmaf(g.beta, g.C[int64_t(row) * g.ldc + col], r);
+        if (row == col) r += g.gamma;
+        g.D[int64_t(row) * g.ldd + col] = r;
+      }
+    }
+  }
+}
+
 // ||A + eps I||_F^2, first level: per-block partial sums in float64 (a fixed
 // order, so the result does not change from run to run).
 constexpr int kNormBlocks = 256;
@@ -216,8 +391,19 @@ __global__ __launch_bounds__(256) void muon_vector_kernel(const float* __restric
 }
 
 template <int kT>
-void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream) {
+void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, bool whole, hipStream_t stream) {
   const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT), block(256);
+  if (whole) {
+    if (!trans_a && !trans_b)
+      gemm_tile_kernel<false, false, kT><<<grid, block, 0, stream>>>(g);
+    else if (!trans_a && trans_b)
+      gemm_tile_kernel<false, true, kT><<<grid, block, 0, stream>>>(g);
+    else if (trans_a && !trans_b)
+      gemm_tile_kernel<true, false, kT><<<grid, block, 0, stream>>>(g);
+    else
+      gemm_tile_kernel<true, true, kT><<<grid, block, 0, stream>>>(g);
+    return;
+  }
   if (!trans_a && !trans_b)
     gemm_kernel<false, false, kT><<<grid, block, 0, stream>>>(g);
   else if (!trans_a && trans_b)
@@ -228,17 +414,26 @@ void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t
     gemm_kernel<true, true, kT><<<grid, block, 0, stream>>>(g);
 }
 
+bool aligned16(const void* p, int64_t ld) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && ld % 4 == 0;
+}
+
 }  // namespace
 
 // 128 x 128 workgroup tiles when they give at least one workgroup per CU,
-// 64 x 64 tiles otherwise (n x n products with n < 2048 on 256 CUs).
+// 64 x 64 tiles otherwise (n x n products with n < 2048 on 256 CUs).  Whole
+// tiles (M, N multiples of the edge, K of 64, 16-byte aligned operands) take
+// gemm_tile_kernel, anything else the bounds-checked gemm_kernel.
 hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int64_t big = int64_t((g.M + 127) / 128) * ((g.N + 127) / 128);
-  if (big >= 256)
-    launch_gemm_tile<128>(g, trans_a, trans_b, stream);
+  const int t = big >= 256 ? 128 : 64;
+  const bool whole = g.M % t == 0 && g.N % t == 0 && g.K > 0 && g.K % (2 * kSK) == 0 && aligned16(g.A, g.lda) &&
+                     aligned16(g.B, g.ldb);
+  if (t == 128)
+    launch_gemm_tile<128>(g, trans_a, trans_b, whole, stream);
   else
-    launch_gemm_tile<64>(g, trans_a, trans_b, stream);
+    launch_gemm_tile<64>(g, trans_a, trans_b, whole, stream);
   return hipGetLastError();
 }
 

@@ -108,3 +108,10 @@ def test_muon_sparse_payloads(dev, k, W, avg):
 
 def test_muon_weight_decay_and_small_eta(dev):
     run_case("muon_decay", [(256, 192), (300,)], 32, 3, 1e-2, 0.1)
+
+
+def test_muon_whole_tile_products(dev):
+    """Matrices large enough for 128 x 128 workgroup tiles: wide (Gram M M^T, then Z M) and tall (Gram M^T M,
+    then M Z) take the whole-tile GEMM for every product; 2048 x 2100 sends the Gram and the last product
+    (K or N not a multiple of the tile) through the bounds-checked GEMM while its iterations stay whole-tile."""
+    run_case("muon_whole_tiles", [(2048, 2304), (2304, 2048), (2048, 2100)], 32, 2, 1.0, 0.0)
