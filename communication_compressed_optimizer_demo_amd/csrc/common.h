@@ -57,6 +57,21 @@ __device__ __forceinline__ float update(float x, float m, const DecodeParams& p)
   return fmaf(-p.eta, fmaf(p.lam, x, ph), x);
 }
 
+// Scatter-add of one payload entry into a wave's LDS accumulator: the sum
+// gains v and the 8-bit contributor count (byte *cnt) gains 1.  Plain LDS
+// loads and stores, no atomic read-modify-write instruction: the lanes of one
+// call hold distinct coefficients, and one wave's LDS operations complete in
+// issue order, so the next call (the next worker) reads what this one wrote
+// and every coefficient sums its terms in worker order.  The relaxed
+// wave-scope atomic load/store only tell the compiler that other lanes touch
+// these locations; they compile to ordinary ds_read / ds_write.
+__device__ __forceinline__ void scatter_add(float* sum, uint8_t* cnt, float v) {
+  const float s = __hip_atomic_load(sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  const uint8_t n = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  __hip_atomic_store(sum, s + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  __hip_atomic_store(cnt, uint8_t(n + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
 // number of set lanes of `mask` below this lane
 __device__ __forceinline__ int lanes_below_mask(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));

@@ -27,9 +27,9 @@
 // decode/apply (§3.4 Server-Side Aggregation, Inverse DCT and Unchunking,
 // Base Optimizer Update):
 //   scatter-add W payloads into an LDS accumulator with 8-bit contributor
-//   counts, one LDS atomic instruction per worker in worker order 0..W-1
-//   (indices are distinct within one payload, so the lanes of one
-//   instruction never collide and the sum order is fixed); average;
+//   counts, atomic-free: one load-add-store per worker in worker order
+//   0..W-1 (indices are distinct within one payload, so the lanes of one
+//   step never collide and the sum order is fixed); average;
 //   M* = P0^T Q_bar P1; X = X - eta (phi(M*) + lambda X).
 #include "common.h"
 #include "launch.h"
@@ -242,10 +242,10 @@ __device__ __forceinline__ void clear_acc(uint32_t* lds, int lane) {
   for (int i = 0; i < kDecodeLdsWords / 256; ++i) l4[i * 64 + lane] = z;
 }
 
-// Add one payload entry (value v at coefficient (u, col)) to the accumulator.
+// Add one payload entry (value v at coefficient (u, col)) to the accumulator
+// and to its 8-bit contributor count (byte col of count row u).
 __device__ __forceinline__ void accumulate(float* acc, uint32_t* cntw, uint32_t u, uint32_t col, float v) {
-  atomicAdd(&acc[u * kLd + col], v);
-  atomicAdd(&cntw[u * kCntLd + (col >> 2)], 1u << ((col & 3u) * 8u));
+  scatter_add(acc + u * kLd + col, reinterpret_cast<uint8_t*>(cntw + u * kCntLd) + col, v);
 }
 
 // Entry f of worker w's payload: the float32 arrays, or the compact wire
@@ -270,8 +270,8 @@ __device__ __forceinline__ void load_entry(const DecodeParams& p, int64_t w, int
 }
 
 // Scatter-add the W payload segments of one 64x64 chunk (entries e0 ..
-// e0 + keff of every worker).  One LDS atomic instruction per (worker, entry
-// block); within it the indices are distinct, so no lanes collide and every
+// e0 + keff of every worker).  One scatter_add per (worker, entry block);
+// within it the indices are distinct, so no lanes collide and every
 // coefficient receives its terms in worker order.
 template <bool kWire>
 __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0,

@@ -684,8 +684,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 // XOR spreads one column of rows 2u + a (the averaging reads) over the banks.
 __device__ __forceinline__ void accumulate128(float* acc, uint32_t* cntw, uint32_t id, float v) {
   const uint32_t r = id >> 7, c = id & 127u, s = (r >> 1) & 31u;
-  atomicAdd(&acc[r * 128 + (c ^ s)], v);
-  atomicAdd(&cntw[r * 32 + ((c >> 2) ^ s)], 1u << ((c & 3u) * 8u));
+  scatter_add(&acc[r * 128 + (c ^ s)], reinterpret_cast<uint8_t*>(&cntw[r * 32 + ((c >> 2) ^ s)]) + (c & 3u), v);
 }
 
 __device__ __forceinline__ void clear_lds(uint32_t* lds, int tid) {
@@ -874,8 +873,8 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
         const int f = f0 + 64 * j + lane;
         if (f < n) {
           const uint32_t g = uint32_t(f / keff), cc = ii[j] & 127u;
-          atomicAdd(&acc[g * 128 + (cc ^ g)], vv[j]);
-          atomicAdd(&cntw[g * 32 + ((cc >> 2) ^ g)], 1u << ((cc & 3u) * 8u));
+          scatter_add(&acc[g * 128 + (cc ^ g)], reinterpret_cast<uint8_t*>(&cntw[g * 32 + ((cc >> 2) ^ g)]) + (cc & 3u),
+                      vv[j]);
         }
       }
     }
