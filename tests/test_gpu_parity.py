@@ -326,6 +326,15 @@ def test_more_workers_than_one_batch(dev, avg):
     Sim(w, avg=avg).run(2)
 
 
+@pytest.mark.parametrize("k,chunk", [(4096, 64), (8, 64), (16384, 128), (8, 128)])
+def test_maximum_workers(dev, k, chunk):
+    """W = 255, the most the 8-bit contributor counts allow: at lossless k every coefficient is sent by
+    all 255 workers (count 255 everywhere); at k = 8 the counts vary per coefficient."""
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"w255_k{k}_s{chunk}", shapes=((chunk, 2 * chunk), (100,)),
+                                         workers=255, k=k)
+    Sim(w, chunk=chunk).run(2)
+
+
 @pytest.mark.parametrize("name,k,avg,rand", [("tiny_256", 8, "count", False), ("edge_mix", 4, "workers", False),
                                               ("edge_mix", 37, "count", True)])
 def test_one_bit_sign_download(dev, name, k, avg, rand):
