@@ -129,23 +129,53 @@ __device__ __forceinline__ int popc64(uint64_t v) { return __popcll(v); }
 // bits below position n (n in 0..64)
 __device__ __forceinline__ uint64_t below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
 
-// per-wave LDS transposes (every wave of the workgroup calls them together)
+// Orders one wave's LDS stores before its later LDS loads (other lanes of the
+// same wave read what a lane wrote).  A wave's LDS operations complete in
+// issue order, so no wait is needed; the fences keep the compiler from
+// moving loads above the stores.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-wave LDS transposes through the wave's own tile.  col_to_row only
+// synchronises the wave: its tile is its own, and whatever LDS the workgroup
+// used before was released by a workgroup barrier.  row_to_col ends with a
+// workgroup barrier because a butterfly exchange, which spans every wave's
+// tile, may follow it.
 __device__ __forceinline__ void col_to_row(float* tile, float (&x)[64], int lane) {
 #pragma unroll
   for (int i = 0; i < 64; ++i) tile[i * kLd + lane] = x[i];
-  __syncthreads();
+  wave_sync();
 #pragma unroll
   for (int v = 0; v < 64; ++v) x[v] = tile[lane * kLd + v];
-  __syncthreads();
+  wave_sync();
 }
 
 __device__ __forceinline__ void row_to_col(float* tile, float (&x)[64], int lane) {
 #pragma unroll
   for (int v = 0; v < 64; ++v) tile[lane * kLd + v] = x[v];
-  __syncthreads();
+  wave_sync();
 #pragma unroll
   for (int i = 0; i < 64; ++i) x[i] = tile[i * kLd + lane];
   __syncthreads();
+}
+
+// Wave W's share of the exchange: x <- (x_0 + sb x_1) + sa (x_2 + sb x_3),
+// sa = (-1)^a, sb = (-1)^b for W = 2a + b, x_q the rows of wave q (x_W is
+// this wave's own registers).  The same operations, in the same order, as a
+// two-point butterfly along dimension 1 followed by one along dimension 0.
+template <int W>
+__device__ __forceinline__ void butterfly_combine(float (&x)[64], const float* xq, int lane) {
+  constexpr float sa = (W & 2) ? -1.f : 1.f, sb = (W & 1) ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = q == W ? x[i] : xq[q * kQuad + i * 64 + lane];
+    x[i] = fmaf(sa, fmaf(sb, v[3], v[2]), fmaf(sb, v[1], v[0]));
+  }
 }
 
 // One butterfly stage between wave w and wave w ^ bit: the wave without `bit`
@@ -161,14 +191,29 @@ __device__ __forceinline__ void butterfly_stage(float (&x)[64], float* xq, int w
   __syncthreads();
 }
 
-// x <- sum over the four waves' x (same i, same lane) with sign (-1)^(a qa + b qb),
-// (a, b) the bits of this wave, (qa, qb) those of the other: the two-point
-// butterfly along dimension 1 (bit 1), then along dimension 0 (bit 2).
-// Forward: quadrants -> S_ab; inverse: S'_ab -> quadrants.  Leaves the
-// exchange area free.
-__device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int lane) {
+// The same exchange as butterfly() in two stages (along dimension 1, then 0),
+// each through LDS: two more barriers, fewer live registers, bitwise the same
+// result.  Used where the registers are full (decode updating X and M).
+__device__ __forceinline__ void butterfly_staged(float (&x)[64], float* xq, int w, int lane) {
   butterfly_stage(x, xq, w, lane, 1);
   butterfly_stage(x, xq, w, lane, 2);
+}
+
+// x <- sum over the four waves' x (same i, same lane) with sign (-1)^(a qa + b qb),
+// (a, b) the bits of this wave, (qa, qb) those of the other.
+// Forward: quadrants -> S_ab; inverse: S'_ab -> quadrants.  One exchange
+// through LDS; leaves the exchange area free.
+__device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) xq[w * kQuad + i * 64 + lane] = x[i];
+  __syncthreads();
+  switch (w) {
+    case 0: butterfly_combine<0>(x, xq, lane); break;
+    case 1: butterfly_combine<1>(x, xq, lane); break;
+    case 2: butterfly_combine<2>(x, xq, lane); break;
+    default: butterfly_combine<3>(x, xq, lane); break;
+  }
+  __syncthreads();
 }
 
 struct Chunk128 {
@@ -799,7 +844,10 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
     }
   }
   inv_half(q, a);
-  butterfly(q, reinterpret_cast<float*>(lds), w, lane);  // -> M* of quadrant w
+  if constexpr (kTargets == (kToParams | kToMomentum))
+    butterfly_staged(q, reinterpret_cast<float*>(lds), w, lane);  // -> M* of quadrant w
+  else
+    butterfly(q, reinterpret_cast<float*>(lds), w, lane);
 
   if constexpr ((kTargets & kToParams) != 0) {
 #pragma unroll
