@@ -169,19 +169,19 @@ constexpr int kSK = 32;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// One operand's stage: kT rows (along M for A, N for B) by kSK values of k.
-// kKc: element (row, k) sits at X[row * ld + k] (rows along K in memory);
-// otherwise at X[k * ld + row].
-template <bool kKc, int kT>
+// One operand's stage: kT rows (along M for A, N for B) by kSK values of k,
+// moved by kThreads threads.  kKc: element (row, k) sits at X[row * ld + k]
+// (rows along K in memory); otherwise at X[k * ld + row].
+template <bool kKc, int kT, int kThreads>
 struct TileOperand {
-  static constexpr int kV = kT / 32;  // f32x4 per thread and stage
+  static constexpr int kV = kT * kSK / 4 / kThreads;  // f32x4 per thread and stage
   static constexpr int kPitch = kKc ? kSK + 4 : kT + 2;
   static constexpr int kFloats = kKc ? kT * kPitch : kSK * kPitch;
 
   __device__ static void load(f32x4 (&r)[kV], const float* __restrict__ X, int64_t ld, int r0, int k0, int tid) {
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
-      const int f = tid + 256 * j;
+      const int f = tid + kThreads * j;
       if constexpr (kKc) {
         const int c4 = f & 7, row = f >> 3;
         r[j] = *reinterpret_cast<const f32x4*>(X + int64_t(r0 + row) * ld + k0 + 4 * c4);
@@ -195,7 +195,7 @@ struct TileOperand {
   __device__ static void store(const f32x4 (&r)[kV], float* s, int tid) {
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
-      const int f = tid + 256 * j;
+      const int f = tid + kThreads * j;
       if constexpr (kKc) {
         const int c4 = f & 7, row = f >> 3;
         *reinterpret_cast<f32x4*>(s + row * kPitch + 4 * c4) = r[j];
@@ -209,12 +209,14 @@ struct TileOperand {
   }
 };
 
-template <bool kTA, bool kTB, int kT>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
-  using OA = TileOperand<!kTA, kT>;
-  using OB = TileOperand<kTB, kT>;
-  constexpr int kMT = kT / 64;
-  constexpr int kAcc = kMT == 1 ? 2 : 1;  // a lone 32 x 32 tile alternates two accumulators
+// kWM x 2 waves; wave tile (kT / kWM) x (kT / 2), i.e. kMI x kMJ MFMA tiles.
+template <bool kTA, bool kTB, int kT, int kWM>
+__global__ __launch_bounds__(128 * kWM) void gemm_tile_kernel(GemmArgs g) {
+  constexpr int kThreads = 128 * kWM;
+  using OA = TileOperand<!kTA, kT, kThreads>;
+  using OB = TileOperand<kTB, kT, kThreads>;
+  constexpr int kMI = kT / kWM / 32, kMJ = kT / 64;
+  constexpr int kAcc = kMI * kMJ == 1 ? 2 : 1;  // a lone 32 x 32 tile alternates two accumulators
   __shared__ __align__(16) float As[2][OA::kFloats];
   __shared__ __align__(16) float Bs[2][OB::kFloats];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -223,11 +225,11 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   const int nk = g.K / kSK;
 
-  floatx16 acc[kMT][kMT][kAcc];
+  floatx16 acc[kMI][kMJ][kAcc];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i)
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < kMT; ++j)
+    for (int j = 0; j < kMJ; ++j)
 #pragma unroll
       for (int a = 0; a < kAcc; ++a)
 #pragma unroll
@@ -235,14 +237,17 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 
   // Multiply one LDS stage: 16 MFMA k-steps, step kk uses k = 16h + kk.
   auto compute = [&](const float* sa, const float* sb) {
-    f32x4 av[kMT][4], bv[kMT][4];
+    f32x4 av[kMI][4], bv[kMJ][4];
 #pragma unroll
-    for (int t = 0; t < kMT; ++t) {
+    for (int t = 0; t < kMI; ++t) {
       if constexpr (!kTA) {
-        const float* p = sa + (wm * (kT / 2) + t * 32 + i32) * OA::kPitch + 16 * h;
+        const float* p = sa + (wm * (kT / kWM) + t * 32 + i32) * OA::kPitch + 16 * h;
 #pragma unroll
         for (int q = 0; q < 4; ++q) av[t][q] = *reinterpret_cast<const f32x4*>(p + 4 * q);
       }
+    }
+#pragma unroll
+    for (int t = 0; t < kMJ; ++t) {
       if constexpr (kTB) {
         const float* p = sb + (wn * (kT / 2) + t * 32 + i32) * OB::kPitch + 16 * h;
 #pragma unroll
@@ -251,22 +256,25 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      float a[kMT], b[kMT];
+      float a[kMI], b[kMJ];
 #pragma unroll
-      for (int t = 0; t < kMT; ++t) {
+      for (int t = 0; t < kMI; ++t) {
         if constexpr (!kTA)
           a[t] = av[t][kk >> 2][kk & 3];
         else
-          a[t] = sa[(16 * h + kk) * OA::kPitch + wm * (kT / 2) + t * 32 + i32];
+          a[t] = sa[(16 * h + kk) * OA::kPitch + wm * (kT / kWM) + t * 32 + i32];
+      }
+#pragma unroll
+      for (int t = 0; t < kMJ; ++t) {
         if constexpr (kTB)
           b[t] = bv[t][kk >> 2][kk & 3];
         else
           b[t] = sb[(16 * h + kk) * OB::kPitch + wn * (kT / 2) + t * 32 + i32];
       }
 #pragma unroll
-      for (int i = 0; i < kMT; ++i)
+      for (int i = 0; i < kMI; ++i)
 #pragma unroll
-        for (int j = 0; j < kMT; ++j)
+        for (int j = 0; j < kMJ; ++j)
           acc[i][j][kk % kAcc] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j][kk % kAcc], 0, 0, 0);
     }
   };
@@ -305,13 +313,13 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
   // read and written by the same lane)
   const float alpha = g.alpha * (g.alpha_scale ? *g.alpha_scale : 1.f);
 #pragma unroll
-  for (int ti = 0; ti < kMT; ++ti) {
+  for (int ti = 0; ti < kMI; ++ti) {
 #pragma unroll
-    for (int tj = 0; tj < kMT; ++tj) {
+    for (int tj = 0; tj < kMJ; ++tj) {
       const int col = n0 + wn * (kT / 2) + tj * 32 + i32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * (kT / 2) + ti * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int row = m0 + wm * (kT / kWM) + ti * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         float sum = acc[ti][tj][0][v];
         if constexpr (kAcc == 2) sum += acc[ti][tj][1][v];
         float r = alpha * sum;
@@ -394,14 +402,17 @@ template <int kT>
 void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, bool whole, hipStream_t stream) {
   const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT), block(256);
   if (whole) {
+    // 128 x 128 tiles: 4 x 2 waves (two per SIMD at one workgroup per CU)
+    constexpr int kWM = kT == 128 ? 4 : 2;
+    const dim3 wblock(128 * kWM);
     if (!trans_a && !trans_b)
-      gemm_tile_kernel<false, false, kT><<<grid, block, 0, stream>>>(g);
+      gemm_tile_kernel<false, false, kT, kWM><<<grid, wblock, 0, stream>>>(g);
     else if (!trans_a && trans_b)
-      gemm_tile_kernel<false, true, kT><<<grid, block, 0, stream>>>(g);
+      gemm_tile_kernel<false, true, kT, kWM><<<grid, wblock, 0, stream>>>(g);
     else if (trans_a && !trans_b)
-      gemm_tile_kernel<true, false, kT><<<grid, block, 0, stream>>>(g);
+      gemm_tile_kernel<true, false, kT, kWM><<<grid, wblock, 0, stream>>>(g);
     else
-      gemm_tile_kernel<true, true, kT><<<grid, block, 0, stream>>>(g);
+      gemm_tile_kernel<true, true, kT, kWM><<<grid, wblock, 0, stream>>>(g);
     return;
   }
   if (!trans_a && !trans_b)
