@@ -113,36 +113,39 @@ def cpu_baseline(w: DI.Workload):
         res = list(ex.map(_foreign_payload, jobs))
     foreign = {(t, wk): r for (_, wk, t), r in zip(jobs, res)}
     def timed(tensors):
-        dt = 0.0
+        """Wall and CPU seconds (all threads of the process) of the oracle over `tensors`."""
+        dt = cpu = 0.0
         for t in tensors:
             g0 = DI.gradient(w, 0, 0, t)
             x0 = DI.initial_params(w, t)
-            t0 = time.perf_counter()
+            t0, c0 = time.perf_counter(), time.process_time()
             out = O.encode(np.zeros_like(g0), g0, beta=w.beta, alpha=w.alpha, k=w.k)
             vals = np.stack([out["values"]] + [foreign[(t, wk)][0] for wk in range(1, w.workers)])
             idx = np.stack([out["idx"]] + [foreign[(t, wk)][1] for wk in range(1, w.workers)])
             O.decode_apply(x0, vals, idx, phi=w.phi, eta=w.eta, lam=w.lam)
             dt += time.perf_counter() - t0
-        return dt
+            cpu += time.process_time() - c0
+        return dt, cpu
 
     log("cpu baseline: timing the oracle")
-    dt = timed(sample)
-    log(f"cpu baseline: {dt:.2f} s")
+    dt, cpu = timed(sample)
+    log(f"cpu baseline: {dt:.2f} s wall, {cpu:.2f} s CPU")
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     # the same oracle on one thread, over the first tensor only (a few seconds)
     with threadpool_limits(1):
-        dt1 = timed(sample[:1])
+        dt1, _ = timed(sample[:1])
     n1 = int(np.prod(w.shapes[sample[0]]))
     log(f"cpu baseline, one thread: {dt1:.2f} s")
     return {
         "value": n / dt,
         "unit": "params/s",
-        "cores": int(threads),
+        # cores actually used: CPU seconds over wall seconds of the timed region
+        "cores": max(1, round(cpu / dt)),
         "kind": "oracle",
         "sample": (f"the first {len(sample)} tensors of the list ({n} params, "
                    f"{sum(1 for t in sample if len(w.shapes[t]) == 2)} matrices): worker-0 encode + decode/apply "
                    f"over W={w.workers} payloads, tensor by tensor (W-1 foreign payloads precomputed, untimed); "
-                   f"{dt:.2f} s"),
+                   f"{dt:.2f} s wall, {cpu:.2f} s CPU with {threads} BLAS threads available"),
         "cpu": cpu_model(),
         "one_thread": {"value": n1 / dt1, "unit": "params/s",
                        "sample": f"the first tensor ({n1} params), same work, BLAS limited to 1 thread; {dt1:.2f} s"},
