@@ -265,30 +265,34 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
 }
 
 // Workspace of the Muon decode: M* of every tensor (offsets rounded up to 64
-// floats), then six n_max x n_max fp32 matrices for the Newton-Schulz
-// iteration (A, Y, Y', Z, Z', T), 256 doubles of partial sums and two floats.
+// floats), then `slots` Newton-Schulz slots, one per matrix of a batch, each
+// six n x n fp32 matrices (A, Y, Y', Z, Z', T) for n up to n_max (rounded up
+// to 64 floats), 256 doubles of partial sums and 64 floats (two used).
+constexpr int64_t kMuonBatch = 8;  // matrices whose iterations share launches
+
 struct MuonLayout {
   std::vector<int64_t> mstar;  // float offset of each tensor's M*
-  int64_t nmax = 0;
-  int64_t ns = 0, partial = 0, scal = 0, bytes = 0;  // float offsets / total bytes
+  int64_t nmax = 0, slots = 0;
+  int64_t ns = 0, slot = 0, partial = 0, scal = 0, bytes = 0;  // float offsets / sizes; total bytes
 };
 
 MuonLayout muon_layout(const std::vector<TensorPlan>& plan) {
   MuonLayout L;
-  int64_t off = 0;
+  int64_t off = 0, matrices = 0;
   for (const auto& t : plan) {
     L.mstar.push_back(off);
     off += (t.rows * t.cols + 63) / 64 * 64;
-    if (t.ndim == 2) L.nmax = std::max(L.nmax, std::min(t.rows, t.cols));
+    if (t.ndim == 2) {
+      L.nmax = std::max(L.nmax, std::min(t.rows, t.cols));
+      ++matrices;
+    }
   }
   L.ns = off;
-  off += 6 * L.nmax * L.nmax;
-  off = (off + 63) / 64 * 64;
-  L.partial = off;
-  off += 2 * 256;  // 256 doubles
-  L.scal = off;
-  off += 64;
-  L.bytes = off * 4;
+  L.slots = std::min(matrices, kMuonBatch);
+  L.partial = (6 * L.nmax * L.nmax + 63) / 64 * 64;  // inside a slot
+  L.scal = L.partial + 2 * 256;
+  L.slot = L.scal + 64;
+  L.bytes = (L.ns + L.slots * L.slot) * 4;
   return L;
 }
 
@@ -515,89 +519,112 @@ demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* s
                                     std::to_string(L.bytes));
   if (L.bytes > 0 && workspace == nullptr) return fail(DEMO_ERR_INVALID, "workspace is NULL");
   if (!aligned(workspace, 16)) return fail(DEMO_ERR_ALIGN, "workspace misaligned (16 bytes)");
-  float* ws = static_cast<float*>(workspace);
-  std::vector<float*> mstar(size_t(n > 0 ? n : 0));
-  for (int32_t i = 0; i < n; ++i) mstar[i] = ws + L.mstar[i];
-  // rows a7, a8: M* of every tensor into the workspace (validates the rest)
-  s = decode_common(ctx, n, shapes, nullptr, nullptr, cfg, workers, pay_values, pay_idx, n_entries, DEMO_PHI_IDENTITY,
-                    eta, lambda, avg, stream, nullptr, 0, mstar.data());
-  if (s != DEMO_OK) return s;
   for (int32_t i = 0; i < n; ++i) {
     if (params[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
     if (!aligned(params[i], 4)) return fail(DEMO_ERR_ALIGN, "tensor " + std::to_string(i) + ": misaligned pointer");
   }
+  float* ws = static_cast<float*>(workspace);
+  std::vector<float*> mstar(size_t(n > 0 ? n : 0));
+  for (int32_t i = 0; i < n; ++i) mstar[i] = ws + L.mstar[i];
+  // rows a7, a8: M* of every tensor into the workspace (validates the rest,
+  // the context last; nothing is enqueued unless all of it passes)
+  s = decode_common(ctx, n, shapes, nullptr, nullptr, cfg, workers, pay_values, pay_idx, n_entries, DEMO_PHI_IDENTITY,
+                    eta, lambda, avg, stream, nullptr, 0, mstar.data());
+  if (s != DEMO_OK) return s;
   auto check = [&](hipError_t e) -> demo_status {
     if (e != hipSuccess) return fail(DEMO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return DEMO_OK;
   };
-  float* scal = ws + L.scal;
-  double* partial = reinterpret_cast<double*>(ws + L.partial);
+  // Vectors now; matrices in list order, batched while they share n: their
+  // Newton-Schulz products go out as one launch per step with one slot each.
+  std::vector<int32_t> mats;
   for (int32_t i = 0; i < n; ++i) {
     const TensorPlan& t = plan[i];
-    const float* Ms = mstar[i];
-    float* X = params[i];
     if (t.ndim == 1) {
-      if ((s = check(demo::launch_muon_vector(Ms, X, t.rows, eps, eta, lambda, stream))) != DEMO_OK) return s;
-      continue;
+      if ((s = check(demo::launch_muon_vector(mstar[i], params[i], t.rows, eps, eta, lambda, stream))) != DEMO_OK)
+        return s;
+    } else {
+      mats.push_back(i);
     }
-    const int32_t r = int32_t(t.rows), c = int32_t(t.cols);
-    const bool wide = r <= c;
-    const int32_t nn = wide ? r : c;
+  }
+  auto small_dim = [&](int32_t i) { return int32_t(std::min(plan[i].rows, plan[i].cols)); };
+  for (size_t b0 = 0; b0 < mats.size();) {
+    const int32_t nn = small_dim(mats[b0]);
+    size_t b1 = b0 + 1;
+    while (b1 < mats.size() && int64_t(b1 - b0) < L.slots && small_dim(mats[b1]) == nn) ++b1;
+    const int32_t nb = int32_t(b1 - b0);
     const int64_t sq = int64_t(nn) * nn;
-    float* A = ws + L.ns;
-    float *Y = A + sq, *Y2 = Y + sq, *Z = Y2 + sq, *Z2 = Z + sq, *T = Z2 + sq;
-    demo::GemmArgs g{};
-    // Gram: A = M M^T (wide) or M^T M
-    g.A = Ms;
-    g.B = Ms;
-    g.D = A;
-    g.M = g.N = nn;
-    g.K = wide ? c : r;
-    g.lda = g.ldb = c;
-    g.ldd = nn;
-    g.alpha = 1.f;
-    if ((s = check(demo::launch_gemm(g, !wide, wide, stream))) != DEMO_OK) return s;
-    if ((s = check(demo::launch_ns_prepare(A, nn, eps, partial, scal, Y, Z, stream))) != DEMO_OK) return s;
+    float* base = ws + L.ns;  // slot j starts at base + j * L.slot
+    // per matrix: Gram A = M M^T (wide) or M^T M, then Y0, Z0 and the scale
+    for (int32_t j = 0; j < nb; ++j) {
+      const TensorPlan& t = plan[mats[b0 + j]];
+      const int32_t r = int32_t(t.rows), c = int32_t(t.cols);
+      const bool wide = r <= c;
+      float* slot = base + j * L.slot;
+      demo::GemmArgs g{};
+      g.A = mstar[mats[b0 + j]];
+      g.B = g.A;
+      g.D = slot;
+      g.M = g.N = nn;
+      g.K = wide ? c : r;
+      g.lda = g.ldb = c;
+      g.ldd = nn;
+      g.alpha = 1.f;
+      if ((s = check(demo::launch_gemm(g, !wide, wide, 1, stream))) != DEMO_OK) return s;
+      if ((s = check(demo::launch_ns_prepare(slot, nn, eps, reinterpret_cast<double*>(slot + L.partial),
+                                             slot + L.scal, slot + sq, slot + 3 * sq, stream))) != DEMO_OK)
+        return s;
+    }
+    float *Y = base + sq, *Y2 = base + 2 * sq, *Z = base + 3 * sq, *Z2 = base + 4 * sq, *T = base + 5 * sq;
     for (int32_t it = 0; it < iters; ++it) {
       demo::GemmArgs h{};
       h.M = h.N = h.K = nn;
       h.lda = h.ldb = h.ldd = nn;
+      h.sA = h.sB = h.sD = L.slot;
       // T = 1.5 I - 0.5 Z Y
       h.A = Z;
       h.B = Y;
       h.D = T;
       h.alpha = -0.5f;
       h.gamma = 1.5f;
-      if ((s = check(demo::launch_gemm(h, false, false, stream))) != DEMO_OK) return s;
+      if ((s = check(demo::launch_gemm(h, false, false, nb, stream))) != DEMO_OK) return s;
       h.gamma = 0.f;
       h.alpha = 1.f;
       h.A = Y;  // Y' = Y T
       h.B = T;
       h.D = Y2;
-      if ((s = check(demo::launch_gemm(h, false, false, stream))) != DEMO_OK) return s;
+      if ((s = check(demo::launch_gemm(h, false, false, nb, stream))) != DEMO_OK) return s;
       h.A = T;  // Z' = T Z
       h.B = Z;
       h.D = Z2;
-      if ((s = check(demo::launch_gemm(h, false, false, stream))) != DEMO_OK) return s;
+      if ((s = check(demo::launch_gemm(h, false, false, nb, stream))) != DEMO_OK) return s;
       std::swap(Y, Y2);
       std::swap(Z, Z2);
     }
-    // X = (1 - eta lambda) X - eta / sqrt(s) * (Z M  or  M Z), Z ~ (A + eps I)^(-1/2) sqrt(s)
-    demo::GemmArgs f{};
-    f.A = wide ? Z : Ms;
-    f.B = wide ? Ms : Z;
-    f.C = X;
-    f.D = X;
-    f.M = r;
-    f.N = c;
-    f.K = wide ? r : c;
-    f.lda = wide ? nn : c;
-    f.ldb = wide ? c : nn;
-    f.ldc = f.ldd = c;
-    f.alpha = -eta;
-    f.alpha_scale = scal + 1;
-    f.beta = 1.f - eta * lambda;
-    if ((s = check(demo::launch_gemm(f, false, false, stream))) != DEMO_OK) return s;
+    // per matrix: X = (1 - eta lambda) X - eta / sqrt(s) * (Z M  or  M Z), Z ~ (A + eps I)^(-1/2) sqrt(s)
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t i = mats[b0 + j];
+      const TensorPlan& t = plan[i];
+      const int32_t r = int32_t(t.rows), c = int32_t(t.cols);
+      const bool wide = r <= c;
+      const float* Zj = Z + j * L.slot;
+      demo::GemmArgs f{};
+      f.A = wide ? Zj : mstar[i];
+      f.B = wide ? mstar[i] : Zj;
+      f.C = params[i];
+      f.D = params[i];
+      f.M = r;
+      f.N = c;
+      f.K = wide ? r : c;
+      f.lda = wide ? nn : c;
+      f.ldb = wide ? c : nn;
+      f.ldc = f.ldd = c;
+      f.alpha = -eta;
+      f.alpha_scale = base + j * L.slot + L.scal + 1;
+      f.beta = 1.f - eta * lambda;
+      if ((s = check(demo::launch_gemm(f, false, false, 1, stream))) != DEMO_OK) return s;
+    }
+    b0 = b1;
   }
   return DEMO_OK;
 }

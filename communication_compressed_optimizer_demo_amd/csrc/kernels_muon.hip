@@ -31,10 +31,20 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 16, kPad = 4;
 
+// Product blockIdx.z of a batch: move the operand pointers to it.
+__device__ __forceinline__ void select_product(GemmArgs& g) {
+  const int64_t z = blockIdx.z;
+  g.A += z * g.sA;
+  g.B += z * g.sB;
+  if (g.C) g.C += z * g.sC;
+  g.D += z * g.sD;
+}
+
 // kT: workgroup tile edge (128 or 64); the four waves form a 2 x 2 grid of
 // kT/2 x kT/2 wave tiles, each (kT/64) x (kT/64) MFMA tiles of 32 x 32.
 template <bool kTA, bool kTB, int kT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  select_product(g);
   constexpr int E = kT / 16;    // floats each thread stages per operand and K stage
   constexpr int kMT = kT / 64;  // MFMA tiles per wave and dimension
   __shared__ float As[2][kBK][kT + kPad];
@@ -212,6 +222,7 @@ struct TileOperand {
 // kWM x 2 waves; wave tile (kT / kWM) x (kT / 2), i.e. kMI x kMJ MFMA tiles.
 template <bool kTA, bool kTB, int kT, int kWM>
 __global__ __launch_bounds__(128 * kWM) void gemm_tile_kernel(GemmArgs g) {
+  select_product(g);
   constexpr int kThreads = 128 * kWM;
   using OA = TileOperand<!kTA, kT, kThreads>;
   using OB = TileOperand<kTB, kT, kThreads>;
@@ -399,8 +410,8 @@ __global__ __launch_bounds__(256) void muon_vector_kernel(const float* __restric
 }
 
 template <int kT>
-void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, bool whole, hipStream_t stream) {
-  const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT), block(256);
+void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, bool whole, int32_t batch, hipStream_t stream) {
+  const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT, batch), block(256);
   if (whole) {
     // 128 x 128 tiles: 4 x 2 waves (two per SIMD at one workgroup per CU)
     constexpr int kWM = kT == 128 ? 4 : 2;
@@ -431,20 +442,20 @@ bool aligned16(const void* p, int64_t ld) {
 
 }  // namespace
 
-// 128 x 128 workgroup tiles when they give at least one workgroup per CU,
-// 64 x 64 tiles otherwise (n x n products with n < 2048 on 256 CUs).  Whole
-// tiles (M, N multiples of the edge, K of 64, 16-byte aligned operands) take
-// gemm_tile_kernel, anything else the bounds-checked gemm_kernel.
-hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const int64_t big = int64_t((g.M + 127) / 128) * ((g.N + 127) / 128);
+// 128 x 128 workgroup tiles when the batch has at least one such workgroup
+// per CU, 64 x 64 tiles otherwise.  Whole tiles (M, N multiples of the edge,
+// K of 64, 16-byte aligned operands and strides) take gemm_tile_kernel,
+// anything else the bounds-checked gemm_kernel.
+hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, int32_t batch, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+  const int64_t big = int64_t((g.M + 127) / 128) * ((g.N + 127) / 128) * batch;
   const int t = big >= 256 ? 128 : 64;
   const bool whole = g.M % t == 0 && g.N % t == 0 && g.K > 0 && g.K % (2 * kSK) == 0 && aligned16(g.A, g.lda) &&
-                     aligned16(g.B, g.ldb);
+                     aligned16(g.B, g.ldb) && (batch == 1 || (g.sA % 4 == 0 && g.sB % 4 == 0));
   if (t == 128)
-    launch_gemm_tile<128>(g, trans_a, trans_b, whole, stream);
+    launch_gemm_tile<128>(g, trans_a, trans_b, whole, batch, stream);
   else
-    launch_gemm_tile<64>(g, trans_a, trans_b, whole, stream);
+    launch_gemm_tile<64>(g, trans_a, trans_b, whole, batch, stream);
   return hipGetLastError();
 }
 

@@ -107,8 +107,11 @@ struct GemmArgs {
   int64_t lda, ldb, ldc, ldd;
   float alpha, beta, gamma;
   const float* alpha_scale;
+  int64_t sA, sB, sC, sD;  // element strides between the products of a batch
 };
-hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, hipStream_t stream);
+// `batch` products of the same shape: product z reads A + z sA, B + z sB,
+// C + z sC and writes D + z sD.
+hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, int32_t batch, hipStream_t stream);
 // partial: 256 doubles; scal: 2 floats (1/s, 1/sqrt(s)), s = ||A + eps I||_F;
 // Y = (A + eps I) / s, Z = I (all n x n)
 hipError_t launch_ns_prepare(const float* A, int n, float eps, double* partial, float* scal, float* Y, float* Z,

@@ -263,7 +263,10 @@ demo_status demo_decode_apply_wire(demo_ctx* ctx, int32_t n, const demo_shape* s
  * cores), a vector (one column) through m / sqrt(m.m + eps).  Built for chunk
  * edge 64. */
 
-/* Host-only: bytes of device workspace demo_decode_apply_muon needs for a list. */
+/* Host-only: bytes of device workspace demo_decode_apply_muon needs for a list:
+ * M* of every tensor, then one slot of Newton-Schulz matrices (six n x n,
+ * n the largest smaller dimension) per matrix of a batch, up to 8 matrices
+ * with equal smaller dimension sharing each iteration launch. */
 demo_status demo_muon_workspace(const demo_shape* shapes, int32_t n, int64_t* ws_bytes);
 
 /* demo_decode_apply with phi = Muon: X <- X - eta * (phi(M*) + lambda * X).

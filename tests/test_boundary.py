@@ -309,12 +309,21 @@ def test_chunk128_valid_arguments_reach_the_context_check(lib):
 # --------------------------------------------------------------------------- phi = Muon
 
 def test_muon_workspace_size(lib):
-    # M* of every tensor (64-float rounded), six n_max^2 matrices, 256 doubles, 64 floats
+    # M* of every tensor (64-float rounded), then one slot per matrix (at most 8): six n_max^2 matrices
+    # (64-float rounded), 256 doubles, 64 floats
     shapes = [(70, 90), (100,), (130, 200)]
     mstar = (6336 + 128 + 26048)
-    ns = 6 * 130 * 130
-    want = (((mstar + ns) + 63) // 64 * 64 + 512 + 64) * 4
-    assert B.demo_muon_workspace(shapes) == want
+    slot = (6 * 130 * 130 + 63) // 64 * 64 + 512 + 64
+    assert B.demo_muon_workspace(shapes) == (mstar + 2 * slot) * 4
+    many = [(64, 96)] * 11 + [(10,)]
+    assert B.demo_muon_workspace(many) == (11 * 6144 + 64 + 8 * (6 * 64 * 64 + 576)) * 4
+
+
+def test_muon_params_checked_before_any_work(lib):
+    # a NULL parameter pointer is refused before the decode of M* could be enqueued: with every other
+    # argument valid and no context, the status names the tensor, not the context
+    assert _call_muon(lib, [(70, 90), (100,)], params=0) == 1
+    assert "NULL device pointer" in _msg(lib)
 
 
 def _call_muon(lib, shapes, k=8, workers=2, eps=1e-6, iters=24, ws=0x7000, ws_bytes=None, chunk=64, params=0x1000,
