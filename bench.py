@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmo_1b", choices=sorted(DI.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--basis", default="dct", choices=("dct", "identity"),
+    ap.add_argument("--basis", default="dct", choices=("dct", "identity", "random"),
                     help="projection (identity: the ablation that ranks in the parameter domain)")
     ap.add_argument("--subtraction", default="local", choices=("local", "aggregated"),
                     help="momentum subtraction of the worker's own coefficients, or of the averaged ones")
@@ -301,6 +301,13 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     aggregated = subtraction == "aggregated"
     codec = B.Codec(shapes, w.k, w.beta, w.alpha, identity=basis == "identity", aggregated=aggregated, chunk=chunk)
     launches = -(-len(shapes) // B.DEMO_MAX_TENSORS_PER_LAUNCH)
+    basis_kw = {}
+    if basis == "random":
+        # the caller's orthonormal projection: rows of the Q factor of the step's seeded N(0, 1) draws
+        # (any orthonormal basis is a valid one; the same two matrices serve every worker)
+        import numpy as np
+        P = [np.linalg.qr(DI.gaussian_matrix(w, 0, which).T)[0].T.astype(np.float32) for which in (0, 1)]
+        basis_kw = {"P0": torch.from_numpy(P[0].copy()).to(dev), "P1": torch.from_numpy(P[1].copy()).to(dev)}
     G = [DI.device_gradient(w, 0, 0, i, dev) for i in range(len(shapes))]
     M = [torch.zeros(s, device=dev) for s in shapes]
     X = [DI.device_initial_params(w, i, dev) for i in range(len(shapes))]
@@ -312,7 +319,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
         for t in scratch_m:
             t.zero_()
         gf = [DI.device_gradient(w, wk, 0, i, dev) for i in range(len(shapes))]
-        codec.encode(gf, scratch_m, vals[wk * ne:(wk + 1) * ne], pidx[wk * ne:(wk + 1) * ne])
+        codec.encode(gf, scratch_m, vals[wk * ne:(wk + 1) * ne], pidx[wk * ne:(wk + 1) * ne], **basis_kw)
         del gf
     del scratch_m
     torch.cuda.synchronize()
@@ -341,7 +348,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     muon_eps = 1e-12
 
     # the step's calls in order; HIP events between them time each one
-    calls = [("encode", lambda: codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream))]
+    calls = [("encode", lambda: codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream, **basis_kw))]
     if download == "signs":  # server: packed sign(M*); worker: apply the bits
         calls.append(("decode", lambda: codec.decode_signs(W, vals, pidx, signs, stream=stream)))
         calls.append(("apply", lambda: codec.apply_signs(X, signs, w.eta, w.lam, stream=stream)))
@@ -355,7 +362,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
         calls.append(("decode", lambda: codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam,
                                                                     stream=stream)))
     else:
-        calls.append(("decode", lambda: codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream)))
+        calls.append(("decode", lambda: codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream,
+                                                           **basis_kw)))
 
     def one_step(ev):
         for j, (_, fn) in enumerate(calls):
@@ -438,6 +446,10 @@ def main():
         for name, rec in pmc_summary(w, *args.pmc_summary).items():
             print(json.dumps(rec))
         return
+    if args.basis == "random" and (args.chunk != 64 or args.download != "apply" or args.subtraction != "local"
+                                   or args.phi):
+        print("--basis random runs with chunk 64, the apply download and the local subtraction", file=sys.stderr)
+        sys.exit(2)
     if args.chunk == 128 and (args.basis != "dct" or args.download != "apply"):
         print("--chunk 128 is built for the DCT basis and the apply download", file=sys.stderr)
         sys.exit(2)

@@ -129,7 +129,8 @@ demo_status check_basis(const demo_codec_cfg* cfg, const std::vector<TensorPlan>
   for (const auto& t : plan) any2d = any2d || t.ndim == 2;
   if (cfg->P0 == nullptr) return fail(DEMO_ERR_INVALID, "user basis without P0");
   if (any2d && cfg->P1 == nullptr) return fail(DEMO_ERR_INVALID, "user basis without P1 for a matrix");
-  if (!aligned(cfg->P0, 4) || (cfg->P1 && !aligned(cfg->P1, 4))) return fail(DEMO_ERR_ALIGN, "basis misaligned");
+  if (!aligned(cfg->P0, 16) || (cfg->P1 && !aligned(cfg->P1, 16)))
+    return fail(DEMO_ERR_ALIGN, "basis misaligned (16 bytes)");
   *kind = demo::BasisKind::kUser;
   *p0 = cfg->P0;
   *p1 = cfg->P1 ? cfg->P1 : cfg->P0;

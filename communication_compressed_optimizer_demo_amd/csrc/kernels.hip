@@ -134,18 +134,26 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
       store_rows<false>(q, ts.dst + c.base, ts.cols, c, lane);
   }
 
-  basis.fwd0(q);
-  col_to_row(tile, q, lane);
-  basis.fwd1(q);
+  if constexpr (Basis::kMatrixCores) {
+    basis.template forward2d<kLd>(q, tile, lane);
+  } else {
+    basis.fwd0(q);
+    col_to_row(tile, q, lane);
+    basis.fwd1(q);
+  }
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
   tk::topk_chunk(q, p.keff2, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
   if (!p.subtract_local) return;
   __syncthreads();
 
-  basis.inv1(q);
-  row_to_col(tile, q, lane);
-  basis.inv0(q);
+  if constexpr (Basis::kMatrixCores) {
+    basis.template inverse2d<kLd>(q, tile, lane);
+  } else {
+    basis.inv1(q);
+    row_to_col(tile, q, lane);
+    basis.inv0(q);
+  }
 
   if (c.full)
     store_rows<true>(q, ts.dst + c.base, ts.cols, c, lane);
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void en
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(64) void encode_dense_kernel(LaunchTable tab, EncodeParams p, DenseBasis basis) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void encode_dense_kernel(LaunchTable tab, EncodeParams p, DenseBasis basis) {
   __shared__ float tile[64 * kLd];
   encode_item<DenseBasis, kBf16>(tab, p, basis, tile);
 }
@@ -387,11 +395,14 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   // with both targets the momentum rows are fetched after the transforms
   // (registers: X, M and the transform together would halve occupancy)
   constexpr bool kEarlyM = kTargets == kToMomentum;
+  // the matrix-core transform needs those registers too: there the parameter
+  // rows follow the transform (a second wave per SIMD hides them instead)
+  constexpr bool kEarlyX = !Basis::kMatrixCores;
   float x[64], m[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     const int64_t row = int64_t(min(i, c.vr - 1)) * ld;
-    if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&(xp + row)[col]);
+    if constexpr ((kTargets & kToParams) != 0 && kEarlyX) x[i] = stream_load(&(xp + row)[col]);
     if constexpr (kEarlyM) m[i] = stream_load(&(mp + row)[col]);
   }
 
@@ -413,11 +424,19 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   float q[64];
   average_row(q, acc, cntw, p, lane);
   __syncthreads();
-  basis.inv1(q);
-  row_to_col(acc, q, lane);
-  basis.inv0(q);
+  if constexpr (Basis::kMatrixCores) {
+    basis.template inverse2d<kLd>(q, acc, lane);
+  } else {
+    basis.inv1(q);
+    row_to_col(acc, q, lane);
+    basis.inv0(q);
+  }
 
   if constexpr ((kTargets & kToParams) != 0) {
+    if constexpr (!kEarlyX) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = stream_load(&(xp + int64_t(min(i, c.vr - 1)) * ld)[col]);
+    }
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
     if (c.full)
@@ -526,7 +545,7 @@ __global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParam
 }
 
 template <int kTargets, bool kWire = false>
-__global__ __launch_bounds__(64) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
   __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
   decode_item<DenseBasis, kTargets, kWire>(tab, p, basis, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }

@@ -257,6 +257,7 @@ __host__ __device__ __forceinline__ void dct3(float (&x)[N]) {
 
 // Orthonormal DCT-II on both dimensions (P0 = P1 = P).
 struct DctBasis {
+  static constexpr bool kMatrixCores = false;
   // y = P x
   __host__ __device__ __forceinline__ void fwd0(float (&x)[64]) const { dct2<64, Ortho<64>>(x); }
   __host__ __device__ __forceinline__ void fwd1(float (&x)[64]) const { dct2<64, Ortho<64>>(x); }
@@ -267,6 +268,7 @@ struct DctBasis {
 
 // P0 = P1 = I: the chunk is ranked and sparsified in the parameter domain.
 struct IdentityBasis {
+  static constexpr bool kMatrixCores = false;
   __host__ __device__ __forceinline__ void fwd0(float (&)[64]) const {}
   __host__ __device__ __forceinline__ void fwd1(float (&)[64]) const {}
   __host__ __device__ __forceinline__ void inv0(float (&)[64]) const {}
@@ -274,9 +276,15 @@ struct IdentityBasis {
 };
 
 // Caller-supplied orthonormal P0 / P1 (64 x 64, row-major, rows are basis vectors).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct DenseBasis {
   const float* __restrict__ p0;
   const float* __restrict__ p1;
+  // A 64x64 block goes through the fp32 matrix cores (two 64x64x64 products
+  // per direction) instead of one matrix-vector product per lane.
+  static constexpr bool kMatrixCores = true;
 
   static __device__ __forceinline__ void apply(const float* __restrict__ P, float (&x)[64]) {
     float y[64];
@@ -306,6 +314,108 @@ struct DenseBasis {
   __device__ __forceinline__ void fwd1(float (&x)[64]) const { apply(p1, x); }
   __device__ __forceinline__ void inv0(float (&x)[64]) const { apply_t(p0, x); }
   __device__ __forceinline__ void inv1(float (&x)[64]) const { apply_t(p1, x); }
+
+  // --- 64x64 blocks on the matrix cores (one wave; `tile` is 64 rows of kLd
+  // floats in LDS).  v_mfma_f32_32x32x2f32: lane l supplies A[l % 32][slot]
+  // and B[slot][l % 32], slot = l / 32; the 32x32 result sits in register v
+  // of lane l at row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.  Step kk
+  // of a 64-deep product uses k = kk + 32 slot, so a lane's slot walks one
+  // contiguous half of a row or column.
+
+  // D = A * B for 64x64 operands given as functions (m, k) -> A, (k, n) -> B
+  // of this lane's (row / column within a 32-tile, slot, kk).
+  template <class FA, class FB>
+  static __device__ __forceinline__ void product(f32x16 (&d)[2][2], FA a_of, FB b_of) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) d[i][j][v] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      const float a0 = a_of(0, kk), a1 = a_of(1, kk);
+      const float b0 = b_of(0, kk), b1 = b_of(1, kk);
+      d[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, d[0][0], 0, 0, 0);
+      d[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, d[0][1], 0, 0, 0);
+      d[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, d[1][0], 0, 0, 0);
+      d[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, d[1][1], 0, 0, 0);
+    }
+  }
+
+  // The 64x64 result into the tile, row-major.
+  template <int kLd>
+  static __device__ __forceinline__ void store_result(const f32x16 (&d)[2][2], float* tile, int lane) {
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tile[(32 * i + 8 * (v >> 2) + 4 * h + (v & 3)) * kLd + 32 * j + c] = d[i][j][v];
+  }
+
+  // Forward: x holds column `lane` of the block B (x[i] = B[i][lane]); on
+  // return x holds row `lane` of Q = P0 B P1^T.
+  template <int kLd>
+  __device__ __forceinline__ void forward2d(float (&x)[64], float* tile, int lane) const {
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) tile[i * kLd + lane] = x[i];
+    // this lane's rows of P0 (A of the first product) and P1 (B^T of the second): 32 contiguous k each
+    f32x4 pr[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pr[t][q] = *reinterpret_cast<const f32x4*>(p0 + (32 * t + c) * 64 + 32 * h + 4 * q);
+    __syncthreads();
+    f32x16 d[2][2];
+    // C = P0 B
+    product(d, [&](int t, int kk) { return pr[t][kk >> 2][kk & 3]; },
+            [&](int t, int kk) { return tile[(kk + 32 * h) * kLd + 32 * t + c]; });
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pr[t][q] = *reinterpret_cast<const f32x4*>(p1 + (32 * t + c) * 64 + 32 * h + 4 * q);
+    __syncthreads();
+    store_result<kLd>(d, tile, lane);
+    __syncthreads();
+    // Q = C P1^T: B[k][n] = P1[n][k]
+    product(d, [&](int t, int kk) { return tile[(32 * t + c) * kLd + kk + 32 * h]; },
+            [&](int t, int kk) { return pr[t][kk >> 2][kk & 3]; });
+    __syncthreads();
+    store_result<kLd>(d, tile, lane);
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 64; ++v) x[v] = tile[lane * kLd + v];
+    __syncthreads();
+  }
+
+  // Inverse: x holds row `lane` of Q (x[v] = Q[lane][v]); on return x holds
+  // column `lane` of P0^T Q P1.
+  template <int kLd>
+  __device__ __forceinline__ void inverse2d(float (&x)[64], float* tile, int lane) const {
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int v = 0; v < 64; ++v) tile[lane * kLd + v] = x[v];
+    __syncthreads();
+    f32x16 d[2][2];
+    // D = Q P1 (rows of P1 read a coalesced 128 bytes per lane half)
+    product(d, [&](int t, int kk) { return tile[(32 * t + c) * kLd + kk + 32 * h]; },
+            [&](int t, int kk) { return p1[(kk + 32 * h) * 64 + 32 * t + c]; });
+    __syncthreads();
+    store_result<kLd>(d, tile, lane);
+    __syncthreads();
+    // X = P0^T D: A[m][k] = P0[k][m]
+    product(d, [&](int t, int kk) { return p0[(kk + 32 * h) * 64 + 32 * t + c]; },
+            [&](int t, int kk) { return tile[(kk + 32 * h) * kLd + 32 * t + c]; });
+    __syncthreads();
+    store_result<kLd>(d, tile, lane);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = tile[i * kLd + lane];
+    __syncthreads();
+  }
 };
 
 }  // namespace xf

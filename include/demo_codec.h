@@ -120,8 +120,9 @@ typedef struct demo_codec_cfg {
   int32_t momentum_form; /* demo_momentum_form */
   int32_t basis;         /* demo_basis */
   const float* P0;       /* DEMO_BASIS_USER: device 64x64 fp32 row-major, rows are the basis
-                            vectors; acts on dimension 0 and on vectors */
-  const float* P1;       /* DEMO_BASIS_USER with any matrix: device 64x64, acts on dimension 1 */
+                            vectors, 16-byte aligned; acts on dimension 0 and on vectors */
+  const float* P1;       /* DEMO_BASIS_USER with any matrix: device 64x64, 16-byte aligned, acts on
+                            dimension 1 */
   int32_t subtraction;   /* demo_subtraction */
 } demo_codec_cfg;
 

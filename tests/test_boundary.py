@@ -143,6 +143,7 @@ def test_valid_arguments_reach_the_context_check(lib):
     (dict(basis=1), 1),
     (dict(basis=1, P0=0x5000), 1),
     (dict(basis=1, P0=0x5002, P1=0x6000), 7),
+    (dict(basis=1, P0=0x5000, P1=0x6004), 7),  # the basis is read 16 bytes at a time
     (dict(basis=3), 1),
     (dict(subtraction=2), 1),
     (dict(subtraction=-1), 1),
