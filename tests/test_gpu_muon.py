@@ -115,3 +115,9 @@ def test_muon_whole_tile_products(dev):
     then M Z) take the whole-tile GEMM for every product; 2048 x 2100 sends the Gram and the last product
     (K or N not a multiple of the tile) through the bounds-checked GEMM while its iterations stay whole-tile."""
     run_case("muon_whole_tiles", [(2048, 2304), (2304, 2048), (2048, 2100)], 32, 2, 1.0, 0.0)
+
+
+def test_muon_batched_small_tiles(dev):
+    """Three matrices with n = 256 share each Newton-Schulz launch; too few 128 x 128 tiles for the GPU, so the
+    batch runs the whole-tile GEMM with 64 x 64 tiles (grid z = matrix); a vector sits between them in the list."""
+    run_case("muon_batch_256", [(256, 320), (300,), (320, 256), (256, 256)], 16, 3, 1.0, 0.0)
