@@ -20,8 +20,8 @@ Pages followed (cited below by these tags):
   [N] papernotes.org ICLR 2026 note "DeMo: Decoupled Momentum
       Optimization", section 方法详解 (整体框架 flowchart, 关键设计 1-3).
 
-Readings taken where the pages are silent or disagree (each is listed in
-the design doc with its reason):
+Readings taken where the pages are silent or disagree (the kernels take
+the same ones):
   * momentum form: (1-beta)*G by default, plain G behind ``plain=True``;
   * momentum subtraction uses the worker's OWN selected coefficients
     (``subtract="aggregated"`` with ``subtract_aggregated`` gives the

@@ -65,7 +65,9 @@ def test_plan_matches_oracle_payload_count(lib, name):
 
 
 def test_plan_olmo_sizes(lib):
-    # payload sizes the survey tabulates for the OLMo-shaped sets
+    # chunk and entry counts counted from the shapes: an OLMo-1B block has 32x96 + 32x32 + 32x128 + 128x32
+    # chunks of 64x64 and two 2048-vectors of 32 chunks, 16 blocks, keff 32; OLMo-300M: 24 blocks at d = 1024,
+    # keff 8
     assert B.demo_plan(DI.WORKLOADS["olmo_1b"].shapes, 32)[:2] == (197632, 6324224)
     assert B.demo_plan(DI.WORKLOADS["olmo_300m"].shapes, 8)[:2] == (74496, 595968)
     assert DI.WORKLOADS["olmo_1b"].n_params == 805371904
