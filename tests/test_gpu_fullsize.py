@@ -79,15 +79,25 @@ def wire_entries(wv: torch.Tensor, wi: torch.Tensor, wire_bytes: int, ne: int, w
     return codes, idx
 
 
-@pytest.mark.parametrize("name,s,wire", [("olmo_300m", 64, False), ("olmo_1b", 64, False), ("olmo_1b", 128, False),
-                                         ("olmo_1b", 64, True)])
-def test_full_size_sampled(dev, name, s, wire):
+@pytest.mark.parametrize("name,s,wire,rand", [("olmo_300m", 64, False, False), ("olmo_1b", 64, False, False),
+                                              ("olmo_1b", 128, False, False), ("olmo_1b", 64, True, False),
+                                              ("olmo_1b", 64, False, True)])
+def test_full_size_sampled(dev, name, s, wire, rand):
+    """rand: a caller basis (random orthonormal P0, P1, fresh every step, the same float32 matrices on both
+    sides), whose 64x64 blocks the kernels transform on the matrix cores."""
     w = DI.WORKLOADS[name]
     W, steps = w.workers, 2
     phi_c = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
-    P = O.dct_basis(s)
     rng = np.random.default_rng(7 + w.config_id)
-    name = f"{name} s={s}" + (" wire" if wire else "")
+    name = f"{name} s={s}" + (" wire" if wire else "") + (" random basis" if rand else "")
+
+    def basis(t):
+        """(oracle P0, P1 as float64 or None, keyword arguments for the codec calls)"""
+        if not rand:
+            return None, None, {}
+        P0, P1 = (O.orthonormal_rows(DI.gaussian_matrix(w, t, which)).astype(np.float32) for which in (0, 1))
+        return (P0.astype(np.float64), P1.astype(np.float64),
+                {"P0": torch.from_numpy(P0).to(dev), "P1": torch.from_numpy(P1).to(dev)})
 
     shapes = [tuple(d) for d in w.shapes]
     groups = [{"ids": list(range(len(shapes))), "shapes": shapes,
@@ -110,6 +120,9 @@ def test_full_size_sampled(dev, name, s, wire):
     report = PR.EncodeReport()
 
     for t in range(steps):
+        P0, P1, bkw = basis(t)
+        Pc0 = P0 if rand else O.dct_basis(s)
+        Pc1 = P1 if rand else O.dct_basis(s)
         or_vals = {key: [None] * W for key in M_or}
         or_idx = {key: [None] * W for key in M_or}
         or_q = {key: [None] * W for key in M_or}
@@ -119,7 +132,7 @@ def test_full_size_sampled(dev, name, s, wire):
             for gr in groups:
                 ne = gr["codec"].n_entries
                 gr["codec"].encode([G[i] for i in gr["ids"]], [M[i][wk] for i in gr["ids"]],
-                                   gr["vals"][wk * ne:(wk + 1) * ne], gr["pidx"][wk * ne:(wk + 1) * ne])
+                                   gr["vals"][wk * ne:(wk + 1) * ne], gr["pidx"][wk * ne:(wk + 1) * ne], **bkw)
             torch.cuda.synchronize()
             for gr in groups:
                 ne = gr["codec"].n_entries
@@ -138,10 +151,10 @@ def test_full_size_sampled(dev, name, s, wire):
                         m_prev = M_or[(i, c)][wk]
                         if m_prev is None:
                             m_prev = np.zeros_like(g_blk)
-                        out = O.encode(m_prev, g_blk, beta=w.beta, alpha=w.alpha, k=w.k, s=s)
+                        out = O.encode(m_prev, g_blk, beta=w.beta, alpha=w.alpha, k=w.k, s=s, P0=P0, P1=P1)
                         s0 = e0 + c * keff
                         cdiv[(i, c, wk)] = PR.compare_encode(
-                            out, g_blk.shape, keff, w.alpha, P, P, chunk_block(M[i][wk], shape, c, s),
+                            out, g_blk.shape, keff, w.alpha, Pc0, Pc1, chunk_block(M[i][wk], shape, c, s),
                             gv_h[s0:s0 + keff].reshape(1, keff), gi_h[s0:s0 + keff].reshape(1, keff),
                             cdiv[(i, c, wk)], report, where=f"{name} step {t} worker {wk} tensor {i} chunk {c}", s=s)
                         M_or[(i, c)][wk] = out["M"]
@@ -156,7 +169,8 @@ def test_full_size_sampled(dev, name, s, wire):
                 gr["codec"].pack_wire(W, gr["vals"], gr["pidx"], gr["wv"], gr["wi"])
                 gr["codec"].decode_apply_wire([X[i] for i in gr["ids"]], W, gr["wv"], gr["wi"], phi_c, w.eta, w.lam)
             else:
-                gr["codec"].decode_apply([X[i] for i in gr["ids"]], W, gr["vals"], gr["pidx"], phi_c, w.eta, w.lam)
+                gr["codec"].decode_apply([X[i] for i in gr["ids"]], W, gr["vals"], gr["pidx"], phi_c, w.eta, w.lam,
+                                         **bkw)
         torch.cuda.synchronize()
         for (i, c), xo in X_or.items():
             assert torch.isfinite(X[i]).all(), f"{name}: non-finite parameters, tensor {i}"
@@ -176,7 +190,7 @@ def test_full_size_sampled(dev, name, s, wire):
                 vals_in = [O.unpack_wire(*O.pack_wire(v, ix), v.size)[0].reshape(v.shape)
                            for v, ix in zip(or_vals[(i, c)], or_idx[(i, c)])]
             dec = O.decode_apply(xo, np.stack(vals_in), np.stack(or_idx[(i, c)]), phi=w.phi,
-                                 eta=w.eta, lam=w.lam, s=s)
+                                 eta=w.eta, lam=w.lam, s=s, P0=P0, P1=P1)
             ediv[(i, c)] = PR.compare_decode(dec, xo.shape, w.phi, w.eta, chunk_block(X[i], w.shapes[i], c, s), div,
                                              ediv.get((i, c)), where=f"{name} step {t} tensor {i} chunk {c}", s=s)
             X_or[(i, c)] = dec["X"]
