@@ -232,6 +232,12 @@ def test_single_4096_bf16_gradients(dev):
     Sim(w).run(2)
 
 
+def test_bf16_gradients_random_basis(dev):
+    """bfloat16 gradients with a caller basis: the matrix-core transform behind the bfloat16 loads."""
+    w = DI.WORKLOADS["single_4096"].replace(name="bf16_random", shapes=((256, 320), (130,)), random_basis=True)
+    Sim(w).run(2)
+
+
 @pytest.mark.parametrize("k", [1, 8, 64, 4096])
 def test_tiny_and_ragged_shapes(dev, k):
     w = DI.WORKLOADS["tiny_256"].replace(
