@@ -72,6 +72,17 @@ __device__ __forceinline__ void scatter_add(float* sum, uint8_t* cnt, float v) {
   __hip_atomic_store(cnt, uint8_t(n + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
+// Work item of workgroup b of n.  Workgroups go to the 8 XCDs round-robin
+// (workgroup b to XCD b mod 8); this gives each XCD one contiguous range of
+// items, so neighbouring chunks, whose payload entries share cache lines,
+// meet in the same L2.  A bijection of 0 .. n-1.
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  constexpr int kXcds = 8;
+  const int x = b % kXcds, j = b / kXcds;
+  const int q = n / kXcds, r = n % kXcds;  // XCDs below r take q + 1 items
+  return x * q + min(x, r) + j;
+}
+
 // number of set lanes of `mask` below this lane
 __device__ __forceinline__ int lanes_below_mask(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));

@@ -360,9 +360,9 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
 
 template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
-                                              float* acc, uint32_t* cntw) {
+                                              float* acc, uint32_t* cntw, int item) {
   const int lane = threadIdx.x;
-  const ChunkPos c = chunk_pos(ts, blockIdx.x);
+  const ChunkPos c = chunk_pos(ts, item);
 
   // Memory order matters: a wave's loads complete in issue order, so the
   // payload entries (needed first) are requested before the tensors to
@@ -479,9 +479,9 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
 
 template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
-                                              float* acc, uint32_t* cntw) {
+                                              float* acc, uint32_t* cntw, int item) {
   const int lane = threadIdx.x;
-  const int slab = blockIdx.x - ts.item_begin;
+  const int slab = item - ts.item_begin;
   const int64_t first = int64_t(slab) * 64 * 64 + lane;  // this lane's element of the slab's chunk 0
   const int64_t rem = int64_t(ts.rows) - first;          // elements c * 64 < rem exist
   const int nc = min(64, int((uint32_t(ts.rows) + 63u) >> 6) - slab * 64);  // chunks in this slab
@@ -531,11 +531,12 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
 template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_item(const LaunchTable& tab, const DecodeParams& p, const Basis& basis,
                                             float* acc, uint32_t* cntw) {
-  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
   if (ts.cols == 0)
-    decode_vector<Basis, kTargets, kWire>(ts, p, basis, acc, cntw);
+    decode_vector<Basis, kTargets, kWire>(ts, p, basis, acc, cntw, item);
   else
-    decode_matrix<Basis, kTargets, kWire>(ts, p, basis, acc, cntw);
+    decode_matrix<Basis, kTargets, kWire>(ts, p, basis, acc, cntw, item);
 }
 
 template <class Basis, int kTargets, bool kWire = false>
