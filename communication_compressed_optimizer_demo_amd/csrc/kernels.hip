@@ -118,9 +118,9 @@ __device__ __forceinline__ void load_momentum(float (&q)[64], const TensorSlot& 
 
 template <class Basis, bool kBf16>
 __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const EncodeParams& p, const Basis& basis,
-                                              float* tile) {
+                                              float* tile, int item) {
   const int lane = threadIdx.x;
-  const ChunkPos c = chunk_pos(ts, blockIdx.x);
+  const ChunkPos c = chunk_pos(ts, item);
 
   float q[64];
   if (c.full)
@@ -169,9 +169,9 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
 // selects its own chunk.
 template <class Basis, bool kBf16>
 __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const EncodeParams& p, const Basis& basis,
-                                              float* tile) {
+                                              float* tile, int item) {
   const int lane = threadIdx.x;
-  const int slab = blockIdx.x - ts.item_begin;
+  const int slab = item - ts.item_begin;
   const int64_t first = int64_t(slab) * 64 * 64 + lane;  // this lane's element of the slab's chunk 0
   const int64_t rem = int64_t(ts.rows) - first;          // elements c * 64 < rem exist
   float* __restrict__ m = ts.dst + first;
@@ -213,11 +213,12 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
 template <class Basis, bool kBf16>
 __device__ __forceinline__ void encode_item(const LaunchTable& tab, const EncodeParams& p, const Basis& basis,
                                             float* tile) {
-  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
   if (ts.cols == 0)
-    encode_vector<Basis, kBf16>(ts, p, basis, tile);
+    encode_vector<Basis, kBf16>(ts, p, basis, tile, item);
   else
-    encode_matrix<Basis, kBf16>(ts, p, basis, tile);
+    encode_matrix<Basis, kBf16>(ts, p, basis, tile, item);
 }
 
 // The DCT and identity kernels fit 168 VGPRs, i.e. three waves per SIMD; the
