@@ -618,11 +618,12 @@ __device__ __forceinline__ float apply_bit(float x, uint64_t word, int bit, cons
 // element j = lane j).  The word index is wave-uniform, so the words arrive
 // through scalar loads while the rows stream through vector loads.
 __global__ __launch_bounds__(64) void apply_signs_kernel(LaunchTable tab, ApplyParams p) {
-  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const TensorSlot& ts = tab.t[find_tensor(tab, item)];
   const int lane = threadIdx.x;
   const uint64_t* __restrict__ words = static_cast<const uint64_t*>(ts.aux);
   if (ts.cols == 0) {
-    const int slab = blockIdx.x - ts.item_begin;
+    const int slab = item - ts.item_begin;
     const int64_t first = int64_t(slab) * 64 * 64 + lane;
     const int64_t rem = int64_t(ts.rows) - first;
     const int nc = min(64, int((uint32_t(ts.rows) + 63u) >> 6) - slab * 64);
@@ -634,7 +635,7 @@ __global__ __launch_bounds__(64) void apply_signs_kernel(LaunchTable tab, ApplyP
     }
     return;
   }
-  const ChunkPos c = chunk_pos(ts, blockIdx.x);
+  const ChunkPos c = chunk_pos(ts, item);
   const uint64_t* __restrict__ wp = words + int64_t(c.local) * 64;
   float* __restrict__ xp = ts.dst + c.base;
   const int64_t ld = ts.cols;
