@@ -14,13 +14,17 @@
 // carries the parameter update in its epilogue.  A vector is one column:
 // m / sqrt(m.m + eps).
 //
-// GEMM: 128 x 128 output tile per 256-thread workgroup, 2 x 2 waves of 64 x 64,
-// each wave 2 x 2 tiles of v_mfma_f32_32x32x2f32.  Operand layout of that
-// instruction: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the
-// accumulator holds D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v.
-// K advances kBK per LDS stage, double-buffered; global loads of the next
-// stage are issued before the current stage's MFMAs.  Whole tiles take a
-// second kernel (gemm_tile_kernel) with deeper prefetch and 16-byte moves.
+// GEMM on v_mfma_f32_32x32x2f32.  Operand layout of that instruction: lane l
+// supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the accumulator holds
+// D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v.  Two kernels:
+//  - gemm_kernel (any shape): 128 x 128 (or 64 x 64) output tile per
+//    256-thread workgroup, 2 x 2 waves; K advances kBK per LDS stage,
+//    double-buffered, bounds-checked 4-byte loads of the next stage issued
+//    before the current stage's MFMAs;
+//  - gemm_tile_kernel (whole tiles): the same tiles with 4 x 2 waves at
+//    128 x 128, K stages of kSK, 16-byte loads two stages ahead.
+// Both take a batch of same-shape products (grid z), which the Newton-Schulz
+// steps of several matrices with equal n share.
 #include "common.h"
 #include "launch.h"
 
