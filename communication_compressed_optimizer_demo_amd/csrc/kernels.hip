@@ -44,7 +44,7 @@ using xf::DenseBasis;
 using xf::IdentityBasis;
 
 constexpr int kLd = 65;     // LDS tile row stride in floats
-constexpr int kCntLd = 17;  // count rows: 16 words of 8-bit counts + 1 pad word
+constexpr int kCntLd = 15;  // count rows: words 0..14 of a row's 8-bit counts (word 15: see count_word)
 constexpr int kWorkerBatch = 16;
 
 
@@ -239,9 +239,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void en
 // ---------------------------------------------------------------- decode / apply
 
 // The decode's LDS: the 64 x kLd fp32 accumulator, then 64 x kCntLd words of
-// 8-bit counts, rounded up so that 64 lanes x 16 bytes clear it in whole
-// instructions.
-constexpr int kDecodeLdsWords = ((64 * kLd + 64 * kCntLd) + 255) / 256 * 256;
+// 8-bit counts; the 16th count word of row u sits in the accumulator row's
+// padding slot (column 64, which no transform touches).  20 KB: eight waves
+// per CU.
+constexpr int kDecodeLdsWords = 64 * kLd + 64 * kCntLd;
+static_assert(kDecodeLdsWords % 256 == 0 && kDecodeLdsWords * 4 == 20480, "cleared in whole 16-byte stores");
+// The decode that updates both X and M streams twice the bytes per chunk and
+// ran 1 % faster with seven waves per CU: its allocation is 1 KB larger
+// (unused) to keep it there.
+template <int kTargets>
+constexpr int decode_lds_words() {
+  return kTargets == (kToParams | kToMomentum) ? kDecodeLdsWords + 256 : kDecodeLdsWords;
+}
+
+// Count word j (counts of columns 4j .. 4j + 3) of row u.  Rows of 15 words
+// and the padding slots both put 64 lanes' reads of their own rows on 64
+// banks (15 u and 65 u are distinct mod 64).
+template <class F, class W>
+__device__ __forceinline__ W* count_word(F* acc, W* cntw, uint32_t u, uint32_t j) {
+  return j < 15u ? cntw + u * kCntLd + j : reinterpret_cast<W*>(acc + u * kLd + 64);
+}
 
 // Zero the accumulator tile and the count rows: unguarded 16-byte stores.
 __device__ __forceinline__ void clear_acc(uint32_t* lds, int lane) {
@@ -254,7 +271,7 @@ __device__ __forceinline__ void clear_acc(uint32_t* lds, int lane) {
 // Add one payload entry (value v at coefficient (u, col)) to the accumulator
 // and to its 8-bit contributor count (byte col of count row u).
 __device__ __forceinline__ void accumulate(float* acc, uint32_t* cntw, uint32_t u, uint32_t col, float v) {
-  scatter_add(acc + u * kLd + col, reinterpret_cast<uint8_t*>(cntw + u * kCntLd) + col, v);
+  scatter_add(acc + u * kLd + col, reinterpret_cast<uint8_t*>(count_word(acc, cntw, u, col >> 2)) + (col & 3u), v);
 }
 
 // Entry f of worker w's payload: the float32 arrays, or the compact wire
@@ -348,7 +365,7 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const uint32_t w = cntw[lane * kCntLd + j];
+      const uint32_t w = *count_word(acc, cntw, uint32_t(lane), uint32_t(j));
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const float n = float((w >> (8 * b)) & 255u);
@@ -542,13 +559,13 @@ __device__ __forceinline__ void decode_item(const LaunchTable& tab, const Decode
 
 template <class Basis, int kTargets, bool kWire = false>
 __global__ __launch_bounds__(64) void decode_kernel(LaunchTable tab, DecodeParams p) {
-  __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
+  __shared__ __align__(16) uint32_t lds[decode_lds_words<kTargets>()];
   decode_item<Basis, kTargets, kWire>(tab, p, Basis{}, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }
 
 template <int kTargets, bool kWire = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_dense_kernel(LaunchTable tab, DecodeParams p, DenseBasis basis) {
-  __shared__ __align__(16) uint32_t lds[kDecodeLdsWords];
+  __shared__ __align__(16) uint32_t lds[decode_lds_words<kTargets>()];
   decode_item<DenseBasis, kTargets, kWire>(tab, p, basis, reinterpret_cast<float*>(lds), lds + 64 * kLd);
 }
 
