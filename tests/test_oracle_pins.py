@@ -612,3 +612,112 @@ def test_wire_format_round_trip_and_rounding_bound():
     assert np.all(np.abs(vals - v) <= np.abs(v) * 2.0 ** -8)
     with pytest.raises(ValueError):
         O.pack_wire(v[:2], np.array([1, 4096]))
+
+
+# --------------------------------------------------------------------------- multi-step trajectories, lossless limits
+#
+# With k = numel nothing is dropped, so DeMo over T steps reduces to known
+# data-parallel optimizers whose iterates have explicit sums.  These pin the
+# oracle's step loop (state carried from step to step, momentum update before
+# the selection, subtraction after it, X updated from the pre-update X) and
+# not only single steps.  Closed forms are written as sums over the gradient
+# history, never as the oracle's recursion.
+
+def _bounded_gradients(rng, T, W, shape):
+    """N(0,1) magnitudes pushed away from zero, so that sign() of float32 rounding cannot flip."""
+    z = rng.standard_normal((T, W, *shape))
+    return (np.sign(z) * (0.1 + np.abs(z))).astype(np.float32)
+
+
+def _run_lossless(G, *, beta, alpha, phi, eta, lam, plain=False, subtract="local"):
+    """Runs the oracle's encode / decode loop over G[t, w]; returns X_T and every M*_t."""
+    T, W = G.shape[:2]
+    shape = G.shape[2:]
+    k = 64 * 64
+    X = np.linspace(-1.0, 1.0, int(np.prod(shape))).reshape(shape).astype(np.float32)
+    X0 = X.copy()
+    Ms = [np.zeros(shape, np.float32) for _ in range(W)]
+    Mstars = []
+    for t in range(T):
+        outs = [O.encode(Ms[w], G[t, w], beta=beta, alpha=alpha, k=k, plain=plain, subtract=subtract)
+                for w in range(W)]
+        d = O.decode_apply(X, np.stack([o["values"] for o in outs]), np.stack([o["idx"] for o in outs]),
+                           phi=phi, eta=eta, lam=lam)
+        X = d["X"]
+        Mstars.append(d["Mstar"])
+        if subtract == "aggregated":
+            Ms = [O.subtract_aggregated(o["M"], d["Mstar"], alpha) for o in outs]
+        else:
+            Ms = [o["M"] for o in outs]
+    return X0, X, Mstars, Ms
+
+
+def _x_closed_form(X0, updates, eta, lam):
+    """X_T = (1 - eta lam)^T X_0 - eta sum_t (1 - eta lam)^(T - 1 - t) u_t for X_{t+1} = X_t - eta (u_t + lam X_t)."""
+    T = len(updates)
+    r = 1.0 - eta * lam
+    return r ** T * X0.astype(np.float64) - eta * sum(r ** (T - 1 - t) * u for t, u in enumerate(updates))
+
+
+@pytest.mark.parametrize("shape,plain", [((130, 70), False), ((64, 64), True), ((100,), False)])
+def test_trajectory_alpha1_is_data_parallel_sgd(shape, plain):
+    """alpha = 1 and k = numel: every step sends all of M' and leaves M = 0, so M*_t is the
+    workers' mean of (1 - beta) G_t (G_t with the plain form) and X follows SGD with weight decay."""
+    beta, eta, lam, T, W = 0.9, 0.05, 0.1, 6, 3
+    G = _bounded_gradients(_rng(40), T, W, shape)
+    X0, X, Mstars, Ms = _run_lossless(G, beta=beta, alpha=1.0, phi="identity", eta=eta, lam=lam, plain=plain)
+    c = 1.0 if plain else 1.0 - beta
+    gbar = [c * G[t].astype(np.float64).mean(axis=0) for t in range(T)]
+    for t in range(T):
+        assert np.abs(Mstars[t] - gbar[t]).max() <= 1e-6 * np.abs(gbar[t]).max()
+    for M in Ms:
+        assert np.abs(M).max() <= 1e-6 * max(np.abs(g).max() for g in gbar)
+    ref = _x_closed_form(X0, gbar, eta, lam)
+    assert np.abs(X - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("shape", [(130, 70), (100,)])
+def test_trajectory_alpha0_is_momentum_sgd(shape):
+    """alpha = 0 and k = numel: nothing is subtracted, each worker's M_t is the EMA
+    (1 - beta) sum_tau beta^(t - tau) G_tau, M*_t is its workers' mean and X is momentum SGD."""
+    beta, eta, lam, T, W = 0.8, 0.05, 0.02, 7, 2
+    G = _bounded_gradients(_rng(41), T, W, shape).astype(np.float64)
+    X0, X, Mstars, Ms = _run_lossless(G.astype(np.float32), beta=beta, alpha=0.0, phi="identity", eta=eta, lam=lam)
+    ema = [(1 - beta) * sum(beta ** (t - tau) * G[tau].mean(axis=0) for tau in range(t + 1)) for t in range(T)]
+    for t in range(T):
+        assert np.abs(Mstars[t] - ema[t]).max() <= 1e-5 * np.abs(ema[t]).max()
+    for w in range(W):
+        own = (1 - beta) * sum(beta ** (T - 1 - tau) * G[tau, w] for tau in range(T))
+        assert np.abs(Ms[w] - own).max() <= 1e-5 * np.abs(own).max()
+    ref = _x_closed_form(X0, ema, eta, lam)
+    assert np.abs(X - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_trajectory_alpha1_signum_single_worker_is_signsgd():
+    """One worker, alpha = 1, k = numel, phi = sign: X_T = X_0 - eta sum_t sign(G_t) exactly
+    as signSGD (no weight decay); gradients are kept away from zero so no sign can flip."""
+    eta, T = 0.01, 5
+    G = _bounded_gradients(_rng(42), T, 1, (70, 130))
+    X0, X, _, _ = _run_lossless(G, beta=0.95, alpha=1.0, phi="sign", eta=eta, lam=0.0)
+    ref = _x_closed_form(X0, [np.sign(G[t, 0]).astype(np.float64) for t in range(T)], eta, 0.0)
+    assert np.abs(X - ref).max() <= 1e-6
+
+
+def test_trajectory_aggregated_subtraction_mean_closed_form():
+    """Aggregated subtraction, k = numel: M*_t = mean of the M'_w and M_w <- M'_w - alpha M*_t,
+    so the workers' mean momentum m_t obeys m_t = (1 - alpha) M*_t with
+    M*_t = beta m_(t-1) + (1 - beta) gbar_t, i.e.
+    M*_t = (1 - beta) sum_tau ((1 - alpha) beta)^(t - tau) gbar_tau."""
+    beta, alpha, eta, lam, T, W = 0.9, 0.4, 0.05, 0.0, 6, 3
+    G = _bounded_gradients(_rng(43), T, W, (64, 96)).astype(np.float64)
+    X0, X, Mstars, Ms = _run_lossless(G.astype(np.float32), beta=beta, alpha=alpha, phi="identity", eta=eta,
+                                      lam=lam, subtract="aggregated")
+    gbar = [G[t].mean(axis=0) for t in range(T)]
+    closed = [(1 - beta) * sum(((1 - alpha) * beta) ** (t - tau) * gbar[tau] for tau in range(t + 1))
+              for t in range(T)]
+    for t in range(T):
+        assert np.abs(Mstars[t] - closed[t]).max() <= 1e-5 * np.abs(closed[t]).max()
+    mean_M = np.mean([M.astype(np.float64) for M in Ms], axis=0)
+    assert np.abs(mean_M - (1 - alpha) * closed[-1]).max() <= 1e-5 * np.abs(closed[-1]).max()
+    ref = _x_closed_form(X0, closed, eta, lam)
+    assert np.abs(X - ref).max() <= 1e-5 * np.abs(ref).max()
