@@ -745,6 +745,30 @@ __device__ __forceinline__ float avg_scale(uint32_t n, const DecodeParams& p) {
   return p.avg_workers ? p.inv_workers : __builtin_amdgcn_rcpf(fmaxf(float(n), 1.f));
 }
 
+// Quadrant q's rows of X (and, for the momentum-only target, of M) for the
+// decode: clamped addresses, so every load is valid; clamped lanes are not
+// stored.
+template <int kTargets>
+__device__ __forceinline__ void decode_rows128(float (&x)[64], float (&m)[64], const float* __restrict__ xp,
+                                               const float* __restrict__ mp, int64_t ld, const Chunk128& c, int q,
+                                               int lane, int col) {
+  if (c.full) {
+    const int64_t o = quad_origin(q, lane, ld), step = quad_step(q, ld);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[o + i * step]);
+      if constexpr (kTargets == kToMomentum) m[i] = stream_load(&mp[o + i * step]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int64_t off = int64_t(min(quad_row(q >> 1, i), c.vr - 1)) * ld + col;
+      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
+      if constexpr (kTargets == kToMomentum) m[i] = stream_load(&mp[off]);
+    }
+  }
+}
+
 template <int kTargets>
 __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -753,14 +777,19 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   float* acc = reinterpret_cast<float*>(lds);
   uint32_t* cntw = lds + kAccWords;
 
-  // wave 0 requests the payload entries first
-  // (with both X and M to update there are no registers to spare for early payloads)
-  constexpr bool kEarlyPayload = kTargets != (kToParams | kToMomentum);
+  // With one target, every wave requests the payload entries first and then
+  // its quadrant's rows, which land during the scatter and the inverse
+  // passes.  Only wave 0 scatters; the other waves' payload copies go unused,
+  // which keeps every load unconditional (clamped addresses), so no wait is
+  // placed between the two groups and the payloads, issued first, arrive
+  // first.  With both X and M to update there are no registers to spare: the
+  // payloads are read at the scatter and the rows during the column pass.
+  constexpr bool kEarly = kTargets != (kToParams | kToMomentum);
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  const bool one_batch = kEarlyPayload && p.keff2 <= 64 && p.workers <= kWorkerBatch;
+  const bool one_batch = kEarly && p.keff2 <= 64 && p.workers <= kWorkerBatch;
   float val[kWorkerBatch];
   uint32_t ix[kWorkerBatch];
-  if (w == 0 && one_batch) {
+  if constexpr (kEarly) {
     const uint32_t e = uint32_t(min(lane, p.keff2 - 1));
 #pragma unroll
     for (int j = 0; j < kWorkerBatch; ++j) {
@@ -774,6 +803,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
   const int col = min((w & 1) ? kS - 1 - lane : lane, c.vc - 1);
   float x[64], m[64];
+  if constexpr (kEarly) decode_rows128<kTargets>(x, m, xp, mp, ld, c, w, lane, col);
 
   clear_lds(lds, threadIdx.x);
   __syncthreads();
@@ -824,23 +854,16 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   __syncthreads();  // the accumulator area is reused from here on
   inv_half(q, b);
   row_to_col(reinterpret_cast<float*>(lds) + w * kTile, q, lane);
-  // the rows to update (clamped addresses; clamped lanes are not stored) land
-  // during the column pass and the butterfly exchange; with both targets the
-  // momentum rows follow the exchange (registers)
-  constexpr bool kEarlyM = kTargets == kToMomentum;
-  if (c.full) {
-    const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
+  // with both targets the X rows land during the column pass and the
+  // exchange, and the momentum rows follow the exchange (registers)
+  if constexpr (!kEarly) {
+    if (c.full) {
+      const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[o + i * step]);
-      if constexpr (kEarlyM) m[i] = stream_load(&mp[o + i * step]);
-    }
-  } else {
+      for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[o + i * step]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const int64_t off = int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col;
-      if constexpr ((kTargets & kToParams) != 0) x[i] = stream_load(&xp[off]);
-      if constexpr (kEarlyM) m[i] = stream_load(&mp[off]);
+      for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col]);
     }
   }
   inv_half(q, a);
@@ -858,7 +881,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
       store_quadrant<false>(x, xp, ld, c, w, lane);
   }
   if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
-    if constexpr (!kEarlyM) {
+    if constexpr (kTargets != kToMomentum) {
       if (c.full) {
         const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
 #pragma unroll
