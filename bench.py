@@ -165,15 +165,17 @@ def cpu_model() -> str:
 
 # ----------------------------------------------------------------------------- GPU leg
 
-# The files the encode and decode kernels are built and launched from; the
-# s = 128 and Muon sources are separate translation units.
+# The files the encode and decode kernels are built and launched from, for
+# chunk edge 64 and for 128 (separate translation units; the Muon kernels are
+# a third).
 KERNEL_SOURCES = ("codec.cpp", "common.h", "kernels.hip", "launch.h", "topk.h", "xform.h")
+KERNEL_SOURCES_128 = ("codec.cpp", "common.h", "kernels128.hip", "launch.h", "xform.h")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(chunk: int = 64) -> str:
     """sha256 over the encode/decode kernels' sources (counter figures are void once they change)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES_128 if chunk == 128 else KERNEL_SOURCES):
         h.update(f.encode())
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
@@ -185,7 +187,7 @@ def _traffic(kernel: str, workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sources_sha256") != kernel_source_hash():
+    if rec.get("kernel_sources_sha256") != kernel_source_hash(128 if "128" in kernel else 64):
         return None
     return rec.get("bytes_per_launch")
 
@@ -215,13 +217,13 @@ def pmc_summary(w: DI.Workload, fetch_csv: str, write_csv: str):
         return max(vals) * 1024
     f_cal = probe(fetch) / COPY_PROBE_BYTES
     w_cal = probe(write) / COPY_PROBE_BYTES
-    src = kernel_source_hash()
     recs = {}
     for k in fetch:
-        m = re.search(r"(encode|decode)(_dense)?_kernel", k)
+        m = re.search(r"(encode|decode)(128|_dense)?_kernel", k)
         if m is None:
             continue
         short = m.group(0)
+        src = kernel_source_hash(128 if m.group(2) == "128" else 64)
         fb = [v * 1024 / f_cal for v in fetch[k]]
         wb = [v * 1024 / w_cal for v in write.get(k, [])]
         # the timed launches are the last ones of a kernel (foreign-payload encodes come first)
@@ -425,9 +427,9 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
         "kernels": kern,
         "roofline": {
             **roof,
-            "traffic": (_traffic(f"{dom}_kernel", w.name)
+            "traffic": (_traffic(f"{dom}{'128' if chunk == 128 else ''}_kernel", w.name)
                         if launches == 1 and basis == "dct" and subtraction == "local" and download == "apply"
-                        and chunk == 64 and not muon_iters else None),
+                        and not muon_iters else None),
         },
     }
 
