@@ -437,8 +437,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures the "
-              "codec on one GPU's share; collectives across GPUs are not part of it.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): it measures the codec on "
+              "one GPU's share; collectives across GPUs are not part of the library.", file=sys.stderr)
         sys.exit(2)
     w = DI.WORKLOADS[args.workload]
     if args.hbm_probe:
