@@ -777,19 +777,18 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   float* acc = reinterpret_cast<float*>(lds);
   uint32_t* cntw = lds + kAccWords;
 
-  // With one target, every wave requests the payload entries first and then
-  // its quadrant's rows, which land during the scatter and the inverse
-  // passes.  Only wave 0 scatters; the other waves' payload copies go unused,
-  // which keeps every load unconditional (clamped addresses), so no wait is
-  // placed between the two groups and the payloads, issued first, arrive
-  // first.  With both X and M to update there are no registers to spare: the
-  // payloads are read at the scatter and the rows during the column pass.
-  constexpr bool kEarly = kTargets != (kToParams | kToMomentum);
+  // Every wave requests the payload entries first and then its quadrant's
+  // rows of X (of M for the momentum-only target), which land during the
+  // scatter and the inverse passes.  Only wave 0 scatters; the other waves'
+  // payload copies go unused, which keeps every load unconditional (clamped
+  // addresses), so no wait is placed between the two groups and the
+  // payloads, issued first, arrive first.  With both X and M to update, the
+  // momentum rows follow the exchange (registers).
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  const bool one_batch = kEarly && p.keff2 <= 64 && p.workers <= kWorkerBatch;
+  const bool one_batch = p.keff2 <= 64 && p.workers <= kWorkerBatch;
   float val[kWorkerBatch];
   uint32_t ix[kWorkerBatch];
-  if constexpr (kEarly) {
+  {
     const uint32_t e = uint32_t(min(lane, p.keff2 - 1));
 #pragma unroll
     for (int j = 0; j < kWorkerBatch; ++j) {
@@ -803,7 +802,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   float* __restrict__ mp = static_cast<float*>(ts.aux) + c.base;
   const int col = min((w & 1) ? kS - 1 - lane : lane, c.vc - 1);
   float x[64], m[64];
-  if constexpr (kEarly) decode_rows128<kTargets>(x, m, xp, mp, ld, c, w, lane, col);
+  decode_rows128<kTargets>(x, m, xp, mp, ld, c, w, lane, col);
 
   clear_lds(lds, threadIdx.x);
   __syncthreads();
@@ -854,18 +853,6 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   __syncthreads();  // the accumulator area is reused from here on
   inv_half(q, b);
   row_to_col(reinterpret_cast<float*>(lds) + w * kTile, q, lane);
-  // with both targets the X rows land during the column pass and the
-  // exchange, and the momentum rows follow the exchange (registers)
-  if constexpr (!kEarly) {
-    if (c.full) {
-      const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
-#pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[o + i * step]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[int64_t(min(quad_row(w >> 1, i), c.vr - 1)) * ld + col]);
-    }
-  }
   inv_half(q, a);
   if constexpr (kTargets == (kToParams | kToMomentum))
     butterfly_staged(q, reinterpret_cast<float*>(lds), w, lane);  // -> M* of quadrant w
