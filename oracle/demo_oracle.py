@@ -7,8 +7,11 @@ and this module imports nothing from the product.
 
 Plain NumPy.  Every arithmetic step runs in float64; float32 appears only
 where the method stores state (momentum M, parameters X, the transmitted
-coefficient values) and where a float decides an integer: the top-k ranks
-are taken on float32 magnitudes, the precision the GPU kernels decide in.
+coefficient values), where a float decides an integer (the top-k ranks are
+taken on float32 magnitudes, the precision the GPU kernels decide in), and
+in the scalar hyper-parameters beta, alpha, eta and lambda, which are taken
+at their float32 values (``hp``), the precision in which the codec receives
+them; from those values on, every product and sum is float64.
 The transforms are explicit O(s^3) matrix products against the basis built
 from its definition, and top-k is a full stable sort: slow and plain on
 purpose.
@@ -92,17 +95,24 @@ def orthonormal_rows(gauss: np.ndarray) -> np.ndarray:
 # encode: momentum update, chunking, projection, top-k, momentum subtraction
 # ---------------------------------------------------------------------------
 
+def hp(x: float) -> float:
+    """A scalar hyper-parameter at its float32 value (returned as a Python float)."""
+    return float(np.float32(x))
+
+
 def momentum_update(M: np.ndarray, G: np.ndarray, beta: float, plain: bool = False) -> np.ndarray:
     """Local momentum, no gradient all-reduce.
 
     [S] Decoupled Local Momentum Updates: M_t = beta * M_{t-1} + (1 - beta) * G_t.
     [N] 整体框架 flowchart states the plain form M_t = beta * M_{t-1} + G_t
-    (``plain=True``).
+    (``plain=True``).  beta is taken at float32; 1 - beta is then formed in
+    float64 from that value.
     """
     M64 = np.asarray(M, dtype=F64)
     G64 = np.asarray(G, dtype=F64)
-    c = 1.0 if plain else (1.0 - float(beta))
-    return float(beta) * M64 + c * G64
+    b = hp(beta)
+    c = 1.0 if plain else (1.0 - b)
+    return b * M64 + c * G64
 
 
 def chunk_grid(shape: Sequence[int], s: int = 64) -> Tuple[int, ...]:
@@ -200,7 +210,7 @@ def subtract_selected(Mp_chunks: np.ndarray, Q: np.ndarray, S: np.ndarray, alpha
     rows = np.arange(n)[:, None]
     Qhat[rows, S] = Qflat[rows, S]
     R = unproject(Qhat.reshape(Q.shape), P0, P1)
-    return Mp_chunks - float(alpha) * R
+    return Mp_chunks - hp(alpha) * R
 
 
 def encode(M: np.ndarray, G: np.ndarray, *, beta: float, alpha: float, k: int,
@@ -214,8 +224,10 @@ def encode(M: np.ndarray, G: np.ndarray, *, beta: float, alpha: float, k: int,
     writes the subtraction with the server's averaged coefficients, which
     only exist after the exchange (see ``subtract_aggregated``).
     Returns float32 ``M`` (new momentum), float32 ``values`` [n_chunks, keff],
-    uint16 ``idx`` [n_chunks, keff] (ascending per chunk), and the float64
-    intermediates ``Mp_chunks`` and ``Q`` for the tests.
+    uint16 ``idx`` [n_chunks, keff] (ascending per chunk), and for the tests
+    the float64 intermediates ``Mp_chunks`` and ``Q``, and ``terms_chunks``:
+    per element |beta M| + |c G|, the magnitudes of the momentum update's two
+    terms (the scale of a float32 evaluation's rounding error).
     """
     P0 = dct_basis(s) if P0 is None else np.asarray(P0, dtype=F64)
     P1 = dct_basis(s) if P1 is None else np.asarray(P1, dtype=F64)
@@ -235,12 +247,14 @@ def encode(M: np.ndarray, G: np.ndarray, *, beta: float, alpha: float, k: int,
     else:
         raise ValueError(subtract)
     M_new = merge_chunks(new_chunks, M.shape, s).astype(F32)
+    terms = momentum_update(np.abs(np.asarray(M, dtype=F64)), np.abs(np.asarray(G, dtype=F64)), beta, plain)
     return {
         "M": M_new,
         "values": vals.astype(F32),
         "idx": S.astype(np.uint16),
         "Mp_chunks": chunks,
         "Q": Q,
+        "terms_chunks": split_chunks(terms, s),
     }
 
 
@@ -316,7 +330,10 @@ def decode_apply(X: np.ndarray, values: np.ndarray, idx: np.ndarray, *, phi: str
     [S] Server-Side Aggregation and Momentum Reconstruction, Inverse DCT and
     Unchunking: M* = B^-1(T^-1(Q_bar)).  [S] Base Optimizer Update:
     X_{t+1} = X_t - eta * (phi(M*_t) + lambda * X_t), with the pre-update X.
-    Returns float32 ``X`` and the float64 ``Mstar`` (cropped) for the tests.
+    Returns float32 ``X``, and for the tests the float64 ``Mstar`` (cropped),
+    ``Qbar`` [n_chunks, numel], the averaged coefficients, and ``Qabs``, the
+    same average taken over the values' magnitudes (the scale of a float32
+    evaluation's rounding error).
     """
     P0 = dct_basis(s) if P0 is None else np.asarray(P0, dtype=F64)
     P1 = dct_basis(s) if P1 is None else np.asarray(P1, dtype=F64)
@@ -325,11 +342,12 @@ def decode_apply(X: np.ndarray, values: np.ndarray, idx: np.ndarray, *, phi: str
     numel = s if X.ndim == 1 else s * s
     n = int(np.prod(grid))
     Qbar = aggregate(values, idx, numel, mode)
+    Qabs = aggregate(np.abs(np.asarray(values, dtype=F64)), idx, numel, mode)
     cshape = (n, s) if X.ndim == 1 else (n, s, s)
     Mstar = merge_chunks(unproject(Qbar.reshape(cshape), P0, P1), X.shape, s)
     X64 = X.astype(F64)
-    X_new = X64 - float(eta) * (phi_map(Mstar, phi, eps) + float(lam) * X64)
-    return {"X": X_new.astype(F32), "Mstar": Mstar}
+    X_new = X64 - hp(eta) * (phi_map(Mstar, phi, eps) + hp(lam) * X64)
+    return {"X": X_new.astype(F32), "Mstar": Mstar, "Qbar": Qbar, "Qabs": Qabs}
 
 
 def subtract_aggregated(M: np.ndarray, Mstar: np.ndarray, alpha: float) -> np.ndarray:
@@ -339,7 +357,7 @@ def subtract_aggregated(M: np.ndarray, Mstar: np.ndarray, alpha: float) -> np.nd
     B^-1(T^-1(Q_bar)), Q_bar the server's average, i.e. M - alpha * M* with
     M* from ``decode_apply``.  Returns float32.
     """
-    return (np.asarray(M, dtype=F64) - float(alpha) * np.asarray(Mstar, dtype=F64)).astype(F32)
+    return (np.asarray(M, dtype=F64) - hp(alpha) * np.asarray(Mstar, dtype=F64)).astype(F32)
 
 
 # ---------------------------------------------------------------------------
@@ -381,7 +399,7 @@ def apply_signs(X: np.ndarray, words: np.ndarray, *, eta: float, lam: float, s: 
     bits = np.unpackbits(by, axis=1, bitorder="little").reshape(cshape)
     phi = merge_chunks(np.where(bits != 0, -1.0, 1.0), X.shape, s)
     X64 = X.astype(F64)
-    return (X64 - float(eta) * (phi + float(lam) * X64)).astype(F32)
+    return (X64 - hp(eta) * (phi + hp(lam) * X64)).astype(F32)
 
 
 # ---------------------------------------------------------------------------

@@ -19,6 +19,11 @@ from oracle import demo_oracle as O
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")
 
 
+def f32(x):
+    """A hyper-parameter as the codec receives it: its float32 value."""
+    return float(np.float32(x))
+
+
 def _rng(seed):
     return np.random.default_rng(seed)
 
@@ -113,7 +118,9 @@ def test_momentum_half_life_printed_on_the_page():
     M0 = M.copy()
     for _ in range(gold["steps"]):
         M = O.momentum_update(M, np.zeros(4), beta)
-    assert M0[0] == pytest.approx(1.0 - beta)
+    # the codec receives beta as float32: the impulse weight is 1 - float32(beta)
+    assert M0[0] == pytest.approx(1.0 - float(np.float32(beta)), rel=1e-12)
+    assert M0[0] == pytest.approx(1.0 - beta, rel=2e-5)
     assert M[0] / M0[0] == pytest.approx(gold["weight"], rel=2e-3)
 
 
@@ -373,8 +380,10 @@ def test_signum_update_on_lossless_single_worker():
     o = O.encode(M, G, beta=0.9, alpha=0.2, k=4096)
     X = rng.standard_normal((64, 64)).astype(np.float32)
     d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="sign", eta=0.01, lam=0.1)
-    Mp = 0.9 * M.astype(np.float64) + 0.1 * G.astype(np.float64)
-    ref = X.astype(np.float64) * (1 - 0.01 * 0.1) - 0.01 * np.sign(Mp)
+    # the hyper-parameters as the codec receives them (float32)
+    b, eta, lam = (float(np.float32(v)) for v in (0.9, 0.01, 0.1))
+    Mp = b * M.astype(np.float64) + (1 - b) * G.astype(np.float64)
+    ref = X.astype(np.float64) * (1 - eta * lam) - eta * np.sign(Mp)
     # one float32 rounding of the stored result
     assert np.all(np.abs(d["X"] - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
 
@@ -422,15 +431,16 @@ def test_aggregated_subtraction_lossless_closed_form(W):
     alpha = 0.3
     Gs = [rng.standard_normal((70, 100)).astype(np.float32) for _ in range(W)]
     outs = [O.encode(np.zeros_like(g), g, beta=0.9, alpha=alpha, k=4096, subtract="aggregated") for g in Gs]
+    c = 1.0 - f32(0.9)
     for g, o in zip(Gs, outs):
-        assert np.array_equal(o["M"], (0.1 * g.astype(np.float64)).astype(np.float32))  # M' kept as is
+        assert np.array_equal(o["M"], (c * g.astype(np.float64)).astype(np.float32))  # M' kept as is
     dec = O.decode_apply(np.zeros((70, 100), np.float32), np.stack([o["values"] for o in outs]),
                          np.stack([o["idx"] for o in outs]), phi="identity", eta=1.0, lam=0.0)
-    mean = np.mean([0.1 * g.astype(np.float64) for g in Gs], axis=0)
+    mean = np.mean([c * g.astype(np.float64) for g in Gs], axis=0)
     assert np.abs(dec["Mstar"] - mean).max() <= 1e-6 * np.abs(mean).max()
     for o in outs:
         new = O.subtract_aggregated(o["M"], dec["Mstar"], alpha)
-        ref = o["M"].astype(np.float64) - alpha * mean
+        ref = o["M"].astype(np.float64) - f32(alpha) * mean
         assert np.abs(new - ref).max() <= 1e-6 * np.abs(ref).max()
     same = [O.encode(np.zeros_like(Gs[0]), Gs[0], beta=0.9, alpha=1.0, k=4096, subtract="aggregated")
             for _ in range(W)]
@@ -493,7 +503,7 @@ def test_apply_signs_closed_forms_and_agreement_with_signum_decode():
     n = O.sign_words([X.shape])
     for fill, phi in ((0, 1.0), (~np.uint64(0), -1.0)):
         got = O.apply_signs(X, np.full(n, fill, np.uint64), eta=0.01, lam=0.1)
-        ref = X64 - 0.01 * (phi + 0.1 * X64)
+        ref = X64 - f32(0.01) * (phi + f32(0.1) * X64)
         assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
     # the bit path reproduces the Signum decode wherever M* != 0
     G = rng.standard_normal(X.shape).astype(np.float32)
@@ -504,7 +514,7 @@ def test_apply_signs_closed_forms_and_agreement_with_signum_decode():
     assert np.array_equal(got, d["X"])
     # zero M* (no coefficient kept anywhere) reads as +1
     z = O.apply_signs(X, O.pack_signs(np.zeros(X.shape)), eta=0.01, lam=0.0)
-    assert np.all(np.abs(z - (X64 - 0.01)) <= np.spacing(np.abs(X64 - 0.01).astype(np.float32)))
+    assert np.all(np.abs(z - (X64 - f32(0.01))) <= np.spacing(np.abs(X64 - f32(0.01)).astype(np.float32)))
 
 
 # --------------------------------------------------------------------------- chunk edge 128
@@ -581,7 +591,7 @@ def test_muon_decode_apply_update():
     G = rng.standard_normal((70, 90)).astype(np.float32)
     o = O.encode(np.zeros_like(G), G, beta=0.5, alpha=0.2, k=4096)
     d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="muon", eta=0.01, lam=0.1, eps=1e-3)
-    ref = X.astype(np.float64) - 0.01 * (O.phi_muon(d["Mstar"], 1e-3) + 0.1 * X.astype(np.float64))
+    ref = X.astype(np.float64) - f32(0.01) * (O.phi_muon(d["Mstar"], 1e-3) + f32(0.1) * X.astype(np.float64))
     assert np.all(np.abs(d["X"] - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
     assert np.abs(d["Mstar"] - 0.5 * G.astype(np.float64)).max() < 1e-6  # lossless k: M* = M'
 
