@@ -22,8 +22,12 @@
 //   Q = P0 M' P1^T  (column pass, LDS transpose, row pass)
 //   exact top-k of |Q| over the chunk, lower index wins ties; payload
 //   (value, index) in index order
-//   M = P0^T (Q - alpha Q_hat) P1 (row pass, LDS transpose, column pass),
-//   which equals M' - alpha P0^T Q_hat P1 because P0, P1 are orthonormal
+//   R = P0^T Q_hat P1 (row pass, LDS transpose, column pass);
+//   M = M' - alpha R, with M' kept in registers since the load (the DCT and
+//   identity bases) or loaded and formed again, bit for bit (the caller
+//   basis, whose matrix-core transform has no registers to spare).  Only the
+//   selected part goes through the float32 transforms, so the rounding of
+//   the rest of M' does not accumulate in the momentum from step to step.
 // decode/apply (§3.4 Server-Side Aggregation, Inverse DCT and Unchunking,
 // Base Optimizer Update):
 //   scatter-add W payloads into an LDS accumulator with 8-bit contributor
@@ -133,6 +137,14 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
     else
       store_rows<false>(q, ts.dst + c.base, ts.cols, c, lane);
   }
+  // M' (column layout) for the subtraction.  The matrix-core transform needs
+  // these registers; it forms M' again from G and M at the end instead.
+  constexpr bool kHold = !Basis::kMatrixCores;
+  float mp[kHold ? 64 : 1];
+  if constexpr (kHold) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) mp[i] = q[i];
+  }
 
   if constexpr (Basis::kMatrixCores) {
     basis.template forward2d<kLd>(q, tile, lane);
@@ -143,10 +155,11 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
   }
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  tk::topk_chunk(q, p.keff2, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
+  tk::topk_chunk(q, p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
   if (!p.subtract_local) return;
   __syncthreads();
 
+  // q holds Q_hat (row layout); R = P0^T Q_hat P1 in column layout
   if constexpr (Basis::kMatrixCores) {
     basis.template inverse2d<kLd>(q, tile, lane);
   } else {
@@ -155,6 +168,18 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
     basis.inv0(q);
   }
 
+  if constexpr (!kHold) {
+    float m2[64];
+    if (c.full)
+      load_momentum<true, kBf16>(m2, ts, c, lane, p.beta, p.gcoef);
+    else
+      load_momentum<false, kBf16>(m2, ts, c, lane, p.beta, p.gcoef);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) q[i] = fmaf(-p.alpha, q[i], m2[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) q[i] = fmaf(-p.alpha, q[i], mp[i]);
+  }
   if (c.full)
     store_rows<true>(q, ts.dst + c.base, ts.cols, c, lane);
   else
@@ -177,7 +202,10 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
   float* __restrict__ m = ts.dst + first;
   const char* __restrict__ g = static_cast<const char*>(ts.aux) + first * (kBf16 ? 2 : 4);
 
-  float q[64];
+  // M' is held for the subtraction, except with the caller basis (whose
+  // per-lane products need the registers), which forms it again at the end.
+  constexpr bool kHold = !Basis::kMatrixCores;
+  float q[64], mp[kHold ? 64 : 1];
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
     float gv = 0.f, mv = 0.f;
@@ -186,6 +214,7 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
       mv = stream_load(&m[c * 64]);
     }
     q[c] = fmaf(p.beta, mv, p.gcoef * gv);
+    if constexpr (kHold) mp[c] = q[c];
   }
   if (!p.subtract_local) {  // aggregated subtraction: M = M' now, the decode side subtracts
 #pragma unroll
@@ -199,14 +228,21 @@ __device__ __forceinline__ void encode_vector(const TensorSlot& ts, const Encode
   const int chunk = slab * 64 + lane;  // this lane's chunk within the tensor
   const bool live = chunk < int((uint32_t(ts.rows) + 63u) >> 6);
   const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff1;
-  tk::topk_lane(q, p.keff1, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
+  tk::topk_lane(q, p.keff1, live, p.pay_val + e0, p.pay_idx + e0);
   if (!p.subtract_local) return;
 
-  basis.inv0(q);
+  basis.inv0(q);  // R = P0^T q_hat per chunk
   row_to_col(tile, q, lane);
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
-    if (c * 64 < rem) stream_store(q[c], &m[c * 64]);
+    if (c * 64 < rem) {
+      float mc;
+      if constexpr (kHold)
+        mc = mp[c];
+      else
+        mc = fmaf(p.beta, stream_load(&m[c * 64]), p.gcoef * load_src<kBf16>(g, c * 64));  // M' again
+      stream_store(fmaf(-p.alpha, q[c], mc), &m[c * 64]);
+    }
   }
 }
 
@@ -221,10 +257,10 @@ __device__ __forceinline__ void encode_item(const LaunchTable& tab, const Encode
     encode_matrix<Basis, kBf16>(ts, p, basis, tile, item);
 }
 
-// The DCT and identity kernels fit 168 VGPRs, i.e. three waves per SIMD; the
-// dense (caller-basis) kernel needs more and is left to the compiler.
+// The DCT and identity kernels hold M' next to the block: up to 256 VGPRs,
+// two waves per SIMD (eight per CU; the 16.6 KB LDS tile alone allows nine).
 template <class Basis, bool kBf16>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void encode_kernel(LaunchTable tab,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void encode_kernel(LaunchTable tab,
                                                                                              EncodeParams p) {
   __shared__ float tile[64 * kLd];
   encode_item<Basis, kBf16>(tab, p, Basis{}, tile);
@@ -296,31 +332,39 @@ __device__ __forceinline__ void load_entry(const DecodeParams& p, int64_t w, int
 }
 
 // Scatter-add the W payload segments of one 64x64 chunk (entries e0 ..
-// e0 + keff of every worker).  One scatter_add per (worker, entry block);
-// within it the indices are distinct, so no lanes collide and every
-// coefficient receives its terms in worker order.
+// e0 + keff of every worker).  The (worker, 64-entry block) steps run
+// worker-major: every entry of worker w is added before any of worker w + 1,
+// so each coefficient receives its terms in worker order 0..W-1.  Loads are
+// issued kWorkerBatch steps at a time; inside one step the indices are
+// distinct (one worker's payload), so no lanes collide.
 template <bool kWire>
 __device__ __forceinline__ void scatter_chunk(float* acc, uint32_t* cntw, const DecodeParams& p, int64_t e0,
                                               int lane) {
   const int keff = p.keff2;
-  for (int eb = 0; eb < keff; eb += 64) {
-    const int e = eb + lane;
-    const bool on = e < keff;
-    for (int w0 = 0; w0 < p.workers; w0 += kWorkerBatch) {
-      float val[kWorkerBatch];
-      uint32_t ix[kWorkerBatch];
+  const int nb = (keff + 63) >> 6;  // entry blocks per worker
+  const int steps = p.workers * nb;
+  int w = 0, eb = 0;  // worker and block of step t0 (wave-uniform)
+  for (int t0 = 0; t0 < steps; t0 += kWorkerBatch) {
+    float val[kWorkerBatch];
+    uint32_t ix[kWorkerBatch];
+    bool on[kWorkerBatch];
 #pragma unroll
-      for (int j = 0; j < kWorkerBatch; ++j) {
-        val[j] = 0.f;
-        ix[j] = 0u;
-        if (on && (w0 + j) < p.workers) load_entry<kWire>(p, w0 + j, e0 + e, val[j], ix[j]);
+    for (int j = 0; j < kWorkerBatch; ++j) {
+      const int e = eb * 64 + lane;
+      on[j] = t0 + j < steps && e < keff;
+      val[j] = 0.f;
+      ix[j] = 0u;
+      if (on[j]) load_entry<kWire>(p, w, e0 + e, val[j], ix[j]);
+      if (++eb == nb) {
+        eb = 0;
+        ++w;
       }
+    }
 #pragma unroll
-      for (int j = 0; j < kWorkerBatch; ++j) {
-        if (on && (w0 + j) < p.workers) {
-          const uint32_t id = ix[j] & 4095u;
-          accumulate(acc, cntw, id >> 6, id & 63u, val[j]);
-        }
+    for (int j = 0; j < kWorkerBatch; ++j) {
+      if (on[j]) {
+        const uint32_t id = ix[j] & 4095u;
+        accumulate(acc, cntw, id >> 6, id & 63u, val[j]);
       }
     }
   }

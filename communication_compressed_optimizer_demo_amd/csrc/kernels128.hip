@@ -244,7 +244,8 @@ __device__ __forceinline__ int quad_row(int qa, int i) { return qa ? (kS - 1 - i
 // Wave w = 2a + b holds sub-block (a, b) in row layout: lane u, q[v] =
 // Q[2u+a][2v+b], chunk-local index (2u+a)*128 + 2v + b.  Keeps the keff
 // largest magnitudes (float32; equal magnitudes: lower index first), writes
-// them in index order and scales them by (1 - alpha) in place.
+// them in index order and leaves Q_hat in q (kept coefficients unchanged,
+// the others zero).
 //
 // Fast path (keff <= 64), one workgroup barrier:
 //   1. each wave finds T_w = the keff-th largest of its 64 lane maxima (wave
@@ -254,15 +255,15 @@ __device__ __forceinline__ int quad_row(int qa, int i) { return qa ? (kS - 1 - i
 //      threshold K and the tie cut over the union.  The union holds every
 //      coefficient >= K: K >= each wave's own keff-th largest >= T_w;
 //   3. wave 0 ranks the keff kept candidates by index and writes the payload;
-//      every wave scales its own kept coefficients.
+//      every wave zeroes its own coefficients that were not kept.
 // Otherwise (keff > 64, or a region overflows, e.g. a block of equal
 // magnitudes) the same bitwise searches run over all 16384 coefficients with
 // workgroup-wide counts, and the payload positions come from kept-bit masks.
 
 // Returns true when the payload is still to be written by emit_kept (fast
 // path: wave 0 holds the kept list in LDS scratch that nothing else reuses).
-__device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lane, float alpha,
-                                        float* __restrict__ outv, uint16_t* __restrict__ outi, uint32_t* scr) {
+__device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lane, float* __restrict__ outv,
+                                        uint16_t* __restrict__ outi, uint32_t* scr) {
   const int a = w >> 1, b = w & 1;
   const uint32_t idx0 = uint32_t((2 * lane + a) * kS + b);  // index of q[0]; q[v] sits at idx0 + 2v
   uint32_t* hdr = scr;                             // [0, 4): candidates per wave (~0u: none)
@@ -278,7 +279,6 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
       const uint32_t id = idx0 + 2 * v;
       outv[id] = q[v];
       outi[id] = static_cast<uint16_t>(id);
-      q[v] = fmaf(-alpha, q[v], q[v]);
     }
     return false;
   }
@@ -385,7 +385,7 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
       for (int v = 0; v < 64; ++v) {
         const float m = fabsf(q[v]);
         const bool keep = m > kf || (m == kf && idx0 + 2 * v <= cut);
-        q[v] = keep ? fmaf(-alpha, q[v], q[v]) : q[v];
+        q[v] = keep ? q[v] : 0.f;
       }
       return true;
     }
@@ -464,8 +464,8 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
       const int pos = rbase + popc64(mine & below(v)) + popc64(partner & below(v + b));
       outv[pos] = q[v];
       outi[pos] = static_cast<uint16_t>(idx0 + 2 * v);
-      q[v] = fmaf(-alpha, q[v], q[v]);
     }
+    q[v] = ((mine >> v) & 1ull) ? q[v] : 0.f;
   }
   return false;
 }
@@ -490,9 +490,9 @@ __device__ __forceinline__ void emit_kept(int keff, int lane, float* __restrict_
 
 // The chunk is held by a lane pair: lane h has y[m] = coefficient 2m + h.
 // Same rule as above over the pair; `write` is false for lanes past the
-// tensor's last chunk.
-__device__ __forceinline__ void topk_pair(float (&y)[64], int keff, int h, bool write, float alpha,
-                                          float* __restrict__ outv, uint16_t* __restrict__ outi) {
+// tensor's last chunk.  Leaves the pair's half of Q_hat in y.
+__device__ __forceinline__ void topk_pair(float (&y)[64], int keff, int h, bool write, float* __restrict__ outv,
+                                          uint16_t* __restrict__ outi) {
   float lm = 0.f;
 #pragma unroll
   for (int m = 0; m < 64; ++m) lm = fmaxf(lm, fabsf(y[m]));
@@ -549,8 +549,8 @@ __device__ __forceinline__ void topk_pair(float (&y)[64], int keff, int h, bool 
         outv[pos] = y[m];
         outi[pos] = static_cast<uint16_t>(2 * m + h);
       }
-      y[m] = fmaf(-alpha, y[m], y[m]);
     }
+    y[m] = ((mine >> m) & 1ull) ? y[m] : 0.f;
   }
 }
 
@@ -619,21 +619,31 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
   fwd_half(x, b);
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  const bool deferred = topk128(x, p.keff2, w, lane, p.alpha, p.pay_val + e0, p.pay_idx + e0, scr);
+  const bool deferred = topk128(x, p.keff2, w, lane, p.pay_val + e0, p.pay_idx + e0, scr);
   if (!p.subtract_local) {
     if (deferred && w == 0) emit_kept(p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, scr);
     return;
   }
 
-  inv_half(x, b);
+  inv_half(x, b);  // x holds Q_hat: R = P^T Q_hat P, quadrant by quadrant
   row_to_col(lds + w * kTile, x, lane);
   inv_half(x, a);
   butterfly(x, lds, w, lane);  // S'_ab -> quadrants
 
-  if (c.full)
+  // M = M' - alpha R.  The quadrant's M' is formed again, bit for bit, from
+  // G and M (untouched so far): the registers hold no copy of it.
+  float mp[64];
+  if (c.full) {
+    load_quadrant<true, kBf16>(mp, ts, c, w, lane, p.beta, p.gcoef);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = fmaf(-p.alpha, x[i], mp[i]);
     store_quadrant<true>(x, mdst, ts.cols, c, w, lane);
-  else
+  } else {
+    load_quadrant<false, kBf16>(mp, ts, c, w, lane, p.beta, p.gcoef);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = fmaf(-p.alpha, x[i], mp[i]);
     store_quadrant<false>(x, mdst, ts.cols, c, w, lane);
+  }
   if (deferred && w == 0) emit_kept(p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, scr);
 }
 
@@ -699,15 +709,18 @@ __device__ __forceinline__ void encode_vector128(const TensorSlot& ts, const Enc
   const int nchunks = int((uint32_t(ts.rows) + 127u) >> 7);
   const bool live = chunk < nchunks;
   const int64_t e0 = ts.entry_begin + int64_t(live ? chunk : 0) * p.keff1;
-  topk_pair(x, p.keff1, h, live, p.alpha, p.pay_val + e0, p.pay_idx + e0);
+  topk_pair(x, p.keff1, h, live, p.pay_val + e0, p.pay_idx + e0);
   if (!p.subtract_local) return;
 
-  inv_half(x, h);
+  inv_half(x, h);  // R = P^T q_hat per chunk
   pair_unbutterfly(x, h);
   row_to_col(tile, x, lane);
 #pragma unroll
   for (int r = 0; r < 64; ++r) {
-    if (r * 64 < rem) stream_store(x[r], &m[r * 64]);
+    if (r * 64 < rem) {
+      const float mp = fmaf(p.beta, stream_load(&m[r * 64]), p.gcoef * load_src<kBf16>(g, r * 64));  // M' again
+      stream_store(fmaf(-p.alpha, x[r], mp), &m[r * 64]);
+    }
   }
 }
 
@@ -813,23 +826,30 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
         if (lane < p.keff2 && j < p.workers) accumulate128(acc, cntw, ix[j] & 16383u, val[j]);
       }
     } else {
-      for (int eb = 0; eb < p.keff2; eb += 64) {
-        const int e = eb + lane;
-        const bool on = e < p.keff2;
-        for (int w0 = 0; w0 < p.workers; w0 += kWorkerBatch) {
-          float v2[kWorkerBatch];
-          uint32_t i2[kWorkerBatch];
+      // (worker, 64-entry block) steps worker-major, kWorkerBatch loads at a
+      // time: every entry of worker w is added before any of worker w + 1
+      const int nb = (p.keff2 + 63) >> 6;
+      const int steps = p.workers * nb;
+      int wk = 0, eb = 0;
+      for (int t0 = 0; t0 < steps; t0 += kWorkerBatch) {
+        float v2[kWorkerBatch];
+        uint32_t i2[kWorkerBatch];
+        bool on[kWorkerBatch];
 #pragma unroll
-          for (int j = 0; j < kWorkerBatch; ++j) {
-            const int64_t off = int64_t(w0 + j) * p.entries + e0 + e;
-            const bool ok = on && (w0 + j) < p.workers;
-            v2[j] = ok ? p.pay_val[off] : 0.f;
-            i2[j] = ok ? p.pay_idx[off] : 0u;
+        for (int j = 0; j < kWorkerBatch; ++j) {
+          const int e = eb * 64 + lane;
+          on[j] = t0 + j < steps && e < p.keff2;
+          const int64_t off = int64_t(wk) * p.entries + e0 + e;
+          v2[j] = on[j] ? p.pay_val[off] : 0.f;
+          i2[j] = on[j] ? p.pay_idx[off] : 0u;
+          if (++eb == nb) {
+            eb = 0;
+            ++wk;
           }
+        }
 #pragma unroll
-          for (int j = 0; j < kWorkerBatch; ++j) {
-            if (on && (w0 + j) < p.workers) accumulate128(acc, cntw, i2[j] & 16383u, v2[j]);
-          }
+        for (int j = 0; j < kWorkerBatch; ++j) {
+          if (on[j]) accumulate128(acc, cntw, i2[j] & 16383u, v2[j]);
         }
       }
     }

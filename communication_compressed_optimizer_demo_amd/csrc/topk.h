@@ -1,13 +1,12 @@
-// Exact per-chunk top-k of a 64x64 coefficient block held by one wave64, fused
-// with the momentum subtraction of the selected coefficients.
+// Exact per-chunk top-k of a 64x64 coefficient block held by one wave64.
 //
 // DeMo ("DeMo: Decoupled Momentum Optimization", §3.4 Top-k Sparsification)
 // keeps the k largest-magnitude transform coefficients of every chunk and
-// zeroes the rest; §3.4 Momentum Subtraction then removes alpha times what was
-// kept from the momentum.  Because the transform is orthonormal, subtracting
-// alpha * P0^T Q_hat P1 from the momentum is the same as inverse-transforming
-// Q with every kept coefficient scaled by (1 - alpha); the kernels use that
-// form, so this file rewrites q in place as q - alpha * [kept] * q.
+// zeroes the rest; §3.4 Momentum Subtraction then removes alpha times the
+// inverse transform of what was kept from the momentum.  The selection writes
+// the payload and leaves Q_hat in place of the block: every kept coefficient
+// unchanged, every other one zero, ready for the inverse transform of the
+// subtraction.
 //
 // Ranking is on float32 magnitudes; equal magnitudes go to the lower
 // chunk-local index u*64 + v.  Layout: row layout, lane u holds q[v] = Q[u][v].
@@ -56,8 +55,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Magnitudes are compared as floats through the |x| operand modifier (the
 // order of non-negative floats is the order of their bit patterns), so no
 // second copy of the block is held in registers.
-__device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int lane, float alpha,
-                                                 float* __restrict__ outv, uint16_t* __restrict__ outi) {
+__device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int lane, float* __restrict__ outv,
+                                                 uint16_t* __restrict__ outi) {
   float lmax = 0.f;
 #pragma unroll
   for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(q[v]));
@@ -102,26 +101,24 @@ __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int l
       outv[off] = q[v];
       outi[off] = static_cast<uint16_t>(lane * 64 + v);
       ++off;
-      q[v] = fmaf(-alpha, q[v], q[v]);
     }
+    q[v] = keep ? q[v] : 0.f;
   }
 }
 
 // cand: LDS scratch of 2 * kMaxCand words (free during the call).
-__device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, float alpha,
-                                           float* __restrict__ outv, uint16_t* __restrict__ outi,
-                                           uint32_t* __restrict__ cand) {
-  if (keff >= 4096) {  // lossless: every coefficient, already in index order
+__device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, float* __restrict__ outv,
+                                           uint16_t* __restrict__ outi, uint32_t* __restrict__ cand) {
+  if (keff >= 4096) {  // lossless: every coefficient, already in index order, all kept
 #pragma unroll
     for (int v = 0; v < 64; ++v) {
       outv[lane * 64 + v] = q[v];
       outi[lane * 64 + v] = static_cast<uint16_t>(lane * 64 + v);
-      q[v] = fmaf(-alpha, q[v], q[v]);
     }
     return;
   }
   if (keff > 64) {
-    topk_full_search(q, keff, lane, alpha, outv, outi);
+    topk_full_search(q, keff, lane, outv, outi);
     return;
   }
 
@@ -145,7 +142,7 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
   const int incl = wave_incl_scan(cnt, lane);
   const int total = __shfl(incl, 63);
   if (T0 == 0 || total > kMaxCand) {
-    topk_full_search(q, keff, lane, alpha, outv, outi);
+    topk_full_search(q, keff, lane, outv, outi);
     return;
   }
   uint32_t* cmag = cand;             // magnitude bits
@@ -217,7 +214,7 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
   if (eq_total == quota) {
     // no tie is dropped: kept <=> |q| >= K
 #pragma unroll
-    for (int v = 0; v < 64; ++v) q[v] = fabsf(q[v]) >= kf ? fmaf(-alpha, q[v], q[v]) : q[v];
+    for (int v = 0; v < 64; ++v) q[v] = fabsf(q[v]) >= kf ? q[v] : 0.f;
   } else {
     // some coefficients equal to K are dropped: keep those up to the last tie taken
     uint32_t lt = last_tie;
@@ -227,16 +224,16 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
     for (int v = 0; v < 64; ++v) {
       const float a = fabsf(q[v]);
       const bool keep = a > kf || (a == kf && uint32_t(lane * 64 + v) <= lt);
-      q[v] = keep ? fmaf(-alpha, q[v], q[v]) : q[v];
+      q[v] = keep ? q[v] : 0.f;
     }
   }
 }
 
 // Top-k of one 64-element vector chunk held in one lane (vector chunks: lane
 // = chunk).  Same rule; writes only when `write` (lanes past the tensor's last
-// chunk hold zeros and write nothing).  Scales kept entries by (1 - alpha).
-__device__ __forceinline__ void topk_lane(float (&q)[64], int keff, bool write, float alpha,
-                                          float* __restrict__ outv, uint16_t* __restrict__ outi) {
+// chunk hold zeros and write nothing).  Leaves Q_hat in q.
+__device__ __forceinline__ void topk_lane(float (&q)[64], int keff, bool write, float* __restrict__ outv,
+                                          uint16_t* __restrict__ outi) {
   if (keff >= 64) {
 #pragma unroll
     for (int v = 0; v < 64; ++v) {
@@ -244,7 +241,6 @@ __device__ __forceinline__ void topk_lane(float (&q)[64], int keff, bool write, 
         outv[v] = q[v];
         outi[v] = static_cast<uint16_t>(v);
       }
-      q[v] = fmaf(-alpha, q[v], q[v]);
     }
     return;
   }
@@ -280,8 +276,8 @@ __device__ __forceinline__ void topk_lane(float (&q)[64], int keff, bool write, 
         outi[off] = static_cast<uint16_t>(v);
       }
       ++off;
-      q[v] = fmaf(-alpha, q[v], q[v]);
     }
+    q[v] = keep ? q[v] : 0.f;
   }
 }
 

@@ -42,20 +42,22 @@ def dev():
     return torch.device("cuda:0")
 
 
-def sample_chunks(shape, rng, s=64):
-    """Chunk ordinals to check: first, last, and one seeded random chunk."""
+def sample_chunks(shape, rng, s=64, extra=1):
+    """Chunk ordinals to check: first, last, and `extra` seeded random chunks."""
     n = int(np.prod(O.chunk_grid(shape, s)))
-    picks = {0, n - 1, int(rng.integers(n))}
+    picks = {0, n - 1} | {int(r) for r in rng.integers(n, size=extra)}
     return sorted(picks)
 
 
 def chunk_block(t: torch.Tensor, shape, c: int, s: int = 64) -> np.ndarray:
-    """The (unpadded) sub-block of chunk c, copied to the host."""
+    """The (unpadded) sub-block of chunk c, copied to the host (bfloat16 widened to float32)."""
     if len(shape) == 1:
-        return t[c * s:(c + 1) * s].cpu().numpy()
-    g1 = O.chunk_grid(shape, s)[1]
-    cr, cc = divmod(c, g1)
-    return t[cr * s:(cr + 1) * s, cc * s:(cc + 1) * s].cpu().numpy()
+        blk = t[c * s:(c + 1) * s]
+    else:
+        g1 = O.chunk_grid(shape, s)[1]
+        cr, cc = divmod(c, g1)
+        blk = t[cr * s:(cr + 1) * s, cc * s:(cc + 1) * s]
+    return blk.float().cpu().numpy()
 
 
 def check_payload_properties(vals: torch.Tensor, idx: torch.Tensor, layout, limits, where: str):
@@ -81,14 +83,22 @@ def wire_entries(wv: torch.Tensor, wi: torch.Tensor, wire_bytes: int, ne: int, w
 
 @pytest.mark.parametrize("name,s,wire,rand", [("olmo_300m", 64, False, False), ("olmo_1b", 64, False, False),
                                               ("olmo_1b", 128, False, False), ("olmo_1b", 64, True, False),
-                                              ("olmo_1b", 64, False, True)])
+                                              ("olmo_1b", 64, False, True), ("single_4096", 64, False, False)])
 def test_full_size_sampled(dev, name, s, wire, rand):
     """rand: a caller basis (random orthonormal P0, P1, fresh every step, the same float32 matrices on both
-    sides), whose 64x64 blocks the kernels transform on the matrix cores."""
+    sides), whose 64x64 blocks the kernels transform on the matrix cores.
+
+    single_4096 (one 4096x4096 weight, bfloat16 gradients, W = 4) runs its stated 20 steps with 130
+    sampled chunks; the OLMo lists run 2 steps with 3 chunks of every tensor.  After every decode the
+    payloads are decoded once more into zeros with eta = 1, lambda = 0, phi = identity, which leaves -M*:
+    the sampled chunks' M* is compared with the oracle's too."""
     w = DI.WORKLOADS[name]
-    W, steps = w.workers, 2
+    W = w.workers
+    steps = w.steps if name == "single_4096" else 2
+    extra = 128 if name == "single_4096" else 1
     phi_c = B.DEMO_PHI_SIGN if w.phi == "sign" else B.DEMO_PHI_IDENTITY
     rng = np.random.default_rng(7 + w.config_id)
+    noise = PR.NOISE_DENSE if rand else PR.NOISE
     name = f"{name} s={s}" + (" wire" if wire else "") + (" random basis" if rand else "")
 
     def basis(t):
@@ -111,7 +121,8 @@ def test_full_size_sampled(dev, name, s, wire, rand):
     say(f"[{name}] {len(w.shapes)} tensors, {w.n_params} params, W={W}: allocating momenta")
     M = {i: [torch.zeros(w.shapes[i], device=dev) for _ in range(W)] for i in range(len(w.shapes))}
     X = {i: DI.device_initial_params(w, i, dev) for i in range(len(w.shapes))}
-    samples = {i: sample_chunks(w.shapes[i], rng, s) for i in range(len(w.shapes))}
+    samples = {i: sample_chunks(w.shapes[i], rng, s, extra) for i in range(len(w.shapes))}
+    probe = {i: torch.zeros(w.shapes[i], device=dev) for i in range(len(w.shapes))}
     # oracle state of every sampled chunk: momentum per worker, parameters
     M_or = {(i, c): [None] * W for i in samples for c in samples[i]}
     X_or = {(i, c): chunk_block(X[i], w.shapes[i], c, s).copy() for i in samples for c in samples[i]}
@@ -156,21 +167,28 @@ def test_full_size_sampled(dev, name, s, wire, rand):
                         cdiv[(i, c, wk)] = PR.compare_encode(
                             out, g_blk.shape, keff, w.alpha, Pc0, Pc1, chunk_block(M[i][wk], shape, c, s),
                             gv_h[s0:s0 + keff].reshape(1, keff), gi_h[s0:s0 + keff].reshape(1, keff),
-                            cdiv[(i, c, wk)], report, where=f"{name} step {t} worker {wk} tensor {i} chunk {c}", s=s)
+                            cdiv[(i, c, wk)], report, where=f"{name} step {t} worker {wk} tensor {i} chunk {c}", s=s,
+                            noise=noise)
                         M_or[(i, c)][wk] = out["M"]
                         or_vals[(i, c)][wk] = out["values"]
                         or_idx[(i, c)][wk] = out["idx"]
-                        or_q[(i, c)][wk] = out["Q"]
+                        or_q[(i, c)][wk] = out["terms_chunks"]
                         or_at[(i, c)] = (s0, keff)
             del G
         say(f"[{name}] step {t}: encode of {W} workers checked; decode/apply")
         for gr in groups:
+            for i in gr["ids"]:
+                probe[i].zero_()
             if wire:  # the bench's wire variant: pack all W payloads, decode from the wire
                 gr["codec"].pack_wire(W, gr["vals"], gr["pidx"], gr["wv"], gr["wi"])
                 gr["codec"].decode_apply_wire([X[i] for i in gr["ids"]], W, gr["wv"], gr["wi"], phi_c, w.eta, w.lam)
+                gr["codec"].decode_apply_wire([probe[i] for i in gr["ids"]], W, gr["wv"], gr["wi"],
+                                              B.DEMO_PHI_IDENTITY, 1.0, 0.0)
             else:
                 gr["codec"].decode_apply([X[i] for i in gr["ids"]], W, gr["vals"], gr["pidx"], phi_c, w.eta, w.lam,
                                          **bkw)
+                gr["codec"].decode_apply([probe[i] for i in gr["ids"]], W, gr["vals"], gr["pidx"],
+                                         B.DEMO_PHI_IDENTITY, 1.0, 0.0, **bkw)
         torch.cuda.synchronize()
         for (i, c), xo in X_or.items():
             assert torch.isfinite(X[i]).all(), f"{name}: non-finite parameters, tensor {i}"
@@ -191,6 +209,8 @@ def test_full_size_sampled(dev, name, s, wire, rand):
                            for v, ix in zip(or_vals[(i, c)], or_idx[(i, c)])]
             dec = O.decode_apply(xo, np.stack(vals_in), np.stack(or_idx[(i, c)]), phi=w.phi,
                                  eta=w.eta, lam=w.lam, s=s, P0=P0, P1=P1)
+            PR.compare_mstar(dec["Qabs"], dec["Mstar"], -chunk_block(probe[i], w.shapes[i], c, s), xo.shape, div,
+                             where=f"{name} step {t} tensor {i} chunk {c} (M*)", s=s, noise=noise)
             ediv[(i, c)] = PR.compare_decode(dec, xo.shape, w.phi, w.eta, chunk_block(X[i], w.shapes[i], c, s), div,
                                              ediv.get((i, c)), where=f"{name} step {t} tensor {i} chunk {c}", s=s)
             X_or[(i, c)] = dec["X"]

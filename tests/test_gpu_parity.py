@@ -30,12 +30,20 @@ def dev():
 
 
 class Sim:
-    """W workers of one workload, GPU next to the oracle."""
+    """W workers of one workload, GPU next to the oracle.
+
+    After every step's decode the same payloads are decoded once more into a
+    zero tensor with eta = 1, lambda = 0 and phi = identity, which leaves
+    exactly -M* there: M* itself is compared with the oracle's element by
+    element (parity.compare_mstar), not only through the parameters.
+    """
 
     def __init__(self, w: DI.Workload, *, plain=False, avg="count", inputs=None, identity=False, aggregated=False,
-                 signs=False, chunk=64, wire=False):
+                 signs=False, chunk=64, wire=False, noise=None, mstar=True):
         self.w = w
         self.s = chunk
+        self.noise = noise if noise is not None else (PR.NOISE_DENSE if w.random_basis else PR.NOISE)
+        self.mstar = mstar
         self.wire = wire  # payloads go through the compact wire format: pack, then decode_apply_wire
         assert not (wire and (signs or aggregated))
         self.signs = signs  # one-bit download: decode_signs, then apply_signs (phi = sign)
@@ -59,6 +67,7 @@ class Sim:
         self.X_gpu = [torch.from_numpy(x.copy()).cuda() for x in X0]
         self.X_or = [x.copy() for x in X0]
         self.vals, self.idx = self.codec.alloc_payload(W)
+        self.probe = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in self.shapes]
         self.sign_words = self.codec.alloc_signs() if signs else None
         if wire:
             self.wv, self.wi = self.codec.alloc_wire(W)
@@ -113,11 +122,12 @@ class Sim:
                     out, shp, keff, 0.0 if self.aggregated else w.alpha,
                     O.dct_basis(self.s) if P0 is None else P0, O.dct_basis(self.s) if P1 is None else P1, gM,
                     gv[e0:e0 + n * keff].reshape(n, keff), gi[e0:e0 + n * keff].reshape(n, keff),
-                    self.cdiv[wk][i], self.report, where=f"{w.name} step {t} worker {wk} tensor {i} {shp}", s=self.s)
+                    self.cdiv[wk][i], self.report, where=f"{w.name} step {t} worker {wk} tensor {i} {shp}", s=self.s,
+                    noise=self.noise)
                 self.M_or[wk][i] = out["M"]
                 or_vals[i][wk] = out["values"]
                 or_idx[i][wk] = out["idx"]
-                or_q[i][wk] = out["Q"]
+                or_q[i][wk] = out["terms_chunks"]
         if self.wire:
             return self.step_wire(t, or_vals, or_idx, or_q, phi_c, avg_c, P0, P1, P0d, P1d)
         say(f"  [{w.name}] step {t}: GPU decode/apply over {W} payloads")
@@ -137,12 +147,16 @@ class Sim:
         else:
             self.codec.decode_apply(self.X_gpu, W, self.vals, self.idx, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
         torch.cuda.synchronize()
+        probe = self.probe_mstar(avg_c, P0d, P1d)
         for i, shp in enumerate(self.shapes):
             dec = O.decode_apply(self.X_or[i], np.stack(or_vals[i]), np.stack(or_idx[i]), phi=w.phi, eta=w.eta,
                                  lam=w.lam, mode=self.avg, P0=P0, P1=P1, s=self.s)
             cd = np.zeros_like(self.cdiv[0][i])
             for wk in range(W):
                 cd |= self.cdiv[wk][i]
+            if probe is not None:
+                PR.compare_mstar(dec["Qabs"], dec["Mstar"], -probe[i], shp, cd, noise=self.noise,
+                                 where=f"{w.name} step {t} tensor {i} {shp} (M*)", s=self.s)
             if self.signs:
                 wb = self.codec.sign_word_begin
                 PR.compare_signs(dec["Mstar"], shp, words[wb[i]:wb[i + 1]], cd,
@@ -156,8 +170,24 @@ class Sim:
                 for wk in range(W):
                     self.M_or[wk][i] = O.subtract_aggregated(self.M_or[wk][i], dec["Mstar"], w.alpha)
                     PR.compare_momentum(self.M_or[wk][i], self.M_gpu[wk][i].cpu().numpy(), shp, cd,
-                                        where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (aggregated)", s=self.s)
+                                        where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (aggregated)", s=self.s,
+                                        scale=O.hp(w.alpha) * dec["Mstar"], noise=self.noise)
                     self.cdiv[wk][i] = self.cdiv[wk][i] | cd
+
+    def probe_mstar(self, avg_c, P0d, P1d, wire=False):
+        """-M* of this step's payloads (host arrays per tensor), or None when disabled."""
+        if not self.mstar:
+            return None
+        for t in self.probe:
+            t.zero_()
+        if wire:
+            self.codec.decode_apply_wire(self.probe, self.w.workers, self.wv, self.wi, B.DEMO_PHI_IDENTITY, 1.0, 0.0,
+                                         avg_c, P0d, P1d)
+        else:
+            self.codec.decode_apply(self.probe, self.w.workers, self.vals, self.idx, B.DEMO_PHI_IDENTITY, 1.0, 0.0,
+                                    avg_c, P0d, P1d)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in self.probe]
 
     def step_wire(self, t, or_vals, or_idx, or_q, phi_c, avg_c, P0, P1, P0d, P1d):
         """Pack all W payloads into the wire format, check it, decode from it."""
@@ -173,6 +203,7 @@ class Sim:
         wi = self.wi.cpu().numpy()
         self.codec.decode_apply_wire(self.X_gpu, W, self.wv, self.wi, phi_c, w.eta, w.lam, avg_c, P0d, P1d)
         torch.cuda.synchronize()
+        probe = self.probe_mstar(avg_c, P0d, P1d, wire=True)
         wb = self.wire_bytes
         used = 3 * ((ne + 1) // 2)
         codes, gidx = [], []
@@ -197,6 +228,9 @@ class Sim:
                   for wk in range(W)]
             dec = O.decode_apply(self.X_or[i], np.stack(vr), np.stack(or_idx[i]), phi=w.phi, eta=w.eta, lam=w.lam,
                                  mode=self.avg, P0=P0, P1=P1, s=self.s)
+            if probe is not None:
+                PR.compare_mstar(dec["Qabs"], dec["Mstar"], -probe[i], shp, cd, noise=self.noise,
+                                 where=f"{w.name} step {t} tensor {i} {shp} (wire M*)", s=self.s)
             self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
                                              where=f"{w.name} step {t} tensor {i} {shp} (wire)", s=self.s)
             self.X_or[i] = dec["X"]
@@ -259,6 +293,120 @@ def test_unit_scale_inputs(dev):
     w = DI.WORKLOADS["tiny_256"].replace(name="unit_scale", shapes=((192, 320), (129,)), grad_std=1.0,
                                          param_std=1.0, beta=0.9, k=16, workers=3, eta=0.01)
     Sim(w, plain=True).run(3)
+
+
+UNIT_CASES = {
+    # name: (Sim keyword arguments, workload overrides)
+    "s64_damped": (dict(), dict()),
+    "s64_damped_k100_w20": (dict(), dict(k=100, workers=20)),
+    "s128_damped": (dict(chunk=128), dict(shapes=((256, 300), (130,)))),
+    "s128_plain_workers": (dict(chunk=128, plain=True, avg="workers"), dict(shapes=((300, 256), (257,)), phi="identity")),
+    "s128_k100": (dict(chunk=128), dict(shapes=((256, 256), (300,)), k=100, workers=5)),
+    "identity": (dict(identity=True), dict()),
+    "identity_workers": (dict(identity=True, avg="workers"), dict(phi="identity")),
+    "caller_basis": (dict(), dict(random_basis=True)),
+    "caller_basis_plain": (dict(plain=True), dict(random_basis=True, phi="identity")),
+    "aggregated": (dict(aggregated=True), dict()),
+    "aggregated_s128": (dict(aggregated=True, chunk=128), dict(shapes=((256, 128), (200,)))),
+    "aggregated_caller_basis": (dict(aggregated=True), dict(random_basis=True, k=4)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(UNIT_CASES))
+def test_unit_scale_variants(dev, case):
+    """Unit-scale gradients and parameters (std 1) through every variant: the encode's payload and
+    momentum, M* and the parameters all at a scale where the relative tolerance decides."""
+    kw, over = UNIT_CASES[case]
+    base = dict(name=f"unit_{case}", shapes=((192, 320), (129,)), grad_std=1.0, param_std=1.0, k=16, workers=3,
+                eta=0.01)
+    base.update(over)
+    w = DI.WORKLOADS["tiny_256"].replace(**base)
+    Sim(w, **kw).run(3)
+
+
+def test_long_run_drift(dev):
+    """The 256x256 workload free-running for 700 steps (the pages' momentum half-life at beta = 0.999 is
+    about 693 steps), GPU and oracle each from their own state.  The momentum's rounding differences
+    accumulate over the momentum's memory; the floor each step needs (per unit of chunk norm) must stay
+    under parity.NOISE, the same floor as the short runs, and every chunk must stay on the oracle's top-k
+    sets or within a tie window."""
+    w = DI.WORKLOADS["tiny_256"].replace(name="long_run", steps=700)
+    sim = Sim(w)
+    curve, worst = [], {}
+    for t in range(w.steps):
+        sim.step(t)
+        for kind in list(PR.STATS):
+            worst[kind] = max(worst.get(kind, 0.0), PR.STATS[kind])
+        curve.append(PR.STATS.get("momentum", 0.0))
+        PR.STATS.clear()
+        if t + 1 in (1, 10, 50, 100, 200, 300, 400, 500, 600, 700):
+            say(f"  [long_run] step {t + 1}: momentum floor needed this step {curve[-1]:.3e} "
+                f"(2^{np.log2(max(curve[-1], 1e-300)):.1f}), largest so far {max(curve):.3e}")
+    PR.STATS.update(worst)
+    r = sim.report
+    say(f"  [long_run] chunks checked {r.chunks}: exact {r.exact} ({r.exact / r.chunks:.4f}), near-tie {r.ties}, "
+        f"skipped {r.skipped}")
+    assert max(curve) <= PR.NOISE
+    assert r.ties + r.skipped <= 0.02 * r.chunks
+
+
+def _sum_order_payloads(s, keff, c, split):
+    """Payloads of 4 workers for one s x s chunk (keff entries each, ascending indices) where
+    coefficient c is at entry position >= 64 for worker 0 and < 64 for workers 1 and 2; worker 3
+    lacks it.  split: the three values at c."""
+    numel = s * s
+    below = list(range(0, 30))
+    above_hi = list(range(c + 1, c + 1 + (keff - 31)))
+    assert above_hi[-1] < numel
+    w0 = sorted(set(range(c - (keff - 1), c)) | {c})  # c last: position keff - 1 >= 64
+    w12 = sorted(set(below) | {c} | set(above_hi))     # c at position 30 < 64
+    w3 = sorted(set(range(c - keff, c)))
+    vals, idx = [], []
+    for wk, ix in enumerate([w0, w12, w12, w3]):
+        assert len(ix) == keff
+        v = np.zeros(keff, np.float32)
+        if wk < 3:
+            v[ix.index(c)] = split[wk]
+        vals.append(v)
+        idx.append(np.array(ix, np.uint16))
+    return np.concatenate(vals), np.concatenate(idx)
+
+
+@pytest.mark.parametrize("chunk,c", [(64, 4000), (128, 16000)])
+def test_summation_follows_worker_order(dev, chunk, c):
+    """Coefficients are summed in worker order 0..W-1 also when one worker holds the coefficient in its
+    second 64-entry block and later workers in their first (keff = 100).  With values 1, 2^-24, 2^-24 the
+    float32 sum in worker order is 1, the same as a payload that sends 1, 0, 0: M* must be bitwise equal
+    for the two.  Summed block by block (workers 1 and 2 first) it would be 1 + 2^-23.  Repeated calls are
+    bitwise equal too, also with 20 workers."""
+    keff = 100
+    shapes = ((chunk, chunk),)
+    codec = B.Codec(shapes, keff, chunk=chunk)
+    outs = []
+    for split in ([1.0, 2.0 ** -24, 2.0 ** -24], [1.0, 0.0, 0.0]):
+        v, ix = _sum_order_payloads(chunk, keff, c, split)
+        X = [torch.zeros(shapes[0], device="cuda")]
+        codec.decode_apply(X, 4, torch.from_numpy(v).cuda(), torch.from_numpy(ix.view(np.int16)).cuda(),
+                           B.DEMO_PHI_IDENTITY, 1.0, 0.0, B.DEMO_AVG_WORKERS)
+        torch.cuda.synchronize()
+        outs.append(X[0].cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "coefficients not summed in worker order"
+    # determinism with W = 20 workers, keff = 100 (several register batches and entry blocks)
+    lay = [(n, k, chunk * chunk if len(sh) == 2 else chunk) for (n, k, _), sh in
+           zip(PR.layout(((chunk, 2 * chunk), (300,)), keff, chunk), ((chunk, 2 * chunk), (300,)))]
+    codec.close()
+    codec = B.Codec(((chunk, 2 * chunk), (300,)), keff, chunk=chunk)
+    v, ix = DI.synthetic_payload(lay, 20, seed=91, scale=1.0)
+    vd, idd = torch.from_numpy(v).cuda(), torch.from_numpy(ix.view(np.int16)).cuda()
+    res = []
+    for _ in range(2):
+        X = [torch.zeros((chunk, 2 * chunk), device="cuda"), torch.zeros((300,), device="cuda")]
+        codec.decode_apply(X, 20, vd, idd, B.DEMO_PHI_IDENTITY, 1.0, 0.0)
+        torch.cuda.synchronize()
+        res.append([x.cpu().numpy() for x in X])
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    codec.close()
 
 
 def test_degenerate_chunks(dev):
