@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.demo_decode_apply_muon.restype = i32
     lib.demo_decode_apply_muon.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32, vp, vp, i64, f32,
                                            f32, f32, i32, i32, vp, i64, vp]
+    lib.demo_decode_apply_muon_noalloc.restype = i32
+    lib.demo_decode_apply_muon_noalloc.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32, vp, vp,
+                                                   i64, f32, f32, f32, i32, i32, vp]
     lib.demo_wire_size.restype = i32
     lib.demo_wire_size.argtypes = [i64, P(i64), P(i64)]
     lib.demo_pack_wire.restype = i32
@@ -333,6 +336,28 @@ def demo_decode_apply_muon(ctx: int, params, cfg: demo_codec_cfg, workers: int, 
                                       workspace.numel() * workspace.element_size(), _stream_handle(stream)))
 
 
+DEMO_MUON_SCRATCH_BYTES = 64 << 20
+
+
+def demo_decode_apply_muon_noalloc(ctx: int, params, cfg: demo_codec_cfg, workers: int, pay_values, pay_idx,
+                                   eta: float = 1e-3, lam: float = 0.0, eps: float = 1e-8, iters: int = 24,
+                                   avg: int = DEMO_AVG_CONTRIBUTORS, stream=None) -> None:
+    """demo_decode_apply_muon on the library's static scratch (no workspace, nothing allocated)."""
+    lib = load_library()
+    import torch
+    for x in params:
+        if x.dtype != torch.float32:
+            raise ValueError("parameters must be float32")
+    if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
+        raise ValueError("payload arrays must hold workers x entries elements")
+    per = pay_values.numel() // workers
+    _check(lib.demo_decode_apply_muon_noalloc(ctx, len(params), _shapes([tuple(x.shape) for x in params]),
+                                              _ptrs([_device_ptr(x, 4) for x in params]), ctypes.byref(cfg),
+                                              int(workers), _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per,
+                                              float(eta), float(lam), float(eps), int(iters), int(avg),
+                                              _stream_handle(stream)))
+
+
 def demo_wire_size(n_entries: int) -> Tuple[int, int]:
     """(value bytes, index bytes) of one worker's wire payload of n_entries entries; host-only."""
     lib = load_library()
@@ -466,6 +491,11 @@ class Codec:
         """Device workspace of the Muon decode for this list (uint8 storage)."""
         import torch
         return torch.empty(demo_muon_workspace(self.shapes), dtype=torch.uint8, device=device)
+
+    def decode_apply_muon_noalloc(self, params, workers, pay_values, pay_idx, eta=1e-3, lam=0.0, eps=1e-8,
+                                  iters=24, avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:
+        demo_decode_apply_muon_noalloc(self.ctx, params, self.cfg(P0, P1), workers, pay_values, pay_idx, eta, lam,
+                                       eps, iters, avg, stream)
 
     def decode_apply_muon(self, params, workers, pay_values, pay_idx, workspace, eta=1e-3, lam=0.0, eps=1e-8,
                           iters=24, avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:

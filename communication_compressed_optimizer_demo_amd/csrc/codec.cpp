@@ -16,6 +16,7 @@
 
 struct demo_ctx {
   int device;
+  float* scratch;  // the device's static Muon scratch (demo::kMuonScratchBytes), looked up at creation
 };
 
 namespace {
@@ -26,6 +27,7 @@ using demo::kMaxTensorsPerLaunch;
 static_assert(kMaxTensorsPerLaunch == DEMO_MAX_TENSORS_PER_LAUNCH, "header and launch table disagree");
 static_assert(demo::kMaxWorkers == DEMO_MAX_WORKERS, "header and kernels disagree");
 static_assert(kChunk == DEMO_CHUNK && kChunkLarge == DEMO_CHUNK_LARGE, "header and kernels disagree on chunk edges");
+static_assert(demo::kMuonScratchBytes == DEMO_MUON_SCRATCH_BYTES, "header and kernels disagree on the scratch size");
 using demo::LaunchTable;
 
 thread_local std::string g_last_error;
@@ -313,9 +315,21 @@ demo_status demo_ctx_create(int32_t device, demo_ctx** out) {
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) return fail(DEMO_ERR_HIP, "hipGetDeviceProperties failed");
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(DEMO_ERR_DEVICE, std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
+  if (device >= demo::kMaxDevices) return fail(DEMO_ERR_DEVICE, "device ordinal beyond the library's device table");
+  // The static Muon scratch's address on this device, looked up with the
+  // device current (once per device; later contexts reuse it).
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(DEMO_ERR_HIP, "hipGetDevice failed");
+  if (prev != device && hipSetDevice(device) != hipSuccess) return fail(DEMO_ERR_HIP, "hipSetDevice failed");
+  float* scratch = nullptr;
+  const hipError_t se = demo::muon_scratch(device, &scratch);
+  if (prev != device && hipSetDevice(prev) != hipSuccess) return fail(DEMO_ERR_HIP, "hipSetDevice failed");
+  if (se != hipSuccess)
+    return fail(DEMO_ERR_HIP, std::string("hipGetSymbolAddress of the Muon scratch failed: ") + hipGetErrorString(se));
   demo_ctx* c = new (std::nothrow) demo_ctx;
   if (c == nullptr) return fail(DEMO_ERR_INVALID, "out of host memory");
   c->device = device;
+  c->scratch = scratch;
   *out = c;
   return DEMO_OK;
 }
@@ -501,11 +515,21 @@ demo_status demo_muon_workspace(const demo_shape* shapes, int32_t n, int64_t* ws
   return DEMO_OK;
 }
 
-demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
-                                   const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
-                                   const uint16_t* pay_idx, int64_t n_entries, float eta, float lambda, float eps,
-                                   int32_t iters, demo_average avg, void* workspace, int64_t ws_bytes,
-                                   hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The Muon decode over a caller workspace, or (from_scratch) over the
+// context's static scratch: then workspace and ws_bytes are ignored, and a
+// NULL context is still reported last, after every other check.
+demo_status muon_decode(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                        const demo_codec_cfg* cfg, int32_t workers, const float* pay_values, const uint16_t* pay_idx,
+                        int64_t n_entries, float eta, float lambda, float eps, int32_t iters, demo_average avg,
+                        void* workspace, int64_t ws_bytes, hipStream_t stream, bool from_scratch = false) {
+  if (from_scratch) {
+    workspace = ctx != nullptr ? ctx->scratch : nullptr;
+    ws_bytes = demo::kMuonScratchBytes;
+  }
   if (cfg == nullptr) return fail(DEMO_ERR_INVALID, "cfg is NULL");
   if (cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the Muon decode is built for chunk 64");
   if (n > 0 && params == nullptr) return fail(DEMO_ERR_INVALID, "parameter pointer list is NULL");
@@ -518,7 +542,7 @@ demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* s
   if (ws_bytes < L.bytes)
     return fail(DEMO_ERR_RANGE, "workspace holds " + std::to_string(ws_bytes) + " bytes, the list needs " +
                                     std::to_string(L.bytes));
-  if (L.bytes > 0 && workspace == nullptr) return fail(DEMO_ERR_INVALID, "workspace is NULL");
+  if (!from_scratch && L.bytes > 0 && workspace == nullptr) return fail(DEMO_ERR_INVALID, "workspace is NULL");
   if (!aligned(workspace, 16)) return fail(DEMO_ERR_ALIGN, "workspace misaligned (16 bytes)");
   for (int32_t i = 0; i < n; ++i) {
     if (params[i] == nullptr) return fail(DEMO_ERR_INVALID, "tensor " + std::to_string(i) + ": NULL device pointer");
@@ -526,7 +550,10 @@ demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* s
   }
   float* ws = static_cast<float*>(workspace);
   std::vector<float*> mstar(size_t(n > 0 ? n : 0));
-  for (int32_t i = 0; i < n; ++i) mstar[i] = ws + L.mstar[i];
+  // addresses inside the workspace (integer arithmetic: with from_scratch and
+  // no context the base is NULL, and decode_common fails before any launch)
+  for (int32_t i = 0; i < n; ++i)
+    mstar[i] = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(workspace) + uintptr_t(L.mstar[i]) * 4u);
   // rows a7, a8: M* of every tensor into the workspace (validates the rest,
   // the context last; nothing is enqueued unless all of it passes)
   s = decode_common(ctx, n, shapes, nullptr, nullptr, cfg, workers, pay_values, pay_idx, n_entries, DEMO_PHI_IDENTITY,
@@ -628,6 +655,35 @@ demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* s
     b0 = b1;
   }
   return DEMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                   const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                                   const uint16_t* pay_idx, int64_t n_entries, float eta, float lambda, float eps,
+                                   int32_t iters, demo_average avg, void* workspace, int64_t ws_bytes,
+                                   hipStream_t stream) {
+  return muon_decode(ctx, n, shapes, params, cfg, workers, pay_values, pay_idx, n_entries, eta, lambda, eps, iters,
+                     avg, workspace, ws_bytes, stream);
+}
+
+demo_status demo_decode_apply_muon_noalloc(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                           const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                                           const uint16_t* pay_idx, int64_t n_entries, float eta, float lambda,
+                                           float eps, int32_t iters, demo_average avg, hipStream_t stream) {
+  std::vector<TensorPlan> plan;
+  demo_status s = plan_list(shapes, n, kChunk, 1, &plan, nullptr, nullptr);
+  if (s != DEMO_OK) return s;
+  const int64_t need = muon_layout(plan).bytes;
+  if (need > demo::kMuonScratchBytes)
+    return fail(DEMO_ERR_RANGE, "the list needs " + std::to_string(need) + " bytes of Muon workspace; the static " +
+                                    "scratch holds " + std::to_string(demo::kMuonScratchBytes) +
+                                    " (use demo_decode_apply_muon with a workspace)");
+  return muon_decode(ctx, n, shapes, params, cfg, workers, pay_values, pay_idx, n_entries, eta, lambda, eps, iters,
+                     avg, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

@@ -25,6 +25,8 @@
 //    128 x 128, K stages of kSK, 16-byte loads two stages ahead.
 // Both take a batch of same-shape products (grid z), which the Newton-Schulz
 // steps of several matrices with equal n share.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -476,6 +478,34 @@ hipError_t launch_muon_vector(const float* m, float* x, int64_t len, float eps, 
                               hipStream_t stream) {
   muon_vector_kernel<<<1, 256, 0, stream>>>(m, x, len, eps, eta, lam);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- static scratch
+
+}  // namespace demo
+
+// The Muon decode's workspace for callers that cannot allocate device memory
+// (graph capture, tight serving loops): one array per device, held until the
+// process ends.  Host code must not pass `scratch` itself to a kernel (in
+// host code it names a host-side stand-in); it uses the device address that
+// muon_scratch looks up.
+static __device__ __align__(256) float scratch[demo::kMuonScratchBytes / sizeof(float)];
+
+namespace demo {
+
+hipError_t muon_scratch(int device, float** out) {
+  static std::mutex mu;
+  static float* address[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (address[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    address[device] = static_cast<float*>(p);
+  }
+  *out = address[device];
+  return hipSuccess;
 }
 
 }  // namespace demo

@@ -118,6 +118,13 @@ hipError_t launch_ns_prepare(const float* A, int n, float eps, double* partial, 
                              hipStream_t stream);
 hipError_t launch_muon_vector(const float* m, float* x, int64_t len, float eps, float eta, float lam,
                               hipStream_t stream);
+// The Muon decode's static device scratch (kernels_muon.hip), for callers
+// that cannot allocate: kMuonScratchBytes per device.  muon_scratch returns
+// its device address on `device`, which must be the current device; the
+// address is looked up once per device and kept.
+constexpr int64_t kMuonScratchBytes = int64_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t muon_scratch(int device, float** out);
 
 // Chunk edge 128 (kernels128.hip): DCT basis; a work item is one 128x128
 // chunk or 128 vector chunks, 256 threads each.

@@ -283,6 +283,28 @@ demo_status demo_decode_apply_muon(demo_ctx* ctx, int32_t n, const demo_shape* s
                                    int32_t iters, demo_average avg, void* workspace, int64_t ws_bytes,
                                    hipStream_t stream);
 
+/* ---- The Muon decode without allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).
+ *
+ * demo_decode_apply_muon with the workspace taken from a static device array
+ * of DEMO_MUON_SCRATCH_BYTES that the library holds on every device it runs
+ * on, until the process ends.  Nothing is allocated by the call.
+ *   - A list whose workspace (demo_muon_workspace) exceeds
+ *     DEMO_MUON_SCRATCH_BYTES is refused with DEMO_ERR_RANGE before anything
+ *     is enqueued.
+ *   - All calls on one GPU share that GPU's scratch.  Calls that overlap on
+ *     one GPU (different streams, or different threads without ordering)
+ *     race; calls ordered on one stream do not.  The scratch keeps the last
+ *     call's contents; no part of it has to start at zero.
+ * Other arguments, validation and errors as for demo_decode_apply_muon. */
+#define DEMO_MUON_SCRATCH_BYTES (64ll << 20)
+
+demo_status demo_decode_apply_muon_noalloc(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
+                                           const demo_codec_cfg* cfg, int32_t workers, const float* pay_values,
+                                           const uint16_t* pay_idx, int64_t n_entries, float eta, float lambda,
+                                           float eps, int32_t iters, demo_average avg, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

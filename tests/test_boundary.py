@@ -406,3 +406,43 @@ def test_wire_decode_arguments(lib, kw, status, text):
 def test_pack_wire_arguments(lib, args, status, text):
     assert lib.demo_pack_wire(None, *args, None) == status
     assert text in _msg(lib)
+
+
+# --------------------------------------------------------------------------- Muon decode without allocation
+
+def _call_muon_noalloc(lib, shapes, k=8, workers=2, eps=1e-6, iters=24, chunk=64, params=0x1000):
+    cfg = B.demo_codec_cfg(chunk, k, 0.9, 0.2, 0, 0, None, None, 0)
+    n = len(shapes)
+    return lib.demo_decode_apply_muon_noalloc(None, n, B._shapes(shapes), B._ptrs([params] * n), ctypes.byref(cfg),
+                                              workers, 0x3000, 0x4000, O.payload_entries(shapes, k), 1e-3, 0.0, eps,
+                                              iters, 0, None)
+
+
+def test_muon_noalloc_scratch_size_matches_header(lib):
+    text = open(os.path.join(ROOT, "include", "demo_codec.h")).read()
+    m = re.search(r"#define DEMO_MUON_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.DEMO_MUON_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("shapes,status,text", [
+    ([(70, 90), (100,)], 1, "context"),            # fits: every other check passes, then the context is NULL
+    ([(2048, 2048)], 3, "static scratch"),          # 112 MB of workspace: refused before anything else
+    ([(1024, 1024), (1024, 1024), (1024, 1024)], 3, "static scratch"),
+])
+def test_muon_noalloc_arguments(lib, shapes, status, text):
+    assert _call_muon_noalloc(lib, shapes) == status
+    assert text in _msg(lib)
+    fits = B.demo_muon_workspace(shapes) <= B.DEMO_MUON_SCRATCH_BYTES
+    assert fits == (status != 3)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(eps=-1.0), 1, "eps"),
+    (dict(iters=0), 3, "iters"),
+    (dict(chunk=128), 3, "chunk 64"),
+    (dict(workers=0), 3, "workers"),
+    (dict(params=0), 1, "NULL device pointer"),
+])
+def test_muon_noalloc_checks_the_rest_before_the_context(lib, kw, status, text):
+    assert _call_muon_noalloc(lib, [(70, 90), (100,)], **kw) == status
+    assert text in _msg(lib)
