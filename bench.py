@@ -8,7 +8,11 @@ update, 64x64 chunking, DCT, per-chunk top-k, payload, momentum subtraction)
 of every tensor, then decode/apply of all W workers' payloads (sparse
 average, inverse DCT, phi, weight-decayed update) of every tensor.  The
 whole tensor list goes into one call per half (one launch each for up to 96
-tensors); HIP events on the launch stream time each half.
+tensors).  The step is captured once into a HIP graph and replayed, as a
+training loop would replay its optimizer step; the host clock around the
+replays gives the step time.  Per-kernel times come from HIP events on the
+launch stream between eager calls of the same step (--no-graph: the step
+time from those eager calls too).
 
 Inputs are synthetic and resident in HBM before timing: gradients drawn once
 with a seeded device generator, momentum starting at zero, parameters
@@ -63,6 +67,8 @@ def parse():
                          "decode to packed sign bits then apply them (phi = sign); wire: this worker's payload "
                          "packed into the compact wire format (bfloat16 values, 12-bit indices), the decode "
                          "reading all W payloads in that format")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every call eagerly instead of replaying a captured HIP graph of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one untimed 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -287,7 +293,8 @@ def muon_flops(shapes, iters: int) -> int:
 
 
 def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False, basis: str = "dct",
-              subtraction: str = "local", download: str = "apply", chunk: int = 64, muon_iters: int = 0):
+              subtraction: str = "local", download: str = "apply", chunk: int = 64, muon_iters: int = 0,
+              graph: bool = True):
     import torch
 
     from communication_compressed_optimizer_demo_amd import binding as B
@@ -349,29 +356,29 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     # Gram eigenvalues of these M*
     muon_eps = 1e-12
 
-    # the step's calls in order; HIP events between them time each one
-    calls = [("encode", lambda: codec.encode(G, M, vals[:ne], pidx[:ne], stream=stream, **basis_kw))]
+    # the step's calls in order, each taking the stream to launch on
+    calls = [("encode", lambda st: codec.encode(G, M, vals[:ne], pidx[:ne], stream=st, **basis_kw))]
     if download == "signs":  # server: packed sign(M*); worker: apply the bits
-        calls.append(("decode", lambda: codec.decode_signs(W, vals, pidx, signs, stream=stream)))
-        calls.append(("apply", lambda: codec.apply_signs(X, signs, w.eta, w.lam, stream=stream)))
+        calls.append(("decode", lambda st: codec.decode_signs(W, vals, pidx, signs, stream=st)))
+        calls.append(("apply", lambda st: codec.apply_signs(X, signs, w.eta, w.lam, stream=st)))
     elif download == "wire":
-        calls.append(("pack", lambda: codec.pack_wire(1, vals[:ne], pidx[:ne], wv[:ne], wi[:wb], stream=stream)))
-        calls.append(("decode", lambda: codec.decode_apply_wire(X, W, wv, wi, phi, w.eta, w.lam, stream=stream)))
+        calls.append(("pack", lambda st: codec.pack_wire(1, vals[:ne], pidx[:ne], wv[:ne], wi[:wb], stream=st)))
+        calls.append(("decode", lambda st: codec.decode_apply_wire(X, W, wv, wi, phi, w.eta, w.lam, stream=st)))
     elif muon_iters:
-        calls.append(("decode", lambda: codec.decode_apply_muon(X, W, vals, pidx, muon_ws, w.eta, w.lam, muon_eps,
-                                                                muon_iters, stream=stream)))
+        calls.append(("decode", lambda st: codec.decode_apply_muon(X, W, vals, pidx, muon_ws, w.eta, w.lam, muon_eps,
+                                                                   muon_iters, stream=st)))
     elif aggregated:  # this worker's parameters and momentum, one pass
-        calls.append(("decode", lambda: codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam,
-                                                                    stream=stream)))
+        calls.append(("decode", lambda st: codec.decode_apply_subtract(X, M, W, vals, pidx, phi, w.eta, w.lam,
+                                                                       stream=st)))
     else:
-        calls.append(("decode", lambda: codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=stream,
-                                                           **basis_kw)))
+        calls.append(("decode", lambda st: codec.decode_apply(X, W, vals, pidx, phi, w.eta, w.lam, stream=st,
+                                                              **basis_kw)))
 
     def one_step(ev):
         for j, (_, fn) in enumerate(calls):
             if ev:
                 ev[j].record(stream)
-            fn()
+            fn(stream)
         if ev:
             ev[len(calls)].record(stream)
 
@@ -379,7 +386,8 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     for _ in range(warmup):
         one_step(None)
     torch.cuda.synchronize()
-    log(f"timing {steps} steps")
+    # per-kernel times: HIP events on the launch stream between eager calls
+    log(f"timing {steps} eager steps")
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -387,8 +395,22 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
         one_step(events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
     per = {name: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j, (name, _) in enumerate(calls)}
+    if graph:
+        # the step time: replays of the whole step captured once as a HIP graph
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            for _, fn in calls:
+                fn(torch.cuda.current_stream())
+        for _ in range(2):
+            g_step.replay()
+        torch.cuda.synchronize()
+        log(f"timing {steps} graph replays of the step")
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g_step.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     gbytes = 2 if w.grad_bf16 else 4
     numel = w.n_params
     kern = {}
@@ -470,7 +492,7 @@ def main():
         w = w.replace(phi="sign")  # the one-bit download exists for the Signum variant only
     cpu = None if args.no_cpu_baseline or args.phi else cpu_baseline(w)
     g = gpu_bench(w, args.steps, args.warmup, args.copy_probe, args.basis, args.subtraction, args.download,
-                  args.chunk, args.muon_iters if args.phi == "muon" else 0)
+                  args.chunk, args.muon_iters if args.phi == "muon" else 0, graph=not args.no_graph)
     line = {
         "metric": METRIC,
         "value": g["value"],
@@ -500,6 +522,7 @@ def main():
             "basis": args.basis,
             "subtraction": args.subtraction,
             "download": args.download,
+            "launch": "eager" if args.no_graph else "hip_graph",
             **({"muon_iters": args.muon_iters} if args.phi == "muon" else {}),
         },
         "step_GBps": round(g["step_GBps"], 1),

@@ -30,13 +30,17 @@ __device__ __forceinline__ T stream_load(const T* p) {
 
 __device__ __forceinline__ void stream_store(float v, float* p) { __builtin_nontemporal_store(v, p); }
 
-template <bool kBf16>
+// A gradient element widened to float32; kKeep: a plain load (the line may
+// stay cached for a second read), otherwise a streaming one.
+template <bool kBf16, bool kKeep = false>
 __device__ __forceinline__ float load_src(const void* p, int64_t off) {
   if constexpr (kBf16) {
-    const uint32_t b = stream_load(static_cast<const uint16_t*>(p) + off);
+    const uint16_t* q = static_cast<const uint16_t*>(p) + off;
+    const uint32_t b = kKeep ? uint32_t(*q) : uint32_t(stream_load(q));
     return __uint_as_float(b << 16);
   } else {
-    return stream_load(static_cast<const float*>(p) + off);
+    const float* q = static_cast<const float*>(p) + off;
+    return kKeep ? *q : stream_load(q);
   }
 }
 

@@ -23,11 +23,11 @@
 //   exact top-k of |Q| over the chunk, lower index wins ties; payload
 //   (value, index) in index order
 //   R = P0^T Q_hat P1 (row pass, LDS transpose, column pass);
-//   M = M' - alpha R, with M' kept in registers since the load (the DCT and
-//   identity bases) or loaded and formed again, bit for bit (the caller
-//   basis, whose matrix-core transform has no registers to spare).  Only the
-//   selected part goes through the float32 transforms, so the rounding of
-//   the rest of M' does not accumulate in the momentum from step to step.
+//   M = M' - alpha R, with M' held in registers since the load (vector
+//   chunks under a caller basis, whose per-lane products need the registers,
+//   load G and M again and form M' bit for bit).  Only the selected part goes
+//   through the float32 transforms, so the rounding of the rest of M' does
+//   not accumulate in the momentum from step to step.
 // decode/apply (§3.4 Server-Side Aggregation, Inverse DCT and Unchunking,
 // Base Optimizer Update):
 //   scatter-add W payloads into an LDS accumulator with 8-bit contributor
@@ -137,14 +137,9 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
     else
       store_rows<false>(q, ts.dst + c.base, ts.cols, c, lane);
   }
-  // M' (column layout) for the subtraction.  The matrix-core transform needs
-  // these registers; it forms M' again from G and M at the end instead.
-  constexpr bool kHold = !Basis::kMatrixCores;
-  float mp[kHold ? 64 : 1];
-  if constexpr (kHold) {
+  float mp[64];  // M' (column layout), held for the subtraction
 #pragma unroll
-    for (int i = 0; i < 64; ++i) mp[i] = q[i];
-  }
+  for (int i = 0; i < 64; ++i) mp[i] = q[i];
 
   if constexpr (Basis::kMatrixCores) {
     basis.template forward2d<kLd>(q, tile, lane);
@@ -155,7 +150,8 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
   }
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  tk::topk_chunk(q, p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile));
+  tk::topk_chunk(q, p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile),
+                 tile + lane * kLd);
   if (!p.subtract_local) return;
   __syncthreads();
 
@@ -168,18 +164,8 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
     basis.inv0(q);
   }
 
-  if constexpr (!kHold) {
-    float m2[64];
-    if (c.full)
-      load_momentum<true, kBf16>(m2, ts, c, lane, p.beta, p.gcoef);
-    else
-      load_momentum<false, kBf16>(m2, ts, c, lane, p.beta, p.gcoef);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) q[i] = fmaf(-p.alpha, q[i], m2[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) q[i] = fmaf(-p.alpha, q[i], mp[i]);
-  }
+  for (int i = 0; i < 64; ++i) q[i] = fmaf(-p.alpha, q[i], mp[i]);  // M = M' - alpha R
   if (c.full)
     store_rows<true>(q, ts.dst + c.base, ts.cols, c, lane);
   else

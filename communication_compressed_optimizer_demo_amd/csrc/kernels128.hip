@@ -262,8 +262,9 @@ __device__ __forceinline__ int quad_row(int qa, int i) { return qa ? (kS - 1 - i
 
 // Returns true when the payload is still to be written by emit_kept (fast
 // path: wave 0 holds the kept list in LDS scratch that nothing else reuses).
+template <bool kSmallK>
 __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lane, float* __restrict__ outv,
-                                        uint16_t* __restrict__ outi, uint32_t* scr) {
+                                        uint16_t* __restrict__ outi, uint32_t* scr, float* tile) {
   const int a = w >> 1, b = w & 1;
   const uint32_t idx0 = uint32_t((2 * lane + a) * kS + b);  // index of q[0]; q[v] sits at idx0 + 2v
   uint32_t* hdr = scr;                             // [0, 4): candidates per wave (~0u: none)
@@ -273,12 +274,14 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
   uint32_t* cid = cval + 4 * kCandPerWave;         // candidate indices
   uint32_t* kl = cid + 4 * kCandPerWave;           // wave 0: kept list (64 values, 64 indices)
 
-  if (keff >= kS * kS) {  // lossless: every coefficient, at its own index
+  if (!kSmallK && keff >= kS * kS) {  // lossless: every coefficient, at its own index
+    // one base per lane, constant offsets per v (no 64 separate addresses)
+    float* __restrict__ ov = outv + idx0;
+    uint16_t* __restrict__ oi = outi + idx0;
 #pragma unroll
     for (int v = 0; v < 64; ++v) {
-      const uint32_t id = idx0 + 2 * v;
-      outv[id] = q[v];
-      outi[id] = static_cast<uint16_t>(id);
+      ov[2 * v] = q[v];
+      oi[2 * v] = static_cast<uint16_t>(idx0 + 2 * v);
     }
     return false;
   }
@@ -287,7 +290,7 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
 #pragma unroll
   for (int v = 0; v < 64; ++v) lm = fmaxf(lm, fabsf(q[v]));
   uint32_t K = 0, cut = 0xffffffffu;  // cut: largest index admitted among |q| == K
-  bool fast = keff <= 64;
+  bool fast = kSmallK || keff <= 64;
   if (fast) {
     const uint32_t lmb = __float_as_uint(lm);
     uint32_t T = 0;
@@ -391,7 +394,14 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
     }
   }
 
-  // bitwise searches over all 16384 magnitudes, counted across the workgroup
+  // bitwise searches over all 16384 magnitudes, counted across the workgroup.
+  // The lane's 64 coefficients go to the wave's transpose tile (unused during
+  // top-k) and the searches read them there, one lane its own row: their
+  // registers are then free for the search, which keeps this rarely taken
+  // path from setting the kernel's register count.
+  float* __restrict__ row = tile + lane * kLd;
+#pragma unroll
+  for (int v = 0; v < 64; ++v) row[v] = q[v];
   int parity = 0;
   float hmax = lm;
 #pragma unroll
@@ -407,7 +417,7 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
     const float cf = __uint_as_float(c);
     int n = 0;
 #pragma unroll
-    for (int v = 0; v < 64; ++v) n += fabsf(q[v]) >= cf ? 1 : 0;
+    for (int v = 0; v < 64; ++v) n += fabsf(row[v]) >= cf ? 1 : 0;
     if (wg_sum(wave_sum(n), red, parity, w, lane) >= keff) T = c;
   }
   K = T;
@@ -416,14 +426,14 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
     int gt = 0, eq = 0;
 #pragma unroll
     for (int v = 0; v < 64; ++v) {
-      gt += fabsf(q[v]) > kf ? 1 : 0;
-      eq += fabsf(q[v]) == kf ? 1 : 0;
+      gt += fabsf(row[v]) > kf ? 1 : 0;
+      eq += fabsf(row[v]) == kf ? 1 : 0;
     }
     const int quota = keff - wg_sum(wave_sum(gt), red, parity, w, lane);
     if (wg_sum(wave_sum(eq), red, parity, w, lane) > quota) {
-      uint64_t eqm = 0;  // ties of this lane; q[v] has index idx0 + 2v
+      uint64_t eqm = 0;  // ties of this lane; row[v] has index idx0 + 2v
 #pragma unroll
-      for (int v = 0; v < 64; ++v) eqm |= fabsf(q[v]) == kf ? (1ull << v) : 0ull;
+      for (int v = 0; v < 64; ++v) eqm |= fabsf(row[v]) == kf ? (1ull << v) : 0ull;
       uint32_t L = 0;
       for (int bit = 13; bit >= 0; --bit) {
         const uint32_t c = L | (1u << bit);
@@ -442,7 +452,7 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
   uint64_t mine = 0;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    const float m = fabsf(q[v]);
+    const float m = fabsf(row[v]);
     const bool keep = m > kf || (m == kf && idx0 + 2 * v <= cut);
     mine |= keep ? (1ull << v) : 0ull;
   }
@@ -458,14 +468,19 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
   const int tot = c0 + c1;
   const int rbase = wave_incl_scan(tot, lane) - tot + (a ? c0 : 0);
   const uint64_t partner = mk[w ^ 1];
+  // positions by running counts: this lane's kept entries before v, and the
+  // partner's before column 2v + b (bits below v + b of its mask)
+  int pos = rbase + (b ? int(partner & 1ull) : 0);
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    if ((mine >> v) & 1ull) {
-      const int pos = rbase + popc64(mine & below(v)) + popc64(partner & below(v + b));
-      outv[pos] = q[v];
+    const bool keep = (mine >> v) & 1ull;
+    const float qv = row[v];
+    if (keep) {
+      outv[pos] = qv;
       outi[pos] = static_cast<uint16_t>(idx0 + 2 * v);
     }
-    q[v] = ((mine >> v) & 1ull) ? q[v] : 0.f;
+    q[v] = keep ? qv : 0.f;
+    pos += int(keep) + ((v + b < 64) ? int((partner >> (v + b)) & 1ull) : 0);
   }
   return false;
 }
@@ -563,7 +578,7 @@ __device__ __forceinline__ int64_t quad_origin(int q, int lane, int64_t ld) {
 }
 __device__ __forceinline__ int64_t quad_step(int q, int64_t ld) { return (q >> 1) ? -ld : ld; }
 
-template <bool kFull, bool kBf16>
+template <bool kFull, bool kBf16, bool kKeep = false>
 __device__ __forceinline__ void load_quadrant(float (&x)[64], const TensorSlot& ts, const Chunk128& c, int q,
                                               int lane, float beta, float gcoef) {
   const int64_t ld = ts.cols, step = quad_step(q, ld), o = c.base + quad_origin(q, lane, ld);
@@ -574,8 +589,8 @@ __device__ __forceinline__ void load_quadrant(float (&x)[64], const TensorSlot& 
   for (int i = 0; i < 64; ++i) {
     float gv = 0.f, mv = 0.f;
     if (kFull || (quad_row(q >> 1, i) < c.vr && col < c.vc)) {
-      gv = load_src<kBf16>(g, i * step);
-      mv = stream_load(&m[i * step]);
+      gv = load_src<kBf16, kKeep>(g, i * step);
+      mv = kKeep ? m[i * step] : stream_load(&m[i * step]);
     }
     x[i] = fmaf(beta, mv, gcoef * gv);
   }
@@ -593,7 +608,7 @@ __device__ __forceinline__ void store_quadrant(const float (&x)[64], float* __re
   }
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kSmallK>
 __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const EncodeParams& p, float* lds,
                                                  uint32_t* scr) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -612,6 +627,9 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
     else
       store_quadrant<false>(x, mdst, ts.cols, c, w, lane);
   }
+  float mp[64];  // the quadrant's M', held for the subtraction
+#pragma unroll
+  for (int i = 0; i < 64; ++i) mp[i] = x[i];
 
   butterfly(x, lds, w, lane);  // quadrants -> S_ab
   fwd_half(x, a);
@@ -619,7 +637,7 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
   fwd_half(x, b);
 
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
-  const bool deferred = topk128(x, p.keff2, w, lane, p.pay_val + e0, p.pay_idx + e0, scr);
+  const bool deferred = topk128<kSmallK>(x, p.keff2, w, lane, p.pay_val + e0, p.pay_idx + e0, scr, lds + w * kTile);
   if (!p.subtract_local) {
     if (deferred && w == 0) emit_kept(p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, scr);
     return;
@@ -630,20 +648,13 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
   inv_half(x, a);
   butterfly(x, lds, w, lane);  // S'_ab -> quadrants
 
-  // M = M' - alpha R.  The quadrant's M' is formed again, bit for bit, from
-  // G and M (untouched so far): the registers hold no copy of it.
-  float mp[64];
-  if (c.full) {
-    load_quadrant<true, kBf16>(mp, ts, c, w, lane, p.beta, p.gcoef);
+  // M = M' - alpha R
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = fmaf(-p.alpha, x[i], mp[i]);
+  for (int i = 0; i < 64; ++i) x[i] = fmaf(-p.alpha, x[i], mp[i]);
+  if (c.full)
     store_quadrant<true>(x, mdst, ts.cols, c, w, lane);
-  } else {
-    load_quadrant<false, kBf16>(mp, ts, c, w, lane, p.beta, p.gcoef);
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = fmaf(-p.alpha, x[i], mp[i]);
+  else
     store_quadrant<false>(x, mdst, ts.cols, c, w, lane);
-  }
   if (deferred && w == 0) emit_kept(p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, scr);
 }
 
@@ -724,7 +735,10 @@ __device__ __forceinline__ void encode_vector128(const TensorSlot& ts, const Enc
   }
 }
 
-template <bool kBf16>
+// kSmallK: every matrix chunk keeps at most 64 coefficients (keff2 <= 64),
+// the common case; the lossless branch is then compiled out, which keeps the
+// kernel within 256 VGPRs while it holds M' (two workgroups per CU).
+template <bool kBf16, bool kSmallK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void encode128_kernel(LaunchTable tab,
                                                                                                EncodeParams p) {
   __shared__ __align__(16) uint32_t lds[kEncLdsWords];
@@ -732,7 +746,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   if (ts.cols == 0)
     encode_vector128<kBf16>(ts, p, reinterpret_cast<float*>(lds));
   else
-    encode_matrix128<kBf16>(ts, p, reinterpret_cast<float*>(lds), lds + kTilesWords);
+    encode_matrix128<kBf16, kSmallK>(ts, p, reinterpret_cast<float*>(lds), lds + kTilesWords);
 }
 
 // ---------------------------------------------------------------- decode
@@ -1008,10 +1022,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 hipError_t launch_encode128(const LaunchTable& tab, const EncodeParams& p, bool g_bf16, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
   const dim3 grid(tab.items), block(256);
-  if (g_bf16)
-    encode128_kernel<true><<<grid, block, 0, stream>>>(tab, p);
+  const bool small = p.keff2 <= 64;
+  if (g_bf16 && small)
+    encode128_kernel<true, true><<<grid, block, 0, stream>>>(tab, p);
+  else if (g_bf16)
+    encode128_kernel<true, false><<<grid, block, 0, stream>>>(tab, p);
+  else if (small)
+    encode128_kernel<false, true><<<grid, block, 0, stream>>>(tab, p);
   else
-    encode128_kernel<false><<<grid, block, 0, stream>>>(tab, p);
+    encode128_kernel<false, false><<<grid, block, 0, stream>>>(tab, p);
   return hipGetLastError();
 }
 

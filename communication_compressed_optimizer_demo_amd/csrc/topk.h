@@ -53,13 +53,18 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 
 // Bitwise search over all 4096 magnitudes: K = largest T with #(|q| >= T) >= keff.
 // Magnitudes are compared as floats through the |x| operand modifier (the
-// order of non-negative floats is the order of their bit patterns), so no
-// second copy of the block is held in registers.
+// order of non-negative floats is the order of their bit patterns).  The
+// lane's 64 coefficients go to `row` (its 64 floats of LDS, free during the
+// call) and the searches read them there, so their registers are free for
+// the search: this rarely taken path then does not set the kernel's register
+// count.  q is rewritten from `row` at the end.
 __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int lane, float* __restrict__ outv,
-                                                 uint16_t* __restrict__ outi) {
+                                                 uint16_t* __restrict__ outi, float* __restrict__ row) {
+#pragma unroll
+  for (int v = 0; v < 64; ++v) row[v] = q[v];
   float lmax = 0.f;
 #pragma unroll
-  for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(q[v]));
+  for (int v = 0; v < 64; ++v) lmax = fmaxf(lmax, fabsf(row[v]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
   const uint32_t hi = __float_as_uint(lmax);
@@ -71,7 +76,7 @@ __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int l
     const float cf = __uint_as_float(cand);
     int c = 0;
 #pragma unroll
-    for (int v = 0; v < 64; ++v) c += fabsf(q[v]) >= cf ? 1 : 0;
+    for (int v = 0; v < 64; ++v) c += fabsf(row[v]) >= cf ? 1 : 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
     if (c >= keff) T = cand;
@@ -80,8 +85,8 @@ __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int l
   int gt = 0, eq = 0;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    gt += fabsf(q[v]) > kf ? 1 : 0;
-    eq += fabsf(q[v]) == kf ? 1 : 0;
+    gt += fabsf(row[v]) > kf ? 1 : 0;
+    eq += fabsf(row[v]) == kf ? 1 : 0;
   }
   int gt_all = gt;
 #pragma unroll
@@ -93,22 +98,26 @@ __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int l
   int eqr = eq_before;
 #pragma unroll
   for (int v = 0; v < 64; ++v) {
-    const float a = fabsf(q[v]);
+    const float a = fabsf(row[v]);
     const bool is_eq = a == kf;
     const bool keep = a > kf || (is_eq && eqr < quota);
     eqr += is_eq ? 1 : 0;
+    const float qv = row[v];
     if (keep) {
-      outv[off] = q[v];
+      outv[off] = qv;
       outi[off] = static_cast<uint16_t>(lane * 64 + v);
       ++off;
     }
-    q[v] = keep ? q[v] : 0.f;
+    q[v] = keep ? qv : 0.f;
   }
 }
 
-// cand: LDS scratch of 2 * kMaxCand words (free during the call).
+// cand: LDS scratch of 2 * kMaxCand words; row: this lane's 64 floats of
+// LDS (both free during the call; they may overlap, the fast path uses cand
+// and the full search row).
 __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, float* __restrict__ outv,
-                                           uint16_t* __restrict__ outi, uint32_t* __restrict__ cand) {
+                                           uint16_t* __restrict__ outi, uint32_t* __restrict__ cand,
+                                           float* __restrict__ row) {
   if (keff >= 4096) {  // lossless: every coefficient, already in index order, all kept
 #pragma unroll
     for (int v = 0; v < 64; ++v) {
@@ -118,7 +127,7 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
     return;
   }
   if (keff > 64) {
-    topk_full_search(q, keff, lane, outv, outi);
+    topk_full_search(q, keff, lane, outv, outi, row);
     return;
   }
 
@@ -142,7 +151,7 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
   const int incl = wave_incl_scan(cnt, lane);
   const int total = __shfl(incl, 63);
   if (T0 == 0 || total > kMaxCand) {
-    topk_full_search(q, keff, lane, outv, outi);
+    topk_full_search(q, keff, lane, outv, outi, row);
     return;
   }
   uint32_t* cmag = cand;             // magnitude bits

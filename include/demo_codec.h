@@ -196,7 +196,12 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
  * payload.  A 64x64 chunk takes 64 words (word i = chunk row i, bit j = column
  * j), a 64-element vector chunk one word (bit j = element j).  A bit is set
  * where M* < 0; M* = 0 reads as +1, since one bit cannot carry sign(0) = 0.
- * Padding positions hold 0. */
+ * Padding positions hold 0.
+ * This differs from demo_decode_apply with DEMO_PHI_SIGN exactly where M* = 0:
+ * there the Signum decode leaves X <- X (1 - eta lambda), this path applies
+ * X <- X - eta (1 + lambda X).  M* is exactly 0 only where no worker sent a
+ * non-zero coefficient for the element's chunk (e.g. a tensor whose gradients
+ * are all zero); everywhere else the two paths give the same parameters. */
 
 /* Host-only: words of the packed sign of a list (n_words, may be NULL) and, if
  * word_begin is not NULL, the first word of every tensor (n+1 entries, the

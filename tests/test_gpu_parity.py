@@ -511,6 +511,43 @@ def test_one_bit_sign_download_ragged_and_zero(dev):
     Sim(w, inputs=inputs, signs=True).run(2)
 
 
+def test_sign_download_on_zero_momentum_differs_from_signum_as_documented(dev):
+    """An all-zero tensor (M* = 0 everywhere): the Signum decode applies sign(0) = 0, X(1 - eta lambda);
+    the one-bit download cannot carry 0 and applies +1, X - eta (1 + lambda X).  Both against the oracle."""
+    shapes = ((64, 128), (100,))
+    w = DI.WORKLOADS["tiny_256"].replace(name="signs_zero", shapes=shapes, workers=2, k=8)
+    codec = B.Codec(shapes, w.k, w.beta, w.alpha)
+    v, ix = codec.alloc_payload(2)
+    ne = codec.n_entries
+    for wk in range(2):
+        codec.encode([torch.zeros(sh, device="cuda") for sh in shapes], [torch.zeros(sh, device="cuda") for sh in shapes],
+                      v[wk * ne:(wk + 1) * ne], ix[wk * ne:(wk + 1) * ne])
+    X0 = [DI.initial_params(w, i) for i in range(len(shapes))]
+    Xs = [torch.from_numpy(x.copy()).cuda() for x in X0]
+    Xb = [torch.from_numpy(x.copy()).cuda() for x in X0]
+    codec.decode_apply(Xs, 2, v, ix, B.DEMO_PHI_SIGN, w.eta, w.lam)
+    words = codec.alloc_signs()
+    codec.decode_signs(2, v, ix, words)
+    codec.apply_signs(Xb, words, w.eta, w.lam)
+    torch.cuda.synchronize()
+    assert not words.any(), "zero momentum must give all-clear sign words"
+    for i, sh in enumerate(shapes):
+        z = np.zeros(sh)
+        nch = O.split_chunks(z).shape[0]
+        # the payload of an all-zero chunk: indices 0..7 (ties to the lower index), values 0
+        signum = O.decode_apply(X0[i], np.zeros((2, nch, 8), np.float32),
+                                np.tile(np.arange(8, dtype=np.uint16), (2, nch, 1)), phi="sign", eta=w.eta, lam=w.lam)
+        np.testing.assert_array_equal(signum["Mstar"], z)
+        onebit = O.apply_signs(X0[i], O.pack_signs(z), eta=w.eta, lam=w.lam)
+        gs, gb = Xs[i].cpu().numpy(), Xb[i].cpu().numpy()
+        PR.compare_decode(signum, sh, "sign", w.eta, gs, np.zeros(nch, bool), None,
+                          where=f"signum decode on zero momentum, tensor {i}")
+        PR.compare_decode({"X": onebit, "Mstar": z + 1.0}, sh, "identity", w.eta, gb, np.zeros(nch, bool), None,
+                          where=f"one-bit apply, tensor {i}")
+        assert np.all(np.abs(gs - gb) > 0.5 * w.eta), "the two paths must differ by about eta everywhere"
+    codec.close()
+
+
 def test_sign_download_matches_signum_decode(dev):
     """apply_signs(decode_signs(payloads)) equals decode_apply with phi = sign wherever M* != 0."""
     w = DI.WORKLOADS["tiny_256"].replace(name="signs_vs_signum", shapes=((192, 256), (300,)), workers=3, k=12)
