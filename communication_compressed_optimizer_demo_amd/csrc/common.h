@@ -87,6 +87,17 @@ __device__ __forceinline__ int xcd_item(int b, int n) {
   return x * q + min(x, r) + j;
 }
 
+// Orders one wave's LDS stores before its later LDS loads (other lanes of the
+// same wave read what a lane wrote).  A wave's LDS operations complete in
+// issue order, so no wait is needed; the fences keep the compiler from
+// moving loads above the stores.  In a one-wave workgroup this replaces a
+// workgroup barrier, which would also wait for every LDS operation in flight.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // number of set lanes of `mask` below this lane
 __device__ __forceinline__ int lanes_below_mask(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));

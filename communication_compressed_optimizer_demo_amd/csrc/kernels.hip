@@ -52,24 +52,27 @@ constexpr int kCntLd = 15;  // count rows: words 0..14 of a row's 8-bit counts (
 constexpr int kWorkerBatch = 16;
 
 
+// Every workgroup here is one wave: LDS accesses are ordered with wave_sync,
+// not with workgroup barriers.
+
 // column layout -> row layout through the LDS tile
 __device__ __forceinline__ void col_to_row(float* tile, float (&x)[64], int lane) {
 #pragma unroll
   for (int i = 0; i < 64; ++i) tile[i * kLd + lane] = x[i];
-  __syncthreads();
+  wave_sync();
 #pragma unroll
   for (int v = 0; v < 64; ++v) x[v] = tile[lane * kLd + v];
-  __syncthreads();
+  wave_sync();
 }
 
 // row layout -> column layout through the LDS tile
 __device__ __forceinline__ void row_to_col(float* tile, float (&x)[64], int lane) {
 #pragma unroll
   for (int v = 0; v < 64; ++v) tile[lane * kLd + v] = x[v];
-  __syncthreads();
+  wave_sync();
 #pragma unroll
   for (int i = 0; i < 64; ++i) x[i] = tile[i * kLd + lane];
-  __syncthreads();
+  wave_sync();
 }
 
 struct ChunkPos {
@@ -153,7 +156,7 @@ __device__ __forceinline__ void encode_matrix(const TensorSlot& ts, const Encode
   tk::topk_chunk(q, p.keff2, lane, p.pay_val + e0, p.pay_idx + e0, reinterpret_cast<uint32_t*>(tile),
                  tile + lane * kLd);
   if (!p.subtract_local) return;
-  __syncthreads();
+  wave_sync();
 
   // q holds Q_hat (row layout); R = P0^T Q_hat P1 in column layout
   if constexpr (Basis::kMatrixCores) {
@@ -406,6 +409,12 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
   }
 }
 
+// Lane i of v takes the wave-uniform value x (v_writelane: no compare, no
+// select; i is a compile-time lane number).
+__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t x, int i) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"(i));
+}
+
 template <class Basis, int kTargets, bool kWire>
 __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const DecodeParams& p, const Basis& basis,
                                               float* acc, uint32_t* cntw, int item) {
@@ -455,7 +464,7 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   }
 
   clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
-  __syncthreads();
+  wave_sync();
   if (one_batch) {
 #pragma unroll
     for (int j = 0; j < kWorkerBatch; ++j) {
@@ -467,11 +476,11 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   } else {
     scatter_chunk<kWire>(acc, cntw, p, e0, lane);
   }
-  __syncthreads();
+  wave_sync();
 
   float q[64];
   average_row(q, acc, cntw, p, lane);
-  __syncthreads();
+  wave_sync();
   if constexpr (Basis::kMatrixCores) {
     basis.template inverse2d<kLd>(q, acc, lane);
   } else {
@@ -512,15 +521,18 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
       store_rows<false>(q, sp, ld, c, lane);
   }
   if constexpr ((kTargets & kToSigns) != 0) {
-    // Row i of the chunk is one ballot (bit j = lane j = column j), kept by
-    // lane i; the 64 words go out as one coalesced 512-byte store.
+    // Row i of the chunk is one ballot (bit j = lane j = column j), written
+    // into lane i (rows past the chunk's valid ones stay 0); the 64 words go
+    // out as one coalesced 512-byte store.
     const uint64_t cols = __builtin_amdgcn_ballot_w64(lane < c.vc);
-    uint64_t word = 0;
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
-      const uint64_t b = __builtin_amdgcn_ballot_w64(q[i] < 0.f) & cols;
-      word = (lane == i && i < c.vr) ? b : word;
+      const uint64_t b = i < c.vr ? __builtin_amdgcn_ballot_w64(q[i] < 0.f) & cols : 0ull;
+      write_lane(lo, uint32_t(b), i);
+      write_lane(hi, uint32_t(b >> 32), i);
     }
+    const uint64_t word = (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
     stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(c.local) * 64 + lane);
   }
 }
@@ -535,12 +547,12 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   const int nc = min(64, int((uint32_t(ts.rows) + 63u) >> 6) - slab * 64);  // chunks in this slab
 
   clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
-  __syncthreads();
+  wave_sync();
   scatter_slab<kWire>(acc, cntw, p, ts.entry_begin + int64_t(slab) * 64 * p.keff1, nc, lane);
-  __syncthreads();
+  wave_sync();
   float q[64];
   average_row(q, acc, cntw, p, lane);
-  __syncthreads();
+  wave_sync();
   basis.inv0(q);
   row_to_col(acc, q, lane);
 

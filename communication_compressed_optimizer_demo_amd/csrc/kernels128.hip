@@ -129,16 +129,6 @@ __device__ __forceinline__ int popc64(uint64_t v) { return __popcll(v); }
 // bits below position n (n in 0..64)
 __device__ __forceinline__ uint64_t below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
 
-// Orders one wave's LDS stores before its later LDS loads (other lanes of the
-// same wave read what a lane wrote).  A wave's LDS operations complete in
-// issue order, so no wait is needed; the fences keep the compiler from
-// moving loads above the stores.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Per-wave LDS transposes through the wave's own tile.  col_to_row only
 // synchronises the wave: its tile is its own, and whatever LDS the workgroup
 // used before was released by a workgroup barrier.  row_to_col ends with a

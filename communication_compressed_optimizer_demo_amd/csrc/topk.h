@@ -30,6 +30,8 @@
 
 #include <cstdint>
 
+#include "common.h"
+
 namespace demo {
 namespace tk {
 
@@ -112,6 +114,7 @@ __device__ __forceinline__ void topk_full_search(float (&q)[64], int keff, int l
   }
 }
 
+// One wave owns the block (LDS accesses ordered with wave_sync).
 // cand: LDS scratch of 2 * kMaxCand words; row: this lane's 64 floats of
 // LDS (both free during the call; they may overlap, the fast path uses cand
 // and the full search row).
@@ -169,7 +172,7 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
       }
     }
   }
-  __syncthreads();
+  wave_sync();
   const int slots = (total + 63) >> 6;  // 1..4, wave-uniform
   uint32_t m[4], id[4];
 #pragma unroll
@@ -179,7 +182,7 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
     m[r] = live ? cmag[s] : 0u;
     id[r] = live ? cid[s] : 0u;
   }
-  __syncthreads();
+  wave_sync();
   // 4. K over the candidates.  Every candidate is >= T0 >= 1 and empty slots
   //    hold 0, so empty slots never count for a threshold >= 1.
   uint32_t K = 0;

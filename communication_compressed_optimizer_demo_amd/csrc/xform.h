@@ -355,6 +355,14 @@ struct DenseBasis {
         for (int v = 0; v < 16; ++v) tile[(32 * i + 8 * (v >> 2) + 4 * h + (v & 3)) * kLd + 32 * j + c] = d[i][j][v];
   }
 
+  // The tile belongs to this one wave: its LDS accesses only need ordering
+  // (a wave's LDS operations complete in issue order).
+  static __device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
   // Forward: x holds column `lane` of the block B (x[i] = B[i][lane]); on
   // return x holds row `lane` of Q = P0 B P1^T.
   template <int kLd>
@@ -368,7 +376,7 @@ struct DenseBasis {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int q = 0; q < 8; ++q) pr[t][q] = *reinterpret_cast<const f32x4*>(p0 + (32 * t + c) * 64 + 32 * h + 4 * q);
-    __syncthreads();
+    lds_sync();
     f32x16 d[2][2];
     // C = P0 B
     product(d, [&](int t, int kk) { return pr[t][kk >> 2][kk & 3]; },
@@ -377,18 +385,18 @@ struct DenseBasis {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int q = 0; q < 8; ++q) pr[t][q] = *reinterpret_cast<const f32x4*>(p1 + (32 * t + c) * 64 + 32 * h + 4 * q);
-    __syncthreads();
+    lds_sync();
     store_result<kLd>(d, tile, lane);
-    __syncthreads();
+    lds_sync();
     // Q = C P1^T: B[k][n] = P1[n][k]
     product(d, [&](int t, int kk) { return tile[(32 * t + c) * kLd + kk + 32 * h]; },
             [&](int t, int kk) { return pr[t][kk >> 2][kk & 3]; });
-    __syncthreads();
+    lds_sync();
     store_result<kLd>(d, tile, lane);
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int v = 0; v < 64; ++v) x[v] = tile[lane * kLd + v];
-    __syncthreads();
+    lds_sync();
   }
 
   // Inverse: x holds row `lane` of Q (x[v] = Q[lane][v]); on return x holds
@@ -398,23 +406,23 @@ struct DenseBasis {
     const int h = lane >> 5, c = lane & 31;
 #pragma unroll
     for (int v = 0; v < 64; ++v) tile[lane * kLd + v] = x[v];
-    __syncthreads();
+    lds_sync();
     f32x16 d[2][2];
     // D = Q P1 (rows of P1 read a coalesced 128 bytes per lane half)
     product(d, [&](int t, int kk) { return tile[(32 * t + c) * kLd + kk + 32 * h]; },
             [&](int t, int kk) { return p1[(kk + 32 * h) * 64 + 32 * t + c]; });
-    __syncthreads();
+    lds_sync();
     store_result<kLd>(d, tile, lane);
-    __syncthreads();
+    lds_sync();
     // X = P0^T D: A[m][k] = P0[k][m]
     product(d, [&](int t, int kk) { return p0[(kk + 32 * h) * 64 + 32 * t + c]; },
             [&](int t, int kk) { return tile[(kk + 32 * h) * kLd + 32 * t + c]; });
-    __syncthreads();
+    lds_sync();
     store_result<kLd>(d, tile, lane);
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] = tile[i * kLd + lane];
-    __syncthreads();
+    lds_sync();
   }
 };
 
