@@ -403,7 +403,7 @@ def apply_signs(X: np.ndarray, words: np.ndarray, *, eta: float, lam: float, s: 
 
 
 # ---------------------------------------------------------------------------
-# compact wire format: bfloat16 values, 12-bit indices
+# compact wire format: bfloat16 values, 12- or 14-bit positions
 # ---------------------------------------------------------------------------
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -413,31 +413,37 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return b.astype(np.uint16)
 
 
-def pack_wire(values: np.ndarray, idx: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+def wire_index_bits(s: int = 64) -> int:
+    """Bits of one chunk position on the wire: enough for the s*s positions of a
+    matrix chunk (12 at s = 64, 14 at s = 128)."""
+    return int(s * s - 1).bit_length()
+
+
+def pack_wire(values: np.ndarray, idx: np.ndarray, s: int = 64) -> Tuple[np.ndarray, np.ndarray]:
     """A worker's payload as sent: [T] ("Training over Slow Links", top-k and DeMo
-    slides) counts a kept value as 2 bytes of bfloat16 plus its position, and a
-    64x64 chunk position needs 12 bits.  Values become bfloat16 (uint16 bits,
-    entry order kept); indices are packed two to three bytes: entries 2p and
-    2p+1 give bytes (i0 & 0xFF, (i0 >> 8) | (i1 & 0xF) << 4, i1 >> 4), an odd
-    last entry paired with 0."""
+    slides) counts a kept value as 2 bytes of bfloat16 plus its position.
+    Values become bfloat16 (uint16 bits, entry order kept).  Positions take
+    b = wire_index_bits(s) bits each (12 at s = 64: a 64x64 chunk has 4096
+    positions; 14 at s = 128): entry j's position fills bits b*j .. b*j + b - 1
+    of one little-endian bit string (bit t of the string is bit t mod 8 of byte
+    t // 8), cut to whole bytes.  Returns (uint16 values, uint8 index bytes)."""
+    b = wire_index_bits(s)
     v = bf16_bits(np.asarray(values, dtype=F32).ravel())
     i = np.asarray(idx).ravel().astype(np.uint32)
-    if np.any(i >= 4096):
-        raise ValueError("12-bit indices")
-    if i.size % 2:
-        i = np.concatenate([i, np.zeros(1, np.uint32)])
-    i0, i1 = i[0::2], i[1::2]
-    b = np.stack([i0 & 0xFF, (i0 >> 8) | ((i1 & 0xF) << 4), i1 >> 4], axis=1).astype(np.uint8)
-    return v, b.ravel()
+    if np.any(i >= (1 << b)):
+        raise ValueError(f"{b}-bit indices")
+    bits = ((i[:, None] >> np.arange(b, dtype=np.uint32)[None, :]) & 1).astype(np.uint8).ravel()
+    pad = (-bits.size) % 8
+    bits = np.concatenate([bits, np.zeros(pad, np.uint8)])
+    return v, np.packbits(bits, bitorder="little")
 
 
-def unpack_wire(wv: np.ndarray, wi: np.ndarray, n: int) -> Tuple[np.ndarray, np.ndarray]:
+def unpack_wire(wv: np.ndarray, wi: np.ndarray, n: int, s: int = 64) -> Tuple[np.ndarray, np.ndarray]:
     """Inverse of pack_wire for n entries: float32 values (bfloat16 widened) and indices."""
+    b = wire_index_bits(s)
     vals = (np.asarray(wv, dtype=np.uint16)[:n].astype(np.uint32) << 16).view(F32)
-    b = np.asarray(wi, dtype=np.uint8).reshape(-1, 3).astype(np.uint32)
-    i0 = b[:, 0] | ((b[:, 1] & 0xF) << 8)
-    i1 = (b[:, 1] >> 4) | (b[:, 2] << 4)
-    idx = np.stack([i0, i1], axis=1).ravel()[:n].astype(np.uint16)
+    bits = np.unpackbits(np.asarray(wi, dtype=np.uint8), bitorder="little")[:n * b].reshape(n, b).astype(np.uint32)
+    idx = (bits << np.arange(b, dtype=np.uint32)[None, :]).sum(axis=1).astype(np.uint16)
     return vals, idx
 
 

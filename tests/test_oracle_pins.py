@@ -471,21 +471,53 @@ def test_pack_signs_hand_built_words():
     assert np.array_equal(w, want)
 
 
-@pytest.mark.parametrize("shape", [(130, 70), (64, 64), (3, 200), (777,), (1,)])
-def test_pack_signs_bit_address_formula(shape):
+def test_pack_signs_hand_built_words_chunk128():
+    """s = 128, words written out by hand: a 128x128 chunk takes 256 words, chunk row r in words 2r
+    (columns 0..63) and 2r + 1 (columns 64..127); a 128-element vector chunk two words."""
+    v = np.ones(200)
+    v[[1, 64, 127]] = -1.0     # chunk 0: word 0 bit 1, word 1 bits 0 and 63
+    v[130] = -7.0              # chunk 1 (elements 128..255): word 2, bit 2
+    w = O.pack_signs(v, 128)
+    assert w.shape == (4,) and O.sign_words([(200,)], 128) == 4
+    assert w.tolist() == [2, 1 + (1 << 63), 4, 0]
+    m = np.ones((130, 129))
+    m[0, 0] = -1.0      # chunk (0, 0), row 0, column 0: word 0, bit 0
+    m[0, 100] = -1.0    # chunk (0, 0), row 0, column 100: word 1, bit 36
+    m[127, 127] = -1.0  # chunk (0, 0), row 127, column 127: word 255, bit 63
+    m[5, 128] = -1.0    # chunk (0, 1), row 5, column 0: word 256 + 10, bit 0
+    m[129, 3] = -1.0    # chunk (1, 0), row 1, column 3: word 512 + 2, bit 3
+    m[128, 128] = 0.0   # chunk (1, 1), row 0, column 0: zero reads as +1, no bit
+    w = O.pack_signs(m, 128)
+    assert w.shape == (1024,) and O.sign_words([(130, 129)], 128) == 1024
+    want = np.zeros(1024, np.uint64)
+    want[0], want[1], want[255], want[266], want[514] = 1, 1 << 36, 1 << 63, 1, 1 << 3
+    assert np.array_equal(w, want)
+    # padding: all-negative input sets exactly the valid elements' bits
+    w = O.pack_signs(-np.ones((130, 129)), 128)
+    assert bin(int(w[3 * 256 + 0])).count("1") == 1      # chunk (1, 1) row 0: one valid column
+    assert w[3 * 256 + 4] == 0                           # chunk (1, 1) row 2: past the last row
+    assert int(w[256 + 0]) == 1 and int(w[256 + 1]) == 0  # chunk (0, 1) row 0: column 128 only
+
+
+@pytest.mark.parametrize("s", [64, 128])
+@pytest.mark.parametrize("shape", [(130, 70), (64, 64), (3, 200), (777,), (1,), (257, 131)])
+def test_pack_signs_bit_address_formula(shape, s):
     """Every element's bit, looked up with the address written out per element: matrix
-    element (r, c) sits in chunk (r // 64) * ceil(cols / 64) + c // 64, word r % 64 of that
-    chunk, bit c % 64; vector element e in word e // 64, bit e % 64.  Padding bits stay 0."""
+    element (r, c) sits in chunk (r // s) * ceil(cols / s) + c // s, which starts at word
+    chunk * s * s / 64; inside it the element's row-major position p = (r % s) * s + c % s gives
+    word p // 64, bit p % 64; vector element e in word e // 64, bit e % 64.  Padding bits stay 0."""
     rng = _rng(40)
     M = rng.standard_normal(shape)
-    w = O.pack_signs(M)
-    assert w.shape == (O.sign_words([shape]),)
+    w = O.pack_signs(M, s)
+    assert w.shape == (O.sign_words([shape], s),)
     seen = np.zeros(w.shape[0] * 64, bool)
     for pos in np.ndindex(*shape):
         if len(shape) == 2:
             r, c = pos
-            word = ((r // 64) * -(-shape[1] // 64) + c // 64) * 64 + r % 64
-            bit = c % 64
+            chunk = (r // s) * -(-shape[1] // s) + c // s
+            p = (r % s) * s + c % s
+            word = chunk * s * s // 64 + p // 64
+            bit = p % 64
         else:
             word, bit = pos[0] // 64, pos[0] % 64
         assert bool((int(w[word]) >> bit) & 1) == (M[pos] < 0)
@@ -496,24 +528,25 @@ def test_pack_signs_bit_address_formula(shape):
                 assert (int(w[word]) >> bit) & 1 == 0
 
 
-def test_apply_signs_closed_forms_and_agreement_with_signum_decode():
+@pytest.mark.parametrize("s", [64, 128])
+def test_apply_signs_closed_forms_and_agreement_with_signum_decode(s):
     rng = _rng(41)
     X = rng.standard_normal((70, 130)).astype(np.float32)
     X64 = X.astype(np.float64)
-    n = O.sign_words([X.shape])
+    n = O.sign_words([X.shape], s)
     for fill, phi in ((0, 1.0), (~np.uint64(0), -1.0)):
-        got = O.apply_signs(X, np.full(n, fill, np.uint64), eta=0.01, lam=0.1)
+        got = O.apply_signs(X, np.full(n, fill, np.uint64), eta=0.01, lam=0.1, s=s)
         ref = X64 - f32(0.01) * (phi + f32(0.1) * X64)
         assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
     # the bit path reproduces the Signum decode wherever M* != 0
     G = rng.standard_normal(X.shape).astype(np.float32)
-    o = O.encode(np.zeros_like(G), G, beta=0.9, alpha=0.2, k=37)
-    d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="sign", eta=0.01, lam=0.1)
+    o = O.encode(np.zeros_like(G), G, beta=0.9, alpha=0.2, k=37, s=s)
+    d = O.decode_apply(X, o["values"][None], o["idx"][None], phi="sign", eta=0.01, lam=0.1, s=s)
     assert np.all(d["Mstar"] != 0)
-    got = O.apply_signs(X, O.pack_signs(d["Mstar"]), eta=0.01, lam=0.1)
+    got = O.apply_signs(X, O.pack_signs(d["Mstar"], s), eta=0.01, lam=0.1, s=s)
     assert np.array_equal(got, d["X"])
     # zero M* (no coefficient kept anywhere) reads as +1
-    z = O.apply_signs(X, O.pack_signs(np.zeros(X.shape)), eta=0.01, lam=0.0)
+    z = O.apply_signs(X, O.pack_signs(np.zeros(X.shape), s), eta=0.01, lam=0.0, s=s)
     assert np.all(np.abs(z - (X64 - f32(0.01))) <= np.spacing(np.abs(X64 - f32(0.01)).astype(np.float32)))
 
 
@@ -604,10 +637,30 @@ def test_wire_format_hand_built():
     # 1 + 2^-8 is a tie between 0x3F80 and 0x3F81: even wins; 1 + 3*2^-8 ties 0x3F81 / 0x3F82: even wins
     wv, wi = O.pack_wire(v, np.array([0x123, 0xABC, 0xFFF, 0, 7]))
     assert wv.tolist() == [0x3F80, 0xC020, 0x3F80, 0x3F82, 0x0000]
-    assert wi.tolist() == [0x23, 0xC1, 0xAB, 0xFF, 0x0F, 0x00, 0x07, 0x00, 0x00]
+    # 12-bit positions, a little-endian bit string: 5 entries = 60 bits, 8 bytes
+    assert wi.tolist() == [0x23, 0xC1, 0xAB, 0xFF, 0x0F, 0x00, 0x07, 0x00]
     vals, idx = O.unpack_wire(wv, wi, 5)
     assert idx.tolist() == [0x123, 0xABC, 0xFFF, 0, 7]
     assert vals.tolist() == [1.0, -2.5, 1.0, 1.0 + 2 * 2.0 ** -7, 0.0]
+
+
+def test_wire_format_14_bit_positions_hand_built():
+    """s = 128: a 128x128 chunk has 16384 positions, 14 bits each.  Positions 0x1234, 0x3FFF, 0, 5 at
+    bits 0-13, 14-27, 28-41, 42-55: byte 0 = 0x34; byte 1 = 0x12 (bits 8-13) | 0b11 << 6 = 0xD2; byte 2 =
+    0xFF; byte 3 = 0x0F (the last four ones of 0x3FFF, then four zero bits); byte 4 = 0x00; byte 5 =
+    5 << 2 = 0x14; byte 6 = 0x00."""
+    assert O.wire_index_bits(64) == 12 and O.wire_index_bits(128) == 14
+    wv, wi = O.pack_wire(np.array([1.0, 2.0, 0.0, -1.0], np.float32), np.array([0x1234, 0x3FFF, 0, 5]), s=128)
+    assert wi.tolist() == [0x34, 0xD2, 0xFF, 0x0F, 0x00, 0x14, 0x00]
+    assert wv.tolist() == [0x3F80, 0x4000, 0x0000, 0xBF80]
+    assert O.unpack_wire(wv, wi, 4, s=128)[1].tolist() == [0x1234, 0x3FFF, 0, 5]
+    with pytest.raises(ValueError):
+        O.pack_wire(np.zeros(1, np.float32), np.array([1 << 14]), s=128)
+    rng = _rng(71)
+    i = rng.integers(0, 1 << 14, 777)
+    wv, wi = O.pack_wire(np.zeros(777, np.float32), i, s=128)
+    assert wi.size == (777 * 14 + 7) // 8
+    assert np.array_equal(O.unpack_wire(wv, wi, 777, s=128)[1], i.astype(np.uint16))
 
 
 def test_wire_format_round_trip_and_rounding_bound():
@@ -615,7 +668,7 @@ def test_wire_format_round_trip_and_rounding_bound():
     v = (rng.standard_normal(1001) * 1e-3).astype(np.float32)
     i = rng.integers(0, 4096, 1001)
     wv, wi = O.pack_wire(v, i)
-    assert wi.size == 3 * 501
+    assert wi.size == (1001 * 12 + 7) // 8
     vals, idx = O.unpack_wire(wv, wi, 1001)
     assert np.array_equal(idx, i.astype(np.uint16))
     # round to nearest: at most half a bfloat16 ulp (2^-8 relative) away
