@@ -96,9 +96,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.demo_decode_apply_muon_noalloc.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32, vp, vp,
                                                    i64, f32, f32, f32, i32, i32, vp]
     lib.demo_wire_size.restype = i32
-    lib.demo_wire_size.argtypes = [i64, P(i64), P(i64)]
+    lib.demo_wire_size.argtypes = [i32, i64, P(i64), P(i64)]
     lib.demo_pack_wire.restype = i32
-    lib.demo_pack_wire.argtypes = [vp, i32, vp, vp, i64, vp, vp, vp]
+    lib.demo_pack_wire.argtypes = [vp, i32, i32, vp, vp, i64, vp, vp, vp]
     lib.demo_decode_apply_wire.restype = i32
     lib.demo_decode_apply_wire.argtypes = [vp, i32, P(demo_shape), P(vp), P(demo_codec_cfg), i32,
                                            vp, vp, i64, i32, f32, f32, i32, vp]
@@ -358,26 +358,27 @@ def demo_decode_apply_muon_noalloc(ctx: int, params, cfg: demo_codec_cfg, worker
                                               _stream_handle(stream)))
 
 
-def demo_wire_size(n_entries: int) -> Tuple[int, int]:
+def demo_wire_size(n_entries: int, chunk: int = DEMO_CHUNK) -> Tuple[int, int]:
     """(value bytes, index bytes) of one worker's wire payload of n_entries entries; host-only."""
     lib = load_library()
     vb, ib = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib.demo_wire_size(int(n_entries), ctypes.byref(vb), ctypes.byref(ib)))
+    _check(lib.demo_wire_size(int(chunk), int(n_entries), ctypes.byref(vb), ctypes.byref(ib)))
     return vb.value, ib.value
 
 
-def demo_pack_wire(ctx: int, workers: int, pay_values, pay_idx, wire_values, wire_idx, stream=None) -> None:
+def demo_pack_wire(ctx: int, workers: int, pay_values, pay_idx, wire_values, wire_idx, stream=None,
+                   chunk: int = DEMO_CHUNK) -> None:
     """``workers`` payloads (worker-major) -> wire values (int16 storage) and wire index bytes (uint8)."""
     lib = load_library()
     if pay_values.numel() % workers or pay_idx.numel() != pay_values.numel():
         raise ValueError("payload arrays must hold workers x entries elements")
     per = pay_values.numel() // workers
-    vb, ib = demo_wire_size(per)
+    vb, ib = demo_wire_size(per, chunk)
     if wire_values.numel() * wire_values.element_size() != workers * vb:
         raise ValueError("wire value buffer must hold workers x entries 16-bit values")
     if wire_idx.numel() * wire_idx.element_size() != workers * ib:
         raise ValueError("wire index buffer must hold workers x demo_wire_size index bytes")
-    _check(lib.demo_pack_wire(ctx, int(workers), _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per,
+    _check(lib.demo_pack_wire(ctx, int(chunk), int(workers), _device_ptr(pay_values, 4), _device_ptr(pay_idx, 2), per,
                               _device_ptr(wire_values, 2), _device_ptr(wire_idx, wire_idx.element_size()), _stream_handle(stream)))
 
 
@@ -393,7 +394,7 @@ def demo_decode_apply_wire(ctx: int, params, cfg: demo_codec_cfg, workers: int, 
     if wire_values.element_size() != 2 or wire_values.numel() % workers:
         raise ValueError("wire values must hold workers x entries 16-bit values")
     per = wire_values.numel() // workers
-    _, ib = demo_wire_size(per)
+    _, ib = demo_wire_size(per, cfg.chunk)
     if wire_idx.numel() * wire_idx.element_size() != workers * ib:
         raise ValueError("wire index buffer must hold workers x demo_wire_size index bytes")
     _check(lib.demo_decode_apply_wire(ctx, len(params), _shapes([tuple(x.shape) for x in params]),
@@ -417,10 +418,7 @@ class Codec:
         self.identity = bool(identity)
         self.aggregated = bool(aggregated)
         self.n_chunks, self.n_entries, self.entry_begin = demo_plan(self.shapes, self.k, self.chunk)
-        if self.chunk == DEMO_CHUNK:
-            self.n_sign_words, self.sign_word_begin = demo_plan_signs(self.shapes)
-        else:
-            self.n_sign_words, self.sign_word_begin = 0, None
+        self.n_sign_words, self.sign_word_begin = demo_plan_signs(self.shapes, self.chunk)
         self.ctx = demo_ctx_create(device)
 
     def close(self) -> None:
@@ -469,18 +467,18 @@ class Codec:
                           stream)
 
     def apply_signs(self, params, signs, eta=1e-3, lam=0.0, stream=None) -> None:
-        demo_apply_signs(self.ctx, params, signs, eta, lam, stream=stream)
+        demo_apply_signs(self.ctx, params, signs, eta, lam, chunk=self.chunk, stream=stream)
 
     def alloc_wire(self, workers: int = 1, device="cuda"):
-        """Empty wire buffers: bfloat16 bits (int16 storage) and packed 12-bit indices (uint8)."""
+        """Empty wire buffers: bfloat16 bits (int16 storage) and packed 12- or 14-bit positions (uint8)."""
         import torch
-        vb, ib = demo_wire_size(self.n_entries)
+        vb, ib = demo_wire_size(self.n_entries, self.chunk)
         v = torch.empty(workers * vb // 2, dtype=torch.int16, device=device)
         i = torch.empty(workers * ib, dtype=torch.uint8, device=device)
         return v, i
 
     def pack_wire(self, workers, pay_values, pay_idx, wire_values, wire_idx, stream=None) -> None:
-        demo_pack_wire(self.ctx, workers, pay_values, pay_idx, wire_values, wire_idx, stream)
+        demo_pack_wire(self.ctx, workers, pay_values, pay_idx, wire_values, wire_idx, stream, chunk=self.chunk)
 
     def decode_apply_wire(self, params, workers, wire_values, wire_idx, phi=DEMO_PHI_SIGN, eta=1e-3, lam=0.0,
                           avg=DEMO_AVG_CONTRIBUTORS, P0=None, P1=None, stream=None) -> None:

@@ -47,9 +47,8 @@ struct TensorPlan {
   int64_t word_begin;   // first 64-bit word of the tensor's packed sign
 };
 
-// Packed-sign words per chunk (chunk edge 64): one per 64 elements of the (padded) chunk.
-constexpr int64_t kWordsPerMatrixChunk = kChunk * kChunk / 64;
-constexpr int64_t kWordsPerVectorChunk = kChunk / 64;
+// Packed-sign words per chunk: one per 64 elements of the (padded) chunk.
+int64_t words_per_chunk(int32_t chunk, int ndim) { return ndim == 2 ? int64_t(chunk) * chunk / 64 : chunk / 64; }
 
 // Vector chunks per work item: 64 (one wave, one chunk per lane) at chunk
 // edge 64, 128 (four waves, one chunk per lane pair) at chunk edge 128.
@@ -93,7 +92,7 @@ demo_status plan_list(const demo_shape* shapes, int32_t n, int32_t chunk, int32_
     t.word_begin = w;
     e += t.chunks * t.keff;
     c += t.chunks;
-    w += t.chunks * (t.ndim == 2 ? kWordsPerMatrixChunk : kWordsPerVectorChunk);
+    w += t.chunks * words_per_chunk(chunk, t.ndim);
     if (out) out->push_back(t);
   }
   if (entries) *entries = e;
@@ -172,8 +171,14 @@ demo_status for_each_batch(const std::vector<TensorPlan>& plan, Fill&& fill, Lau
   return flush();
 }
 
-// 32-bit words of one worker's wire indices: three per 8-entry group.
-int64_t wire_idx_words(int64_t entries) { return (entries + 7) / 8 * 3; }
+// Bits of a wire position: 12 inside a 64x64 chunk, 14 inside a 128x128 one.
+int32_t wire_bits(int32_t chunk) { return chunk == kChunkLarge ? 14 : 12; }
+
+// 32-bit words of one worker's wire indices: whole groups of 32 positions'
+// worth of words, 3 words per 8 positions (12 bits) or 7 per 16 (14 bits).
+int64_t wire_idx_words(int32_t chunk, int64_t entries) {
+  return chunk == kChunkLarge ? (entries + 15) / 16 * 7 : (entries + 7) / 8 * 3;
+}
 
 // Shared body of the decode entry points: params and/or moms (either may be
 // NULL) receive X - eta (phi(M*) + lambda X) and M - alpha M*; or, with
@@ -192,8 +197,6 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   demo_status s = plan_list(shapes, n, cfg->chunk, cfg->k, &plan, &entries, nullptr, &words);
   if (s != DEMO_OK) return s;
   const bool to_signs = params == nullptr && moms == nullptr && mstar == nullptr;
-  if (to_signs && cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
-  if (wire && cfg->chunk != kChunk) return fail(DEMO_ERR_RANGE, "the wire format is built for chunk 64");
   if (to_signs) {
     if (n_words != words)
       return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +
@@ -250,7 +253,7 @@ demo_status decode_common(demo_ctx* ctx, int32_t n, const demo_shape* shapes, fl
   p.wire = wire ? 1 : 0;
   p.wire_val = wire_values;
   p.wire_idx = static_cast<const uint32_t*>(wire_idx);
-  p.wire_words = wire_idx_words(entries);
+  p.wire_words = wire_idx_words(cfg->chunk, entries);
   auto fill = [&](demo::TensorSlot& slot, size_t i) {
     slot.aux = moms != nullptr    ? static_cast<void*>(moms[i])
                : mstar != nullptr ? static_cast<void*>(mstar[i])
@@ -416,15 +419,18 @@ demo_status demo_decode_apply(demo_ctx* ctx, int32_t n, const demo_shape* shapes
                        lambda, avg, stream);
 }
 
-demo_status demo_wire_size(int64_t n_entries, int64_t* value_bytes, int64_t* idx_bytes) {
+demo_status demo_wire_size(int32_t chunk, int64_t n_entries, int64_t* value_bytes, int64_t* idx_bytes) {
+  if (chunk != kChunk && chunk != kChunkLarge) return fail(DEMO_ERR_RANGE, "chunk size must be 64 or 128");
   if (n_entries < 0 || n_entries > (int64_t(1) << 40)) return fail(DEMO_ERR_RANGE, "entry count out of range");
   if (value_bytes != nullptr) *value_bytes = 2 * n_entries;
-  if (idx_bytes != nullptr) *idx_bytes = 4 * wire_idx_words(n_entries);
+  if (idx_bytes != nullptr) *idx_bytes = 4 * wire_idx_words(chunk, n_entries);
   return DEMO_OK;
 }
 
-demo_status demo_pack_wire(demo_ctx* ctx, int32_t workers, const float* pay_values, const uint16_t* pay_idx,
-                           int64_t n_entries, uint16_t* wire_values, void* wire_idx, hipStream_t stream) {
+demo_status demo_pack_wire(demo_ctx* ctx, int32_t chunk, int32_t workers, const float* pay_values,
+                           const uint16_t* pay_idx, int64_t n_entries, uint16_t* wire_values, void* wire_idx,
+                           hipStream_t stream) {
+  if (chunk != kChunk && chunk != kChunkLarge) return fail(DEMO_ERR_RANGE, "chunk size must be 64 or 128");
   if (workers < 1 || workers > demo::kMaxWorkers) return fail(DEMO_ERR_RANGE, "workers must be in 1..255");
   if (n_entries < 0 || n_entries > (int64_t(1) << 40)) return fail(DEMO_ERR_RANGE, "entry count out of range");
   if (n_entries > 0 && (pay_values == nullptr || pay_idx == nullptr || wire_values == nullptr || wire_idx == nullptr))
@@ -433,7 +439,7 @@ demo_status demo_pack_wire(demo_ctx* ctx, int32_t workers, const float* pay_valu
     return fail(DEMO_ERR_ALIGN, "payload or wire buffer misaligned");
   demo_status s = check_device(ctx);
   if (s != DEMO_OK) return s;
-  const hipError_t e = demo::launch_pack_wire(pay_values, pay_idx, n_entries, workers, wire_values,
+  const hipError_t e = demo::launch_pack_wire(wire_bits(chunk), pay_values, pay_idx, n_entries, workers, wire_values,
                                               static_cast<uint32_t*>(wire_idx), stream);
   return e == hipSuccess ? DEMO_OK : fail(DEMO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
 }
@@ -458,7 +464,6 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
 
 demo_status demo_plan_signs(const demo_shape* shapes, int32_t n, int32_t chunk, int64_t* n_words,
                             int64_t* word_begin) {
-  if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
   std::vector<TensorPlan> plan;
   int64_t w = 0;
   const demo_status s = plan_list(shapes, n, chunk, 1, &plan, nullptr, nullptr, &w);
@@ -485,7 +490,6 @@ demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes,
   int64_t words = 0;
   demo_status s = plan_list(shapes, n, chunk, 1, &plan, nullptr, nullptr, &words);
   if (s != DEMO_OK) return s;
-  if (chunk != kChunk) return fail(DEMO_ERR_RANGE, "the one-bit download is built for chunk 64");
   if (!std::isfinite(eta) || !std::isfinite(lambda)) return fail(DEMO_ERR_INVALID, "eta/lambda not finite");
   if (n_words != words)
     return fail(DEMO_ERR_PAYLOAD, "sign buffer holds " + std::to_string(n_words) + " words, plan needs " +
@@ -503,6 +507,8 @@ demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes,
     slot.aux = const_cast<uint64_t*>(signs) + plan[i].word_begin;  // read only in the kernel
     slot.dst = params[i];
   };
+  if (chunk == kChunkLarge)
+    return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_apply_signs128(t, p, stream); });
   return for_each_batch(plan, fill, [&](const LaunchTable& t) { return demo::launch_apply_signs(t, p, stream); });
 }
 

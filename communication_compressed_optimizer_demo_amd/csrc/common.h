@@ -98,6 +98,33 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Lane i of v takes the wave-uniform value x (v_writelane: no compare, no
+// select; i is a compile-time lane number).  x is read from the first active
+// lane, which moves it into a scalar register where the compiler cannot
+// prove it uniform (it is free where x already is one).
+__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t x, int i) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(__builtin_amdgcn_readfirstlane(x)), "i"(i));
+}
+
+// Compact wire format: chunk positions of kBits bits (12 at chunk edge 64,
+// 14 at 128) packed as one little-endian bit string per worker, in groups of
+// kWireGroup entries that fill whole 32-bit words.
+template <int kBits>
+struct WireFormat {
+  static constexpr int kGroup = kBits == 12 ? 8 : 16;        // entries per group
+  static constexpr int kWords = kGroup * kBits / 32;          // 32-bit words per group
+  static_assert(kBits == 12 || kBits == 14, "positions of 12 or 14 bits");
+  static_assert(kGroup * kBits == 32 * kWords, "groups fill whole words");
+  // position of entry f from a worker's words (two words of f's group)
+  static __device__ __forceinline__ uint32_t index(const uint32_t* __restrict__ s, int64_t f) {
+    const int64_t bit = f * kBits;
+    const int64_t d = bit >> 5;
+    const int64_t last = (f / kGroup) * kWords + kWords - 1;
+    const uint64_t pair = (uint64_t(s[d < last ? d + 1 : d]) << 32) | s[d];
+    return uint32_t(pair >> (bit & 31)) & ((1u << kBits) - 1u);
+  }
+};
+
 // number of set lanes of `mask` below this lane
 __device__ __forceinline__ int lanes_below_mask(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));

@@ -307,12 +307,7 @@ template <bool kWire>
 __device__ __forceinline__ void load_entry(const DecodeParams& p, int64_t w, int64_t f, float& v, uint32_t& ix) {
   if constexpr (kWire) {
     v = __uint_as_float(uint32_t(p.wire_val[w * p.entries + f]) << 16);
-    const uint32_t* __restrict__ s = p.wire_idx + w * p.wire_words;
-    const int64_t bit = f * 12;
-    const int64_t d = bit >> 5;
-    const int64_t last = (f >> 3) * 3 + 2;
-    const uint64_t pair = (uint64_t(s[d < last ? d + 1 : d]) << 32) | s[d];
-    ix = uint32_t(pair >> (bit & 31)) & 4095u;
+    ix = WireFormat<12>::index(p.wire_idx + w * p.wire_words, f);
   } else {
     const int64_t off = w * p.entries + f;
     v = p.pay_val[off];
@@ -407,12 +402,6 @@ __device__ __forceinline__ void average_row(float (&q)[64], const float* acc, co
       }
     }
   }
-}
-
-// Lane i of v takes the wave-uniform value x (v_writelane: no compare, no
-// select; i is a compile-time lane number).
-__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t x, int i) {
-  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"(i));
 }
 
 template <class Basis, int kTargets, bool kWire>
@@ -636,32 +625,40 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// One thread per 8-entry group of one worker: eight bfloat16 values, and the
-// eight 12-bit indices as three little-endian words (entry j at bits 12j);
-// entries past the end count as index 0 and store no value.
+// One thread per group of one worker's entries (8 at 12 bits, 16 at 14):
+// the group's bfloat16 values, and its positions as whole little-endian
+// 32-bit words (entry j at bits kBits * j); entries past the end count as
+// position 0 and store no value.
+template <int kBits>
 __global__ __launch_bounds__(256) void pack_wire_kernel(const float* __restrict__ pay_val,
                                                         const uint16_t* __restrict__ pay_idx, int64_t entries,
                                                         int64_t groups, int64_t total, uint16_t* __restrict__ wire_val,
                                                         uint32_t* __restrict__ wire_idx) {
+  using F = WireFormat<kBits>;
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t w = t / groups;
   const int64_t g = t - w * groups;
   const int64_t base = w * entries;
-  uint32_t f[8];
+  uint32_t* __restrict__ out = wire_idx + t * F::kWords;  // worker w's words start at w * groups * kWords
+  uint64_t bits = 0;  // pending bits, low first
+  int nb = 0, o = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t e = g * 8 + j;
-    f[j] = 0u;
+  for (int j = 0; j < F::kGroup; ++j) {
+    const int64_t e = g * F::kGroup + j;
+    uint32_t f = 0u;
     if (e < entries) {
-      f[j] = pay_idx[base + e] & 4095u;
+      f = pay_idx[base + e] & ((1u << kBits) - 1u);
       wire_val[base + e] = uint16_t(bf16_rne(pay_val[base + e]));
     }
+    bits |= uint64_t(f) << nb;
+    nb += kBits;
+    if (nb >= 32) {  // resolved at compile time: j is a constant
+      out[o++] = uint32_t(bits);
+      bits >>= 32;
+      nb -= 32;
+    }
   }
-  uint32_t* __restrict__ out = wire_idx + t * 3;  // worker w's words start at w * groups * 3
-  out[0] = f[0] | (f[1] << 12) | (f[2] << 24);
-  out[1] = (f[2] >> 8) | (f[3] << 4) | (f[4] << 16) | (f[5] << 28);
-  out[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
 }
 
 // ---------------------------------------------------------------- one-bit sign apply
@@ -761,13 +758,18 @@ hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKin
   return hipGetLastError();
 }
 
-hipError_t launch_pack_wire(const float* pay_val, const uint16_t* pay_idx, int64_t entries, int32_t workers,
-                            uint16_t* wire_val, uint32_t* wire_idx, hipStream_t stream) {
-  const int64_t groups = (entries + 7) / 8;
+hipError_t launch_pack_wire(int32_t bits, const float* pay_val, const uint16_t* pay_idx, int64_t entries,
+                            int32_t workers, uint16_t* wire_val, uint32_t* wire_idx, hipStream_t stream) {
+  const int64_t per = bits == 12 ? WireFormat<12>::kGroup : WireFormat<14>::kGroup;
+  const int64_t groups = (entries + per - 1) / per;
   const int64_t total = groups * workers;
   if (total <= 0) return hipSuccess;
-  pack_wire_kernel<<<dim3(uint32_t((total + 255) / 256)), dim3(256), 0, stream>>>(pay_val, pay_idx, entries, groups,
-                                                                                  total, wire_val, wire_idx);
+  if ((total + 255) / 256 > int64_t(UINT32_MAX)) return hipErrorInvalidValue;
+  const dim3 grid(uint32_t((total + 255) / 256)), block(256);
+  if (bits == 12)
+    pack_wire_kernel<12><<<grid, block, 0, stream>>>(pay_val, pay_idx, entries, groups, total, wire_val, wire_idx);
+  else
+    pack_wire_kernel<14><<<grid, block, 0, stream>>>(pay_val, pay_idx, entries, groups, total, wire_val, wire_idx);
   return hipGetLastError();
 }
 

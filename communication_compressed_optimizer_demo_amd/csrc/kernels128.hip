@@ -786,7 +786,20 @@ __device__ __forceinline__ void decode_rows128(float (&x)[64], float (&m)[64], c
   }
 }
 
-template <int kTargets>
+// Entry f of worker w's payload: the float32 arrays, or the compact wire
+// format (bfloat16 value in the high half of a float; 14-bit position).
+template <bool kWire>
+__device__ __forceinline__ void load_entry128(const DecodeParams& p, int64_t w, int64_t f, float& v, uint32_t& ix) {
+  if constexpr (kWire) {
+    v = __uint_as_float(uint32_t(p.wire_val[w * p.entries + f]) << 16);
+    ix = WireFormat<14>::index(p.wire_idx + w * p.wire_words, f);
+  } else {
+    v = p.pay_val[w * p.entries + f];
+    ix = p.pay_idx[w * p.entries + f];
+  }
+}
+
+template <int kTargets, bool kWire>
 __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int a = w >> 1, b = w & 1;
@@ -809,9 +822,13 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
     const uint32_t e = uint32_t(min(lane, p.keff2 - 1));
 #pragma unroll
     for (int j = 0; j < kWorkerBatch; ++j) {
-      const int64_t w0 = int64_t(min(j, p.workers - 1)) * p.entries + e0;
-      val[j] = (p.pay_val + w0)[e];
-      ix[j] = (p.pay_idx + w0)[e];
+      if constexpr (kWire) {
+        load_entry128<true>(p, min(j, p.workers - 1), e0 + e, val[j], ix[j]);
+      } else {
+        const int64_t w0 = int64_t(min(j, p.workers - 1)) * p.entries + e0;
+        val[j] = (p.pay_val + w0)[e];
+        ix[j] = (p.pay_idx + w0)[e];
+      }
     }
   }
   const int64_t ld = ts.cols;
@@ -843,9 +860,9 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
         for (int j = 0; j < kWorkerBatch; ++j) {
           const int e = eb * 64 + lane;
           on[j] = t0 + j < steps && e < p.keff2;
-          const int64_t off = int64_t(wk) * p.entries + e0 + e;
-          v2[j] = on[j] ? p.pay_val[off] : 0.f;
-          i2[j] = on[j] ? p.pay_idx[off] : 0u;
+          v2[j] = 0.f;
+          i2[j] = 0u;
+          if (on[j]) load_entry128<kWire>(p, wk, e0 + e, v2[j], i2[j]);
           if (++eb == nb) {
             eb = 0;
             ++wk;
@@ -883,6 +900,26 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   else
     butterfly(q, reinterpret_cast<float*>(lds), w, lane);
 
+  if constexpr ((kTargets & kToSigns) != 0) {
+    // Chunk row r's sign bits fill words 2r (columns 0..63) and 2r + 1
+    // (64..127), bit = column within the half.  Quadrant row i is chunk row
+    // r(i) = quad_row(a, i) and half b; in the second column half lane j holds
+    // column 127 - j, bit 63 - j, so the ballot is bit-reversed.  Row i's word
+    // goes into lane i, which stores it; rows and columns past the chunk's
+    // valid ones give 0 bits.
+    const int colq = b ? kS - 1 - lane : lane;
+    const uint64_t cols = __builtin_amdgcn_ballot_w64(colq < c.vc);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      uint64_t bb = quad_row(a, i) < c.vr ? __builtin_amdgcn_ballot_w64(q[i] < 0.f) & cols : 0ull;
+      bb = b ? __builtin_bitreverse64(bb) : bb;
+      write_lane(lo, uint32_t(bb), i);
+      write_lane(hi, uint32_t(bb >> 32), i);
+    }
+    const uint64_t word = (uint64_t(hi) << 32) | lo;
+    stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(c.local) * 256 + 2 * quad_row(a, lane) + b);
+  }
   if constexpr ((kTargets & kToParams) != 0) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
@@ -914,7 +951,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
 // Vector item: each wave owns 32 chunks and its own fifth of the LDS:
 // accumulator (chunk g, coefficient c) at g*128 + (c ^ g), counts in byte
 // c & 3 of word g*32 + ((c >> 2) ^ g).
-template <int kTargets>
+template <int kTargets, bool kWire>
 __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int kWaveWords = kDecLdsWords / 4;
@@ -939,16 +976,15 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
   const int n = nc * keff;
   const int64_t e0 = ts.entry_begin + int64_t(chunk0) * keff;
   for (int wk = 0; wk < p.workers; ++wk) {
-    const float* __restrict__ pv = p.pay_val + int64_t(wk) * p.entries + e0;
-    const uint16_t* __restrict__ pi = p.pay_idx + int64_t(wk) * p.entries + e0;
     for (int f0 = 0; f0 < n; f0 += 64 * 8) {
       float vv[8];
       uint32_t ii[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int f = f0 + 64 * j + lane;
-        vv[j] = f < n ? pv[f] : 0.f;
-        ii[j] = f < n ? pi[f] : 0u;
+        vv[j] = 0.f;
+        ii[j] = 0u;
+        if (f < n) load_entry128<kWire>(p, wk, e0 + f, vv[j], ii[j]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -980,6 +1016,21 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
   float (&x)[64] = y;
   row_to_col(reinterpret_cast<float*>(my), x, lane);  // column layout: x[r] = M* at element first + 64 r
 
+  if constexpr ((kTargets & kToSigns) != 0) {
+    // A 128-element chunk's signs are two words (its elements 0..63 and
+    // 64..127), so this wave's 32 chunks own words 2 chunk0 + r, r < 64:
+    // word r covers elements chunk0 * 128 + 64 r + j, which is x[r] of lane
+    // j.  Only the words of existing chunks are stored.
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      const uint64_t bb = __builtin_amdgcn_ballot_w64(r * 64 < rem && x[r] < 0.f);
+      write_lane(lo, uint32_t(bb), r);
+      write_lane(hi, uint32_t(bb >> 32), r);
+    }
+    if (lane < 2 * nc)
+      stream_store((uint64_t(hi) << 32) | lo, static_cast<uint64_t*>(ts.aux) + int64_t(chunk0) * 2 + lane);
+  }
   if constexpr ((kTargets & kToParams) != 0) {
     float* __restrict__ xp = ts.dst + first;
 #pragma unroll
@@ -996,15 +1047,66 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
   }
 }
 
-template <int kTargets>
+template <int kTargets, bool kWire = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode128_kernel(LaunchTable tab,
                                                                                                DecodeParams p) {
   __shared__ __align__(16) uint32_t lds[kDecLdsWords];
   const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
   if (ts.cols == 0)
-    decode_vector128<kTargets>(ts, p, lds);
+    decode_vector128<kTargets, kWire>(ts, p, lds);
   else
-    decode_matrix128<kTargets>(ts, p, lds);
+    decode_matrix128<kTargets, kWire>(ts, p, lds);
+}
+
+// ---------------------------------------------------------------- one-bit sign apply
+
+// X = X - eta (s + lambda X), s = -1 where the element's bit is set, else +1.
+// A workgroup (four waves) takes one 128x128 chunk, wave 2 rb + h its 64x64
+// sub-block of rows 64 rb .. and columns 64 h ..: chunk row r's bit for
+// column 64 h + j is bit j of word 2 r + h.  Or, for a vector, 128 chunks,
+// wave w the 64 words of elements 4096 w .. 4096 w + 4095 of the item (word
+// = 64 consecutive elements, as at chunk edge 64).  Words arrive through
+// wave-uniform (scalar) loads.
+__global__ __launch_bounds__(256) void apply_signs128_kernel(LaunchTable tab, ApplyParams p) {
+  const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t* __restrict__ words = static_cast<const uint64_t*>(ts.aux);
+  if (ts.cols == 0) {
+    const int slab = blockIdx.x - ts.item_begin;
+    const int64_t base = int64_t(slab) * kVecChunksPerItem * kS + int64_t(w) * 64 * 64;  // the wave's first element
+    const int64_t nwords = 2 * ((int64_t(ts.rows) + kS - 1) / kS);                        // words of the tensor
+    const int64_t rem = int64_t(ts.rows) - (base + lane);
+    float* __restrict__ x = ts.dst + base + lane;
+    for (int c = 0; c < 64 && base / 64 + c < nwords; ++c) {
+      const uint64_t wd = words[base / 64 + c];
+      if (c * 64 < rem) {
+        const float s = ((wd >> lane) & 1u) ? -1.f : 1.f;
+        const float xv = stream_load(&x[c * 64]);
+        stream_store(fmaf(-p.eta, fmaf(p.lam, xv, s), xv), &x[c * 64]);
+      }
+    }
+    return;
+  }
+  const Chunk128 c = chunk_pos128(ts, blockIdx.x);
+  const int rb = w >> 1, h = w & 1;
+  const int vr = min(64, c.vr - 64 * rb), vc = min(64, c.vc - 64 * h);  // valid rows / columns of the sub-block
+  if (vr <= 0 || vc <= 0) return;
+  const uint64_t* __restrict__ wp = words + int64_t(c.local) * 256 + 2 * 64 * rb + h;
+  const int64_t ld = ts.cols;
+  float* __restrict__ xp = ts.dst + c.base + int64_t(64 * rb) * ld + 64 * h;
+  const int col = min(lane, vc - 1);
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[min(i, vr - 1) * ld + col]);
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const float s = ((wp[2 * i] >> lane) & 1u) ? -1.f : 1.f;
+    x[i] = fmaf(-p.eta, fmaf(p.lam, x[i], s), x[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (lane < vc && i < vr) stream_store(x[i], &xp[i * ld + lane]);
+  }
 }
 
 }  // namespace
@@ -1027,12 +1129,22 @@ hipError_t launch_encode128(const LaunchTable& tab, const EncodeParams& p, bool 
 hipError_t launch_decode128(const LaunchTable& tab, const DecodeParams& p, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
   const dim3 grid(tab.items), block(256);
-  if (p.update_x && p.update_m)
+  if (p.wire)
+    decode128_kernel<kToParams, true><<<grid, block, 0, stream>>>(tab, p);
+  else if (p.pack_signs)
+    decode128_kernel<kToSigns><<<grid, block, 0, stream>>>(tab, p);
+  else if (p.update_x && p.update_m)
     decode128_kernel<kToParams | kToMomentum><<<grid, block, 0, stream>>>(tab, p);
   else if (p.update_m)
     decode128_kernel<kToMomentum><<<grid, block, 0, stream>>>(tab, p);
   else
     decode128_kernel<kToParams><<<grid, block, 0, stream>>>(tab, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_signs128(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream) {
+  if (tab.items <= 0) return hipSuccess;
+  apply_signs128_kernel<<<dim3(tab.items), dim3(256), 0, stream>>>(tab, p);
   return hipGetLastError();
 }
 

@@ -91,9 +91,12 @@ hipError_t launch_decode(const LaunchTable& tab, const DecodeParams& p, BasisKin
                          const float* basis_p1, hipStream_t stream);
 hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream);
 // workers x entries payload entries -> wire values (workers x entries) and
-// wire index words (workers x 3 * ceil(entries / 8))
-hipError_t launch_pack_wire(const float* pay_val, const uint16_t* pay_idx, int64_t entries, int32_t workers,
-                            uint16_t* wire_val, uint32_t* wire_idx, hipStream_t stream);
+// wire index words (workers x 3 * ceil(entries / 8) at 12 bits, workers x
+// 7 * ceil(entries / 16) at 14 bits)
+hipError_t launch_pack_wire(int32_t bits, const float* pay_val, const uint16_t* pay_idx, int64_t entries,
+                            int32_t workers, uint16_t* wire_val, uint32_t* wire_idx, hipStream_t stream);
+// Packed signs at chunk edge 128 (kernels128.hip): X update from sign words.
+hipError_t launch_apply_signs128(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream);
 // phi = Muon (kernels_muon.hip).  D = alpha * (*alpha_scale if given) *
 // op(A) op(B) + beta * C + gamma * I, fp32, row-major; op(A) is M x K (the
 // transpose of a row-major K x M matrix when trans_a), op(B) K x N.  C may

@@ -57,7 +57,7 @@ extern "C" {
 #endif
 
 #define DEMO_CHUNK 64        /* default chunk edge s (the pages' default) */
-#define DEMO_CHUNK_LARGE 128 /* the other chunk edge built: DCT basis only, no one-bit download */
+#define DEMO_CHUNK_LARGE 128 /* the other chunk edge built: DCT basis only, no Muon */
 #define DEMO_MAX_WORKERS 255 /* decode keeps per-coefficient contributor counts in 8 bits */
 #define DEMO_MAX_TENSORS_PER_LAUNCH 96 /* longer lists are split into several launches per call */
 
@@ -191,10 +191,12 @@ demo_status demo_decode_apply_subtract(demo_ctx* ctx, int32_t n, const demo_shap
 /* ---- One-bit download of the Signum variant (DeMo summary §3.4 Base Optimizer
  * Update: with phi = sign the server broadcasts only sign(M*), one bit per
  * parameter, and every worker applies it to its own copy of X).
- * Built for chunk edge 64 (other chunk edges return DEMO_ERR_RANGE).
+ * Built for both chunk edges (64, and 128 with the DCT basis).
  * Packed-sign layout: uint64 words, chunk after chunk in the chunk order of the
- * payload.  A 64x64 chunk takes 64 words (word i = chunk row i, bit j = column
- * j), a 64-element vector chunk one word (bit j = element j).  A bit is set
+ * payload; inside a chunk its elements in row-major order, 64 to a word, bit j
+ * the j-th of them.  A 64x64 chunk takes 64 words (word i = chunk row i, bit
+ * j = column j), a 128x128 chunk 256 (word 2i + h = chunk row i, columns
+ * 64h .. 64h + 63), a vector chunk s / 64 words.  A bit is set
  * where M* < 0; M* = 0 reads as +1, since one bit cannot carry sign(0) = 0.
  * Padding positions hold 0.
  * This differs from demo_decode_apply with DEMO_PHI_SIGN exactly where M* = 0:
@@ -228,34 +230,38 @@ demo_status demo_apply_signs(demo_ctx* ctx, int32_t n, const demo_shape* shapes,
 
 /* ---- Compact wire format (teaching deck "Training over Slow Links", top-k
  * and DeMo slides: a kept value travels as 2 bytes of bfloat16 plus its
- * position, and a position inside a 64x64 chunk needs 12 bits).  Built for
- * chunk edge 64 (other chunk edges return DEMO_ERR_RANGE).
+ * position).  A position takes b bits, enough for a matrix chunk's s*s
+ * positions: b = 12 at chunk edge 64, b = 14 at chunk edge 128.
  * A worker's wire payload of E entries is two arrays:
  *   values:  E uint16 bfloat16 bit patterns, entry order kept; float32 ->
  *            bfloat16 rounds to nearest, ties to even
- *   indices: 12 * ceil(E / 8) bytes: entry j's 12-bit index sits at bits
- *            12j .. 12j + 11 of the array read as one little-endian bit
- *            string (so entries 2p, 2p+1 fill bytes 3p .. 3p + 2, low bits
- *            first); the bytes past 3 * ceil(E / 2) are zero.
+ *   indices: entry j's b-bit position sits at bits bj .. bj + b - 1 of the
+ *            array read as one little-endian bit string (bit t = bit t mod 8
+ *            of byte t / 8).  The array is whole groups of 32-bit words, 12
+ *            bytes per 8 entries (b = 12) or 28 bytes per 16 (b = 14), so
+ *            idx_bytes = 12 ceil(E / 8) or 28 ceil(E / 16); the bits past the
+ *            last entry are zero.
  * W wire payloads lie worker-major: values as W x E uint16, indices as
  * W x demo_wire_size's idx_bytes. */
 
-/* Host-only: bytes of one worker's wire values (2E) and indices (12 ceil(E/8)). */
-demo_status demo_wire_size(int64_t n_entries, int64_t* value_bytes, int64_t* idx_bytes);
+/* Host-only: bytes of one worker's wire values (2E) and indices at chunk
+ * edge `chunk` (64 or 128, else DEMO_ERR_RANGE). */
+demo_status demo_wire_size(int32_t chunk, int64_t n_entries, int64_t* value_bytes, int64_t* idx_bytes);
 
 /* Convert `workers` payloads (worker-major, n_entries each, as demo_encode
- * writes them) into the wire format.  Indices are sent modulo 4096 (a 64x64
- * chunk's indices are below that).
+ * writes them at chunk edge `chunk`) into the wire format.  Indices are sent
+ * modulo 2^b (a chunk's indices are below that).
  *   wire_values: device, workers x n_entries uint16 (2-byte aligned); written
  *   wire_idx:    device, workers x idx_bytes bytes (4-byte aligned); written,
  *                padding included */
-demo_status demo_pack_wire(demo_ctx* ctx, int32_t workers, const float* pay_values, const uint16_t* pay_idx,
-                           int64_t n_entries, uint16_t* wire_values, void* wire_idx, hipStream_t stream);
+demo_status demo_pack_wire(demo_ctx* ctx, int32_t chunk, int32_t workers, const float* pay_values,
+                           const uint16_t* pay_idx, int64_t n_entries, uint16_t* wire_values, void* wire_idx,
+                           hipStream_t stream);
 
 /* demo_decode_apply reading W wire payloads directly (values widened from
  * bfloat16, indices unpacked in the kernel; nothing is unpacked into memory).
  * Arguments as for demo_decode_apply, the payload given as wire arrays
- * (read only); cfg->chunk must be 64. */
+ * (read only) packed at cfg->chunk. */
 demo_status demo_decode_apply_wire(demo_ctx* ctx, int32_t n, const demo_shape* shapes, float* const* params,
                                    const demo_codec_cfg* cfg, int32_t workers, const uint16_t* wire_values,
                                    const void* wire_idx, int64_t n_entries, demo_phi phi, float eta, float lambda,

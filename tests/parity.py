@@ -293,26 +293,27 @@ def _bits(words: np.ndarray, n_chunks: int) -> np.ndarray:
     return np.unpackbits(by, axis=1, bitorder="little").reshape(n_chunks, -1).astype(bool)
 
 
-def compare_signs(Mstar: np.ndarray, shape, gpu_words: np.ndarray, chunk_diverged: np.ndarray, where: str = ""):
+def compare_signs(Mstar: np.ndarray, shape, gpu_words: np.ndarray, chunk_diverged: np.ndarray, where: str = "",
+                  s: int = 64):
     """Check one tensor's packed sign words against the oracle's packing of its M*.
 
     Bit-exact on every valid element except where |M*| is within RTOL of its
     chunk's largest |M*| (float rounding may flip such a sign, as for Signum)
     and in chunks whose top-k legitimately diverged; padding bits must be 0."""
     n = chunk_diverged.shape[0]
-    ref = _bits(O.pack_signs(Mstar), n)
+    ref = _bits(O.pack_signs(Mstar, s), n)
     got = _bits(gpu_words, n)
-    valid = O.split_chunks(np.ones(shape)).reshape(n, -1) != 0
+    valid = O.split_chunks(np.ones(shape), s).reshape(n, -1) != 0
     pad = got & ~valid
     assert not pad.any(), f"{where}: {int(pad.sum())} padding bits set"
-    a = O.split_chunks(np.abs(Mstar)).reshape(n, -1)
+    a = O.split_chunks(np.abs(Mstar), s).reshape(n, -1)
     near0 = a <= RTOL * a.max(axis=1, keepdims=True)
     live = valid & ~near0 & ~chunk_diverged[:, None]
     bad = (got != ref) & live
     if bad.any():
         c, e = np.argwhere(bad)[0]
         raise AssertionError(f"{where}: sign bit differs in chunk {c} element {e} "
-                             f"({int(bad.sum())} bits; M* there {O.split_chunks(Mstar).reshape(n, -1)[c, e]!r})")
+                             f"({int(bad.sum())} bits; M* there {O.split_chunks(Mstar, s).reshape(n, -1)[c, e]!r})")
     return int(((got != ref) & valid).sum())
 
 
@@ -321,7 +322,7 @@ def _bf16_value(codes: np.ndarray) -> np.ndarray:
 
 
 def compare_wire(values: np.ndarray, idx: np.ndarray, Q: np.ndarray, gpu_codes: np.ndarray, gpu_idx: np.ndarray,
-                 diverged: np.ndarray, where: str = "") -> np.ndarray:
+                 diverged: np.ndarray, where: str = "", noise: float = NOISE) -> np.ndarray:
     """Check one tensor's wire entries; returns the chunks whose bfloat16 codes differ.
 
     values / idx: the oracle's payload [n, keff] (float32 values); Q: the
@@ -340,7 +341,7 @@ def compare_wire(values: np.ndarray, idx: np.ndarray, Q: np.ndarray, gpu_codes: 
     assert np.array_equal(gi[live], np.asarray(idx).astype(np.int64)[live]), f"{where}: wire indices differ"
     norms = np.linalg.norm(np.asarray(Q, dtype=np.float64).reshape(n, -1), axis=1)
     v = np.asarray(values, dtype=np.float32)
-    tol = _tol(v.astype(np.float64), (NOISE * norms)[:, None])
+    tol = _tol(v.astype(np.float64), (noise * norms)[:, None])
     lo = _bf16_value(O.bf16_bits((v - tol).astype(np.float32)))
     hi = _bf16_value(O.bf16_bits((v + tol).astype(np.float32)))
     g = _bf16_value(gpu_codes)

@@ -214,16 +214,17 @@ def test_ctx_create_without_gpu_fails_cleanly(lib):
 
 # --------------------------------------------------------------------------- one-bit sign download
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("name", sorted(DI.WORKLOADS))
-def test_plan_signs_matches_oracle_word_count(lib, name):
+def test_plan_signs_matches_oracle_word_count(lib, name, chunk):
     import numpy as np
     w = DI.WORKLOADS[name]
-    n_words, begin = B.demo_plan_signs(w.shapes)
-    assert n_words == O.sign_words(w.shapes)
+    n_words, begin = B.demo_plan_signs(w.shapes, chunk)
+    assert n_words == O.sign_words(w.shapes, chunk)
     acc = 0
     for i, s in enumerate(w.shapes):
         assert begin[i] == acc
-        acc += O.sign_words([s])
+        acc += O.sign_words([s], chunk)
     assert begin[len(w.shapes)] == acc == n_words
     if name == "olmo_1b":
         assert n_words * 64 == w.n_params  # no padding in the OLMo shapes: exactly one bit per parameter
@@ -235,9 +236,9 @@ def _call_decode_signs(lib, shapes, k=8, workers=2, avg=0, vals=0x3000, idx=0x40
     cfg = B.demo_codec_cfg(chunk, k, 0.9, 0.2, 0, 0, None, None, 0)
     n = len(shapes)
     if words is None:
-        words = O.sign_words(shapes)
+        words = O.sign_words(shapes, chunk)
     if entries is None:
-        entries = O.payload_entries(shapes, k)
+        entries = O.payload_entries(shapes, k, chunk)
     return lib.demo_decode_signs(None, n, B._shapes(shapes), ctypes.byref(cfg), workers, vals, idx, entries, avg,
                                  signs, words, None)
 
@@ -246,7 +247,7 @@ def _call_apply_signs(lib, shapes, params=0x1000, signs=0x5000, words=None, eta=
                       null_list=False):
     n = len(shapes)
     if words is None:
-        words = O.sign_words(shapes)
+        words = O.sign_words(shapes, chunk if chunk in (64, 128) else 64)
     pl = None if null_list else B._ptrs([params] * n)
     return lib.demo_apply_signs(None, n, B._shapes(shapes), pl, chunk, signs, words, eta, lam, None)
 
@@ -259,7 +260,9 @@ def _call_apply_signs(lib, shapes, params=0x1000, signs=0x5000, words=None, eta=
     (dict(entries=2), 4, "payload"),
     (dict(workers=0), 3, "workers"),
     (dict(avg=5), 1, "average"),
-    (dict(chunk=128), 3, "chunk"),
+    (dict(chunk=32), 3, "chunk"),
+    (dict(chunk=128), 1, "context"),
+    (dict(chunk=128, words=3), 4, "sign buffer"),
     (dict(vals=0), 1, "payload is NULL"),
 ])
 def test_decode_signs_arguments(lib, kw, status, text):
@@ -277,6 +280,7 @@ def test_decode_signs_arguments(lib, kw, status, text):
     (dict(null_list=True), 1, "pointer list"),
     (dict(eta=float("nan")), 1, "eta"),
     (dict(chunk=32), 3, "chunk"),
+    (dict(chunk=128), 1, "context"),
 ])
 def test_apply_signs_arguments(lib, kw, status, text):
     assert _call_apply_signs(lib, [(128, 64), (100,)], **kw) == status
@@ -302,11 +306,13 @@ def test_chunk128_valid_arguments_reach_the_context_check(lib):
     e = O.payload_entries(sh, 16, 128)
     assert lib.demo_decode_apply(None, 2, B._shapes(sh), B._ptrs([0x1000] * 2), ctypes.byref(cfg), 3, 0x3000,
                                  0x4000, e, 0, 1e-3, 0.0, 0, None) == 1 and "context" in _msg(lib)
-    # the one-bit download is built for chunk 64 only
-    assert lib.demo_decode_signs(None, 2, B._shapes(sh), ctypes.byref(cfg), 3, 0x3000, 0x4000, e, 0, 0x5000, 8,
-                                 None) == 3 and "chunk 64" in _msg(lib)
+    # the one-bit download: 2 words per 128-element row of a padded matrix chunk, 2 per vector chunk
     nw = ctypes.c_int64()
-    assert lib.demo_plan_signs(B._shapes(sh), 2, 128, ctypes.byref(nw), None) == 3
+    assert lib.demo_plan_signs(B._shapes(sh), 2, 128, ctypes.byref(nw), None) == 0
+    assert nw.value == 3 * 2 * 256 + 8 * 2 == O.sign_words(sh, 128)
+    assert lib.demo_decode_signs(None, 2, B._shapes(sh), ctypes.byref(cfg), 3, 0x3000, 0x4000, e, 0, 0x5000,
+                                 nw.value, None) == 1 and "context" in _msg(lib)
+    assert lib.demo_plan_signs(B._shapes(sh), 2, 96, ctypes.byref(nw), None) == 3
 
 
 # --------------------------------------------------------------------------- phi = Muon
@@ -359,14 +365,25 @@ def test_muon_arguments(lib, kw, status, text):
 
 # --------------------------------------------------------------------------- compact wire format
 
-@pytest.mark.parametrize("entries", [0, 1, 7, 8, 9, 1000, 6_291_456])
+@pytest.mark.parametrize("entries", [0, 1, 7, 8, 9, 15, 16, 17, 1000, 6_291_456])
 def test_wire_size(lib, entries):
     vb, ib = B.demo_wire_size(entries)
     assert vb == 2 * entries
-    # whole 8-entry groups of 12 bytes, which hold the oracle's pair-packed bytes
+    # whole 8-entry groups of 12 bytes, which hold the oracle's 12-bit string
     assert ib == 12 * ((entries + 7) // 8)
+    vb, ib14 = B.demo_wire_size(entries, 128)
+    assert vb == 2 * entries
+    # whole 16-entry groups of 28 bytes (7 words), which hold the oracle's 14-bit string
+    assert ib14 == 28 * ((entries + 15) // 16)
     if entries < 2000:
         assert O.pack_wire([0.0] * entries, [0] * entries)[1].size <= ib
+        assert O.pack_wire([0.0] * entries, [0] * entries, s=128)[1].size <= ib14
+        assert ib - O.pack_wire([0.0] * entries, [0] * entries)[1].size < 12
+        assert ib14 - O.pack_wire([0.0] * entries, [0] * entries, s=128)[1].size < 28
+
+
+def test_wire_size_rejects_other_chunks(lib):
+    assert lib.demo_wire_size(96, 10, None, None) == 3 and "chunk" in _msg(lib)
 
 
 def _call_wire_decode(lib, k=8, workers=2, chunk=64, wv=0x3000, wi=0x4000, entries=None, phi=0):
@@ -379,7 +396,9 @@ def _call_wire_decode(lib, k=8, workers=2, chunk=64, wv=0x3000, wi=0x4000, entri
 
 @pytest.mark.parametrize("kw,status,text", [
     (dict(), 1, "context"),
-    (dict(chunk=128), 3, "chunk 64"),
+    (dict(chunk=128), 4, "entries"),
+    (dict(chunk=128, entries=O.payload_entries([(70, 90), (100,)], 8, 128)), 1, "context"),
+    (dict(chunk=32), 3, "chunk"),
     (dict(workers=0), 3, "workers"),
     (dict(workers=256), 3, "workers"),
     (dict(entries=5), 4, "entries"),
@@ -395,13 +414,15 @@ def test_wire_decode_arguments(lib, kw, status, text):
 
 
 @pytest.mark.parametrize("args,status,text", [
-    ((2, 0x3000, 0x4000, 100, 0x5000, 0x6000), 1, "context"),
-    ((0, 0x3000, 0x4000, 100, 0x5000, 0x6000), 3, "workers"),
-    ((2, 0x3000, 0x4000, -1, 0x5000, 0x6000), 3, "entry count"),
-    ((2, 0, 0x4000, 100, 0x5000, 0x6000), 1, "NULL"),
-    ((2, 0x3000, 0x4000, 100, 0, 0x6000), 1, "NULL"),
-    ((2, 0x3002, 0x4000, 100, 0x5000, 0x6000), 7, "misaligned"),
-    ((2, 0x3000, 0x4000, 100, 0x5000, 0x6001), 7, "misaligned"),
+    ((64, 2, 0x3000, 0x4000, 100, 0x5000, 0x6000), 1, "context"),
+    ((128, 2, 0x3000, 0x4000, 100, 0x5000, 0x6000), 1, "context"),
+    ((32, 2, 0x3000, 0x4000, 100, 0x5000, 0x6000), 3, "chunk"),
+    ((64, 0, 0x3000, 0x4000, 100, 0x5000, 0x6000), 3, "workers"),
+    ((64, 2, 0x3000, 0x4000, -1, 0x5000, 0x6000), 3, "entry count"),
+    ((64, 2, 0, 0x4000, 100, 0x5000, 0x6000), 1, "NULL"),
+    ((64, 2, 0x3000, 0x4000, 100, 0, 0x6000), 1, "NULL"),
+    ((64, 2, 0x3002, 0x4000, 100, 0x5000, 0x6000), 7, "misaligned"),
+    ((64, 2, 0x3000, 0x4000, 100, 0x5000, 0x6001), 7, "misaligned"),
 ])
 def test_pack_wire_arguments(lib, args, status, text):
     assert lib.demo_pack_wire(None, *args, None) == status

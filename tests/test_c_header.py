@@ -32,7 +32,7 @@ int main(void) {
   printf("plan %lld %lld %lld %lld %lld\n", (long long)chunks, (long long)entries, (long long)begin[0],
          (long long)begin[1], (long long)begin[2]);
   int64_t vb = 0, ib = 0;
-  if (demo_wire_size(entries, &vb, &ib) != DEMO_OK) return 2;
+  if (demo_wire_size(DEMO_CHUNK, entries, &vb, &ib) != DEMO_OK) return 2;
   printf("wire %lld %lld\n", (long long)vb, (long long)ib);
   sh[0].ndim = 3;
   demo_status s = demo_plan(sh, 2, DEMO_CHUNK, 8, &chunks, &entries, NULL);

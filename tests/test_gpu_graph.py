@@ -30,9 +30,10 @@ def _bits(t):
     return t.detach().cpu().numpy().view(np.uint8)
 
 
-@pytest.mark.parametrize("variant", ["apply", "chunk128", "signs", "wire", "aggregated", "muon"])
+@pytest.mark.parametrize("variant", ["apply", "chunk128", "signs", "wire", "signs128", "wire128", "aggregated",
+                                     "muon"])
 def test_graph_replay_matches_eager(dev, variant):
-    chunk = 128 if variant == "chunk128" else 64
+    chunk = 128 if "128" in variant else 64
     shapes = [(192, 320), (300,), (130, 70)]
     W, k = 3, 16
     w = DI.WORKLOADS["tiny_256"].replace(name=f"graph_{variant}", shapes=tuple(shapes), k=k, workers=W)
@@ -50,17 +51,17 @@ def test_graph_replay_matches_eager(dev, variant):
         st[tag] = dict(M=[torch.zeros(s, device="cuda") for s in shapes],
                        X=[torch.from_numpy(DI.initial_params(w, i)).cuda() for i in range(len(shapes))],
                        vals=vals, idx=idx,
-                       signs=codec.alloc_signs() if variant == "signs" else None,
-                       wire=codec.alloc_wire(W) if variant == "wire" else None,
+                       signs=codec.alloc_signs() if variant.startswith("signs") else None,
+                       wire=codec.alloc_wire(W) if variant.startswith("wire") else None,
                        ws=codec.alloc_muon_workspace() if variant == "muon" else None)
     torch.cuda.synchronize()
 
     def step(s, stream):
         codec.encode(G, s["M"], s["vals"][:ne], s["idx"][:ne], stream=stream)
-        if variant == "signs":
+        if variant.startswith("signs"):
             codec.decode_signs(W, s["vals"], s["idx"], s["signs"], stream=stream)
             codec.apply_signs(s["X"], s["signs"], w.eta, w.lam, stream=stream)
-        elif variant == "wire":
+        elif variant.startswith("wire"):
             wv, wi = s["wire"]
             codec.pack_wire(W, s["vals"], s["idx"], wv, wi, stream=stream)
             codec.decode_apply_wire(s["X"], W, wv, wi, B.DEMO_PHI_SIGN, w.eta, w.lam, stream=stream)
@@ -89,9 +90,9 @@ def test_graph_replay_matches_eager(dev, variant):
                 assert np.array_equal(_bits(ta), _bits(tb)), f"replay {r}: {name}[{i}] differs from the eager call"
         assert np.array_equal(_bits(a["vals"][:ne]), _bits(b["vals"][:ne])), f"replay {r}: payload values differ"
         assert np.array_equal(_bits(a["idx"][:ne]), _bits(b["idx"][:ne])), f"replay {r}: payload indices differ"
-        if variant == "signs":
+        if variant.startswith("signs"):
             assert np.array_equal(_bits(a["signs"]), _bits(b["signs"])), f"replay {r}: sign words differ"
-        if variant == "wire":
+        if variant.startswith("wire"):
             for ta, tb in zip(a["wire"], b["wire"]):
                 assert np.array_equal(_bits(ta), _bits(tb)), f"replay {r}: wire arrays differ"
         assert any(bool((x != 0).any()) for x in a["M"]), "the momentum never moved"

@@ -59,7 +59,7 @@ def run_case(shapes, k, W, s=64, avg="count", basis="dct", wire=False, seed=0, w
     X = [torch.zeros(sh, device="cuda") for sh in shapes]
     if wire:
         wv, wi = codec.alloc_wire(W)
-        codec.pack_wire(W, vd, idd, wv, wi)
+        codec.pack_wire(W, vd, idd, wv, wi)  # positions of 12 bits at s = 64, 14 at s = 128
         codec.decode_apply_wire(X, W, wv, wi, B.DEMO_PHI_IDENTITY, 1.0, 0.0, avg_c, **kw)
     else:
         codec.decode_apply(X, W, vd, idd, B.DEMO_PHI_IDENTITY, 1.0, 0.0, avg_c, **kw)
@@ -71,7 +71,7 @@ def run_case(shapes, k, W, s=64, avg="count", basis="dct", wire=False, seed=0, w
         v = np.stack([vals[wk * ne + e0:wk * ne + e0 + n * keff].reshape(n, keff) for wk in range(W)])
         ix = np.stack([idx[wk * ne + e0:wk * ne + e0 + n * keff].reshape(n, keff) for wk in range(W)])
         if wire:  # the wire carries the values rounded to bfloat16
-            v = O.unpack_wire(*O.pack_wire(v.ravel(), ix.ravel()), v.size)[0].reshape(v.shape)
+            v = O.unpack_wire(*O.pack_wire(v.ravel(), ix.ravel(), s), v.size, s)[0].reshape(v.shape)
         dec = O.decode_apply(np.zeros(sh, np.float32), v, ix, phi="identity", eta=1.0, lam=0.0, mode=avg,
                              P0=P0, P1=P1, s=s)
         worst = max(worst, PR.compare_mstar(dec["Qabs"], dec["Mstar"], -X[i].cpu().numpy(), sh, np.zeros(n, bool),
@@ -117,11 +117,13 @@ def test_mstar_bases(dev, basis, avg, W, k):
              where=f"{basis} {avg} W={W} k={k}")
 
 
+@pytest.mark.parametrize("s", [64, 128])
 @pytest.mark.parametrize("avg", ["count", "workers"])
 @pytest.mark.parametrize("W,k", [(1, 8), (3, 32), (16, 32), (20, 100), (255, 4)])
-def test_mstar_wire(dev, avg, W, k):
+def test_mstar_wire(dev, avg, W, k, s):
     """Decoding from the wire format: the oracle decodes the same payload rounded to bfloat16."""
-    run_case(grid_shapes(64, W, k), k, W, wire=True, avg=avg, seed=700 + W + k, where=f"wire {avg} W={W} k={k}")
+    run_case(grid_shapes(s, W, k), k, W, s=s, wire=True, avg=avg, seed=700 + W + k,
+             where=f"wire s={s} {avg} W={W} k={k}")
 
 
 def test_mstar_full_size_olmo1b(dev):

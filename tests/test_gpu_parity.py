@@ -71,7 +71,7 @@ class Sim:
         self.sign_words = self.codec.alloc_signs() if signs else None
         if wire:
             self.wv, self.wi = self.codec.alloc_wire(W)
-            self.wire_bytes = B.demo_wire_size(self.codec.n_entries)[1]
+            self.wire_bytes = B.demo_wire_size(self.codec.n_entries, chunk)[1]
             self.xdiv = [np.zeros(n, dtype=bool) for n, _, _ in self.lay]  # chunks whose X follows other codes
         self.cdiv = [[np.zeros(n, dtype=bool) for n, _, _ in self.lay] for _ in range(W)]
         self.ediv = [None for _ in self.shapes]
@@ -160,8 +160,9 @@ class Sim:
             if self.signs:
                 wb = self.codec.sign_word_begin
                 PR.compare_signs(dec["Mstar"], shp, words[wb[i]:wb[i + 1]], cd,
-                                 where=f"{w.name} step {t} tensor {i} {shp} (signs)")
-                dec = {"X": O.apply_signs(self.X_or[i], O.pack_signs(dec["Mstar"]), eta=w.eta, lam=w.lam),
+                                 where=f"{w.name} step {t} tensor {i} {shp} (signs)", s=self.s)
+                dec = {"X": O.apply_signs(self.X_or[i], O.pack_signs(dec["Mstar"], self.s), eta=w.eta, lam=w.lam,
+                                          s=self.s),
                        "Mstar": dec["Mstar"]}
             self.ediv[i] = PR.compare_decode(dec, shp, w.phi, w.eta, self.X_gpu[i].cpu().numpy(), cd, self.ediv[i],
                                              where=f"{w.name} step {t} tensor {i} {shp}", s=self.s)
@@ -205,13 +206,16 @@ class Sim:
         torch.cuda.synchronize()
         probe = self.probe_mstar(avg_c, P0d, P1d, wire=True)
         wb = self.wire_bytes
-        used = 3 * ((ne + 1) // 2)
+        nbits = ne * O.wire_index_bits(self.s)
+        used = (nbits + 7) // 8
         codes, gidx = [], []
         for wk in range(W):
             blk = wi[wk * wb:(wk + 1) * wb]
             assert not blk[used:].any(), f"{w.name} step {t} worker {wk}: wire padding not zero"
+            if nbits % 8:
+                assert blk[used - 1] >> (nbits % 8) == 0, f"{w.name} step {t} worker {wk}: wire padding bits set"
             codes.append(wv[wk * ne:(wk + 1) * ne])
-            gidx.append(O.unpack_wire(wv[wk * ne:(wk + 1) * ne], blk, ne)[1])
+            gidx.append(O.unpack_wire(wv[wk * ne:(wk + 1) * ne], blk, ne, self.s)[1])
         for i, shp in enumerate(self.shapes):
             n, keff, e0 = self.lay[i]
             cd = self.xdiv[i].copy()
@@ -221,11 +225,12 @@ class Sim:
                 sl = slice(e0, e0 + n * keff)
                 self.xdiv[i] |= PR.compare_wire(or_vals[i][wk], or_idx[i][wk], or_q[i][wk],
                                                 codes[wk][sl].reshape(n, keff), gidx[wk][sl].reshape(n, keff), cd,
-                                                where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (wire)")
+                                                where=f"{w.name} step {t} worker {wk} tensor {i} {shp} (wire)",
+                                                noise=self.noise)
             cd |= self.xdiv[i]
             # the oracle decodes its own payload as the wire carries it: values rounded to bfloat16
-            vr = [O.unpack_wire(*O.pack_wire(or_vals[i][wk], or_idx[i][wk]), n * keff)[0].reshape(n, keff)
-                  for wk in range(W)]
+            vr = [O.unpack_wire(*O.pack_wire(or_vals[i][wk], or_idx[i][wk], self.s), n * keff, self.s)[0]
+                  .reshape(n, keff) for wk in range(W)]
             dec = O.decode_apply(self.X_or[i], np.stack(vr), np.stack(or_idx[i]), phi=w.phi, eta=w.eta, lam=w.lam,
                                  mode=self.avg, P0=P0, P1=P1, s=self.s)
             if probe is not None:
@@ -498,17 +503,33 @@ def test_one_bit_sign_download(dev, name, k, avg, rand):
     Sim(w, avg=avg, signs=True).run(3)
 
 
-def test_one_bit_sign_download_ragged_and_zero(dev):
+@pytest.mark.parametrize("shapes,k,avg,W", [
+    (((256, 384), (1000,)), 16, "count", 3),
+    (((128, 128), (300, 77), (129,)), 4, "workers", 2),
+    (((128, 256), (300,)), 200, "count", 20),      # keff > 64, several worker batches
+    (((256, 128),), 16384, "count", 2),            # lossless
+])
+def test_one_bit_sign_download_chunk128(dev, shapes, k, avg, W):
+    """The one-bit download at chunk edge 128: 256 words per matrix chunk (two per chunk row), two per
+    vector chunk; bits against the oracle's packing, parameters against the oracle's apply."""
+    w = DI.WORKLOADS["tiny_256"].replace(name=f"signs128_k{k}_W{W}", shapes=shapes, k=k, workers=W, phi="sign")
+    Sim(w, avg=avg, signs=True, chunk=128).run(3)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_one_bit_sign_download_ragged_and_zero(dev, chunk):
     """Tiny and ragged shapes plus an all-zero tensor (M* = 0 reads as +1 on both sides)."""
+    s = chunk
     w = DI.WORKLOADS["tiny_256"].replace(
-        name="signs_ragged", shapes=((1, 1), (2, 3), (65, 65), (64, 64), (1,), (63,), (130,)), k=5, workers=2)
+        name=f"signs_ragged_s{s}", shapes=((1, 1), (2, 3), (s + 1, s + 1), (s, s), (1,), (s - 1,), (2 * s + 2,),
+                                           (3 * s + 70,)), k=5, workers=2)
 
     def inputs(worker, step, i):
         if i == 3:
-            return np.zeros((64, 64), np.float32)
+            return np.zeros((s, s), np.float32)
         return DI.gradient(w, worker, step, i)
 
-    Sim(w, inputs=inputs, signs=True).run(2)
+    Sim(w, inputs=inputs, signs=True, chunk=chunk).run(2)
 
 
 def test_sign_download_on_zero_momentum_differs_from_signum_as_documented(dev):
@@ -548,10 +569,12 @@ def test_sign_download_on_zero_momentum_differs_from_signum_as_documented(dev):
     codec.close()
 
 
-def test_sign_download_matches_signum_decode(dev):
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_sign_download_matches_signum_decode(dev, chunk):
     """apply_signs(decode_signs(payloads)) equals decode_apply with phi = sign wherever M* != 0."""
-    w = DI.WORKLOADS["tiny_256"].replace(name="signs_vs_signum", shapes=((192, 256), (300,)), workers=3, k=12)
-    codec = B.Codec(w.shapes, w.k, w.beta, w.alpha)
+    shapes = ((192, 256), (300,)) if chunk == 64 else ((384, 300), (1000,))
+    w = DI.WORKLOADS["tiny_256"].replace(name="signs_vs_signum", shapes=shapes, workers=3, k=12)
+    codec = B.Codec(w.shapes, w.k, w.beta, w.alpha, chunk=chunk)
     v, ix = codec.alloc_payload(w.workers)
     ne = codec.n_entries
     for wk in range(w.workers):
@@ -626,11 +649,28 @@ def test_chunk128_degenerate(dev):
 
 # --------------------------------------------------------------------------- compact wire format
 
-@pytest.mark.parametrize("case", ["tiny", "ragged_k3", "k100_w20", "unit_identity_workers", "user_basis"])
+@pytest.mark.parametrize("case", ["tiny", "ragged_k3", "k100_w20", "unit_identity_workers", "user_basis",
+                                  "s128_tiny", "s128_ragged", "s128_k200_w20", "s128_unit_workers"])
 def test_wire_end_to_end(dev, case):
-    """Encode, pack into the wire format, decode from it; the oracle decodes its own payload rounded the same way."""
+    """Encode, pack into the wire format, decode from it; the oracle decodes its own payload rounded the same way.
+    At chunk edge 128 the positions take 14 bits."""
     base = DI.WORKLOADS["tiny_256"]
     kw = {}
+    if case.startswith("s128"):
+        kw["chunk"] = 128
+        if case == "s128_tiny":
+            w = base.replace(name="wire128_tiny", shapes=((256, 384), (300,)), workers=3, k=16)
+        elif case == "s128_ragged":
+            w = base.replace(name="wire128_ragged", shapes=((1, 1), (129, 130), (300, 77), (127,), (5000,)), k=5,
+                             workers=3)
+        elif case == "s128_k200_w20":  # keff > 64 and more than one worker batch
+            w = base.replace(name="wire128_k200_w20", shapes=((128, 256), (300,)), k=200, workers=20)
+        else:
+            w = base.replace(name="wire128_unit", shapes=((256, 300), (257,)), grad_std=1.0, param_std=1.0, beta=0.9,
+                             k=16, workers=3, eta=0.01, phi="identity")
+            kw.update(plain=True, avg="workers")
+        Sim(w, wire=True, **kw).run(3)
+        return
     if case == "tiny":
         w = base.replace(name="wire_tiny", workers=3)
     elif case == "ragged_k3":
@@ -646,21 +686,24 @@ def test_wire_end_to_end(dev, case):
     Sim(w, wire=True, **kw).run(3)
 
 
-def _lay_chunks(shapes, k):
-    return [(n, keff, 4096 if len(s) == 2 else 64) for (n, keff, _), s in zip(PR.layout(shapes, k), shapes)]
+def _lay_chunks(shapes, k, s=64):
+    return [(n, keff, s * s if len(sh) == 2 else s) for (n, keff, _), sh in zip(PR.layout(shapes, k, s), shapes)]
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("shapes,k,workers", [
     (((256, 256),), 8, 2),
     (((1000, 777), (3, 5000), (777,), (1,)), 3, 5),   # odd entry counts, vectors, ragged chunks
     (((64, 64),), 1, 1),                               # one entry
     (((130, 70), (63,)), 37, 17),
+    (((256, 128),), 15, 3),                            # entry counts that are not whole groups at either width
 ])
-def test_wire_pack_bit_exact(dev, shapes, k, workers):
-    """The pack kernel against the oracle's format on drawn payloads full of rounding edge cases."""
-    codec = B.Codec(shapes, k)
+def test_wire_pack_bit_exact(dev, shapes, k, workers, chunk):
+    """The pack kernel against the oracle's format on drawn payloads full of rounding edge cases: 12-bit
+    positions at chunk edge 64, 14-bit at 128 (indices drawn over the whole 128x128 chunk)."""
+    codec = B.Codec(shapes, k, chunk=chunk)
     ne = codec.n_entries
-    vals, idx = DI.synthetic_payload(_lay_chunks(shapes, k), workers, seed=40 + k, specials=True)
+    vals, idx = DI.synthetic_payload(_lay_chunks(shapes, k, chunk), workers, seed=40 + k, specials=True)
     assert vals.size == workers * ne
     wv, wi = codec.alloc_wire(workers)
     wv.fill_(-1)
@@ -670,9 +713,9 @@ def test_wire_pack_bit_exact(dev, shapes, k, workers):
     torch.cuda.synchronize()
     gv = wv.cpu().numpy().view(np.uint16)
     gb = wi.cpu().numpy()
-    ib = B.demo_wire_size(ne)[1]
+    ib = B.demo_wire_size(ne, chunk)[1]
     for wk in range(workers):
-        ov, ob = O.pack_wire(vals[wk * ne:(wk + 1) * ne], idx[wk * ne:(wk + 1) * ne])
+        ov, ob = O.pack_wire(vals[wk * ne:(wk + 1) * ne], idx[wk * ne:(wk + 1) * ne], chunk)
         assert np.array_equal(gv[wk * ne:(wk + 1) * ne], ov), f"worker {wk}: value codes differ"
         blk = gb[wk * ib:(wk + 1) * ib]
         assert np.array_equal(blk[:ob.size], ob), f"worker {wk}: index bytes differ"
@@ -680,16 +723,17 @@ def test_wire_pack_bit_exact(dev, shapes, k, workers):
     codec.close()
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("phi,avg", [("sign", "count"), ("identity", "workers")])
-def test_wire_decode_synthetic(dev, phi, avg):
+def test_wire_decode_synthetic(dev, phi, avg, chunk):
     """decode_apply_wire on drawn payloads against the oracle's decode of the same wire; and bit-equal to
     decode_apply given the same values rounded to bfloat16 (same arithmetic, same order)."""
-    shapes = ((200, 130), (1000,), (64, 64), (5,))
+    shapes = ((200, 130), (1000,), (64, 64), (5,)) if chunk == 64 else ((300, 260), (1000,), (128, 128), (5,))
     k, W = 12, 6
     w = DI.WORKLOADS["tiny_256"].replace(name="wire_synth", shapes=shapes, k=k, workers=W, phi=phi)
-    codec = B.Codec(shapes, k)
+    codec = B.Codec(shapes, k, chunk=chunk)
     ne = codec.n_entries
-    vals, idx = DI.synthetic_payload(_lay_chunks(shapes, k), W, seed=77)
+    vals, idx = DI.synthetic_payload(_lay_chunks(shapes, k, chunk), W, seed=77)
     vd, idd = torch.from_numpy(vals).cuda(), torch.from_numpy(idx.view(np.int16)).cuda()
     wv, wi = codec.alloc_wire(W)
     codec.pack_wire(W, vd, idd, wv, wi)
@@ -702,17 +746,18 @@ def test_wire_decode_synthetic(dev, phi, avg):
     vr = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).cuda()  # torch's own round-to-nearest-even
     codec.decode_apply(Xf, W, vr, idd, phi_c, w.eta, w.lam, avg_c)
     torch.cuda.synchronize()
-    lay = PR.layout(shapes, k)
+    lay = PR.layout(shapes, k, chunk)
     for i, shp in enumerate(shapes):
         n, keff, e0 = lay[i]
         ov, oi = [], []
         for wk in range(W):
             sl = slice(wk * ne + e0, wk * ne + e0 + n * keff)
-            v_, i_ = O.unpack_wire(*O.pack_wire(vals[sl], idx[sl]), n * keff)
+            v_, i_ = O.unpack_wire(*O.pack_wire(vals[sl], idx[sl], chunk), n * keff, chunk)
             ov.append(v_.reshape(n, keff))
             oi.append(i_.reshape(n, keff))
-        dec = O.decode_apply(X0[i], np.stack(ov), np.stack(oi), phi=phi, eta=w.eta, lam=w.lam, mode=avg)
+        dec = O.decode_apply(X0[i], np.stack(ov), np.stack(oi), phi=phi, eta=w.eta, lam=w.lam, mode=avg, s=chunk)
         gx = Xw[i].cpu().numpy()
-        PR.compare_decode(dec, shp, phi, w.eta, gx, np.zeros(n, bool), None, where=f"wire synthetic tensor {i} {shp}")
+        PR.compare_decode(dec, shp, phi, w.eta, gx, np.zeros(n, bool), None, where=f"wire synthetic tensor {i} {shp}",
+                          s=chunk)
         assert np.array_equal(gx, Xf[i].cpu().numpy()), f"tensor {i}: wire decode differs from the float32 decode"
     codec.close()
