@@ -58,14 +58,14 @@ def parse():
     ap.add_argument("--subtraction", default="local", choices=("local", "aggregated"),
                     help="momentum subtraction of the worker's own coefficients, or of the averaged ones")
     ap.add_argument("--chunk", type=int, default=64, choices=(64, 128),
-                    help="chunk edge s (128: DCT basis, apply download)")
+                    help="chunk edge s (128: DCT basis)")
     ap.add_argument("--phi", default=None, choices=("muon",),
                     help="override the workload's phi: muon runs decode + Newton-Schulz phi on every whole tensor")
     ap.add_argument("--muon-iters", type=int, default=24, help="Newton-Schulz iterations of the Muon phi")
     ap.add_argument("--download", default="apply", choices=("apply", "signs", "wire"),
                     help="apply: decode/apply in one kernel; signs: the Signum variant's one-bit download, "
                          "decode to packed sign bits then apply them (phi = sign); wire: this worker's payload "
-                         "packed into the compact wire format (bfloat16 values, 12-bit indices), the decode "
+                         "packed into the compact wire format (bfloat16 values, 12- or 14-bit positions), the decode "
                          "reading all W payloads in that format")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every call eagerly instead of replaying a captured HIP graph of the step")
@@ -348,7 +348,7 @@ def gpu_bench(w: DI.Workload, steps: int, warmup: int, copy_probe: bool = False,
     signs = codec.alloc_signs() if download == "signs" else None
     if download == "wire":  # the other workers' payloads arrive packed; this worker packs its own in the step
         wv, wi = codec.alloc_wire(W)
-        wb = B.demo_wire_size(ne)[1]
+        wb = B.demo_wire_size(ne, chunk)[1]
         codec.pack_wire(W, vals, pidx, wv, wi)
         torch.cuda.synchronize()
     muon_ws = codec.alloc_muon_workspace() if muon_iters else None
@@ -474,16 +474,16 @@ def main():
                                    or args.phi):
         print("--basis random runs with chunk 64, the apply download and the local subtraction", file=sys.stderr)
         sys.exit(2)
-    if args.chunk == 128 and (args.basis != "dct" or args.download != "apply"):
-        print("--chunk 128 is built for the DCT basis and the apply download", file=sys.stderr)
+    if args.chunk == 128 and args.basis != "dct":
+        print("--chunk 128 is built for the DCT basis", file=sys.stderr)
         sys.exit(2)
     if args.phi == "muon":
         if args.download != "apply" or args.subtraction != "local" or args.chunk != 64:
             print("--phi muon runs with the apply download, the local subtraction and chunk 64", file=sys.stderr)
             sys.exit(2)
         w = w.replace(phi="muon")
-    if args.download == "wire" and (args.subtraction != "local" or args.chunk != 64):
-        print("--download wire runs with the local subtraction and chunk 64", file=sys.stderr)
+    if args.download == "wire" and args.subtraction != "local":
+        print("--download wire runs with the local subtraction", file=sys.stderr)
         sys.exit(2)
     if args.download == "signs":
         if args.subtraction != "local":

@@ -44,6 +44,38 @@ __device__ __forceinline__ float load_src(const void* p, int64_t off) {
   }
 }
 
+// Rows of one chunk through buffer instructions: the chunk origin sits in a
+// buffer resource (scalar registers), row i is the scalar offset i * ldb and
+// the lane's column the vector offset, so a row access needs no vector
+// address arithmetic (a global access would spend a 64-bit vector add per
+// row).  Offsets are 32-bit: usable while the chunk's rows span fewer than
+// 2^31 bytes (buf_rows_fit); the range check of the resource is left open,
+// addresses stay inside the tensor as with the global accesses.
+struct RowBuf {
+  __amdgpu_buffer_rsrc_t r;
+  int32_t ldb;  // row stride in bytes
+};
+constexpr int kBufNt = 2;                 // cache policy: non-temporal
+constexpr int kBufWord3 = 0x00020000;     // resource word 3: 32-bit data format
+__device__ __forceinline__ bool buf_rows_fit(int64_t rows, int64_t ld_bytes) {
+  return rows * ld_bytes < (int64_t(1) << 31);
+}
+__device__ __forceinline__ RowBuf row_buf(const void* base, int64_t ld_bytes) {
+  RowBuf b;
+  b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufWord3);
+  b.ldb = int32_t(ld_bytes);
+  return b;
+}
+__device__ __forceinline__ float buf_load_f32(const RowBuf& b, int row, int32_t voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(b.r, voff, row * b.ldb, kBufNt));
+}
+__device__ __forceinline__ float buf_load_bf16(const RowBuf& b, int row, int32_t voff) {
+  return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(b.r, voff, row * b.ldb, kBufNt)) << 16);
+}
+__device__ __forceinline__ void buf_store_f32(const RowBuf& b, int row, int32_t voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), b.r, voff, row * b.ldb, kBufNt);
+}
+
 __device__ __forceinline__ float sign_of(float m) { return m > 0.f ? 1.f : (m < 0.f ? -1.f : 0.f); }
 
 __device__ __forceinline__ void stream_store(uint64_t v, uint64_t* p) { __builtin_nontemporal_store(v, p); }

@@ -98,9 +98,27 @@ __device__ __forceinline__ ChunkPos chunk_pos(const TensorSlot& ts, int item) {
 template <bool kFull>
 __device__ __forceinline__ void store_rows(const float (&q)[64], float* __restrict__ dst, int64_t ld,
                                            const ChunkPos& c, int lane) {
+  if (kFull && buf_rows_fit(64, ld * 4)) {
+    const RowBuf b = row_buf(dst, ld * 4);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) buf_store_f32(b, i, lane * 4, q[i]);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     if (kFull || (lane < c.vc && i < c.vr)) stream_store(q[i], &dst[i * ld + lane]);
+  }
+}
+
+// Rows 0..63 of a full chunk at src (row stride ld), lane = column.
+__device__ __forceinline__ void load_rows_full(float (&x)[64], const float* __restrict__ src, int64_t ld, int lane) {
+  if (buf_rows_fit(64, ld * 4)) {
+    const RowBuf b = row_buf(src, ld * 4);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = buf_load_f32(b, i, lane * 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = stream_load(&src[i * ld + lane]);
   }
 }
 
@@ -112,6 +130,15 @@ __device__ __forceinline__ void load_momentum(float (&q)[64], const TensorSlot& 
   const int64_t ld = ts.cols;
   const float* __restrict__ m = ts.dst + c.base;
   const char* __restrict__ g = static_cast<const char*>(ts.aux) + c.base * (kBf16 ? 2 : 4);
+  if (kFull && buf_rows_fit(64, ld * 4)) {
+    const RowBuf bm = row_buf(m, ld * 4), bg = row_buf(g, ld * (kBf16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float gv = kBf16 ? buf_load_bf16(bg, i, lane * 2) : buf_load_f32(bg, i, lane * 4);
+      q[i] = fmaf(beta, buf_load_f32(bm, i, lane * 4), gcoef * gv);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     float gv = 0.f, mv = 0.f;
@@ -445,11 +472,16 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   // rows follow the transform (a second wave per SIMD hides them instead)
   constexpr bool kEarlyX = !Basis::kMatrixCores;
   float x[64], m[64];
+  if (c.full) {
+    if constexpr ((kTargets & kToParams) != 0 && kEarlyX) load_rows_full(x, xp, ld, lane);
+    if constexpr (kEarlyM) load_rows_full(m, mp, ld, lane);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const int64_t row = int64_t(min(i, c.vr - 1)) * ld;
-    if constexpr ((kTargets & kToParams) != 0 && kEarlyX) x[i] = stream_load(&(xp + row)[col]);
-    if constexpr (kEarlyM) m[i] = stream_load(&(mp + row)[col]);
+    for (int i = 0; i < 64; ++i) {
+      const int64_t row = int64_t(min(i, c.vr - 1)) * ld;
+      if constexpr ((kTargets & kToParams) != 0 && kEarlyX) x[i] = stream_load(&(xp + row)[col]);
+      if constexpr (kEarlyM) m[i] = stream_load(&(mp + row)[col]);
+    }
   }
 
   clear_acc(reinterpret_cast<uint32_t*>(acc), lane);
@@ -480,8 +512,12 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
 
   if constexpr ((kTargets & kToParams) != 0) {
     if constexpr (!kEarlyX) {
+      if (c.full) {
+        load_rows_full(x, xp, ld, lane);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = stream_load(&(xp + int64_t(min(i, c.vr - 1)) * ld)[col]);
+        for (int i = 0; i < 64; ++i) x[i] = stream_load(&(xp + int64_t(min(i, c.vr - 1)) * ld)[col]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
@@ -492,8 +528,12 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
   }
   if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
     if constexpr (!kEarlyM) {
+      if (c.full) {
+        load_rows_full(m, mp, ld, lane);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) m[i] = stream_load(&(mp + int64_t(min(i, c.vr - 1)) * ld)[col]);
+        for (int i = 0; i < 64; ++i) m[i] = stream_load(&(mp + int64_t(min(i, c.vr - 1)) * ld)[col]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 64; ++i) m[i] = fmaf(-p.alpha, q[i], m[i]);
@@ -696,9 +736,15 @@ __global__ __launch_bounds__(64) void apply_signs_kernel(LaunchTable tab, ApplyP
   float* __restrict__ xp = ts.dst + c.base;
   const int64_t ld = ts.cols;
   const int col = min(lane, c.vc - 1);
+  // all 64 rows are requested before the first store (a store may alias a
+  // later row as far as the compiler knows, so loads are not moved past it)
   float x[64];
+  if (c.full) {
+    load_rows_full(x, xp, ld, lane);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[min(i, c.vr - 1) * ld + col]);
+    for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[min(i, c.vr - 1) * ld + col]);
+  }
 #pragma unroll
   for (int i = 0; i < 64; ++i) x[i] = apply_bit(x[i], wp[i], lane, p);
   if (c.full)

@@ -226,6 +226,10 @@ __device__ __forceinline__ Chunk128 chunk_pos128(const TensorSlot& ts, int item)
   return c;
 }
 
+// The workgroup's wave number, in a scalar register (the compiler cannot see
+// that threadIdx.x >> 6 is the same on every lane of a wave).
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)); }
+
 // quadrant coordinates -> chunk coordinates
 __device__ __forceinline__ int quad_row(int qa, int i) { return qa ? (kS - 1 - i) : i; }
 
@@ -568,11 +572,33 @@ __device__ __forceinline__ int64_t quad_origin(int q, int lane, int64_t ld) {
 }
 __device__ __forceinline__ int64_t quad_step(int q, int64_t ld) { return (q >> 1) ? -ld : ld; }
 
+// Quadrant q's row i of a full chunk through buffer instructions: chunk row
+// quad_row(q >> 1, i) (a scalar offset; q is wave-uniform), the lane's
+// column (q & 1 ? 127 - lane : lane) the vector offset.
+__device__ __forceinline__ void load_quad_rows(float (&x)[64], const float* __restrict__ chunk, int64_t ld, int q,
+                                               int lane) {
+  const RowBuf b = row_buf(chunk, ld * 4);
+  const int col = (q & 1) ? kS - 1 - lane : lane;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) x[i] = buf_load_f32(b, quad_row(q >> 1, i), col * 4);
+}
+
 template <bool kFull, bool kBf16, bool kKeep = false>
 __device__ __forceinline__ void load_quadrant(float (&x)[64], const TensorSlot& ts, const Chunk128& c, int q,
                                               int lane, float beta, float gcoef) {
   const int64_t ld = ts.cols, step = quad_step(q, ld), o = c.base + quad_origin(q, lane, ld);
   const int col = (q & 1) ? kS - 1 - lane : lane;
+  if (kFull && !kKeep && buf_rows_fit(kS, ld * 4)) {
+    const RowBuf bm = row_buf(ts.dst + c.base, ld * 4);
+    const RowBuf bg = row_buf(static_cast<const char*>(ts.aux) + c.base * (kBf16 ? 2 : 4), ld * (kBf16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int r = quad_row(q >> 1, i);
+      const float gv = kBf16 ? buf_load_bf16(bg, r, col * 2) : buf_load_f32(bg, r, col * 4);
+      x[i] = fmaf(beta, buf_load_f32(bm, r, col * 4), gcoef * gv);
+    }
+    return;
+  }
   const float* __restrict__ m = ts.dst + o;
   const char* __restrict__ g = static_cast<const char*>(ts.aux) + o * (kBf16 ? 2 : 4);
 #pragma unroll
@@ -591,6 +617,12 @@ __device__ __forceinline__ void store_quadrant(const float (&x)[64], float* __re
                                                const Chunk128& c, int q, int lane) {
   const int64_t step = quad_step(q, ld);
   const int col = (q & 1) ? kS - 1 - lane : lane;
+  if (kFull && buf_rows_fit(kS, ld * 4)) {
+    const RowBuf b = row_buf(dst, ld * 4);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) buf_store_f32(b, quad_row(q >> 1, i), col * 4, x[i]);
+    return;
+  }
   float* __restrict__ d = dst + quad_origin(q, lane, ld);
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
@@ -601,7 +633,7 @@ __device__ __forceinline__ void store_quadrant(const float (&x)[64], float* __re
 template <bool kBf16, bool kSmallK>
 __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const EncodeParams& p, float* lds,
                                                  uint32_t* scr) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_index(), lane = threadIdx.x & 63;
   const int a = w >> 1, b = w & 1;
   const Chunk128 c = chunk_pos128(ts, blockIdx.x);
   float* __restrict__ mdst = ts.dst + c.base;
@@ -676,7 +708,7 @@ __device__ __forceinline__ void pair_unbutterfly(float (&y)[64], int h) {
 
 template <bool kBf16>
 __device__ __forceinline__ void encode_vector128(const TensorSlot& ts, const EncodeParams& p, float* lds) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_index(), lane = threadIdx.x & 63;
   const int slab = blockIdx.x - ts.item_begin;
   const int chunk0 = slab * kVecChunksPerItem + w * kVecChunksPerWave;  // this wave's first chunk
   const int64_t first = int64_t(chunk0) * kS + lane;  // column layout: x[r] = element first + 64 r
@@ -769,7 +801,10 @@ template <int kTargets>
 __device__ __forceinline__ void decode_rows128(float (&x)[64], float (&m)[64], const float* __restrict__ xp,
                                                const float* __restrict__ mp, int64_t ld, const Chunk128& c, int q,
                                                int lane, int col) {
-  if (c.full) {
+  if (c.full && buf_rows_fit(kS, ld * 4)) {
+    if constexpr ((kTargets & kToParams) != 0) load_quad_rows(x, xp, ld, q, lane);
+    if constexpr (kTargets == kToMomentum) load_quad_rows(m, mp, ld, q, lane);
+  } else if (c.full) {
     const int64_t o = quad_origin(q, lane, ld), step = quad_step(q, ld);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
@@ -801,7 +836,7 @@ __device__ __forceinline__ void load_entry128(const DecodeParams& p, int64_t w, 
 
 template <int kTargets, bool kWire>
 __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_index(), lane = threadIdx.x & 63;
   const int a = w >> 1, b = w & 1;
   const Chunk128 c = chunk_pos128(ts, blockIdx.x);
   float* acc = reinterpret_cast<float*>(lds);
@@ -930,7 +965,9 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   }
   if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
     if constexpr (kTargets != kToMomentum) {
-      if (c.full) {
+      if (c.full && buf_rows_fit(kS, ld * 4)) {
+        load_quad_rows(m, mp, ld, w, lane);
+      } else if (c.full) {
         const int64_t o = quad_origin(w, lane, ld), step = quad_step(w, ld);
 #pragma unroll
         for (int i = 0; i < 64; ++i) m[i] = stream_load(&mp[o + i * step]);
@@ -953,7 +990,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
 // c & 3 of word g*32 + ((c >> 2) ^ g).
 template <int kTargets, bool kWire>
 __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_index(), lane = threadIdx.x & 63;
   constexpr int kWaveWords = kDecLdsWords / 4;
   static_assert(kVecChunksPerWave * kS + kVecChunksPerWave * kS / 4 <= kWaveWords && kTile <= kWaveWords,
                 "per-wave vector LDS");
@@ -1069,7 +1106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 // wave-uniform (scalar) loads.
 __global__ __launch_bounds__(256) void apply_signs128_kernel(LaunchTable tab, ApplyParams p) {
   const TensorSlot& ts = tab.t[find_tensor(tab, blockIdx.x)];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_index(), lane = threadIdx.x & 63;
   const uint64_t* __restrict__ words = static_cast<const uint64_t*>(ts.aux);
   if (ts.cols == 0) {
     const int slab = blockIdx.x - ts.item_begin;
@@ -1094,18 +1131,33 @@ __global__ __launch_bounds__(256) void apply_signs128_kernel(LaunchTable tab, Ap
   const uint64_t* __restrict__ wp = words + int64_t(c.local) * 256 + 2 * 64 * rb + h;
   const int64_t ld = ts.cols;
   float* __restrict__ xp = ts.dst + c.base + int64_t(64 * rb) * ld + 64 * h;
-  const int col = min(lane, vc - 1);
+  // all 64 rows are requested before the first store (a store may alias a
+  // later row as far as the compiler knows, so loads are not moved past it)
   float x[64];
+  const bool full = vr == 64 && vc == 64 && buf_rows_fit(64, ld * 4);
+  const int col = min(lane, vc - 1);
+  if (full) {
+    const RowBuf b = row_buf(xp, ld * 4);
 #pragma unroll
-  for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[min(i, vr - 1) * ld + col]);
+    for (int i = 0; i < 64; ++i) x[i] = buf_load_f32(b, i, lane * 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = stream_load(&xp[min(i, vr - 1) * ld + col]);
+  }
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     const float s = ((wp[2 * i] >> lane) & 1u) ? -1.f : 1.f;
     x[i] = fmaf(-p.eta, fmaf(p.lam, x[i], s), x[i]);
   }
+  if (full) {
+    const RowBuf b = row_buf(xp, ld * 4);
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    if (lane < vc && i < vr) stream_store(x[i], &xp[i * ld + lane]);
+    for (int i = 0; i < 64; ++i) buf_store_f32(b, i, lane * 4, x[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (lane < vc && i < vr) stream_store(x[i], &xp[i * ld + lane]);
+    }
   }
 }
 

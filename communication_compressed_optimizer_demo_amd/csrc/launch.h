@@ -68,7 +68,8 @@ struct DecodeParams {
   int32_t write_mstar;  // 1: write M* itself (the Muon path applies phi afterwards)
   float alpha;
   // compact wire payload (read instead of pay_val / pay_idx when wire is 1):
-  // bfloat16 values and 12-bit indices in a little-endian bit string,
+  // bfloat16 values and 12-bit (chunk edge 64) or 14-bit (128) positions in
+  // a little-endian bit string,
   // wire_words 32-bit words per worker
   int32_t wire;
   const uint16_t* wire_val;
