@@ -20,7 +20,7 @@ def run_bench(*args):
     (["--gpus", "2"], "one GPU only"),
     (["--gpus", "8", "--steps", "3"], "one GPU only"),
     (["--chunk", "128", "--basis", "identity"], "chunk 128"),
-    (["--chunk", "128", "--download", "signs"], "chunk 128"),
+    (["--chunk", "128", "--phi", "muon"], "phi muon"),
     (["--basis", "random", "--chunk", "128"], "basis random"),
     (["--basis", "random", "--subtraction", "aggregated"], "basis random"),
     (["--phi", "muon", "--download", "signs"], "phi muon"),
