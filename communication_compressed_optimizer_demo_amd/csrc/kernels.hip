@@ -709,14 +709,17 @@ __device__ __forceinline__ float apply_bit(float x, uint64_t word, int bit, cons
   return fmaf(-p.eta, fmaf(p.lam, x, s), x);
 }
 
-// Same work items as the decode: a 64x64 chunk (word i = row i, bit j =
-// column j = lane j) or a slab of 64 vector chunks (word c = chunk c, bit j =
-// element j = lane j).  The word index is wave-uniform, so the words arrive
-// through scalar loads while the rows stream through vector loads.
-__global__ __launch_bounds__(64) void apply_signs_kernel(LaunchTable tab, ApplyParams p) {
-  const int item = xcd_item(blockIdx.x, gridDim.x);
+// Same work items as the decode, four to a workgroup (one per wave): a
+// 64x64 chunk (word i = row i, bit j = column j = lane j) or a slab of 64
+// vector chunks (word c = chunk c, bit j = element j = lane j).  The word
+// index is wave-uniform, so the words arrive through scalar loads while the
+// rows stream through vector loads.
+__global__ __launch_bounds__(256) void apply_signs_kernel(LaunchTable tab, ApplyParams p) {
+  // four items per workgroup, one per wave
+  const int item = xcd_item(blockIdx.x, gridDim.x) * 4 + int(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+  if (item >= tab.items) return;
   const TensorSlot& ts = tab.t[find_tensor(tab, item)];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const uint64_t* __restrict__ words = static_cast<const uint64_t*>(ts.aux);
   if (ts.cols == 0) {
     const int slab = item - ts.item_begin;
@@ -821,7 +824,7 @@ hipError_t launch_pack_wire(int32_t bits, const float* pay_val, const uint16_t* 
 
 hipError_t launch_apply_signs(const LaunchTable& tab, const ApplyParams& p, hipStream_t stream) {
   if (tab.items <= 0) return hipSuccess;
-  apply_signs_kernel<<<dim3(tab.items), dim3(64), 0, stream>>>(tab, p);
+  apply_signs_kernel<<<dim3((tab.items + 3) / 4), dim3(256), 0, stream>>>(tab, p);
   return hipGetLastError();
 }
 
