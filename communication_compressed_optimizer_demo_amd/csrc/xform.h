@@ -67,6 +67,9 @@ constexpr double cospi(long p, long q) {
 // sin(pi p / q) = cos(pi (2p - q) / (2q))
 constexpr double sinpi(long p, long q) { return cospi(2 * p - q, 2 * q); }
 
+// tan(theta / 2) = sin(theta) / (1 + cos(theta)), theta = pi p / q in [0, pi/2]
+constexpr double tanhalfpi(long p, long q) { return sinpi(p, q) / (1.0 + cospi(p, q)); }
+
 constexpr double csqrt(double v) {
   double r = v > 1.0 ? v : 1.0;
   for (int i = 0; i < 64; ++i) r = 0.5 * (r + v / r);
@@ -127,10 +130,36 @@ __host__ __device__ __forceinline__ void fft(float (&re)[L], float (&im)[L]) {
         tr = oi[k];
         ti = -orr[k];
       } else {
-        constexpr float c = float(cospi(2 * k, L));
-        constexpr float s = float(sinpi(2 * k, L));
-        tr = fmaf(orr[k], c, oi[k] * s);
-        ti = fmaf(oi[k], c, -(orr[k] * s));
+        // (orr + i oi) exp(-i theta), theta = 2 pi k / L, folded into the
+        // butterfly: with theta = phi (k < L/4) or phi + pi/2 (a free factor
+        // -i), and g = cos phi, w = tan phi for phi <= pi/4, else g = sin phi,
+        // w = cot phi, the product is g (p + i q) with p, q one FMA each;
+        // the four outputs are then one FMA each (6 instead of 8).
+        constexpr bool kRot = 4 * k > L;  // theta > pi/2
+        constexpr int k2 = kRot ? k - L / 4 : k;  // phi = 2 pi k2 / L
+        constexpr bool kLow = 8 * k2 <= L;        // phi <= pi/4
+        constexpr float g = float(kLow ? cospi(2 * k2, L) : sinpi(2 * k2, L));
+        constexpr float w = float(kLow ? sinpi(2 * k2, L) / cospi(2 * k2, L) : cospi(2 * k2, L) / sinpi(2 * k2, L));
+        float p, q;
+        if constexpr (kLow) {
+          p = fmaf(w, oi[k], orr[k]);
+          q = fmaf(-w, orr[k], oi[k]);
+        } else {
+          p = fmaf(w, orr[k], oi[k]);
+          q = fmaf(w, oi[k], -orr[k]);
+        }
+        if constexpr (kRot) {  // times -i: (p, q) -> (q, -p)
+          re[k] = fmaf(g, q, er[k]);
+          re[k + H] = fmaf(-g, q, er[k]);
+          im[k] = fmaf(-g, p, ei[k]);
+          im[k + H] = fmaf(g, p, ei[k]);
+        } else {
+          re[k] = fmaf(g, p, er[k]);
+          re[k + H] = fmaf(-g, p, er[k]);
+          im[k] = fmaf(g, q, ei[k]);
+          im[k + H] = fmaf(-g, q, ei[k]);
+        }
+        return;
       }
       re[k] = er[k] + tr;
       im[k] = ei[k] + ti;
@@ -141,6 +170,18 @@ __host__ __device__ __forceinline__ void fft(float (&re)[L], float (&im)[L]) {
 }
 
 // ---------------------------------------------------------------- DCT-IV
+
+// (u, v) = (a cos t + b sin t, b cos t - a sin t), t = pi P / Q in (0, pi/2):
+// the rotation as three shears (lifting steps) of tan(t/2), sin(t),
+// tan(t/2), each one FMA.
+template <long P, long Q>
+__host__ __device__ __forceinline__ void rotate_lift(float a, float b, float& u, float& v) {
+  constexpr float h = float(tanhalfpi(P, Q));
+  constexpr float s = float(sinpi(P, Q));
+  const float x1 = fmaf(h, b, a);
+  v = fmaf(-s, x1, b);
+  u = fmaf(h, v, x1);
+}
 
 // y[m] = Pre*Post * sum_n x[n] cos(pi (2n+1)(2m+1) / (4M)).
 // Pre and Post are scale tags; only their product matters mathematically,
@@ -161,11 +202,17 @@ __host__ __device__ __forceinline__ void dct4(float (&x)[M]) {
     float re[L], im[L];
     sfor<0, L>([&](auto I) {
       constexpr int n = decltype(I)::value;
-      constexpr float c = float(Pre::v * cospi(4 * n + 1, 4 * M));
-      constexpr float s = float(Pre::v * sinpi(4 * n + 1, 4 * M));
       const float a = x[2 * n], b = x[M - 1 - 2 * n];
-      re[n] = fmaf(a, c, b * s);
-      im[n] = fmaf(b, c, -(a * s));
+      if constexpr (Pre::v == 1.0) {
+        // unscaled rotation by theta < pi/2 as three lifting steps
+        // (tan(theta/2), sin(theta), tan(theta/2)): 3 FMAs instead of 4 ops
+        rotate_lift<4 * n + 1, 4 * M>(a, b, re[n], im[n]);
+      } else {
+        constexpr float c = float(Pre::v * cospi(4 * n + 1, 4 * M));
+        constexpr float s = float(Pre::v * sinpi(4 * n + 1, 4 * M));
+        re[n] = fmaf(a, c, b * s);
+        im[n] = fmaf(b, c, -(a * s));
+      }
     });
     fft<L>(re, im);
     sfor<0, L>([&](auto I) {
@@ -181,6 +228,8 @@ __host__ __device__ __forceinline__ void dct4(float (&x)[M]) {
           ur = re[0] * c;
           ui = im[0] * c;
         }
+      } else if constexpr (Post::v == 1.0) {
+        rotate_lift<k, M>(re[k], im[k], ur, ui);
       } else {
         ur = fmaf(re[k], c, im[k] * s);
         ui = fmaf(im[k], c, -(re[k] * s));

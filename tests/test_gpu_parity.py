@@ -518,7 +518,12 @@ def test_one_bit_sign_download_chunk128(dev, shapes, k, avg, W):
 
 @pytest.mark.parametrize("chunk", [64, 128])
 def test_one_bit_sign_download_ragged_and_zero(dev, chunk):
-    """Tiny and ragged shapes plus an all-zero tensor (M* = 0 reads as +1 on both sides)."""
+    """Tiny and ragged shapes plus an all-zero tensor (M* = 0 reads as +1 on both sides).
+
+    A 1x1 tensor is a single element in its chunk, so Q[u][v] = x P[u][0] P[v][0] = Q[v][u]: every
+    off-diagonal magnitude ties exactly with its transpose, and float32 rounding breaks each tie either
+    way on either side.  Those chunks take the tie window (every GPU set is checked to be a valid top-k
+    set), so this test allows a tenth of its 64-68 chunks to do so."""
     s = chunk
     w = DI.WORKLOADS["tiny_256"].replace(
         name=f"signs_ragged_s{s}", shapes=((1, 1), (2, 3), (s + 1, s + 1), (s, s), (1,), (s - 1,), (2 * s + 2,),
@@ -529,7 +534,7 @@ def test_one_bit_sign_download_ragged_and_zero(dev, chunk):
             return np.zeros((s, s), np.float32)
         return DI.gradient(w, worker, step, i)
 
-    Sim(w, inputs=inputs, signs=True, chunk=chunk).run(2)
+    Sim(w, inputs=inputs, signs=True, chunk=chunk).run(2, max_tie_fraction=0.1)
 
 
 def test_sign_download_on_zero_momentum_differs_from_signum_as_documented(dev):
