@@ -89,6 +89,10 @@ WORKLOADS = {
     # padded chunks, 1-D vectors of awkward lengths, extreme k
     "edge_mix": Workload("edge_mix", 5, ((1000, 777), (3, 5000), (777,), (1000,), (64,), (1,)),
                          1e-3, False, 0.999, 0.2, 1, 4, PHI_SIGN, 1e-3, 0.01, 3),
+    # rows of 2^23 and 2^22 floats: 64 rows of the first (128 of the second) span 2^31 bytes, past what the
+    # kernels' 32-bit buffer offsets cover, so their full chunks take the 64-bit-address path
+    "wide_rows": Workload("wide_rows", 6, ((64, 1 << 23), (128, 1 << 22)), 1e-3, False,
+                          0.999, 0.2, 8, 2, PHI_SIGN, 1e-3, 0.01, 2),
 }
 
 

@@ -83,13 +83,16 @@ def wire_entries(wv: torch.Tensor, wi: torch.Tensor, wire_bytes: int, ne: int, w
 
 @pytest.mark.parametrize("name,s,wire,rand", [("olmo_300m", 64, False, False), ("olmo_1b", 64, False, False),
                                               ("olmo_1b", 128, False, False), ("olmo_1b", 64, True, False),
-                                              ("olmo_1b", 64, False, True), ("single_4096", 64, False, False)])
+                                              ("olmo_1b", 64, False, True), ("single_4096", 64, False, False),
+                                              ("wide_rows", 64, False, False), ("wide_rows", 128, False, False)])
 def test_full_size_sampled(dev, name, s, wire, rand):
     """rand: a caller basis (random orthonormal P0, P1, fresh every step, the same float32 matrices on both
     sides), whose 64x64 blocks the kernels transform on the matrix cores.
 
     single_4096 (one 4096x4096 weight, bfloat16 gradients, W = 4) runs its stated 20 steps with 130
-    sampled chunks; the OLMo lists run 2 steps with 3 chunks of every tensor.  After every decode the
+    sampled chunks; the OLMo lists run 2 steps with 3 chunks of every tensor.  wide_rows (rows of 2^23
+    and 2^22 floats) puts full chunks on the 64-bit-address path the kernels take when 64 (or 128)
+    rows span 2^31 bytes or more.  After every decode the
     payloads are decoded once more into zeros with eta = 1, lambda = 0, phi = identity, which leaves -M*:
     the sampled chunks' M* is compared with the oracle's too."""
     w = DI.WORKLOADS[name]
