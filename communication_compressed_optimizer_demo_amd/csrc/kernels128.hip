@@ -25,8 +25,9 @@
 // form S_ab (wave w = 2a + b takes sub-block (a, b)), and each wave then runs
 // its 64x64 sub-block exactly like a 64x64 chunk: column pass in registers,
 // LDS transpose, row pass.  Top-k is workgroup-wide over the 16384
-// coefficients of the chunk; decode scatters the W payloads into a 128x128
-// LDS accumulator (one wave, in worker order, so sums are deterministic).
+// coefficients of the chunk; in the decode each wave scatters the W
+// payloads' entries of its own sub-block into its own quarter of the LDS, in
+// worker order, so sums are deterministic.
 //
 // A vector is cut into 128-element chunks; a workgroup item is 128 chunks,
 // 32 per wave.  A lane pair holds one chunk (lane 2g + h: half h of chunk g),
@@ -59,10 +60,10 @@ constexpr int kCandPerWave = 64 * kSlots;  // candidates each wave may put in LD
 // indices, the kept list (64 values, 64 indices)
 constexpr int kScrWords = 16 + 512 + 2 * 4 * kCandPerWave + 128;
 constexpr int kEncLdsWords = kTilesWords + kScrWords;
-// decode LDS: 128 x 128 fp32 accumulator + 128 x 32 words of 8-bit counts;
-// the tiles, the butterfly exchange and the vector path reuse it
-constexpr int kAccWords = kS * kS;
-constexpr int kDecLdsWords = kAccWords + kS * kS / 4;
+// decode LDS: 128 x 128 fp32 sums + 128 x 32 words of 8-bit counts, as four
+// per-wave quarters; the tiles, the butterfly exchange and the vector path
+// reuse it
+constexpr int kDecLdsWords = kS * kS + kS * kS / 4;
 static_assert(kTilesWords <= kDecLdsWords && 4 * kQuad <= kTilesWords, "LDS regions");
 static_assert(kDecLdsWords * 4 <= 81920, "two decode workgroups per CU");
 static_assert((kEncLdsWords * 4) * 2 <= 160 * 1024, "two encode workgroups per CU");
@@ -193,6 +194,7 @@ __device__ __forceinline__ void butterfly_staged(float (&x)[64], float* xq, int 
 // (a, b) the bits of this wave, (qa, qb) those of the other.
 // Forward: quadrants -> S_ab; inverse: S'_ab -> quadrants.  One exchange
 // through LDS; leaves the exchange area free.
+template <bool kRelease = true>
 __device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int lane) {
 #pragma unroll
   for (int i = 0; i < 64; ++i) xq[w * kQuad + i * 64 + lane] = x[i];
@@ -203,7 +205,7 @@ __device__ __forceinline__ void butterfly(float (&x)[64], float* xq, int w, int 
     case 2: butterfly_combine<2>(x, xq, lane); break;
     default: butterfly_combine<3>(x, xq, lane); break;
   }
-  __syncthreads();
+  if constexpr (kRelease) __syncthreads();
 }
 
 struct Chunk128 {
@@ -773,26 +775,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 
 // ---------------------------------------------------------------- decode
 
-// Matrix accumulator: coefficient (r, c) at r*128 + (c ^ ((r >> 1) & 31)); its
-// 8-bit count in byte c & 3 of word r*32 + ((c >> 2) ^ ((r >> 1) & 31)).  The
-// XOR spreads one column of rows 2u + a (the averaging reads) over the banks.
-__device__ __forceinline__ void accumulate128(float* acc, uint32_t* cntw, uint32_t id, float v) {
-  const uint32_t r = id >> 7, c = id & 127u, s = (r >> 1) & 31u;
-  scatter_add(&acc[r * 128 + (c ^ s)], reinterpret_cast<uint8_t*>(&cntw[r * 32 + ((c >> 2) ^ s)]) + (c & 3u), v);
+// Per-wave sub-block accumulator (wave w = 2a + b owns the coefficients
+// (2u + a, 2v + b)): its 20 KB quarter of the decode LDS holds the sum of
+// (u, v) at v*64 + u and its 8-bit count in byte v & 3 of word
+// 4096 + (v >> 2)*64 + u.  Stored transposed, so that lane u reads its row
+// at constant offsets from one address, lanes on distinct banks.
+constexpr int kQWords = kDecLdsWords / 4;
+static_assert(64 * 64 + 64 * 16 <= kQWords && kTile <= kQWords, "sub-block accumulator and tile in a quarter");
+__device__ __forceinline__ void accumulate_sub(float* acc, uint32_t* cntw, uint32_t u, uint32_t v, float x) {
+  scatter_add(&acc[v * 64 + u], reinterpret_cast<uint8_t*>(&cntw[(v >> 2) * 64 + u]) + (v & 3u), x);
 }
-
-__device__ __forceinline__ void clear_lds(uint32_t* lds, int tid) {
-  uint4* l4 = reinterpret_cast<uint4*>(lds);
-  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-  static_assert(kDecLdsWords % (256 * 4) == 0, "whole 16-byte stores");
-#pragma unroll
-  for (int i = 0; i < kDecLdsWords / (256 * 4); ++i) l4[i * 256 + tid] = z;
-}
-
-__device__ __forceinline__ float avg_scale(uint32_t n, const DecodeParams& p) {
-  // n == 0: no worker sent the coefficient and its sum is 0 as well
-  return p.avg_workers ? p.inv_workers : __builtin_amdgcn_rcpf(fmaxf(float(n), 1.f));
-}
+// the sub-block (wave) of chunk coefficient id = r*128 + c
+__device__ __forceinline__ int sub_of(uint32_t id) { return int(((id >> 6) & 2u) | (id & 1u)); }
 
 // Quadrant q's rows of X (and, for the momentum-only target, of M) for the
 // decode: clamped addresses, so every load is valid; clamped lanes are not
@@ -839,14 +833,11 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   const int w = wave_index(), lane = threadIdx.x & 63;
   const int a = w >> 1, b = w & 1;
   const Chunk128 c = chunk_pos128(ts, blockIdx.x);
-  float* acc = reinterpret_cast<float*>(lds);
-  uint32_t* cntw = lds + kAccWords;
 
-  // Every wave requests the payload entries first and then its quadrant's
-  // rows of X (of M for the momentum-only target), which land during the
-  // scatter and the inverse passes.  Only wave 0 scatters; the other waves'
-  // payload copies go unused, which keeps every load unconditional (clamped
-  // addresses), so no wait is placed between the two groups and the
+  // Every wave requests all payload entries of the chunk first and then its
+  // quadrant's rows of X (of M for the momentum-only target), which land
+  // during the scatter and the inverse passes.  Every load is unconditional
+  // (clamped addresses), so no wait is placed between the two groups and the
   // payloads, issued first, arrive first.  With both X and M to update, the
   // momentum rows follow the exchange (registers).
   const int64_t e0 = ts.entry_begin + int64_t(c.local) * p.keff2;
@@ -873,67 +864,81 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   float x[64], m[64];
   decode_rows128<kTargets>(x, m, xp, mp, ld, c, w, lane, col);
 
-  clear_lds(lds, threadIdx.x);
-  __syncthreads();
-  if (w == 0) {  // one wave, worker order 0..W-1: a fixed summation order
-    if (one_batch) {
+  // Each wave scatters the entries of its own sub-block into its own quarter
+  // of the LDS, in worker order 0..W-1 (a fixed summation order), and reads
+  // the averages back: no workgroup barrier until the transposes.
+  uint32_t* my = lds + w * kQWords;
+  float* acc = reinterpret_cast<float*>(my);
+  uint32_t* cntw = my + 64 * 64;
+  {
+    uint4* l4 = reinterpret_cast<uint4*>(my);
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kQWords / (64 * 4); ++i) l4[i * 64 + lane] = z;
+  }
+  wave_sync();
+  if (one_batch) {
+#pragma unroll
+    for (int j = 0; j < kWorkerBatch; ++j) {
+      const uint32_t id = ix[j] & 16383u;
+      if (lane < p.keff2 && j < p.workers && sub_of(id) == w) accumulate_sub(acc, cntw, id >> 8, (id & 127u) >> 1, val[j]);
+    }
+  } else {
+    // (worker, 64-entry block) steps worker-major, kWorkerBatch loads at a
+    // time: every entry of worker w is added before any of worker w + 1
+    const int nb = (p.keff2 + 63) >> 6;
+    const int steps = p.workers * nb;
+    int wk = 0, eb = 0;
+    for (int t0 = 0; t0 < steps; t0 += kWorkerBatch) {
+      float v2[kWorkerBatch];
+      uint32_t i2[kWorkerBatch];
+      bool on[kWorkerBatch];
 #pragma unroll
       for (int j = 0; j < kWorkerBatch; ++j) {
-        if (lane < p.keff2 && j < p.workers) accumulate128(acc, cntw, ix[j] & 16383u, val[j]);
+        const int e = eb * 64 + lane;
+        on[j] = t0 + j < steps && e < p.keff2;
+        v2[j] = 0.f;
+        i2[j] = 0u;
+        if (on[j]) load_entry128<kWire>(p, wk, e0 + e, v2[j], i2[j]);
+        if (++eb == nb) {
+          eb = 0;
+          ++wk;
+        }
       }
-    } else {
-      // (worker, 64-entry block) steps worker-major, kWorkerBatch loads at a
-      // time: every entry of worker w is added before any of worker w + 1
-      const int nb = (p.keff2 + 63) >> 6;
-      const int steps = p.workers * nb;
-      int wk = 0, eb = 0;
-      for (int t0 = 0; t0 < steps; t0 += kWorkerBatch) {
-        float v2[kWorkerBatch];
-        uint32_t i2[kWorkerBatch];
-        bool on[kWorkerBatch];
 #pragma unroll
-        for (int j = 0; j < kWorkerBatch; ++j) {
-          const int e = eb * 64 + lane;
-          on[j] = t0 + j < steps && e < p.keff2;
-          v2[j] = 0.f;
-          i2[j] = 0u;
-          if (on[j]) load_entry128<kWire>(p, wk, e0 + e, v2[j], i2[j]);
-          if (++eb == nb) {
-            eb = 0;
-            ++wk;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < kWorkerBatch; ++j) {
-          if (on[j]) accumulate128(acc, cntw, i2[j] & 16383u, v2[j]);
-        }
+      for (int j = 0; j < kWorkerBatch; ++j) {
+        const uint32_t id = i2[j] & 16383u;
+        if (on[j] && sub_of(id) == w) accumulate_sub(acc, cntw, id >> 8, (id & 127u) >> 1, v2[j]);
       }
     }
   }
-  __syncthreads();
+  wave_sync();
 
   // this wave's sub-block (a, b) in row layout: lane u, q[v] = Q_bar[2u+a][2v+b]
   float q[64];
-  {
-    const uint32_t r = uint32_t(2 * lane + a), s = uint32_t(lane) & 31u;
+  if (p.avg_workers) {
 #pragma unroll
-    for (int v2 = 0; v2 < 32; ++v2) {  // one count word covers columns 4 v2 .. 4 v2 + 3
-      const uint32_t cw = cntw[r * 32 + (uint32_t(v2) ^ s)];
+    for (int v = 0; v < 64; ++v) q[v] = acc[v * 64 + lane] * p.inv_workers;
+  } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t col2 = uint32_t(4 * v2 + 2 * t + b);
-        q[2 * v2 + t] = acc[r * 128 + (col2 ^ s)] * avg_scale((cw >> (8 * (2 * t + b))) & 255u, p);
+    for (int j = 0; j < 16; ++j) {  // one count word covers v = 4j .. 4j + 3
+      const uint32_t cw = cntw[j * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // n == 0: no worker sent the coefficient and its sum is 0 as well
+        const float n = float((cw >> (8 * t)) & 255u);
+        q[4 * j + t] = acc[(4 * j + t) * 64 + lane] * __builtin_amdgcn_rcpf(fmaxf(n, 1.f));
       }
     }
   }
-  __syncthreads();  // the accumulator area is reused from here on
+  wave_sync();  // the quarter is reused as this wave's transpose tile
   inv_half(q, b);
-  row_to_col(reinterpret_cast<float*>(lds) + w * kTile, q, lane);
+  row_to_col(reinterpret_cast<float*>(my), q, lane);
   inv_half(q, a);
   if constexpr (kTargets == (kToParams | kToMomentum))
     butterfly_staged(q, reinterpret_cast<float*>(lds), w, lane);  // -> M* of quadrant w
   else
-    butterfly(q, reinterpret_cast<float*>(lds), w, lane);
+    butterfly<false>(q, reinterpret_cast<float*>(lds), w, lane);  // the LDS is not used again
 
   if constexpr ((kTargets & kToSigns) != 0) {
     // Chunk row r's sign bits fill words 2r (columns 0..63) and 2r + 1
@@ -985,9 +990,10 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
   }
 }
 
-// Vector item: each wave owns 32 chunks and its own fifth of the LDS:
-// accumulator (chunk g, coefficient c) at g*128 + (c ^ g), counts in byte
-// c & 3 of word g*32 + ((c >> 2) ^ g).
+// Vector item: each wave owns 32 chunks and its own quarter of the LDS:
+// accumulator (chunk g, coefficient c) at c*32 + g, counts in byte c & 3 of
+// word (c >> 2)*32 + g (transposed: lane 2g + h reads its coefficients
+// 2m + h at constant offsets, lanes on distinct banks).
 template <int kTargets, bool kWire>
 __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const DecodeParams& p, uint32_t* lds) {
   const int w = wave_index(), lane = threadIdx.x & 63;
@@ -1008,7 +1014,7 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
   const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int i = 0; i < kWaveWords / 256; ++i) l4[i * 64 + lane] = z4;
-  __syncthreads();
+  wave_sync();
   const int keff = p.keff1;
   const int n = nc * keff;
   const int64_t e0 = ts.entry_begin + int64_t(chunk0) * keff;
@@ -1028,26 +1034,31 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
         const int f = f0 + 64 * j + lane;
         if (f < n) {
           const uint32_t g = uint32_t(f / keff), cc = ii[j] & 127u;
-          scatter_add(&acc[g * 128 + (cc ^ g)], reinterpret_cast<uint8_t*>(&cntw[g * 32 + ((cc >> 2) ^ g)]) + (cc & 3u),
-                      vv[j]);
+          scatter_add(&acc[cc * 32 + g], reinterpret_cast<uint8_t*>(&cntw[(cc >> 2) * 32 + g]) + (cc & 3u), vv[j]);
         }
       }
     }
   }
-  __syncthreads();
+  wave_sync();
   const int h = lane & 1;
   const uint32_t g = uint32_t(lane >> 1);
   float y[64];  // lane h: coefficients 2m + h of chunk g
+  const float* __restrict__ mine = acc + 32 * h + g;  // coefficient 2m + h at mine[64 m]
+  if (p.avg_workers) {
 #pragma unroll
-  for (int m2 = 0; m2 < 32; ++m2) {
-    const uint32_t cw = cntw[g * 32 + (uint32_t(m2) ^ g)];
+    for (int m = 0; m < 64; ++m) y[m] = mine[64 * m] * p.inv_workers;
+  } else {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t cc = uint32_t(4 * m2 + 2 * t + h);
-      y[2 * m2 + t] = acc[g * 128 + (cc ^ g)] * avg_scale((cw >> (8 * (2 * t + h))) & 255u, p);
+    for (int m2 = 0; m2 < 32; ++m2) {
+      const uint32_t cw = cntw[m2 * 32 + g];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float n = float((cw >> (8 * (2 * t + h))) & 255u);
+        y[2 * m2 + t] = mine[64 * (2 * m2 + t)] * __builtin_amdgcn_rcpf(fmaxf(n, 1.f));
+      }
     }
   }
-  __syncthreads();
+  wave_sync();
   inv_half(y, h);
   pair_unbutterfly(y, h);
   float (&x)[64] = y;
