@@ -294,27 +294,32 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
       const uint32_t c = T | (1u << bit);
       if (ballot_count(lmb >= c) >= keff) T = c;
     }
-    int cnt = 0;
+    // Candidates in column order: column v's ballot places them after the
+    // ones already found (a wave-uniform running count), so no per-lane
+    // count and scan come first.  The order within a region does not matter:
+    // the tie cut searches indices and emit_kept ranks by index.
+    uint32_t cw = 0;
     if (T != 0) {
       const float t = __uint_as_float(T);
-#pragma unroll
-      for (int v = 0; v < 64; ++v) cnt += fabsf(q[v]) >= t ? 1 : 0;
-    }
-    const int incl = wave_incl_scan(cnt, lane);
-    const int cw = __shfl(incl, 63);
-    if (T != 0 && cw <= kCandPerWave) {
-      const float t = __uint_as_float(T);
-      int pos = w * kCandPerWave + incl - cnt;
+      uint32_t* cv = cval + w * kCandPerWave;
+      uint32_t* ci = cid + w * kCandPerWave;
 #pragma unroll
       for (int v = 0; v < 64; ++v) {
-        if (fabsf(q[v]) >= t) {
-          cval[pos] = __float_as_uint(q[v]);
-          cid[pos] = idx0 + 2 * v;
-          ++pos;
+        const bool is_c = fabsf(q[v]) >= t;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(is_c);
+        if (m != 0) {  // wave-uniform
+          if (is_c) {
+            const uint32_t pos = cw + uint32_t(lanes_below_mask(m));
+            if (pos < uint32_t(kCandPerWave)) {
+              cv[pos] = __float_as_uint(q[v]);
+              ci[pos] = idx0 + 2 * v;
+            }
+          }
+          cw += uint32_t(__popcll(m));
         }
       }
     }
-    if (lane == 0) hdr[w] = T != 0 ? uint32_t(cw) : 0xffffffffu;
+    if (lane == 0) hdr[w] = T != 0 ? cw : 0xffffffffu;
     __syncthreads();
     uint32_t C[4];
 #pragma unroll

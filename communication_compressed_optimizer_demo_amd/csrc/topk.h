@@ -146,7 +146,8 @@ __device__ __forceinline__ void topk_chunk(float (&q)[64], int keff, int lane, f
   }
   // 3. candidates |q| >= T0, compacted in index order
   int cnt = 0;
-  if (T0 != 0) {
+  {
+    // T0 == 0 counts every coefficient: 4096 > kMaxCand takes the full search
     const float t0 = __uint_as_float(T0);
 #pragma unroll
     for (int v = 0; v < 64; ++v) cnt += fabsf(q[v]) >= t0 ? 1 : 0;
