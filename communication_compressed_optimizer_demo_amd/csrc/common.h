@@ -88,9 +88,42 @@ constexpr int kToMomentum = 2;
 constexpr int kToSigns = 4;
 constexpr int kToMstar = 8;
 
+// X <- X - eta (phi(m) + lambda X) for one element, phi = sign (kSign) or
+// the identity.
+template <bool kSign>
 __device__ __forceinline__ float update(float x, float m, const DecodeParams& p) {
-  const float ph = p.phi_sign ? sign_of(m) : m;
+  const float ph = kSign ? sign_of(m) : m;
   return fmaf(-p.eta, fmaf(p.lam, x, ph), x);
+}
+
+// The update of a lane's 64 elements, phi chosen once for all of them (a
+// per-element choice would spend the sign's instructions on the identity
+// path as well).
+__device__ __forceinline__ void update_all(float (&x)[64], const float (&m)[64], const DecodeParams& p) {
+  if (p.phi_sign) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = update<true>(x[i], m[i], p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = update<false>(x[i], m[i], p);
+  }
+}
+
+// The same in place for a vector slab: elements 64 r of xp, those with
+// 64 r < rem.
+__device__ __forceinline__ void update_strided(float* __restrict__ xp, const float (&m)[64], int64_t rem,
+                                               const DecodeParams& p) {
+  if (p.phi_sign) {
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      if (r * 64 < rem) stream_store(update<true>(stream_load(&xp[r * 64]), m[r], p), &xp[r * 64]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      if (r * 64 < rem) stream_store(update<false>(stream_load(&xp[r * 64]), m[r], p), &xp[r * 64]);
+    }
+  }
 }
 
 // Scatter-add of one payload entry into a wave's LDS accumulator: the sum

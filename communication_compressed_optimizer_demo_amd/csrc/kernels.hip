@@ -519,8 +519,7 @@ __device__ __forceinline__ void decode_matrix(const TensorSlot& ts, const Decode
         for (int i = 0; i < 64; ++i) x[i] = stream_load(&(xp + int64_t(min(i, c.vr - 1)) * ld)[col]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
+    update_all(x, q, p);
     if (c.full)
       store_rows<true>(x, xp, ld, c, lane);
     else
@@ -586,11 +585,7 @@ __device__ __forceinline__ void decode_vector(const TensorSlot& ts, const Decode
   row_to_col(acc, q, lane);
 
   if constexpr ((kTargets & kToParams) != 0) {
-    float* __restrict__ x = ts.dst + first;
-#pragma unroll
-    for (int c = 0; c < 64; ++c) {
-      if (c * 64 < rem) stream_store(update(stream_load(&x[c * 64]), q[c], p), &x[c * 64]);
-    }
+    update_strided(ts.dst + first, q, rem, p);
   }
   if constexpr ((kTargets & kToMomentum) != 0) {  // aggregated subtraction: M = M - alpha M*
     float* __restrict__ m = static_cast<float*>(ts.aux) + first;

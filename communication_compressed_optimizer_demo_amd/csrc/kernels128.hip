@@ -385,11 +385,16 @@ __device__ __forceinline__ bool topk128(float (&q)[64], int keff, int w, int lan
         }
       }
       const float kf = __uint_as_float(K);
+      if (cut == 0xffffffffu) {  // no tie dropped: kept <=> |q| >= K (the same branch in every wave)
 #pragma unroll
-      for (int v = 0; v < 64; ++v) {
-        const float m = fabsf(q[v]);
-        const bool keep = m > kf || (m == kf && idx0 + 2 * v <= cut);
-        q[v] = keep ? q[v] : 0.f;
+        for (int v = 0; v < 64; ++v) q[v] = fabsf(q[v]) >= kf ? q[v] : 0.f;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 64; ++v) {
+          const float m = fabsf(q[v]);
+          const bool keep = m > kf || (m == kf && idx0 + 2 * v <= cut);
+          q[v] = keep ? q[v] : 0.f;
+        }
       }
       return true;
     }
@@ -675,7 +680,7 @@ __device__ __forceinline__ void encode_matrix128(const TensorSlot& ts, const Enc
   inv_half(x, b);  // x holds Q_hat: R = P^T Q_hat P, quadrant by quadrant
   row_to_col(lds + w * kTile, x, lane);
   inv_half(x, a);
-  butterfly(x, lds, w, lane);  // S'_ab -> quadrants
+  butterfly<false>(x, lds, w, lane);  // S'_ab -> quadrants; the tiles are not used again
 
   // M = M' - alpha R
 #pragma unroll
@@ -966,8 +971,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
     stream_store(word, static_cast<uint64_t*>(ts.aux) + int64_t(c.local) * 256 + 2 * quad_row(a, lane) + b);
   }
   if constexpr ((kTargets & kToParams) != 0) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = update(x[i], q[i], p);
+    update_all(x, q, p);
     if (c.full)
       store_quadrant<true>(x, xp, ld, c, w, lane);
     else
@@ -1085,11 +1089,7 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
       stream_store((uint64_t(hi) << 32) | lo, static_cast<uint64_t*>(ts.aux) + int64_t(chunk0) * 2 + lane);
   }
   if constexpr ((kTargets & kToParams) != 0) {
-    float* __restrict__ xp = ts.dst + first;
-#pragma unroll
-    for (int r = 0; r < 64; ++r) {
-      if (r * 64 < rem) stream_store(update(stream_load(&xp[r * 64]), x[r], p), &xp[r * 64]);
-    }
+    update_strided(ts.dst + first, x, rem, p);
   }
   if constexpr ((kTargets & kToMomentum) != 0) {
     float* __restrict__ mp = static_cast<float*>(ts.aux) + first;
