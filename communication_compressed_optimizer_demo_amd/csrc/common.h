@@ -141,6 +141,18 @@ __device__ __forceinline__ void scatter_add(float* sum, uint8_t* cnt, float v) {
   __hip_atomic_store(cnt, uint8_t(n + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
+// The same through LDS atomic adds whose results are not read (ds_add_f32,
+// ds_add_u32 on the count's word): no wait between calls, and the order
+// argument above still holds, so the sums are bitwise those of scatter_add.
+// A count stays below 256 (at most 255 workers), so no byte carries into its
+// neighbour.  Faster where a wave's calls have few active lanes (the
+// per-sub-block scatter at chunk edge 128); slower than scatter_add for a
+// full 64x64 chunk.
+__device__ __forceinline__ void scatter_add_nowait(float* sum, uint32_t* cntw, uint32_t byte, float v) {
+  __hip_atomic_fetch_add(sum, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  __hip_atomic_fetch_add(cntw, 1u << (8u * byte), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
 // Work item of workgroup b of n.  Workgroups go to the 8 XCDs round-robin
 // (workgroup b to XCD b mod 8); this gives each XCD one contiguous range of
 // items, so neighbouring chunks, whose payload entries share cache lines,

@@ -793,7 +793,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 constexpr int kQWords = kDecLdsWords / 4;
 static_assert(64 * 64 + 64 * 16 <= kQWords && kTile <= kQWords, "sub-block accumulator and tile in a quarter");
 __device__ __forceinline__ void accumulate_sub(float* acc, uint32_t* cntw, uint32_t u, uint32_t v, float x) {
-  scatter_add(&acc[v * 64 + u], reinterpret_cast<uint8_t*>(&cntw[(v >> 2) * 64 + u]) + (v & 3u), x);
+  scatter_add_nowait(&acc[v * 64 + u], &cntw[(v >> 2) * 64 + u], v & 3u, x);
 }
 // the sub-block (wave) of chunk coefficient id = r*128 + c
 __device__ __forceinline__ int sub_of(uint32_t id) { return int(((id >> 6) & 2u) | (id & 1u)); }
@@ -1043,7 +1043,7 @@ __device__ __forceinline__ void decode_vector128(const TensorSlot& ts, const Dec
         const int f = f0 + 64 * j + lane;
         if (f < n) {
           const uint32_t g = uint32_t(f / keff), cc = ii[j] & 127u;
-          scatter_add(&acc[cc * 32 + g], reinterpret_cast<uint8_t*>(&cntw[(cc >> 2) * 32 + g]) + (cc & 3u), vv[j]);
+          scatter_add_nowait(&acc[cc * 32 + g], &cntw[(cc >> 2) * 32 + g], cc & 3u, vv[j]);
         }
       }
     }
