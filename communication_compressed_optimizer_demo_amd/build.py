@@ -3,7 +3,9 @@
     python -m communication_compressed_optimizer_demo_amd.build
 
 Produces ``communication_compressed_optimizer_demo_amd/libdemo_codec.so``.
-Objects go to ``communication_compressed_optimizer_demo_amd/_build/``.
+Objects go to ``communication_compressed_optimizer_demo_amd/_build/``, and so
+does ``valu_issue_probe``, a standalone program that measures the issue cost
+of single VALU instruction forms (the basis of the kernels' VALU rooflines).
 Packed fp32 VALU instructions are switched off for all device code.
 """
 from __future__ import annotations
@@ -23,6 +25,8 @@ LIB = os.path.join(PKG, "libdemo_codec.so")
 ARCH = "gfx950"
 
 SOURCES = ["kernels.hip", "kernels128.hip", "kernels_muon.hip", "codec.cpp"]
+PROBE_SRC = "valu_issue_probe.hip"
+PROBE = os.path.join(BUILD, "valu_issue_probe")
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -56,8 +60,9 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         jobs.append((obj, [cc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-        logs = list(ex.map(lambda j: _run(j[1]), jobs))
+    probe = (PROBE, [cc, *COMMON, os.path.join(CSRC, PROBE_SRC), "-o", PROBE])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs) + 1) as ex:
+        logs = list(ex.map(lambda j: _run(j[1]), jobs + [probe]))
     tmp = LIB + ".tmp"
     logs.append(_run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[j[0] for j in jobs], "-o", tmp]))
     os.replace(tmp, LIB)
