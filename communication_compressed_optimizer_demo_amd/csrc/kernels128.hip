@@ -895,7 +895,7 @@ __device__ __forceinline__ void decode_matrix128(const TensorSlot& ts, const Dec
     }
   } else {
     // (worker, 64-entry block) steps worker-major, kWorkerBatch loads at a
-    // time: every entry of worker w is added before any of worker w + 1
+    // time: every entry of worker wk is added before any of worker wk + 1
     const int nb = (p.keff2 + 63) >> 6;
     const int steps = p.workers * nb;
     int wk = 0, eb = 0;
