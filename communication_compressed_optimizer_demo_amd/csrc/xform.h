@@ -16,7 +16,9 @@
 // arrays live in VGPRs.
 //
 // A caller-supplied basis (random orthonormal projection, same section) has
-// no fast form; DenseBasis applies it as a plain matrix-vector product whose
+// no fast form; DenseBasis applies it to 64x64 blocks as two matrix products
+// on the matrix cores, float32-accurate through a three-way bfloat16 split
+// of both operands, and to vectors as a plain matrix-vector product whose
 // rows are read through uniform (scalar) loads.
 #pragma once
 
@@ -327,12 +329,16 @@ struct IdentityBasis {
 // Caller-supplied orthonormal P0 / P1 (64 x 64, row-major, rows are basis vectors).
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct DenseBasis {
   const float* __restrict__ p0;
   const float* __restrict__ p1;
-  // A 64x64 block goes through the fp32 matrix cores (two 64x64x64 products
-  // per direction) instead of one matrix-vector product per lane.
+  // A 64x64 block goes through the matrix cores (two 64x64x64 products per
+  // direction) instead of one matrix-vector product per lane.
   static constexpr bool kMatrixCores = true;
 
   static __device__ __forceinline__ void apply(const float* __restrict__ P, float (&x)[64]) {
@@ -365,14 +371,31 @@ struct DenseBasis {
   __device__ __forceinline__ void inv1(float (&x)[64]) const { apply_t(p1, x); }
 
   // --- 64x64 blocks on the matrix cores (one wave; `tile` is 64 rows of kLd
-  // floats in LDS).  v_mfma_f32_32x32x2f32: lane l supplies A[l % 32][slot]
-  // and B[slot][l % 32], slot = l / 32; the 32x32 result sits in register v
-  // of lane l at row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.  Step kk
-  // of a 64-deep product uses k = kk + 32 slot, so a lane's slot walks one
-  // contiguous half of a row or column.
+  // floats in LDS).  A 32x32 result sits in register v of lane l at row
+  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.  Each lane half feeds
+  // one contiguous half of the 64-deep k range: k = kk + 32 (l / 32),
+  // kk = 0..31, so a lane walks one half of a row or column.
+
+  // (x, y) -> both rounded to bfloat16 in one packed conversion (returned as
+  // the packed pair), and what the rounding left, in place.  The remainder
+  // is exact in float32.
+  static __device__ __forceinline__ uint32_t peel_pair(float& x, float& y) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+    x -= __uint_as_float(bits << 16);
+    y -= __uint_as_float(bits & 0xffff0000u);
+    return bits;
+  }
 
   // D = A * B for 64x64 operands given as functions (m, k) -> A, (k, n) -> B
-  // of this lane's (row / column within a 32-tile, slot, kk).
+  // of this lane's (row / column within a 32-tile, kk), k = kk + 32 (lane / 32).
+  // Float32-accurate products on the bfloat16 matrix cores: every operand is
+  // split exactly into three bfloat16 parts (8 + 8 + 8 significant bits,
+  // each the rounding of what the previous parts leave) and the six part
+  // products down to the third order (a1b1, a1b2, a2b1, a1b3, a2b2, a3b1;
+  // each of the three dropped ones is at most 2^-24 |ab|) are accumulated in
+  // float32, smallest first.  v_mfma_f32_32x32x16_bf16: lane l gives A[l % 32][8 (l /
+  // 32) + j] and B[8 (l / 32) + j][l % 32], j = 0..7; step s of four takes
+  // kk = 8 s + j, so both operands pair the same k.
   template <class FA, class FB>
   static __device__ __forceinline__ void product(f32x16 (&d)[2][2], FA a_of, FB b_of) {
 #pragma unroll
@@ -382,13 +405,31 @@ struct DenseBasis {
 #pragma unroll
         for (int v = 0; v < 16; ++v) d[i][j][v] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-      const float a0 = a_of(0, kk), a1 = a_of(1, kk);
-      const float b0 = b_of(0, kk), b1 = b_of(1, kk);
-      d[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, d[0][0], 0, 0, 0);
-      d[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, d[0][1], 0, 0, 0);
-      d[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, d[1][0], 0, 0, 0);
-      d[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, d[1][1], 0, 0, 0);
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a[2][3], b[2][3];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = a_of(t, 8 * s + 2 * j), x1 = a_of(t, 8 * s + 2 * j + 1);
+          a[t][0][j] = peel_pair(x0, x1);
+          a[t][1][j] = peel_pair(x0, x1);
+          a[t][2][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+          float y0 = b_of(t, 8 * s + 2 * j), y1 = b_of(t, 8 * s + 2 * j + 1);
+          b[t][0][j] = peel_pair(y0, y1);
+          b[t][1][j] = peel_pair(y0, y1);
+          b[t][2][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y0, y1}, bf16x2));
+        }
+      constexpr int kTa[6] = {2, 1, 0, 1, 0, 0}, kTb[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+      for (int p = 0; p < 6; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            d[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i][kTa[p]]),
+                                                              __builtin_bit_cast(bf16x8, b[j][kTb[p]]), d[i][j], 0, 0,
+                                                              0);
     }
   }
 
