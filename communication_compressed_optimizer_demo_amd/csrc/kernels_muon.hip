@@ -9,20 +9,21 @@
 //   Y0 = (A + eps I) / s,  Z0 = I,
 //   T = (3 I - Z Y) / 2,  Y <- Y T,  Z <- T Z,
 // with s = ||A + eps I||_F (so every eigenvalue of Y0 is in (0, 1]); Z then
-// converges to (A + eps I)^(-1/2) sqrt(s).  Every product is a dense fp32
-// GEMM on the matrix cores; the last one, Z M / sqrt(s) (or M Z / sqrt(s)),
-// carries the parameter update in its epilogue.  A vector is one column:
+// converges to (A + eps I)^(-1/2) sqrt(s).  Every product is a dense GEMM
+// on the matrix cores at float32 accuracy; the last one, Z M / sqrt(s) (or
+// M Z / sqrt(s)), carries the parameter update in its epilogue.  A vector is one column:
 // m / sqrt(m.m + eps).
 //
-// GEMM on v_mfma_f32_32x32x2f32.  Operand layout of that instruction: lane l
-// supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the accumulator holds
-// D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v.  Two kernels:
-//  - gemm_kernel (any shape): 128 x 128 (or 64 x 64) output tile per
-//    256-thread workgroup, 2 x 2 waves; K advances kBK per LDS stage,
-//    double-buffered, bounds-checked 4-byte loads of the next stage issued
-//    before the current stage's MFMAs;
-//  - gemm_tile_kernel (whole tiles): the same tiles with 4 x 2 waves at
-//    128 x 128, K stages of kSK, 16-byte loads two stages ahead.
+// Two GEMM kernels; a 32 x 32 MFMA accumulator holds
+// D[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32] in register v of lane l:
+//  - gemm_kernel (any shape): v_mfma_f32_32x32x2f32 (lane l supplies
+//    A[l % 32][l / 32] and B[l / 32][l % 32]); 128 x 128 (or 64 x 64)
+//    output tile per 256-thread workgroup, 2 x 2 waves; K advances kBK per
+//    LDS stage, double-buffered, bounds-checked 4-byte loads of the next
+//    stage issued before the current stage's MFMAs;
+//  - gemm_tile_kernel (whole tiles, where all of the Newton-Schulz work
+//    runs): the same tiles and waves on the bfloat16 matrix cores, every
+//    float32 operand split exactly into three bfloat16 parts (below).
 // Both take a batch of same-shape products (grid z), which the Newton-Schulz
 // steps of several matrices with equal n share.
 #include <mutex>
@@ -167,141 +168,180 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------- whole-tile GEMM
 //
-// For products whose M and N are multiples of the tile edge and K of 2 kSK, with
-// 16-byte aligned operands.  Same 2 x 2 wave grid and MFMA tiles as above;
-// what differs is how operands reach the matrix cores:
-//  - K advances kSK = 32 per stage; each thread moves its share of a stage
-//    with 16-byte global loads, eight lanes per 128-byte row segment;
-//  - two register sets hold stages s+1 and s+2 while stage s is multiplied,
-//    so a global load has two stages of MFMA work to arrive;
-//  - MFMA k-slot h (lane half) takes the k values 16h .. 16h + 15 of a stage,
-//    so an operand whose rows run along K in memory is kept that way in LDS
-//    (pitch kSK + 4) and read with 16-byte LDS loads, and one whose rows run
-//    along M or N is kept k-major (pitch kT + 2: the two lane halves, 16 rows
-//    apart, fall on opposite halves of the banks).
-constexpr int kSK = 32;
+// For products whose M and N are multiples of the tile edge and K of
+// kWholeK, with 16-byte aligned operands.  Float32-accurate products on the bfloat16 matrix
+// cores (v_mfma_f32_32x32x16_bf16, 16 k values per step): every operand value
+// is split exactly into three bfloat16 parts (8 + 8 + 8 significant bits,
+// each the rounding of what the previous parts leave) as it is staged into
+// LDS, and each MFMA tile accumulates the six part products down to the third
+// order (a1b1, a1b2, a2b1, a1b3, a2b2, a3b1; each of the three dropped ones
+// is at most 2^-24 |ab|) in float32, smallest first.
+//  - K advances kSK per stage (one MFMA k-step at 128 x 128 tiles, two at
+//    64 x 64); each thread loads its share of a stage with two 16-byte
+//    global loads, two register sets holding stages s+1 and s+2 while stage
+//    s is multiplied, and splits it as it stores it to LDS (double-buffered,
+//    so two workgroups fit a CU);
+//  - in LDS each part is kept k-contiguous per row of the tile (row along M
+//    for A, along N for B), so that a lane reads the eight k values it feeds
+//    to one MFMA step with one 16-byte load: lane l gives
+//    A[l % 32][8 (l / 32) + j] and B[8 (l / 32) + j][l % 32], j = 0..7;
+//  - an operand whose rows run along K in memory is staged eight k values
+//    per thread and row (one 16-byte store per part); one whose rows run
+//    along M or N two k values for four rows, eight lanes reading one
+//    128-byte row segment.
+// Whole tiles need K to be a multiple of this (two stages of the deepest kSK).
+constexpr int kWholeK = 64;
 
 // Native vectors (not HIP's float4 struct) so the staging registers stay registers.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// (x, y) -> both rounded to bfloat16 in one packed conversion (returned as
+// the packed pair, x in the low half), and what the rounding left, in place.
+// The remainder is exact in float32.
+__device__ __forceinline__ uint32_t peel_pair(float& x, float& y) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+  x -= __uint_as_float(bits << 16);
+  y -= __uint_as_float(bits & 0xffff0000u);
+  return bits;
+}
+
+// The three packed parts of (x, y), high part first.
+__device__ __forceinline__ void split_pair(float x, float y, uint32_t (&w)[3]) {
+  w[0] = peel_pair(x, y);
+  w[1] = peel_pair(x, y);
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
 
 // One operand's stage: kT rows (along M for A, N for B) by kSK values of k,
-// moved by kThreads threads.  kKc: element (row, k) sits at X[row * ld + k]
-// (rows along K in memory); otherwise at X[k * ld + row].
-template <bool kKc, int kT, int kThreads>
-struct TileOperand {
-  static constexpr int kV = kT * kSK / 4 / kThreads;  // f32x4 per thread and stage
-  static constexpr int kPitch = kKc ? kSK + 4 : kT + 2;
-  static constexpr int kFloats = kKc ? kT * kPitch : kSK * kPitch;
+// moved by 256 threads (kT * kSK / 4 = 512 16-byte loads, two per thread).
+// kKc: element (row, k) sits at X[row * ld + k] (rows along K in memory);
+// otherwise at X[k * ld + row].  LDS: part p, row r, k pair q at word
+// p * kPart + slot(r) * kPitch + q.  The pitch of kSK / 2 + 4 words puts the
+// 16-byte reads of 16 consecutive rows on distinct banks; slot(r) swaps
+// rows r and r ^ 2 in every second block of 16 rows, which keeps that and
+// puts the 4-byte stores of the k-major staging (eight row groups of four
+// rows, eight k pairs) on distinct banks too.
+template <bool kKc, int kT, int kSK>
+struct SplitOperand {
+  static_assert(kT * kSK / 4 == 512, "two 16-byte loads per thread and stage");
+  static constexpr int kPitch = kSK / 2 + 4;
+  static constexpr int kPart = kT * kPitch;
+  static constexpr int kWords = 3 * kPart;
+  static constexpr int kQ = kSK / 2;  // k pairs per row and stage
+  static constexpr int kG = kSK / 8;  // groups of eight k per row and stage
 
-  __device__ static void load(f32x4 (&r)[kV], const float* __restrict__ X, int64_t ld, int r0, int k0, int tid) {
+  static __device__ __forceinline__ int slot(int r) { return r ^ ((r >> 3) & 2); }
+
+  __device__ static void load(f32x4 (&r)[2], const float* __restrict__ X, int64_t ld, int r0, int k0, int tid) {
+    if constexpr (kKc) {
+      // row tid / kG, k 8 (tid % kG) .. + 7
+      const float* p = X + int64_t(r0 + tid / kG) * ld + k0 + 8 * (tid % kG);
+      r[0] = *reinterpret_cast<const f32x4*>(p);
+      r[1] = *reinterpret_cast<const f32x4*>(p + 4);
+    } else {
+      // rows 4 r4 .. 4 r4 + 3 at k = 2 q (j = 0) and 2 q + 1 (j = 1); eight
+      // lanes read one 128-byte row segment
+      const int r4 = tid / (8 * kQ) * 8 + (tid & 7), q = (tid >> 3) % kQ;
 #pragma unroll
-    for (int j = 0; j < kV; ++j) {
-      const int f = tid + kThreads * j;
-      if constexpr (kKc) {
-        const int c4 = f & 7, row = f >> 3;
-        r[j] = *reinterpret_cast<const f32x4*>(X + int64_t(r0 + row) * ld + k0 + 4 * c4);
-      } else {
-        const int c4 = f % (kT / 4), k = f / (kT / 4);
-        r[j] = *reinterpret_cast<const f32x4*>(X + int64_t(k0 + k) * ld + r0 + 4 * c4);
+      for (int j = 0; j < 2; ++j) r[j] = *reinterpret_cast<const f32x4*>(X + int64_t(k0 + 2 * q + j) * ld + r0 + 4 * r4);
+    }
+  }
+
+  __device__ static void store(const f32x4 (&r)[2], uint32_t* s, int tid) {
+    if constexpr (kKc) {
+      uint32_t w[4][3];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        split_pair(r[j][0], r[j][1], w[2 * j]);
+        split_pair(r[j][2], r[j][3], w[2 * j + 1]);
+      }
+      uint32_t* p = s + slot(tid / kG) * kPitch + 4 * (tid % kG);
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+        *reinterpret_cast<u32x4*>(p + part * kPart) = u32x4{w[0][part], w[1][part], w[2][part], w[3][part]};
+    } else {
+      const int r4 = tid / (8 * kQ) * 8 + (tid & 7), q = (tid >> 3) % kQ;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t w[3];
+        split_pair(r[0][c], r[1][c], w);
+#pragma unroll
+        for (int part = 0; part < 3; ++part) s[part * kPart + slot(4 * r4 + c) * kPitch + q] = w[part];
       }
     }
   }
 
-  __device__ static void store(const f32x4 (&r)[kV], float* s, int tid) {
+  // The three parts of this lane's eight k values of step st for tile row r.
+  __device__ static void fragment(const uint32_t* s, int r, int st, int h, u32x4 (&f)[3]) {
+    const uint32_t* p = s + slot(r) * kPitch + 8 * st + 4 * h;
 #pragma unroll
-    for (int j = 0; j < kV; ++j) {
-      const int f = tid + kThreads * j;
-      if constexpr (kKc) {
-        const int c4 = f & 7, row = f >> 3;
-        *reinterpret_cast<f32x4*>(s + row * kPitch + 4 * c4) = r[j];
-      } else {
-        const int c4 = f % (kT / 4), k = f / (kT / 4);
-        f32x2* p = reinterpret_cast<f32x2*>(s + k * kPitch + 4 * c4);
-        p[0] = r[j].xy;
-        p[1] = r[j].zw;
-      }
-    }
+    for (int part = 0; part < 3; ++part) f[part] = *reinterpret_cast<const u32x4*>(p + part * kPart);
   }
 };
 
-// kWM x 2 waves; wave tile (kT / kWM) x (kT / 2), i.e. kMI x kMJ MFMA tiles.
-template <bool kTA, bool kTB, int kT, int kWM>
-__global__ __launch_bounds__(128 * kWM) void gemm_tile_kernel(GemmArgs g) {
+// Four waves in a 2 x 2 grid; wave tile (kT / 2) x (kT / 2), i.e. kMT x kMT
+// MFMA tiles.  K advances kSK per stage: 16 at kT = 128 (one MFMA k-step;
+// 72 KB of LDS, two workgroups per CU), 32 at kT = 64.
+template <bool kTA, bool kTB, int kT>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
   select_product(g);
-  constexpr int kThreads = 128 * kWM;
-  using OA = TileOperand<!kTA, kT, kThreads>;
-  using OB = TileOperand<kTB, kT, kThreads>;
-  constexpr int kMI = kT / kWM / 32, kMJ = kT / 64;
-  constexpr int kAcc = kMI * kMJ == 1 ? 2 : 1;  // a lone 32 x 32 tile alternates two accumulators
-  __shared__ __align__(16) float As[2][OA::kFloats];
-  __shared__ __align__(16) float Bs[2][OB::kFloats];
+  constexpr int kSK = kT == 128 ? 16 : 32;
+  using OA = SplitOperand<!kTA, kT, kSK>;
+  using OB = SplitOperand<kTB, kT, kSK>;
+  constexpr int kMT = kT / 64;
+  constexpr int kAcc = kMT == 1 ? 2 : 1;  // a lone 32 x 32 tile alternates two accumulators
+  __shared__ __align__(16) uint32_t As[2][OA::kWords];
+  __shared__ __align__(16) uint32_t Bs[2][OB::kWords];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, i32 = lane & 31;
   const int wm = w >> 1, wn = w & 1;
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   const int nk = g.K / kSK;
 
-  floatx16 acc[kMI][kMJ][kAcc];
+  floatx16 acc[kMT][kMT][kAcc];
 #pragma unroll
-  for (int i = 0; i < kMI; ++i)
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int j = 0; j < kMJ; ++j)
+    for (int j = 0; j < kMT; ++j)
 #pragma unroll
       for (int a = 0; a < kAcc; ++a)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][a][v] = 0.f;
 
-  // Multiply one LDS stage: 16 MFMA k-steps, step kk uses k = 16h + kk.
-  auto compute = [&](const float* sa, const float* sb) {
-    f32x4 av[kMI][4], bv[kMJ][4];
+  // Multiply one LDS stage: kSK / 16 k-steps of six part products each.
+  auto compute = [&](const uint32_t* sa, const uint32_t* sb) {
 #pragma unroll
-    for (int t = 0; t < kMI; ++t) {
-      if constexpr (!kTA) {
-        const float* p = sa + (wm * (kT / kWM) + t * 32 + i32) * OA::kPitch + 16 * h;
+    for (int st = 0; st < kSK / 16; ++st) {
+      u32x4 a[kMT][3], b[kMT][3];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) av[t][q] = *reinterpret_cast<const f32x4*>(p + 4 * q);
+      for (int t = 0; t < kMT; ++t) {
+        OA::fragment(sa, wm * (kT / 2) + t * 32 + i32, st, h, a[t]);
+        OB::fragment(sb, wn * (kT / 2) + t * 32 + i32, st, h, b[t]);
       }
-    }
+      constexpr int kPa[6] = {2, 1, 0, 1, 0, 0}, kPb[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
-    for (int t = 0; t < kMJ; ++t) {
-      if constexpr (kTB) {
-        const float* p = sb + (wn * (kT / 2) + t * 32 + i32) * OB::kPitch + 16 * h;
+      for (int p = 0; p < 6; ++p)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bv[t][q] = *reinterpret_cast<const f32x4*>(p + 4 * q);
-      }
-    }
+        for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[kMI], b[kMJ];
-#pragma unroll
-      for (int t = 0; t < kMI; ++t) {
-        if constexpr (!kTA)
-          a[t] = av[t][kk >> 2][kk & 3];
-        else
-          a[t] = sa[(16 * h + kk) * OA::kPitch + wm * (kT / kWM) + t * 32 + i32];
-      }
-#pragma unroll
-      for (int t = 0; t < kMJ; ++t) {
-        if constexpr (kTB)
-          b[t] = bv[t][kk >> 2][kk & 3];
-        else
-          b[t] = sb[(16 * h + kk) * OB::kPitch + wn * (kT / 2) + t * 32 + i32];
-      }
-#pragma unroll
-      for (int i = 0; i < kMI; ++i)
-#pragma unroll
-        for (int j = 0; j < kMJ; ++j)
-          acc[i][j][kk % kAcc] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j][kk % kAcc], 0, 0, 0);
+          for (int j = 0; j < kMT; ++j)
+            acc[i][j][p % kAcc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[i][kPa[p]]), __builtin_bit_cast(bf16x8, b[j][kPb[p]]),
+                acc[i][j][p % kAcc], 0, 0, 0);
     }
   };
 
-  f32x4 ra0[OA::kV], rb0[OB::kV], ra1[OA::kV], rb1[OB::kV];
-  auto load = [&](f32x4 (&ra)[OA::kV], f32x4 (&rb)[OB::kV], int kt) {
+  f32x4 ra0[2], rb0[2], ra1[2], rb1[2];
+  auto load = [&](f32x4 (&ra)[2], f32x4 (&rb)[2], int kt) {
     OA::load(ra, g.A, g.lda, m0, kt * kSK, tid);
     OB::load(rb, g.B, g.ldb, n0, kt * kSK, tid);
   };
-  auto store = [&](const f32x4 (&ra)[OA::kV], const f32x4 (&rb)[OB::kV], int buf) {
+  auto store = [&](const f32x4 (&ra)[2], const f32x4 (&rb)[2], int buf) {
     OA::store(ra, As[buf], tid);
     OB::store(rb, Bs[buf], tid);
   };
@@ -330,13 +370,13 @@ __global__ __launch_bounds__(128 * kWM) void gemm_tile_kernel(GemmArgs g) {
   // read and written by the same lane)
   const float alpha = g.alpha * (g.alpha_scale ? *g.alpha_scale : 1.f);
 #pragma unroll
-  for (int ti = 0; ti < kMI; ++ti) {
+  for (int ti = 0; ti < kMT; ++ti) {
 #pragma unroll
-    for (int tj = 0; tj < kMJ; ++tj) {
+    for (int tj = 0; tj < kMT; ++tj) {
       const int col = n0 + wn * (kT / 2) + tj * 32 + i32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * (kT / kWM) + ti * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int row = m0 + wm * (kT / 2) + ti * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         float sum = acc[ti][tj][0][v];
         if constexpr (kAcc == 2) sum += acc[ti][tj][1][v];
         float r = alpha * sum;
@@ -419,17 +459,14 @@ template <int kT>
 void launch_gemm_tile(const GemmArgs& g, bool trans_a, bool trans_b, bool whole, int32_t batch, hipStream_t stream) {
   const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT, batch), block(256);
   if (whole) {
-    // 128 x 128 tiles: 4 x 2 waves (two per SIMD at one workgroup per CU)
-    constexpr int kWM = kT == 128 ? 4 : 2;
-    const dim3 wblock(128 * kWM);
     if (!trans_a && !trans_b)
-      gemm_tile_kernel<false, false, kT, kWM><<<grid, wblock, 0, stream>>>(g);
+      gemm_tile_kernel<false, false, kT><<<grid, block, 0, stream>>>(g);
     else if (!trans_a && trans_b)
-      gemm_tile_kernel<false, true, kT, kWM><<<grid, wblock, 0, stream>>>(g);
+      gemm_tile_kernel<false, true, kT><<<grid, block, 0, stream>>>(g);
     else if (trans_a && !trans_b)
-      gemm_tile_kernel<true, false, kT, kWM><<<grid, wblock, 0, stream>>>(g);
+      gemm_tile_kernel<true, false, kT><<<grid, block, 0, stream>>>(g);
     else
-      gemm_tile_kernel<true, true, kT, kWM><<<grid, wblock, 0, stream>>>(g);
+      gemm_tile_kernel<true, true, kT><<<grid, block, 0, stream>>>(g);
     return;
   }
   if (!trans_a && !trans_b)
@@ -456,7 +493,7 @@ hipError_t launch_gemm(const GemmArgs& g, bool trans_a, bool trans_b, int32_t ba
   if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
   const int64_t big = int64_t((g.M + 127) / 128) * ((g.N + 127) / 128) * batch;
   const int t = big >= 256 ? 128 : 64;
-  const bool whole = g.M % t == 0 && g.N % t == 0 && g.K > 0 && g.K % (2 * kSK) == 0 && aligned16(g.A, g.lda) &&
+  const bool whole = g.M % t == 0 && g.N % t == 0 && g.K > 0 && g.K % kWholeK == 0 && aligned16(g.A, g.lda) &&
                      aligned16(g.B, g.ldb) && (batch == 1 || (g.sA % 4 == 0 && g.sB % 4 == 0));
   if (t == 128)
     launch_gemm_tile<128>(g, trans_a, trans_b, whole, batch, stream);

@@ -6,8 +6,9 @@ Muon phi on both sides.  phi couples every element of a tensor, so a tensor
 any of whose chunks took a legitimately different top-k set (near ties, see
 parity.py) is not compared; the tests assert that this stays rare.
 
-Tolerance: the kernel runs the coupled Newton-Schulz iteration in float32 on
-the matrix cores.  The scalar form of the iteration, z <- z (3 - l z^2) / 2
+Tolerance: the kernel runs the coupled Newton-Schulz iteration at float32
+accuracy on the matrix cores (float32 operands split exactly into three
+bfloat16 parts, six part products accumulated in float32).  The scalar form of the iteration, z <- z (3 - l z^2) / 2
 for an eigenvalue l of the normalised Gram, grows z by 1.5 per step until
 l z^2 nears 1 and then converges quadratically: about log_1.5(l^-1/2) + 5
 steps.  With eps at 1e-3 of the largest mean Gram eigenvalue in the list,
