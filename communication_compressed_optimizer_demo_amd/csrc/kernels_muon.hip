@@ -300,7 +300,18 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, i32 = lane & 31;
   const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
+  // Workgroups reach the eight XCDs round-robin by linear id.  When the tile
+  // grid splits into a 4 x 2 arrangement of equal blocks, XCD k gets block
+  // (k / 2, k % 2), so each XCD's L2 serves a quarter of A's row blocks and
+  // half of B's column blocks instead of all of A.
+  int tx = blockIdx.x, ty = blockIdx.y;
+  if (gridDim.x % 2 == 0 && gridDim.y % 4 == 0) {
+    const int l = blockIdx.x + gridDim.x * blockIdx.y, k = l & 7, m = l >> 3;
+    const int bw = gridDim.x / 2, bh = gridDim.y / 4;
+    tx = (k & 1) * bw + m % bw;
+    ty = (k >> 1) * bh + m / bw;
+  }
+  const int m0 = ty * kT, n0 = tx * kT;
   const int nk = g.K / kSK;
 
   floatx16 acc[kMT][kMT][kAcc];
