@@ -200,11 +200,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// (x, y) -> both rounded to bfloat16 in one packed conversion (returned as
-// the packed pair, x in the low half), and what the rounding left, in place.
-// The remainder is exact in float32.
+// (x, y) rounded to bfloat16 in one packed conversion, x in the low half.
+__device__ __forceinline__ uint32_t pack_pair(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
+
+// The packed rounding of (x, y), leaving what it left out in x and y (exact
+// in float32).
 __device__ __forceinline__ uint32_t peel_pair(float& x, float& y) {
-  const uint32_t bits = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+  const uint32_t bits = pack_pair(x, y);
   x -= __uint_as_float(bits << 16);
   y -= __uint_as_float(bits & 0xffff0000u);
   return bits;
@@ -214,7 +218,7 @@ __device__ __forceinline__ uint32_t peel_pair(float& x, float& y) {
 __device__ __forceinline__ void split_pair(float x, float y, uint32_t (&w)[3]) {
   w[0] = peel_pair(x, y);
   w[1] = peel_pair(x, y);
-  w[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+  w[2] = pack_pair(x, y);
 }
 
 // One operand's stage: kT rows (along M for A, N for B) by kSK values of k,

@@ -376,11 +376,14 @@ struct DenseBasis {
   // one contiguous half of the 64-deep k range: k = kk + 32 (l / 32),
   // kk = 0..31, so a lane walks one half of a row or column.
 
-  // (x, y) -> both rounded to bfloat16 in one packed conversion (returned as
-  // the packed pair), and what the rounding left, in place.  The remainder
-  // is exact in float32.
+  // (x, y) rounded to bfloat16 in one packed conversion, x in the low half.
+  static __device__ __forceinline__ uint32_t pack_pair(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+  }
+  // The packed rounding of (x, y), leaving what it left out in x and y (exact
+  // in float32).
   static __device__ __forceinline__ uint32_t peel_pair(float& x, float& y) {
-    const uint32_t bits = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+    const uint32_t bits = pack_pair(x, y);
     x -= __uint_as_float(bits << 16);
     y -= __uint_as_float(bits & 0xffff0000u);
     return bits;
@@ -393,9 +396,9 @@ struct DenseBasis {
   // each the rounding of what the previous parts leave) and the six part
   // products down to the third order (a1b1, a1b2, a2b1, a1b3, a2b2, a3b1;
   // each of the three dropped ones is at most 2^-24 |ab|) are accumulated in
-  // float32, smallest first.  v_mfma_f32_32x32x16_bf16: lane l gives A[l % 32][8 (l /
-  // 32) + j] and B[8 (l / 32) + j][l % 32], j = 0..7; step s of four takes
-  // kk = 8 s + j, so both operands pair the same k.
+  // float32, smallest first.  v_mfma_f32_32x32x16_bf16: lane l gives
+  // A[l % 32][8 (l / 32) + j] and B[8 (l / 32) + j][l % 32], j = 0..7; step
+  // s of four takes kk = 8 s + j, so both operands pair the same k.
   template <class FA, class FB>
   static __device__ __forceinline__ void product(f32x16 (&d)[2][2], FA a_of, FB b_of) {
 #pragma unroll
@@ -414,11 +417,11 @@ struct DenseBasis {
           float x0 = a_of(t, 8 * s + 2 * j), x1 = a_of(t, 8 * s + 2 * j + 1);
           a[t][0][j] = peel_pair(x0, x1);
           a[t][1][j] = peel_pair(x0, x1);
-          a[t][2][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+          a[t][2][j] = pack_pair(x0, x1);
           float y0 = b_of(t, 8 * s + 2 * j), y1 = b_of(t, 8 * s + 2 * j + 1);
           b[t][0][j] = peel_pair(y0, y1);
           b[t][1][j] = peel_pair(y0, y1);
-          b[t][2][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y0, y1}, bf16x2));
+          b[t][2][j] = pack_pair(y0, y1);
         }
       constexpr int kTa[6] = {2, 1, 0, 1, 0, 0}, kTb[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
