@@ -271,9 +271,9 @@ demo_status demo_decode_apply_wire(demo_ctx* ctx, int32_t n, const demo_shape* s
  * M (M^T M + eps I)^(-1/2), Newton-Schulz normalization).  phi acts on each
  * whole tensor, so the decode first writes M* of every tensor into a
  * workspace; a matrix then goes through its smaller Gram matrix and the
- * coupled Newton-Schulz iteration for the inverse square root (fp32 matrix
- * cores), a vector (one column) through m / sqrt(m.m + eps).  Built for chunk
- * edge 64. */
+ * coupled Newton-Schulz iteration for the inverse square root (products on
+ * the matrix cores at float32 accuracy), a vector (one column) through
+ * m / sqrt(m.m + eps).  Built for chunk edge 64. */
 
 /* Host-only: bytes of device workspace demo_decode_apply_muon needs for a list:
  * M* of every tensor, then one slot of Newton-Schulz matrices (six n x n,
