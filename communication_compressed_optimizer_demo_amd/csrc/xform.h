@@ -436,6 +436,26 @@ struct DenseBasis {
     }
   }
 
+  // Power-of-two factor applied to a block before its products and undone
+  // after them: 1 unless the block's largest magnitude is below 2^-90, where
+  // the bfloat16 parts of its values and their part products would reach
+  // the subnormal range and be lost on the matrix cores (a block at 1e-36
+  // otherwise comes out with errors near 1e-5 of its norm).  Scaling by a
+  // power of two is exact and the products are linear, so the result is
+  // the one without scaling wherever nothing underflows.  Returns the
+  // exponent of the factor (0: none).
+  static __device__ __forceinline__ int block_scale(const float (&x)[64]) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(x[i]));
+    if (__builtin_amdgcn_ballot_w64(m >= 0x1p-90f) != 0) return 0;  // the common case
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (m == 0.f) return 0;
+    const int e = int(__builtin_amdgcn_readfirstlane(__float_as_uint(m) >> 23));  // biased exponent
+    return 127 - e;  // m 2^(127 - e) is in [1, 2)
+  }
+
   // The 64x64 result into the tile, row-major.
   template <int kLd>
   static __device__ __forceinline__ void store_result(const f32x16 (&d)[2][2], float* tile, int lane) {
@@ -461,6 +481,11 @@ struct DenseBasis {
   template <int kLd>
   __device__ __forceinline__ void forward2d(float (&x)[64], float* tile, int lane) const {
     const int h = lane >> 5, c = lane & 31;
+    const int sc = block_scale(x);
+    if (sc != 0) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = ldexpf(x[i], sc);
+    }
 #pragma unroll
     for (int i = 0; i < 64; ++i) tile[i * kLd + lane] = x[i];
     // this lane's rows of P0 (A of the first product) and P1 (B^T of the second): 32 contiguous k each
@@ -490,6 +515,10 @@ struct DenseBasis {
 #pragma unroll
     for (int v = 0; v < 64; ++v) x[v] = tile[lane * kLd + v];
     lds_sync();
+    if (sc != 0) {
+#pragma unroll
+      for (int v = 0; v < 64; ++v) x[v] = ldexpf(x[v], -sc);
+    }
   }
 
   // Inverse: x holds row `lane` of Q (x[v] = Q[lane][v]); on return x holds
@@ -497,6 +526,11 @@ struct DenseBasis {
   template <int kLd>
   __device__ __forceinline__ void inverse2d(float (&x)[64], float* tile, int lane) const {
     const int h = lane >> 5, c = lane & 31;
+    const int sc = block_scale(x);
+    if (sc != 0) {
+#pragma unroll
+      for (int v = 0; v < 64; ++v) x[v] = ldexpf(x[v], sc);
+    }
 #pragma unroll
     for (int v = 0; v < 64; ++v) tile[lane * kLd + v] = x[v];
     lds_sync();
@@ -516,6 +550,10 @@ struct DenseBasis {
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] = tile[i * kLd + lane];
     lds_sync();
+    if (sc != 0) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = ldexpf(x[i], -sc);
+    }
   }
 };
 
